@@ -1,0 +1,63 @@
+"""Work and traffic counters for jagged attention problems (used for reporting, not compute).
+
+"Useful" work counts only the matrix-product flops of unmasked (query, key) pairs, the way the
+pages measure kernels in isolation on one GPU (page "GEM Training: How Meta Doubled the Efficiency
+of Its LLM-Scale Ads Foundation Model", local-MFU part): forward = 2 products = 4*D flops per pair
+and head; backward = 5 products = 10*D flops per pair and head. Padding, recomputation and
+transcendentals are not counted.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def pairs_per_sample(lq, lk, causal):
+    """Unmasked (i, j) pairs per sample. Causal keeps j <= i on local positions."""
+    lq = np.asarray(lq, dtype=np.int64)
+    lk = np.asarray(lk, dtype=np.int64)
+    if not causal:
+        return lq * lk
+    # sum_{i < Lq} min(i + 1, Lk)
+    m = np.minimum(lq, lk)
+    full = m * (m + 1) // 2                 # rows i < m see i + 1 keys
+    rest = np.maximum(lq - lk, 0) * lk      # rows i >= Lk see all Lk keys
+    return full + rest
+
+
+def useful_flops(p, direction="fwd"):
+    pairs = int(pairs_per_sample(p.lq, p.lk, p.causal).sum())
+    per = {"fwd": 4, "bwd": 10, "fwdbwd": 14}[direction]
+    return float(per) * p.D * p.H * pairs
+
+
+def elem_bytes(p):
+    return {"f32": 4, "bf16": 2, "mxfp8": 1}[p.dtype]
+
+
+def fwd_bytes(p):
+    """Each input read once and each output written once (the algorithmic minimum)."""
+    e_in = elem_bytes(p)
+    e_out = 4 if p.dtype == "f32" else 2
+    H, D = p.H, p.D
+    b = (p.total_q * H * D * e_in + 2 * p.total_kv * H * D * e_in + p.total_q * H * D * e_out)
+    if p.dtype == "mxfp8":
+        b += (p.total_q + 2 * p.total_kv) * H * (D // 32)
+    if p.act == "softmax":
+        b += p.total_q * H * 4  # lse
+    if p.bias is not None:
+        b += p.bias.size * 4
+    return float(b)
+
+
+def bwd_bytes(p):
+    """Reads Q, K, V, dO (+ O, lse, and D written then read, for softmax); writes dQ, dK, dV."""
+    e = elem_bytes(p)
+    H, D = p.H, p.D
+    tq, tk = p.total_q, p.total_kv
+    b = (2 * tq * H * D * e + 2 * tk * H * D * e   # Q, dO, K, V
+         + tq * H * D * e + 2 * tk * H * D * e)    # dQ, dK, dV
+    if p.act == "softmax":
+        b += tq * H * D * e + tq * H * 4 + 2 * tq * H * 4  # O, lse, D write + read
+    if p.bias is not None:
+        b += 2 * p.bias.size * 4
+    return float(b)

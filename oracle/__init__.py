@@ -1,0 +1,207 @@
+"""Reference oracle for jagged attention: plain fp64 CPU loops, written from the method's definition.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may import this package. The GPU library never does, and the two share no code.
+
+The C source (``gdpa_oracle.c``) holds the definition and its citations: JFA is FlashAttention on
+jagged tensors (page "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation
+Model", JFA paragraph), so its result is the plain softmax attention over each sample's valid keys;
+GDPA (same page, GDPA paragraph) replaces softmax by an element-wise GELU or SiLU with no
+normalisation. This module only marshals numpy arrays into that library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdpa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+ACT_SOFTMAX, ACT_GELU_TANH, ACT_SILU = 0, 1, 2
+ACTS = {"softmax": ACT_SOFTMAX, "gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (plain C, -O2, OpenMP). Always recompiles."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    up = ctypes.POINTER(ctypes.c_uint8)
+    c_int, c_long, c_double = ctypes.c_int, ctypes.c_long, ctypes.c_double
+    lib.gdpa_oracle_fwd.argtypes = [c_int, c_int, c_int, ip, ip, dp, dp, dp, dp, c_int, c_int,
+                                    c_int, c_double, dp, dp, c_int]
+    lib.gdpa_oracle_fwd.restype = c_int
+    lib.gdpa_oracle_bwd.argtypes = [c_int, c_int, c_int, ip, ip, dp, dp, dp, dp, dp, c_int, c_int,
+                                    c_int, c_double, dp, dp, dp, dp, dp, c_int]
+    lib.gdpa_oracle_bwd.restype = c_int
+    lib.gdpa_oracle_act.argtypes = [c_int, dp, c_long, dp, dp]
+    lib.gdpa_oracle_act.restype = None
+    lib.gdpa_oracle_decode_e4m3.argtypes = [up, c_long, dp]
+    lib.gdpa_oracle_decode_e4m3.restype = None
+    lib.gdpa_oracle_decode_e8m0.argtypes = [up, c_long, dp]
+    lib.gdpa_oracle_decode_e8m0.restype = None
+    lib.gdpa_oracle_decode_mx.argtypes = [up, up, c_long, c_int, dp]
+    lib.gdpa_oracle_decode_mx.restype = c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _act_code(act):
+    return ACTS[act] if isinstance(act, str) else int(act)
+
+
+def fwd(q_off, kv_off, Q, K, V, *, act="softmax", causal=False, scale=None, bias=None,
+        nthreads=None):
+    """Forward pass. Q: [total_q, H, D], K/V: [total_kv, H, D] (any float dtype, upcast exactly).
+
+    Returns (O [total_q, H, D] fp64, lse [total_q, H] fp64; lse is 0 for GDPA).
+    """
+    lib = _load()
+    q_off, kv_off = _i32(q_off), _i32(kv_off)
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    B = len(q_off) - 1
+    assert len(kv_off) == B + 1
+    total_q, H, D = Q.shape
+    assert K.shape == V.shape and K.shape[1:] == (H, D)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    nb = 0
+    bias_arr = np.zeros(1)
+    if bias is not None:
+        bias_arr = _f64(bias)
+        assert bias_arr.shape[0] == H
+        nb = bias_arr.shape[1]
+    O = np.empty((total_q, H, D), dtype=np.float64)
+    lse = np.empty((total_q, H), dtype=np.float64)
+    rc = lib.gdpa_oracle_fwd(B, H, D, _ptr(q_off, ctypes.c_int32), _ptr(kv_off, ctypes.c_int32),
+                             _ptr(Q, ctypes.c_double), _ptr(K, ctypes.c_double),
+                             _ptr(V, ctypes.c_double), _ptr(bias_arr, ctypes.c_double), nb,
+                             _act_code(act), int(bool(causal)), float(scale),
+                             _ptr(O, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle fwd rejected its arguments (rc={rc})")
+    return O, lse
+
+
+def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, bias=None,
+        nthreads=None):
+    """Backward pass of the loss sum(dO * O).
+
+    Returns dict with dQ, dK, dV (fp64, same layouts as Q/K/V), dbias ([H, NB] or None) and
+    D ([total_q, H], the softmax row term sum_j p_ij dp_ij; 0 for GDPA).
+    """
+    lib = _load()
+    q_off, kv_off = _i32(q_off), _i32(kv_off)
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B = len(q_off) - 1
+    total_q, H, D = Q.shape
+    total_kv = K.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    nb = 0
+    bias_arr = np.zeros(1)
+    dbias = np.zeros(1)
+    if bias is not None:
+        bias_arr = _f64(bias)
+        nb = bias_arr.shape[1]
+        dbias = np.empty((H, nb), dtype=np.float64)
+    dQ = np.empty((total_q, H, D))
+    dK = np.empty((total_kv, H, D))
+    dV = np.empty((total_kv, H, D))
+    Dv = np.empty((total_q, H))
+    rc = lib.gdpa_oracle_bwd(B, H, D, _ptr(q_off, ctypes.c_int32), _ptr(kv_off, ctypes.c_int32),
+                             _ptr(Q, ctypes.c_double), _ptr(K, ctypes.c_double),
+                             _ptr(V, ctypes.c_double), _ptr(dO, ctypes.c_double),
+                             _ptr(bias_arr, ctypes.c_double), nb, _act_code(act),
+                             int(bool(causal)), float(scale), _ptr(dQ, ctypes.c_double),
+                             _ptr(dK, ctypes.c_double), _ptr(dV, ctypes.c_double),
+                             _ptr(dbias, ctypes.c_double), _ptr(Dv, ctypes.c_double),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle bwd rejected its arguments (rc={rc})")
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dbias": dbias if nb > 0 else None, "D": Dv}
+
+
+def act(name, x, derivative=False):
+    """The oracle's own activation (or its derivative) on an array."""
+    lib = _load()
+    x = _f64(x)
+    out = np.empty_like(x)
+    if derivative:
+        lib.gdpa_oracle_act(_act_code(name), _ptr(x, ctypes.c_double), x.size, None,
+                            _ptr(out, ctypes.c_double))
+    else:
+        lib.gdpa_oracle_act(_act_code(name), _ptr(x, ctypes.c_double), x.size,
+                            _ptr(out, ctypes.c_double), None)
+    return out
+
+
+def decode_e4m3(codes):
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib.gdpa_oracle_decode_e4m3(_ptr(codes, ctypes.c_uint8), codes.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def decode_e8m0(codes):
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib.gdpa_oracle_decode_e8m0(_ptr(codes, ctypes.c_uint8), codes.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def decode_mx(data, scales):
+    """data: [..., D] e4m3 codes, scales: [..., D/32] e8m0 codes -> fp64 values [..., D]."""
+    lib = _load()
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    D = data.shape[-1]
+    rows = data.size // D
+    assert scales.shape[-1] * 32 == D and scales.size // scales.shape[-1] == rows
+    out = np.empty(data.shape, dtype=np.float64)
+    rc = lib.gdpa_oracle_decode_mx(_ptr(data, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8), rows,
+                                   D, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle decode_mx: D must be a multiple of 32")
+    return out
