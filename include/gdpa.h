@@ -1,0 +1,120 @@
+/*
+ * gdpa.h - C ABI of libgdpa.so: attention over jagged (variable-length) sequences on MI355X.
+ *
+ * Two operations, forward and backward, for two families that share one structure, the product
+ * Q.K^T (plus an optional bias), an element-wise map, and the product with V:
+ *   - JFA: softmax attention computed directly on jagged tensors without padding (page "GEM
+ *     Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA
+ *     paragraph: variable-length jagged tensors, custom attention biases, different query and
+ *     key/value lengths, backward passes).
+ *   - GDPA: the same two products with GELU (tanh form) or SiLU in place of softmax, and no
+ *     normalisation (same page, GDPA paragraph: self-, PMA- and cross-attention as two matrix
+ *     multiplications with an element-wise activation in between).
+ *
+ * Math, per sample b, head h, local query i in [0, Lq_b) and key j in [0, Lk_b):
+ *   valid(i,j) = !causal || j <= i
+ *   s_ij = scale * <q_i, k_j> + bias[h, clamp(i - j, 0, NB - 1)]   (no bias term if NB == 0)
+ *   softmax: o_i = sum_j softmax_j(s_i.) v_j over valid j; lse_i = ln sum_j exp(s_ij)
+ *            (a row with no valid key: o_i = 0, lse_i = -inf)
+ *   GDPA:    o_i = sum_{valid j} act(s_ij) v_j
+ *   gelu_tanh(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), silu(x) = x / (1 + e^-x)
+ * The backward returns the gradients of sum(dO * O) with respect to Q, K, V and the bias table.
+ *
+ * Layout. A jagged tensor is a row-major array [total_rows, H, D] (D contiguous, row stride H*D
+ * elements) plus int32 offsets[B + 1] (non-decreasing, offsets[0] = 0, offsets[B] = total_rows);
+ * sample b owns rows [offsets[b], offsets[b+1]). Q, O, dO, dQ use q_offsets; K, V, dK, dV use
+ * kv_offsets. lse is [total_q, H] fp32 (natural log). bias and dbias are [H, NB] fp32.
+ * Element types: GDPA_F32 -> all tensors fp32; GDPA_BF16 -> Q/K/V/O/dO/dQ/dK/dV bf16;
+ * GDPA_MXFP8_E4M3 (forward only) -> Q/K/V are e4m3 bytes with one e8m0 scale byte per 32
+ * consecutive elements along D ([rows, H, D/32] arrays q_scale/k_scale/v_scale), O is bf16.
+ * This MX encoding follows the OCP Microscaling Formats v1.0 (same page, low-precision part:
+ * MXFP8 block-scaled matrix products).
+ *
+ * Ownership and synchronisation. Every pointer except `p` is device memory owned by the caller and
+ * must stay valid until the work enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ * has finished. Calls are asynchronous: they validate host-side arguments, enqueue kernels and
+ * return. The library allocates no device memory: scratch space comes from the caller's
+ * `workspace`, whose size gdpa_workspace_size() returns from host-known sizes alone. Outputs are
+ * overwritten, never accumulated. Base pointers must be 16-byte aligned.
+ *
+ * Errors. Host-checkable argument errors return a status and enqueue nothing. Data-dependent
+ * errors (offsets not starting at 0, decreasing, or ending at a value other than total_q/total_kv)
+ * are detected on the device: a device error word in the workspace is set, every kernel of the
+ * call then skips its work and the outputs are left unspecified; gdpa_read_device_error() reads
+ * that word. Nothing is printed and no C++ exception crosses this interface. Calls that share a
+ * workspace must be ordered on one stream.
+ */
+#ifndef GDPA_H_
+#define GDPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDPA_ACT_SOFTMAX = 0, GDPA_ACT_GELU_TANH = 1, GDPA_ACT_SILU = 2 } gdpa_act;
+
+typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1, GDPA_MXFP8_E4M3 = 2 } gdpa_dtype;
+
+typedef enum {
+  GDPA_OK = 0,
+  GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
+  GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX backward, ... */
+  GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
+  GDPA_EHIP = 4        /* the HIP runtime refused a launch */
+} gdpa_status;
+
+/* Problem description; plain integers so the layout is stable across compilers. */
+typedef struct {
+  int32_t B;            /* samples (>= 0) */
+  int32_t H;            /* heads (>= 1) */
+  int32_t D;            /* head dimension: 32, 64 or 128 */
+  int32_t dtype;        /* gdpa_dtype */
+  int64_t total_q;      /* rows of Q/O/dO (= q_offsets[B]) */
+  int64_t total_kv;     /* rows of K/V (= kv_offsets[B]) */
+  int32_t max_q;        /* an upper bound on any Lq_b, or 0 if unknown; only tunes scheduling */
+  int32_t max_kv;       /* an upper bound on any Lk_b, or 0 if unknown; only tunes scheduling */
+  int32_t act;          /* gdpa_act */
+  int32_t causal;       /* 0 or 1: keep j <= i on local positions (top-left aligned) */
+  float scale;          /* s = scale * q.k (+ bias) */
+  int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
+} gdpa_problem;
+
+/* ABI version of this header (checked by bindings). */
+#define GDPA_ABI_VERSION 1
+int32_t gdpa_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* gdpa_status_string(int32_t status);
+
+/* Bytes of device workspace that gdpa_fwd (for_bwd = 0) or gdpa_bwd (for_bwd = 1) needs for
+ * problem *p. Depends only on the fields of *p. */
+int32_t gdpa_workspace_size(const gdpa_problem* p, int32_t for_bwd, size_t* bytes);
+
+/* Forward. Writes O ([total_q, H, D]) and, when lse != NULL, lse ([total_q, H]; softmax only, it
+ * is what gdpa_bwd needs). q_scale/k_scale/v_scale are used only for GDPA_MXFP8_E4M3 and must be
+ * NULL otherwise. bias is NULL iff p->bias_buckets == 0. */
+int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias, void* O,
+                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of sum(dO * O). Writes dQ, dK, dV (same layouts and element type as Q, K, V) and,
+ * when p->bias_buckets > 0, dbias ([H, NB] fp32). Softmax needs O and the forward's lse; GDPA
+ * ignores them (they may be NULL). Results are bitwise reproducible run to run. */
+int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                 const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                 float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Waits for `stream`, then reads the device error word of the last call that used `workspace`
+ * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */
+int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDPA_H_ */

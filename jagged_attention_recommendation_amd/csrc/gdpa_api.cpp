@@ -1,0 +1,248 @@
+// C-ABI entry points of libgdpa.so (declared in include/gdpa.h): argument validation, workspace
+// carving and kernel launches on the caller's stream. No device memory is allocated here and no
+// call synchronises the host, except gdpa_read_device_error().
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "gdpa.h"
+#include "gdpa_common.h"
+#include "gdpa_internal.h"
+
+using namespace gdpa;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int32_t check_problem(const gdpa_problem* p) {
+  if (p == nullptr) return GDPA_EINVAL;
+  if (p->B < 0 || p->H < 1 || p->total_q < 0 || p->total_kv < 0) return GDPA_EINVAL;
+  if (p->total_q >= (int64_t)1 << 31 || p->total_kv >= (int64_t)1 << 31) return GDPA_EINVAL;
+  if (p->dtype < GDPA_F32 || p->dtype > GDPA_MXFP8_E4M3) return GDPA_EINVAL;
+  if (p->act < GDPA_ACT_SOFTMAX || p->act > GDPA_ACT_SILU) return GDPA_EINVAL;
+  if (p->causal != 0 && p->causal != 1) return GDPA_EINVAL;
+  if (p->bias_buckets < 0 || p->max_q < 0 || p->max_kv < 0) return GDPA_EINVAL;
+  if (!isfinite(p->scale)) return GDPA_EINVAL;
+  if (p->D != 32 && p->D != 64 && p->D != 128) return GDPA_ENOTSUP;
+  if (p->dtype == GDPA_MXFP8_E4M3 && p->D != 128) return GDPA_ENOTSUP;
+  // element counts must fit the kernels' 64-bit addressing and the scheduler's int32 counters
+  if ((int64_t)p->H * p->D > (1 << 20)) return GDPA_ENOTSUP;
+  return GDPA_OK;
+}
+
+Prob to_prob(const gdpa_problem* p) {
+  Prob r;
+  r.B = p->B; r.H = p->H; r.D = p->D; r.dtype = p->dtype; r.act = p->act; r.causal = p->causal;
+  r.nb = p->bias_buckets; r.total_q = p->total_q; r.total_kv = p->total_kv;
+  r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale;
+  return r;
+}
+
+int fwd_tile_rows(int dtype) { return dtype == GDPA_F32 ? F32_BM : FWD_BM_BF16; }
+int fwd_loop_rows(int dtype) { return dtype == GDPA_F32 ? F32_BN : FWD_BN_BF16; }
+int bwd_tile_q(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_BM; }
+int bwd_tile_k(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_BN; }
+
+struct FwdLayout {
+  size_t header, items, total;
+  int64_t max_items;
+};
+
+FwdLayout fwd_layout(const gdpa_problem* p) {
+  FwdLayout L;
+  L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype));
+  L.header = 0;
+  L.items = ALIGN;
+  L.total = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  return L;
+}
+
+struct BwdLayout {
+  size_t header, items_q, items_k, dvec, tile_base, part, total;
+  int64_t max_q_items, max_k_items, max_qtiles;
+};
+
+BwdLayout bwd_layout(const gdpa_problem* p) {
+  BwdLayout L;
+  const int tq = bwd_tile_q(p->dtype), tk = bwd_tile_k(p->dtype);
+  L.max_q_items = items_bound(p->total_q, p->B, p->H, tq);
+  L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk);
+  L.max_qtiles = (p->total_q + tq - 1) / tq + p->B;
+  L.header = 0;
+  L.items_q = ALIGN;
+  L.items_k = L.items_q + align_up((size_t)L.max_q_items * sizeof(Item));
+  L.dvec = L.items_k + align_up((size_t)L.max_k_items * sizeof(Item));
+  L.tile_base = L.dvec + align_up((size_t)p->total_q * p->H * sizeof(float));
+  L.part = L.tile_base + align_up((size_t)(p->B + 1) * sizeof(int32_t));
+  L.total = L.part;
+  if (p->bias_buckets > 0)
+    L.total += align_up((size_t)L.max_qtiles * p->H * p->bias_buckets * sizeof(float));
+  return L;
+}
+
+int32_t map_hip(hipError_t e) {
+  if (e == hipSuccess) return GDPA_OK;
+  if (e == hipErrorNotSupported) return GDPA_ENOTSUP;
+  return GDPA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdpa_abi_version(void) { return GDPA_ABI_VERSION; }
+
+const char* gdpa_status_string(int32_t s) {
+  switch (s) {
+    case GDPA_OK: return "ok";
+    case GDPA_EINVAL: return "invalid argument";
+    case GDPA_ENOTSUP: return "unsupported configuration";
+    case GDPA_EWORKSPACE: return "workspace too small";
+    case GDPA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t gdpa_workspace_size(const gdpa_problem* p, int32_t for_bwd, size_t* bytes) {
+  if (bytes == nullptr) return GDPA_EINVAL;
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (for_bwd && p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
+  *bytes = for_bwd ? bwd_layout(p).total : fwd_layout(p).total;
+  return GDPA_OK;
+}
+
+int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias, void* O,
+                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
+  if (p->total_q > 0 && (!Q || !O)) return GDPA_EINVAL;
+  if (p->total_kv > 0 && (!K || !V)) return GDPA_EINVAL;
+  if ((p->bias_buckets > 0) != (bias != nullptr)) return GDPA_EINVAL;
+  const bool mx = p->dtype == GDPA_MXFP8_E4M3;
+  if (mx && ((p->total_q > 0 && !q_scale) || (p->total_kv > 0 && (!k_scale || !v_scale))))
+    return GDPA_EINVAL;
+  if (!mx && (q_scale || k_scale || v_scale)) return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace))
+    return GDPA_EINVAL;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)bias & 3u) || ((uintptr_t)q_offsets & 3u) ||
+      ((uintptr_t)kv_offsets & 3u))
+    return GDPA_EINVAL;
+  const FwdLayout L = fwd_layout(p);
+  if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
+  if (L.max_items > INT32_MAX) return GDPA_ENOTSUP;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Prob pr = to_prob(p);
+
+  SchedArgs sa;
+  sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
+  sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
+  sa.causal = p->causal; sa.tile_item = fwd_tile_rows(p->dtype);
+  sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
+  sa.tile_base = nullptr; sa.ws_header = ws + L.header; sa.items = ws + L.items;
+  hipError_t e = launch_sched(sa, s);
+  if (e != hipSuccess) return map_hip(e);
+
+  FwdArgs fa;
+  fa.Q = Q; fa.K = K; fa.V = V; fa.qs = q_scale; fa.ks = k_scale; fa.vs = v_scale;
+  fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
+  fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
+  fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
+  fa.scale = p->scale;
+  const int grid = (int)L.max_items;
+  if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
+  else if (p->dtype == GDPA_BF16) e = launch_fwd_bf16(pr, fa, grid, s);
+  else e = launch_fwd_mx(pr, fa, grid, s);
+  return map_hip(e);
+}
+
+int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                 const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                 float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
+  if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
+  if (p->total_q > 0 && (!Q || !dO || !dQ)) return GDPA_EINVAL;
+  if (p->total_kv > 0 && (!K || !V || !dK || !dV)) return GDPA_EINVAL;
+  const bool softmax = p->act == GDPA_ACT_SOFTMAX;
+  if (softmax && p->total_q > 0 && (!O || !lse)) return GDPA_EINVAL;
+  if ((p->bias_buckets > 0) != (bias != nullptr)) return GDPA_EINVAL;
+  if ((p->bias_buckets > 0) != (dbias != nullptr)) return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+    return GDPA_EINVAL;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)bias & 3u) || ((uintptr_t)dbias & 3u) ||
+      ((uintptr_t)q_offsets & 3u) || ((uintptr_t)kv_offsets & 3u))
+    return GDPA_EINVAL;
+  const BwdLayout L = bwd_layout(p);
+  if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
+  if (L.max_q_items > INT32_MAX || L.max_k_items > INT32_MAX) return GDPA_ENOTSUP;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Prob pr = to_prob(p);
+  const int tq = bwd_tile_q(p->dtype), tk = bwd_tile_k(p->dtype);
+
+  SchedArgs sa;
+  sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
+  sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
+  sa.ws_header = ws + L.header;
+  // query-tile items (dQ, D, bias partials)
+  sa.mode = SCHED_QTILES; sa.tile_item = tq; sa.tile_loop = tk;
+  sa.max_items = (int)L.max_q_items; sa.list = 0;
+  sa.tile_base = (int32_t*)(ws + L.tile_base); sa.items = ws + L.items_q;
+  hipError_t e = launch_sched(sa, s);
+  if (e != hipSuccess) return map_hip(e);
+  // key-tile items (dK, dV)
+  sa.mode = SCHED_KTILES; sa.tile_item = tk; sa.tile_loop = tq;
+  sa.max_items = (int)L.max_k_items; sa.list = 1;
+  sa.tile_base = nullptr; sa.items = ws + L.items_k;
+  e = launch_sched(sa, s);
+  if (e != hipSuccess) return map_hip(e);
+
+  BwdArgs ba;
+  ba.Q = Q; ba.K = K; ba.V = V; ba.O = O; ba.dO = dO; ba.lse = lse;
+  ba.q_off = q_offsets; ba.kv_off = kv_offsets; ba.bias = bias;
+  ba.dQ = dQ; ba.dK = dK; ba.dV = dV; ba.dbias = dbias;
+  ba.Dvec = (float*)(ws + L.dvec); ba.hdr = ws + L.header;
+  ba.items_q = ws + L.items_q; ba.items_k = ws + L.items_k;
+  ba.dbias_part = p->bias_buckets > 0 ? (float*)(ws + L.part) : nullptr;
+  ba.tile_base = (const int32_t*)(ws + L.tile_base);
+  ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale;
+  if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
+  else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
+  if (e != hipSuccess) return map_hip(e);
+  if (p->bias_buckets > 0) {
+    DbiasArgs da;
+    da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
+    da.part = ba.dbias_part; da.dbias = dbias; da.hdr = ws + L.header;
+    da.B = p->B; da.H = p->H; da.nb = p->bias_buckets; da.tile_rows = tq;
+    e = launch_dbias_reduce(da, s);
+  }
+  return map_hip(e);
+}
+
+int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err) {
+  if (!workspace || !err) return GDPA_EINVAL;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return GDPA_EHIP;
+  WsHeader h;
+  e = hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return GDPA_EHIP;
+  *err = h.error;
+  return GDPA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Device-side building blocks shared by the gdpa kernels (gfx950 / CDNA4, wave64).
+//
+// Operand layouts of the matrix instructions used here (checked on the device with an in-bounds
+// probe of the builtins):
+//  * v_mfma_f32_32x32x16_bf16: lane l holds row (A) / column (B) l%32 and the 8 consecutive
+//    k values 8*(l/32)..8*(l/32)+7. Accumulator register r of lane l is element
+//    (row (r/4)*8 + 4*(l/32) + r%4, column l%32).
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with e4m3 operands: bytes 0..15 of a lane belong to the
+//    first 32-wide k block of the instruction and bytes 16..31 to the second; the e8m0 scale of
+//    row m for k block kb is taken from lane m + 32*kb. Which k each byte is inside its block
+//    does not matter as long as A and B agree.
+//  * ds_read_b64_tr_b16: inside every group of 16 lanes, lane j receives element j%4 of the
+//    8-byte chunks addressed by lanes j/4, j/4+4, j/4+8, j/4+12. Pointing lane 4t+q at
+//    row (r0+t), column (c0+4q) of a row-major 16-bit tile therefore hands lane j the column
+//    c0+j of rows r0..r0+3: a transposed read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define GDPA_LDS __attribute__((address_space(3)))
+
+// Work item of the jagged scheduler: sample, tile index (of queries for forward / dQ, of keys
+// for dK/dV), head, and a spare word.
+struct Item {
+  int b, tile, h, aux;
+};
+
+// Workspace header (first 256 bytes of every workspace).
+struct WsHeader {
+  int error;      // 0 ok, 1 bad q_offsets, 2 bad kv_offsets
+  int n_items;    // items written by the scheduler
+  int n_items2;   // second list (backward: key-tile items)
+  int pad[61];
+};
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float GELU_C = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float GELU_A = 0.044715f;
+
+enum { ACT_SOFTMAX = 0, ACT_GELU_TANH = 1, ACT_SILU = 2 };
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Element-wise activations of GDPA in fp32, built on exp2 and the hardware reciprocal.
+// tanh(u) = 1 - 2 / (1 + e^{2u}); at large |u| this saturates to +-1 without NaN.
+__device__ __forceinline__ float act_fwd(int act, float x) {
+  if (act == ACT_GELU_TANH) {
+    float u = GELU_C * (x + GELU_A * x * x * x);
+    float e = fast_exp2(2.0f * LOG2E * u);
+    float t = 1.0f - 2.0f * fast_rcp(1.0f + e);
+    return 0.5f * x * (1.0f + t);
+  }
+  // silu
+  float e = fast_exp2(-LOG2E * x);
+  return x * fast_rcp(1.0f + e);
+}
+
+// Value and derivative together (backward).
+__device__ __forceinline__ void act_fwd_bwd(int act, float x, float& y, float& dy) {
+  if (act == ACT_GELU_TANH) {
+    float x2 = x * x;
+    float u = GELU_C * (x + GELU_A * x2 * x);
+    float e = fast_exp2(2.0f * LOG2E * u);
+    float t = 1.0f - 2.0f * fast_rcp(1.0f + e);
+    y = 0.5f * x * (1.0f + t);
+    dy = 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * GELU_C * (1.0f + 3.0f * GELU_A * x2);
+    return;
+  }
+  float e = fast_exp2(-LOG2E * x);
+  float sg = fast_rcp(1.0f + e);
+  y = x * sg;
+  dy = sg * (1.0f + x * (1.0f - sg));
+}
+
+__device__ __forceinline__ bf16x2 pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 r;
+  bf16x2 p0 = pack_bf16(v[0], v[1]), p1 = pack_bf16(v[2], v[3]);
+  bf16x2 p2 = pack_bf16(v[4], v[5]), p3 = pack_bf16(v[6], v[7]);
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  i32x4 z = {0, 0, 0, 0};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Transposed read of 4 rows x 1 column (see the layout note above).
+__device__ __forceinline__ i16x4 lds_read_tr(const GDPA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDPA_LDS i16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 cat_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Cross-half reductions of a wave64: v_permlane32_swap hands every lane l the pair
+// {x[l % 32], x[l % 32 + 32]} (low half first), so combining the pair reduces over the two
+// half-waves, with the same operand order in both halves (bitwise-identical results).
+__device__ __forceinline__ float half_max(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace gdpa

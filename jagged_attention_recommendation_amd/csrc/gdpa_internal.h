@@ -1,0 +1,114 @@
+// Host-side interface between the C-ABI entry points and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdpa {
+
+struct Prob {
+  int B, H, D, dtype, act, causal, nb;
+  int64_t total_q, total_kv;
+  int max_q, max_kv;
+  float scale;
+};
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_MX = 2 };
+
+// Scheduler modes: items over query tiles (forward, dQ) or over key tiles (dK/dV).
+enum { SCHED_QTILES = 0, SCHED_KTILES = 1 };
+
+struct SchedArgs {
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  int B, H;
+  int64_t total_q, total_kv;
+  int mode, causal;
+  int tile_item, tile_loop;  // rows per item tile / rows per inner-loop tile
+  int max_items;
+  int list;                  // 0: header.n_items, 1: header.n_items2
+  int32_t* tile_base;        // optional [B + 1]: canonical index of each sample's first tile
+  void* ws_header;
+  void* items;
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+
+// dbias[h, r] = sum over samples b and their query tiles t (canonical order) of the tile's
+// partial row, for every r the tile can reach. tile_rows = query rows per tile.
+struct DbiasArgs {
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const int32_t* tile_base;
+  const float* part;
+  float* dbias;
+  const void* hdr;
+  int B, H, nb, tile_rows;
+};
+hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s);
+
+// Upper bound on the number of items the scheduler can emit.
+inline int64_t items_bound(int64_t total_rows, int B, int H, int tile) {
+  return (int64_t)H * ((total_rows + tile - 1) / tile + (int64_t)B);
+}
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const uint8_t* qs;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const float* bias;
+  void* O;
+  float* lse;
+  const void* hdr;
+  const void* items;
+  int H, nb;
+  float scale;
+};
+
+// Rows of queries per forward work item, per element type.
+constexpr int FWD_BM_BF16 = 128;
+constexpr int FWD_BN_BF16 = 64;
+constexpr int F32_BM = 64;
+constexpr int F32_BN = 64;
+
+hipError_t launch_fwd_bf16(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_fwd_mx(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_fwd_f32(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const float* bias;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* dbias;
+  float* Dvec;           // [total_q, H] softmax row term
+  const void* hdr;
+  const void* items_q;   // query-tile items (dQ)
+  const void* items_k;   // key-tile items (dK/dV)
+  float* dbias_part;     // [n_qtiles, H, NB] per query-tile diagonal sums of dS (canonical order)
+  const int32_t* tile_base;  // [B + 1] canonical index of each sample's first query tile
+  int H, nb;
+  float scale;
+};
+
+constexpr int BWD_BM = 64;   // query rows per tile in the backward kernels
+constexpr int BWD_BN = 64;   // key rows per tile in the backward kernels
+
+hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
+hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
+
+}  // namespace gdpa

@@ -1,0 +1,178 @@
+"""Thin ctypes binding of libgdpa.so (C ABI in include/gdpa.h).
+
+Argument marshalling only: every step of forward and backward runs in the library's HIP kernels.
+torch provides device memory and the current stream. There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first so libgdpa.so binds to the HIP runtime torch has loaded
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdpa.so")
+
+ACT = {"softmax": 0, "gelu_tanh": 1, "silu": 2}
+DTYPE = {"f32": 0, "bf16": 1, "mxfp8": 2}
+STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE", 4: "GDPA_EHIP"}
+
+# Every symbol include/gdpa.h declares.
+EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd", "gdpa_bwd",
+           "gdpa_read_device_error"]
+
+
+class GdpaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("total_q", ctypes.c_int64),
+                ("total_kv", ctypes.c_int64), ("max_q", ctypes.c_int32),
+                ("max_kv", ctypes.c_int32), ("act", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("bias_buckets", ctypes.c_int32)]
+
+
+class GdpaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load():
+    """Load libgdpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER(GdpaProblem)
+    lib.gdpa_abi_version.restype = ctypes.c_int32
+    lib.gdpa_abi_version.argtypes = []
+    lib.gdpa_status_string.restype = ctypes.c_char_p
+    lib.gdpa_status_string.argtypes = [ctypes.c_int32]
+    lib.gdpa_workspace_size.restype = ctypes.c_int32
+    lib.gdpa_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz)]
+    lib.gdpa_fwd.restype = ctypes.c_int32
+    lib.gdpa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_bwd.restype = ctypes.c_int32
+    lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_read_device_error.restype = ctypes.c_int32
+    lib.gdpa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    if lib.gdpa_abi_version() != 1:
+        raise RuntimeError("libgdpa.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def problem(B, H, D, total_q, total_kv, *, dtype="bf16", act="softmax", causal=False,
+            scale=None, bias_buckets=0, max_q=0, max_kv=0):
+    if scale is None:
+        scale = D ** -0.5
+    return GdpaProblem(B=B, H=H, D=D, dtype=DTYPE[dtype], total_q=total_q, total_kv=total_kv,
+                       max_q=max_q, max_kv=max_kv, act=ACT[act], causal=int(bool(causal)),
+                       scale=float(scale), bias_buckets=bias_buckets)
+
+
+def workspace_size(prob, for_bwd=False):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.gdpa_workspace_size(ctypes.byref(prob), int(bool(for_bwd)), ctypes.byref(n))
+    if st != 0:
+        raise GdpaError(st, "gdpa_workspace_size")
+    return int(n.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_of(t):
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.uint8:
+        return "mxfp8"
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None, bias=None,
+        q_scale=None, k_scale=None, v_scale=None, max_q=0, max_kv=0, out=None, lse=None,
+        workspace=None, stream=None, return_lse=True):
+    """Forward over jagged tensors q [total_q, H, D], k/v [total_kv, H, D].
+
+    bf16 / fp32 tensors, or uint8 e4m3 codes with uint8 e8m0 scales [rows, H, D/32] (MX).
+    Returns (O, lse); lse is None for GDPA activations.
+    """
+    lib = load()
+    total_q, H, D = q.shape
+    B = q_offsets.numel() - 1
+    dt = _dtype_of(q)
+    prob = problem(B, H, D, total_q, k.shape[0], dtype=dt, act=act, causal=causal, scale=scale,
+                   bias_buckets=0 if bias is None else bias.shape[1], max_q=max_q, max_kv=max_kv)
+    out_dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=out_dtype, device=q.device)
+    if act == "softmax" and return_lse and lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    if act != "softmax":
+        lse = None
+    if workspace is None:
+        workspace = _workspace(workspace_size(prob, False), q.device)
+    st = lib.gdpa_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                      _ptr(k_scale), _ptr(v_scale), _ptr(q_offsets), _ptr(kv_offsets),
+                      _ptr(bias), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                      _stream(stream))
+    if st != 0:
+        raise GdpaError(st, "gdpa_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None,
+        bias=None, max_q=0, max_kv=0, workspace=None, stream=None, grads=None):
+    """Backward of sum(do * O). Returns (dQ, dK, dV, dbias or None)."""
+    lib = load()
+    total_q, H, D = q.shape
+    B = q_offsets.numel() - 1
+    dt = _dtype_of(q)
+    nb = 0 if bias is None else bias.shape[1]
+    prob = problem(B, H, D, total_q, k.shape[0], dtype=dt, act=act, causal=causal, scale=scale,
+                   bias_buckets=nb, max_q=max_q, max_kv=max_kv)
+    if grads is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        dbias = torch.empty_like(bias) if bias is not None else None
+    else:
+        dq, dk, dv, dbias = grads
+    if workspace is None:
+        workspace = _workspace(workspace_size(prob, True), q.device)
+    st = lib.gdpa_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                      _ptr(lse), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq),
+                      _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel(),
+                      _stream(stream))
+    if st != 0:
+        raise GdpaError(st, "gdpa_bwd")
+    return dq, dk, dv, dbias
+
+
+def read_device_error(workspace, stream=None):
+    lib = load()
+    err = ctypes.c_int32(0)
+    st = lib.gdpa_read_device_error(_ptr(workspace), _stream(stream), ctypes.byref(err))
+    if st != 0:
+        raise GdpaError(st, "gdpa_read_device_error")
+    return int(err.value)

@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # name each case on the real stderr before it runs, so a run that dies mid-test still says
+    # which case it was in
+    sys.__stderr__.write(f"[start] {nodeid}\n")
+    sys.__stderr__.flush()

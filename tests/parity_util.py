@@ -1,0 +1,131 @@
+"""Helpers for GPU-vs-oracle parity tests (test infrastructure).
+
+Tolerance, stated before any kernel ran and never tuned to pass: an element g of a GPU output and
+the oracle's r agree when |g - r| <= atol * s + rtol * |r|, where s = max(1, rms of r over the
+output's (sample, head) block). The rms term keeps the check meaningful for GDPA, whose outputs
+are unnormalised sums of up to thousands of terms; for softmax outputs s is 1. bf16 results use
+atol = rtol = 2e-2 (half a bf16 ulp is 2^-9 ~ 2e-3 per rounding, and P is rounded to bf16 before
+the second product), fp32 results 1e-4 / 1e-4, lse 1e-3 / 1e-4.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from jagged_attention_recommendation_amd import inputs
+
+TOL = {
+    "f32": (1e-4, 1e-4),
+    "bf16": (2e-2, 2e-2),
+    "mxfp8": (2e-2, 2e-2),
+    "lse": (1e-3, 1e-4),
+}
+
+
+def to_device(p, device="cuda"):
+    """Upload a Problem's host arrays (identical bits) to the GPU."""
+    def t(a, kind):
+        if a is None:
+            return None
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        if kind == "u8":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    kind = {"bf16": "bf16", "f32": "f32", "mxfp8": "u8"}[p.dtype]
+    d = {
+        "Q": t(p.Q, kind), "K": t(p.K, kind), "V": t(p.V, kind),
+        "dO": t(p.dO, "bf16" if p.dtype != "f32" else "f32"),
+        "q_off": torch.from_numpy(p.q_off.astype(np.int32)).to(device),
+        "kv_off": torch.from_numpy(p.kv_off.astype(np.int32)).to(device),
+        "bias": torch.from_numpy(p.bias).to(device) if p.bias is not None else None,
+        "q_scale": t(p.q_scale, "u8"), "k_scale": t(p.k_scale, "u8"), "v_scale": t(p.v_scale, "u8"),
+    }
+    return d
+
+
+def host_f64(p, which):
+    """Exact fp64 values of a problem tensor (MX decoded by the oracle's own decoder)."""
+    if p.dtype == "mxfp8" and which in ("Q", "K", "V"):
+        return oracle.decode_mx(getattr(p, which), getattr(p, which[0].lower() + "_scale"))
+    return inputs.as_f64(p, which)
+
+
+def oracle_fwd(p, nthreads=None):
+    return oracle.fwd(p.q_off, p.kv_off, host_f64(p, "Q"), host_f64(p, "K"), host_f64(p, "V"),
+                      act=p.act, causal=p.causal, scale=p.scale,
+                      bias=None if p.bias is None else p.bias.astype(np.float64), nthreads=nthreads)
+
+
+def oracle_bwd(p, nthreads=None):
+    return oracle.bwd(p.q_off, p.kv_off, host_f64(p, "Q"), host_f64(p, "K"), host_f64(p, "V"),
+                      host_f64(p, "dO"), act=p.act, causal=p.causal, scale=p.scale,
+                      bias=None if p.bias is None else p.bias.astype(np.float64), nthreads=nthreads)
+
+
+def block_scale(r, off):
+    """s[row, h] = max(1, rms of r over the (sample, head) block containing that row)."""
+    rows, H = r.shape[0], r.shape[1]
+    s = np.ones((rows, H))
+    for b in range(len(off) - 1):
+        lo, hi = int(off[b]), int(off[b + 1])
+        if hi > lo:
+            blk = r[lo:hi].reshape(hi - lo, H, -1)
+            rms = np.sqrt((blk ** 2).mean(axis=(0, 2)))
+            s[lo:hi] = np.maximum(1.0, rms)[None, :]
+    return s
+
+
+def assert_close(g, r, off, kind, name):
+    """Element-wise tolerance check; g may be a torch tensor (any float dtype)."""
+    if isinstance(g, torch.Tensor):
+        g = g.detach().float().cpu().numpy().astype(np.float64)
+    atol, rtol = TOL[kind]
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    if g.ndim == 3:
+        s = block_scale(r, off)[..., None]
+    else:
+        s = np.ones_like(r)
+    err = np.abs(g - r)
+    bound = atol * s + rtol * np.abs(r)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; "
+                             f"max abs err {err.max():.3e}; first bad {idx.tolist()} "
+                             f"g={g[tuple(idx[0])]:.6g} r={r[tuple(idx[0])]:.6g}")
+    return float(err.max())
+
+
+def assert_lse_close(g, r, name="lse"):
+    if isinstance(g, torch.Tensor):
+        g = g.detach().double().cpu().numpy()
+    atol, rtol = TOL["lse"]
+    neg = np.isneginf(r)
+    assert np.array_equal(np.isneginf(g), neg), f"{name}: -inf pattern differs"
+    err = np.abs(g[~neg] - r[~neg])
+    bound = atol + rtol * np.abs(r[~neg])
+    assert (err <= bound).all(), f"{name}: max err {err.max():.3e}"
+
+
+def subproblem(p, b, heads=None):
+    """Sample b of p as a one-sample problem (same bits), optionally restricted to some heads."""
+    import copy
+    q = slice(int(p.q_off[b]), int(p.q_off[b + 1]))
+    k = slice(int(p.kv_off[b]), int(p.kv_off[b + 1]))
+    hs = slice(None) if heads is None else heads
+    sp = copy.copy(p)
+    sp.B = 1
+    sp.q_off = np.array([0, q.stop - q.start], np.int32)
+    sp.kv_off = np.array([0, k.stop - k.start], np.int32)
+    for name, sl in (("Q", q), ("K", k), ("V", k), ("dO", q), ("q_scale", q), ("k_scale", k),
+                     ("v_scale", k)):
+        a = getattr(p, name)
+        if a is not None:
+            setattr(sp, name, np.ascontiguousarray(a[sl][:, hs]))
+    if p.bias is not None:
+        sp.bias = np.ascontiguousarray(p.bias[hs])
+    sp.H = sp.Q.shape[1]
+    return sp
