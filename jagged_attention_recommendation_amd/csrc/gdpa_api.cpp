@@ -45,8 +45,10 @@ Prob to_prob(const gdpa_problem* p) {
 
 int fwd_tile_rows(int dtype) { return dtype == GDPA_F32 ? F32_BM : FWD_BM_BF16; }
 int fwd_loop_rows(int dtype) { return dtype == GDPA_F32 ? F32_BN : FWD_BN_BF16; }
-int bwd_tile_q(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_BM; }
-int bwd_tile_k(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_BN; }
+int bwd_q_item(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_Q_ITEM; }
+int bwd_k_loop(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_K_LOOP; }
+int bwd_k_item(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_K_ITEM; }
+int bwd_q_loop(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_Q_LOOP; }
 
 struct FwdLayout {
   size_t header, items, total;
@@ -69,7 +71,7 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(const gdpa_problem* p) {
   BwdLayout L;
-  const int tq = bwd_tile_q(p->dtype), tk = bwd_tile_k(p->dtype);
+  const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
   L.max_q_items = items_bound(p->total_q, p->B, p->H, tq);
   L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk);
   L.max_qtiles = (p->total_q + tq - 1) / tq + p->B;
@@ -193,20 +195,20 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const Prob pr = to_prob(p);
-  const int tq = bwd_tile_q(p->dtype), tk = bwd_tile_k(p->dtype);
+  const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
 
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
   sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials)
-  sa.mode = SCHED_QTILES; sa.tile_item = tq; sa.tile_loop = tk;
+  sa.mode = SCHED_QTILES; sa.tile_item = tq; sa.tile_loop = bwd_k_loop(p->dtype);
   sa.max_items = (int)L.max_q_items; sa.list = 0;
   sa.tile_base = (int32_t*)(ws + L.tile_base); sa.items = ws + L.items_q;
   hipError_t e = launch_sched(sa, s);
   if (e != hipSuccess) return map_hip(e);
   // key-tile items (dK, dV)
-  sa.mode = SCHED_KTILES; sa.tile_item = tk; sa.tile_loop = tq;
+  sa.mode = SCHED_KTILES; sa.tile_item = tk; sa.tile_loop = bwd_q_loop(p->dtype);
   sa.max_items = (int)L.max_k_items; sa.list = 1;
   sa.tile_base = nullptr; sa.items = ws + L.items_k;
   e = launch_sched(sa, s);

@@ -105,8 +105,10 @@ struct BwdArgs {
   float scale;
 };
 
-constexpr int BWD_BM = 64;   // query rows per tile in the backward kernels
-constexpr int BWD_BN = 64;   // key rows per tile in the backward kernels
+constexpr int BWD_Q_ITEM = 128;  // queries per dQ work item (bf16)
+constexpr int BWD_K_LOOP = 64;   // keys per tile in the dQ loop (bf16)
+constexpr int BWD_K_ITEM = 128;  // keys per dK/dV work item (bf16)
+constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);

@@ -1,0 +1,93 @@
+// 64-row bf16 tiles in LDS, read two ways by the MFMA kernels:
+//   * row reads: lane reads 16 bytes of logical row R (an A operand whose k runs along D);
+//   * transposed reads (ds_read_b64_tr_b16): a 16-lane group reads 4 consecutive logical rows
+//     x 32 bytes, and a half-wave 4 rows x 64 bytes (an A operand whose k runs along the rows).
+// Row pitch is 2D + 16 bytes and logical row R sits at physical row
+//   (R & ~15) | ((R & 3) << 2) | ((R >> 2) & 3)
+// i.e. each 16-row block is stored with its 4x4 (row%4, row/4) grid transposed. Then the 16
+// rows of a row read land on 16 distinct 16-byte bank groups, and the 4 rows of a transposed
+// read on 4 distinct 64-byte bank groups (256-byte bank span).
+#pragma once
+
+#include "gdpa_common.h"
+
+namespace gdpa {
+
+template <int D>
+struct Tile {
+  static constexpr int ROWS = 64;
+  static constexpr int P = 2 * D + 16;
+  static constexpr int BYTES = ROWS * P;
+  static constexpr int CHUNKS = ROWS * D / 8;  // 16-byte chunks
+  __device__ static __forceinline__ int prow(int r) {
+    return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+  // byte offset of (logical row r, element col)
+  __device__ static __forceinline__ int off(int r, int col) { return prow(r) * P + col * 2; }
+};
+
+// Global -> register staging of a 64-row tile of one head of a jagged tensor; rows at or beyond
+// nrows (local) are zero. NT threads cooperate.
+template <int D, int NT>
+struct TileLoader {
+  static constexpr int PER = Tile<D>::CHUNKS / NT;
+  static_assert(PER >= 1 && Tile<D>::CHUNKS % NT == 0, "tile / thread count mismatch");
+  i32x4 r[PER];
+  __device__ __forceinline__ void load(const __bf16* src, int row0, int nrows, int base, int H,
+                                       int h, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + NT * u;
+      const int row = c / (D / 8), col = c % (D / 8);
+      if (row0 + row < nrows) {
+        r[u] = *(const i32x4*)(src + ((int64_t)(base + row0 + row) * H + h) * D + col * 8);
+      } else {
+        r[u] = i32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(GDPA_LDS char* dst, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + NT * u;
+      const int row = c / (D / 8), col = c % (D / 8);
+      *(GDPA_LDS i32x4*)(dst + Tile<D>::off(row, col * 8)) = r[u];
+    }
+  }
+};
+
+// A operand (rows = tile rows rbase..rbase+31, k = D) for k-step s: lane reads logical row
+// rbase + l%32, elements 16s + 8(l/32) .. +8.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row_op(const GDPA_LDS char* t, int rbase, int s, int lane) {
+  return *(const GDPA_LDS bf16x8*)(t + Tile<D>::off(rbase + (lane & 31), 16 * s + 8 * (lane >> 5)));
+}
+
+// A operand of a transposed product (rows = D index n*32 + l%32, k = 8 tile rows): the 8 rows
+// are key0 + 4(l/32) + {0..3} and key0 + 8 + 4(l/32) + {0..3}, matching the k order of an
+// accumulator-derived B operand (registers 8*s2..8*s2+7 of a 32x32 block, key0 = 16*s2 within
+// the block).
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr_op(const GDPA_LDS char* t, int key0, int n, int lane) {
+  const int i16 = lane & 15;
+  const int rr = key0 + 4 * (lane >> 5) + (i16 >> 2);
+  const int col = n * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+  const i16x4 lo = lds_read_tr(t + Tile<D>::off(rr, col));
+  const i16x4 hi = lds_read_tr(t + Tile<D>::off(rr + 8, col));
+  return cat_tr(lo, hi);
+}
+
+// Store a lane's 32x32-block accumulator column (16 values, D index n*32 + (r/4)*8 + 4g + r%4)
+// as bf16 into a row of a [rows, H, D] tensor, multiplied by mul.
+__device__ __forceinline__ void store_acc_row_bf16(__bf16* row, const f32x16& acc, int n, int g,
+                                                   float mul) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    bf16x2 lo = pack_bf16(acc[4 * r4 + 0] * mul, acc[4 * r4 + 1] * mul);
+    bf16x2 hi = pack_bf16(acc[4 * r4 + 2] * mul, acc[4 * r4 + 3] * mul);
+    bf16x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
+    *(bf16x4*)(row + n * 32 + r4 * 8 + 4 * g) = v4;
+  }
+}
+
+}  // namespace gdpa

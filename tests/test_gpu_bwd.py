@@ -1,0 +1,130 @@
+"""Backward parity: libgdpa.so (HIP, gfx950) against the fp64 oracle on identical inputs."""
+import numpy as np
+import pytest
+import torch
+
+from jagged_attention_recommendation_amd import inputs
+from parity_util import TOL, assert_close, oracle_bwd, subproblem, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from jagged_attention_recommendation_amd import gdpa
+    gdpa.load()
+
+
+def run_fwd_bwd(p):
+    from jagged_attention_recommendation_amd import gdpa
+    d = to_device(p)
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"])
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], **kw)
+    dq, dk, dv, dbias = gdpa.bwd(d["Q"], d["K"], d["V"], O, d["dO"], lse, d["q_off"],
+                                 d["kv_off"], **kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv, dbias
+
+
+def assert_dbias_close(g, r, name):
+    g = g.detach().double().cpu().numpy()
+    atol, rtol = TOL["bf16"]
+    s = max(1.0, float(np.sqrt((r ** 2).mean())))
+    err = np.abs(g - r)
+    bad = err > atol * s + rtol * np.abs(r)
+    assert not bad.any(), f"{name}: {bad.sum()} bad, max err {err.max():.3e}, rms {s:.3e}"
+
+
+def check_bwd(p):
+    dq, dk, dv, dbias = run_fwd_bwd(p)
+    ref = oracle_bwd(p)
+    kind = "f32" if p.dtype == "f32" else "bf16"
+    assert_close(dq, ref["dQ"], p.q_off, kind, f"{p.name} dQ")
+    assert_close(dk, ref["dK"], p.kv_off, kind, f"{p.name} dK")
+    assert_close(dv, ref["dV"], p.kv_off, kind, f"{p.name} dV")
+    if p.bias is not None:
+        assert_dbias_close(dbias, ref["dbias"], f"{p.name} dbias")
+
+
+def small(seed, D, act, causal, nb, dtype="bf16", B=5, H=2, lo=1, hi=300, same=True):
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(lo, hi + 1, size=B)
+    lk = lq if same else rng.integers(lo, hi + 1, size=B)
+    return inputs.make_problem(f"small-{seed}", seed=seed, H=H, D=D, lq=lq, lk=lk, dtype=dtype,
+                               act=act, causal=causal, bias_buckets=nb)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
+@pytest.mark.parametrize("causal,nb,same", [(False, 0, False), (True, 0, True), (True, 48, True),
+                                            (False, 40, False)])
+def test_bf16_small(D, act, causal, nb, same):
+    check_bwd(small(200 + D, D, act, causal, nb, same=same))
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+@pytest.mark.parametrize("causal,nb", [(False, 0), (True, 20)])
+def test_f32_small(act, causal, nb):
+    check_bwd(small(17, 32, act, causal, nb, dtype="f32", hi=150))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_lengths(dtype):
+    lq = np.array([1, 63, 64, 65, 127, 128, 129, 0, 5, 200])
+    lk = np.array([1, 63, 64, 65, 127, 128, 129, 7, 0, 3])
+    for act, causal in (("softmax", False), ("silu", True)):
+        p = inputs.make_problem("edges", seed=15, H=3, D=32, lq=lq, lk=lk, dtype=dtype, act=act,
+                                causal=causal, bias_buckets=16)
+        check_bwd(p)
+
+
+def test_single_long_sample():
+    p = inputs.make_problem("long", seed=19, H=1, D=128, lq=[2048], lk=[2048], act="softmax",
+                            causal=True, bias_buckets=4096)
+    check_bwd(p)
+
+
+def test_config2_reduced():
+    check_bwd(inputs.config_problem(2, B=3))
+
+
+def test_config3_reduced():
+    check_bwd(inputs.config_problem(3, B=6))
+
+
+def test_config4_reduced():
+    check_bwd(inputs.config_problem(4, B=24))
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_full_config_sampled(k):
+    """Full-size workload; the oracle recomputes dQ/dK/dV of a few whole samples on their own.
+    The bias gradient mixes all samples, so at full size it is checked through the softmax
+    invariant sum_r dbias[h, r] = 0 (rows of dS sum to zero)."""
+    p = inputs.config_problem(k)
+    dq, dk, dv, dbias = run_fwd_bwd(p)
+    dqh, dkh, dvh = (t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+    L = p.lq * np.maximum(p.lk, 1)
+    for b in sorted({int(np.argmax(L)), int(np.argmin(L)), len(L) // 2}):
+        sp = subproblem(p, b)
+        sp.bias = p.bias  # same table (all heads)
+        ref = oracle_bwd(sp)
+        qr = slice(int(p.q_off[b]), int(p.q_off[b + 1]))
+        kr = slice(int(p.kv_off[b]), int(p.kv_off[b + 1]))
+        assert_close(dqh[qr], ref["dQ"], sp.q_off, "bf16", f"config{k} sample {b} dQ")
+        assert_close(dkh[kr], ref["dK"], sp.kv_off, "bf16", f"config{k} sample {b} dK")
+        assert_close(dvh[kr], ref["dV"], sp.kv_off, "bf16", f"config{k} sample {b} dV")
+    if dbias is not None and p.act == "softmax":
+        db = dbias.double().cpu().numpy()
+        scale = np.abs(db).sum(axis=1)
+        assert np.all(np.abs(db.sum(axis=1)) <= 1e-3 * np.maximum(scale, 1.0))
+
+
+def test_bitwise_repeatable():
+    p = small(21, 128, "softmax", True, 64)
+    a = run_fwd_bwd(p)
+    b = run_fwd_bwd(p)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
