@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the jagged-attention hot path on one MI355X.
+
+One step = one forward + backward pass (work scheduler, forward kernel, backward dQ and dK/dV
+kernels, bias-gradient reduction) over the causal JFA softmax workload: B=64 samples, lengths
+uniform in [1, 2048] (token sparsity ~0.5 against the longest length), H=4 heads, D=128, bf16
+inputs with fp32 accumulation, a learned per-head relative-position bias table of 4096 entries
+indexed by clamp(i-j). Inputs are seeded synthetic data, resident in HBM before timing starts.
+
+Metric: useful (unpadded) TFLOPS of forward + backward, i.e. matrix-product flops of unmasked
+(query, key) pairs only (4*D per pair and head forward, 10*D backward), divided by the measured
+step time. Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+WORKLOADS = {
+    2: "jfa_softmax_causal_bias_B64_H4_D128_L1-2048_bf16",
+    3: "gdpa_cross_gelu_B256_H4_D128_Lq64-4096_Lk8-64_bf16",
+    4: "gdpa_pma_silu_B512_H8_D64_Lq32_Lk_lognormal_bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
+                    help="workload (default: the causal JFA softmax workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def dominant_kernel_flops(p, kernel):
+    """Algorithmic flops one launch of the kernel must do: pairs x flops-per-pair."""
+    from jagged_attention_recommendation_amd import workload
+    pairs = int(workload.pairs_per_sample(p.lq, p.lk, p.causal).sum()) * p.H
+    per_pair = {"fwd": 4, "dq": 6, "dkdv": 8}[kernel] * p.D  # products: 2 / 3 / 4
+    return float(per_pair) * pairs
+
+
+def prefix_problem(p, n):
+    """The first n samples of p as a problem of their own (same bits)."""
+    import copy
+    sp = copy.copy(p)
+    qe, ke = int(p.q_off[n]), int(p.kv_off[n])
+    sp.B = n
+    sp.q_off, sp.kv_off = p.q_off[:n + 1].copy(), p.kv_off[:n + 1].copy()
+    sp.Q, sp.dO = p.Q[:qe], p.dO[:qe]
+    sp.K, sp.V = p.K[:ke], p.V[:ke]
+    return sp
+
+
+def cpu_baseline(p, target_s):
+    """Time the fp64 oracle (forward + backward) on the first samples of the same workload.
+
+    A one-sample run calibrates the oracle's rate; the sample is then grown to about target_s
+    of work and timed in one call (OpenMP over samples x heads on every host thread).
+    """
+    import oracle
+    from jagged_attention_recommendation_amd import inputs, workload
+
+    nthreads = oracle.default_threads()
+
+    def run(sp):
+        Q, K, V, dO = (inputs.as_f64(sp, n) for n in ("Q", "K", "V", "dO"))
+        bias = None if sp.bias is None else sp.bias.astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.fwd(sp.q_off, sp.kv_off, Q, K, V, act=sp.act, causal=sp.causal, scale=sp.scale,
+                   bias=bias, nthreads=nthreads)
+        oracle.bwd(sp.q_off, sp.kv_off, Q, K, V, dO, act=sp.act, causal=sp.causal,
+                   scale=sp.scale, bias=bias, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    # calibrate on enough samples to occupy every thread, then size the timed sample
+    n0 = max(1, min(p.B, -(-nthreads // p.H)))
+    sp0 = prefix_problem(p, n0)
+    t_cal = run(sp0)
+    rate = workload.useful_flops(sp0, "fwdbwd") / max(t_cal, 1e-9)
+    per_sample = 14.0 * p.D * p.H * workload.pairs_per_sample(p.lq, p.lk, p.causal)
+    cum = np.cumsum(per_sample)
+    n = int(np.searchsorted(cum, rate * target_s)) + 1
+    n = max(n0, min(n, p.B))
+    sp = prefix_problem(p, n)
+    secs = run(sp)
+    flops = workload.useful_flops(sp, "fwdbwd")
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOPS", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward on the first {n} of {p.B} samples of the "
+                      f"same workload ({sp.total_q} tokens, {flops / 1e12:.4f} useful TFLOP), "
+                      f"{secs:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from jagged_attention_recommendation_amd import gdpa, inputs, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdpa.load()
+    dev = torch.device("cuda:0")
+    p = inputs.config_problem(args.config)
+
+    def up_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V, dO = up_bf16(p.Q), up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
+    q_off = torch.from_numpy(p.q_off).to(dev)
+    kv_off = torch.from_numpy(p.kv_off).to(dev)
+    bias = torch.from_numpy(p.bias).to(dev) if p.bias is not None else None
+    nb = 0 if bias is None else bias.shape[1]
+    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
+    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, act=p.act, causal=p.causal,
+                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv)
+    ws_f = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if p.act == "softmax" else None
+    grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
+             torch.empty_like(bias) if bias is not None else None)
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv)
+
+    def step():
+        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
+        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region; the library brackets each launch of the main kernels with HIP events on
+    # the launch stream, which gives every kernel's average duration over this same region
+    kernels = ("fwd", "dq", "dkdv")
+    torch.cuda.synchronize()
+    gdpa.profile_start(kernels)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdpa.profile_stop()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {}
+    for kern in kernels:
+        n, ms = gdpa.profile_read(kern)
+        kern_ms[kern] = ms / max(n, 1)
+
+    # forward-only and backward-only splits (secondary numbers)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms = bwd_ms = 0.0
+    for _ in range(args.steps):
+        ev[0].record()
+        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
+        ev[1].record()
+        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd_ms += ev[0].elapsed_time(ev[1])
+        bwd_ms += ev[1].elapsed_time(ev[2])
+    fwd_ms /= args.steps
+    bwd_ms /= args.steps
+    for t in (O, *grads[:3]):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError("non-finite output")
+
+    if args.copy_calibration:
+        # plain copy of known size, for scaling the HBM byte counters of a profiling run
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    f_fwd = workload.useful_flops(p, "fwd")
+    f_bwd = workload.useful_flops(p, "bwd")
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_flops = dominant_kernel_flops(p, dom)
+    achieved = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(kern_ms[dom], 4),
+                "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()}}
+
+    out = {
+        "metric": "useful (unpadded) TFLOPS fwd+bwd, jagged sparsity 0.5, and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "B": p.B, "H": p.H, "D": p.D,
+                   "total_tokens": p.total_q, "causal": p.causal, "act": p.act,
+                   "bias_buckets": nb,
+                   "token_sparsity": round(1 - p.total_q / (p.B * max(max_q, 1)), 4)},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

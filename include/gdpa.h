@@ -113,6 +113,17 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
  * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err);
 
+/* Profiling aid for benchmarks (not thread-safe). Between gdpa_profile_start(mask) and
+ * gdpa_profile_stop(), every launch of a selected kernel is bracketed by a pair of HIP events
+ * recorded on its launch stream. Bit k of mask selects kernel k: 0 = forward main kernel,
+ * 1 = backward dQ kernel, 2 = backward dK/dV kernel, 3 = scheduler. At most 1024 launches per
+ * kernel are timed. gdpa_profile_read() waits for the recorded events of one kernel and returns
+ * how many of its launches were timed and their summed duration in milliseconds. Events are
+ * created on the first start and kept for the life of the process. */
+int32_t gdpa_profile_start(int32_t mask);
+int32_t gdpa_profile_read(int32_t kernel, int32_t* launches, double* total_ms);
+int32_t gdpa_profile_stop(void);
+
 #ifdef __cplusplus
 }
 #endif

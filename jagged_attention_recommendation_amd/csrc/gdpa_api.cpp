@@ -87,6 +87,17 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   return L;
 }
 
+// ---- profiling hook state
+constexpr int PROF_KERNELS = 4;
+constexpr int PROF_MAX = 1024;
+struct ProfState {
+  int mask = 0;
+  int n[PROF_KERNELS] = {0, 0, 0, 0};
+  bool created = false;
+  hipEvent_t ev[PROF_KERNELS][2 * PROF_MAX];
+};
+ProfState g_prof;
+
 int32_t map_hip(hipError_t e) {
   if (e == hipSuccess) return GDPA_OK;
   if (e == hipErrorNotSupported) return GDPA_ENOTSUP;
@@ -95,7 +106,54 @@ int32_t map_hip(hipError_t e) {
 
 }  // namespace
 
+namespace gdpa {
+void prof_before(int kernel, hipStream_t s) {
+  if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
+  hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel]], s);
+}
+void prof_after(int kernel, hipStream_t s) {
+  if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
+  hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel] + 1], s);
+  ++g_prof.n[kernel];
+}
+}  // namespace gdpa
+
 extern "C" {
+
+int32_t gdpa_profile_start(int32_t mask) {
+  if (mask < 0 || mask >= (1 << PROF_KERNELS)) return GDPA_EINVAL;
+  if (!g_prof.created) {
+    for (int k = 0; k < PROF_KERNELS; ++k)
+      for (int i = 0; i < 2 * PROF_MAX; ++i)
+        if (hipEventCreate(&g_prof.ev[k][i]) != hipSuccess) return GDPA_EHIP;
+    g_prof.created = true;
+  }
+  g_prof.mask = mask;
+  for (int k = 0; k < PROF_KERNELS; ++k) g_prof.n[k] = 0;
+  return GDPA_OK;
+}
+
+int32_t gdpa_profile_read(int32_t kernel, int32_t* launches, double* total_ms) {
+  if (!launches || !total_ms || kernel < 0 || kernel >= PROF_KERNELS) return GDPA_EINVAL;
+  double tot = 0.0;
+  const int n = g_prof.n[kernel];
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(g_prof.ev[kernel][2 * i + 1]) != hipSuccess) return GDPA_EHIP;
+    if (hipEventElapsedTime(&ms, g_prof.ev[kernel][2 * i], g_prof.ev[kernel][2 * i + 1]) !=
+        hipSuccess)
+      return GDPA_EHIP;
+    tot += ms;
+  }
+  *launches = n;
+  *total_ms = tot;
+  return GDPA_OK;
+}
+
+int32_t gdpa_profile_stop(void) {
+  g_prof.mask = 0;
+  return GDPA_OK;
+}
 
 int32_t gdpa_abi_version(void) { return GDPA_ABI_VERSION; }
 

@@ -343,10 +343,18 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
 
 template <int D, int ACT, bool C, bool BI>
 hipError_t launch_t(const BwdArgs& a, int gq, int gk, hipStream_t s) {
-  if (gq > 0) hipLaunchKernelGGL((dq_kernel<D, ACT, C, BI>), dim3(gq), dim3(NT), 0, s, a);
+  if (gq > 0) {
+    prof_before(PROF_DQ, s);
+    hipLaunchKernelGGL((dq_kernel<D, ACT, C, BI>), dim3(gq), dim3(NT), 0, s, a);
+    prof_after(PROF_DQ, s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (gk > 0) hipLaunchKernelGGL((dkdv_kernel<D, ACT, C, BI>), dim3(gk), dim3(NT), 0, s, a);
+  if (gk > 0) {
+    prof_before(PROF_DKDV, s);
+    hipLaunchKernelGGL((dkdv_kernel<D, ACT, C, BI>), dim3(gk), dim3(NT), 0, s, a);
+    prof_after(PROF_DKDV, s);
+  }
   return hipGetLastError();
 }
 

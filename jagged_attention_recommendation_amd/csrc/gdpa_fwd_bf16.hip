@@ -240,7 +240,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
 template <int D, int ACT, bool CAUSAL, bool BIAS>
 hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
+  prof_before(PROF_FWD, s);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, ACT, CAUSAL, BIAS>), dim3(grid), dim3(256), 0, s, a);
+  prof_after(PROF_FWD, s);
   return hipGetLastError();
 }
 

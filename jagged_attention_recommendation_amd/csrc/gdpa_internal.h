@@ -113,4 +113,9 @@ constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
+// Profiling hook: brackets launches of one kernel with HIP events (see gdpa_profile_start).
+enum { PROF_FWD = 0, PROF_DQ = 1, PROF_DKDV = 2, PROF_SCHED = 3 };
+void prof_before(int kernel, hipStream_t s);
+void prof_after(int kernel, hipStream_t s);
+
 }  // namespace gdpa

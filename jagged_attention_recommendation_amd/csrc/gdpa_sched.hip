@@ -172,7 +172,9 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
+  prof_before(PROF_SCHED, s);
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(NBUCKET), 0, s, a);
+  prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }
 

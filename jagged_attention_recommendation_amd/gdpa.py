@@ -20,7 +20,11 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE
 
 # Every symbol include/gdpa.h declares.
 EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd", "gdpa_bwd",
-           "gdpa_read_device_error"]
+           "gdpa_read_device_error", "gdpa_profile_start", "gdpa_profile_read",
+           "gdpa_profile_stop"]
+
+# kernels selectable by the profiling hook
+PROFILE_KERNELS = {"fwd": 0, "dq": 1, "dkdv": 2, "sched": 3}
 
 
 class GdpaProblem(ctypes.Structure):
@@ -62,6 +66,13 @@ def load():
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_read_device_error.restype = ctypes.c_int32
     lib.gdpa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.gdpa_profile_start.restype = ctypes.c_int32
+    lib.gdpa_profile_start.argtypes = [ctypes.c_int32]
+    lib.gdpa_profile_read.restype = ctypes.c_int32
+    lib.gdpa_profile_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_double)]
+    lib.gdpa_profile_stop.restype = ctypes.c_int32
+    lib.gdpa_profile_stop.argtypes = []
     if lib.gdpa_abi_version() != 1:
         raise RuntimeError("libgdpa.so ABI version mismatch")
     _lib = lib
@@ -176,3 +187,27 @@ def read_device_error(workspace, stream=None):
     if st != 0:
         raise GdpaError(st, "gdpa_read_device_error")
     return int(err.value)
+
+
+def profile_start(kernels):
+    """Bracket every launch of the given kernels ("fwd", "dq", "dkdv", "sched") with HIP events."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << PROFILE_KERNELS[k]
+    st = load().gdpa_profile_start(mask)
+    if st != 0:
+        raise GdpaError(st, "gdpa_profile_start")
+
+
+def profile_read(kernel):
+    """(launches timed, summed duration in ms) of one kernel since profile_start."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    st = load().gdpa_profile_read(PROFILE_KERNELS[kernel], ctypes.byref(n), ctypes.byref(ms))
+    if st != 0:
+        raise GdpaError(st, "gdpa_profile_read")
+    return int(n.value), float(ms.value)
+
+
+def profile_stop():
+    load().gdpa_profile_stop()
