@@ -1,0 +1,318 @@
+// Forward kernel template: JFA (softmax) and GDPA (GELU-tanh / SiLU), bf16 or MX-fp8 inputs,
+// fp32 accumulation.
+//
+// Method (page "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation
+// Model"): JFA paragraph - FlashAttention run directly on jagged tensors (no padding), with
+// attention biases and different query / key lengths; GDPA paragraph - the same two products
+// with an element-wise GELU or SiLU instead of softmax and no normalisation; low-precision part -
+// attention with MXFP8 block-scaled matrix products. FlashAttention's tiling with online max /
+// sum rescaling gives exactly the plain softmax result; GDPA needs no rescaling since every
+// score is mapped on its own.
+//
+// Work decomposition: one workgroup (4 waves) per scheduler item = 128 query rows of one
+// (sample, head). Each wave owns 32 queries. Keys stream through LDS in tiles of 64 rows; the
+// next tile's global loads are issued before the current tile is computed.
+//
+// Operand choice (wave64 MFMA):
+//   S^T = K Q^T  : A = K rows from LDS, B = Q^T from registers. The accumulator puts one query
+//                  per lane (column) and 16 keys per lane (rows), so row statistics need only a
+//                  swap between the two half-waves. bf16: 32x32x16 bf16 MFMA. MX: 32x32x64
+//                  f8f6f4 scaled MFMA with e4m3 operands, whose per-32-element e8m0 scales run
+//                  along D, the contraction dimension, so they are the instruction's own operand
+//                  scales.
+//   O^T += V^T P^T: A = V^T read transposed from the row-major bf16 V tile (ds_read_b64_tr_b16),
+//                  B = P^T (bf16) straight from the S^T accumulator (the key order inside a
+//                  16-key k-step is permuted identically on both operands). For MX, V is
+//                  dequantised exactly into the bf16 tile: an e4m3 value times a power of two has
+//                  at most 4 significant bits. P is rounded to bf16 in both paths.
+// The exp of softmax uses exp2 with log2(e) folded into the score scale.
+#pragma once
+
+#include <math.h>
+
+#include "gdpa_common.h"
+#include "gdpa_internal.h"
+#include "gdpa_tiles.h"
+
+namespace gdpa {
+namespace fwdk {
+
+constexpr int BM = FWD_BM_BF16;  // queries per item (4 waves x 32)
+constexpr int BN = FWD_BN_BF16;  // keys per tile
+constexpr int NT = 256;
+
+// e4m3 code (low byte of c) times the power of two sc, in fp32 (exact).
+__device__ __forceinline__ float e4m3_times(uint32_t c, float sc) {
+  const uint32_t em = c & 0x7Fu;
+  float mag = em >= 8u ? __builtin_bit_cast(float, (em + 960u) << 20) : (float)em * 0x1p-9f;
+  mag *= sc;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// 2^(X-127) for an e8m0 code X (0xFF, NaN in the format, is not produced by this path's inputs)
+__device__ __forceinline__ float e8m0_value(uint32_t X) {
+  return X == 0u ? 0x1p-127f : __builtin_bit_cast(float, X << 23);
+}
+
+template <int D, bool MX>
+struct Smem {
+  // MX K tile: 64 rows x 128 bytes, pitch 144 (16 rows of a read hit distinct bank groups),
+  // then 64 scale words.
+  static constexpr int KMX_P = 144;
+  static constexpr int K_BYTES = MX ? BN * KMX_P + BN * 4 : Tile<D>::BYTES;
+  static constexpr int V_BYTES = Tile<D>::BYTES;
+};
+
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX>
+__global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
+  static_assert(!MX || D == 128, "MX path is for D = 128");
+  using S = Smem<D, MX>;
+  __shared__ __attribute__((aligned(16))) char smem[S::K_BYTES + S::V_BYTES];
+  GDPA_LDS char* Ks = (GDPA_LDS char*)smem;
+  GDPA_LDS char* Vs = Ks + S::K_BYTES;
+
+  const WsHeader* hdr = (const WsHeader*)a.hdr;
+  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
+  const Item it = ((const Item*)a.items)[blockIdx.x];
+  const int b = it.b, h = it.h, H = a.H;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int row_blk = it.tile * BM;   // first query of the item (local index)
+  const int wrow = row_blk + w * 32;  // first query of this wave
+  const int iq = wrow + l32;          // this lane's query
+  const bool wave_active = wrow < Lq;
+  const bool qv = iq < Lq;
+  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+
+  int nkt = (Lk + BN - 1) / BN;
+  if (CAUSAL) {
+    const int i_max = min(Lq, row_blk + BM) - 1;
+    nkt = min(nkt, i_max / BN + 1);
+  }
+
+  // ---- Q^T operand: lane holds query iq
+  bf16x8 qop[MX ? 1 : D / 16];
+  i32x8 q8[MX ? 2 : 1];
+  uint32_t qsc = 0;
+  if constexpr (!MX) {
+    const __bf16* Q = (const __bf16*)a.Q;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qop[s] = qv ? *(const bf16x8*)(Q + qrow * D + 16 * s + 8 * g) : zero_bf16x8();
+  } else {
+    const uint8_t* Q8 = (const uint8_t*)a.Q;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+      if (qv) {
+        lo = *(const i32x4*)(Q8 + qrow * D + 64 * s + 16 * g);
+        hi = *(const i32x4*)(Q8 + qrow * D + 64 * s + 32 + 16 * g);
+      }
+      q8[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    qsc = qv ? *(const uint32_t*)(a.qs + qrow * 4) : 0x7F7F7F7Fu;
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float sl2 = a.scale * LOG2E;
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
+
+  // ---- global -> register staging of one K/V tile
+  TileLoader<D, NT> lk_, lv_;           // bf16 path
+  constexpr int MXC = BN * 128 / 16 / NT;  // 16-byte code chunks per thread (MX): 2
+  i32x4 kc[MX ? MXC : 1], vc[MX ? MXC : 1];
+  uint32_t ksw = 0, vsb[MX ? MXC : 1];
+  auto load_tile = [&](int kt) {
+    if constexpr (!MX) {
+      lk_.load((const __bf16*)a.K, kt * BN, Lk, kv0, H, h, tid);
+      lv_.load((const __bf16*)a.V, kt * BN, Lk, kv0, H, h, tid);
+    } else {
+      const uint8_t* K8 = (const uint8_t*)a.K;
+      const uint8_t* V8 = (const uint8_t*)a.V;
+#pragma unroll
+      for (int u = 0; u < MXC; ++u) {
+        const int c = tid + NT * u, r = c >> 3, col = c & 7;
+        const int j = kt * BN + r;
+        if (j < Lk) {
+          const int64_t off = ((int64_t)(kv0 + j) * H + h) * 128 + col * 16;
+          kc[u] = *(const i32x4*)(K8 + off);
+          vc[u] = *(const i32x4*)(V8 + off);
+          vsb[u] = a.vs[((int64_t)(kv0 + j) * H + h) * 4 + (col >> 1)];
+        } else {
+          kc[u] = i32x4{0, 0, 0, 0};
+          vc[u] = i32x4{0, 0, 0, 0};
+          vsb[u] = 127u;
+        }
+      }
+      if (tid < BN) {
+        const int j = kt * BN + tid;
+        ksw = j < Lk ? *(const uint32_t*)(a.ks + ((int64_t)(kv0 + j) * H + h) * 4) : 0x7F7F7F7Fu;
+      }
+    }
+  };
+  auto store_tile = [&]() {
+    if constexpr (!MX) {
+      lk_.store(Ks, tid);
+      lv_.store(Vs, tid);
+    } else {
+#pragma unroll
+      for (int u = 0; u < MXC; ++u) {
+        const int c = tid + NT * u, r = c >> 3, col = c & 7;
+        *(GDPA_LDS i32x4*)(Ks + r * S::KMX_P + col * 16) = kc[u];
+        // dequantise 16 V codes into two 16-byte bf16 chunks
+        const float sc = e8m0_value(vsb[u]);
+        float f[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = e4m3_times((uint32_t)vc[u][e >> 2] >> (8 * (e & 3)), sc);
+        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16)) = pack8(&f[0]);
+        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16 + 8)) = pack8(&f[8]);
+      }
+      if (tid < BN) *(GDPA_LDS uint32_t*)(Ks + BN * S::KMX_P + tid * 4) = ksw;
+    }
+  };
+
+  if (nkt > 0) load_tile(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < nkt) load_tile(kt + 1);
+    const int k0 = kt * BN;
+    if (!wave_active) continue;
+    if (CAUSAL && k0 > wrow + 31) continue;  // every key of the tile is after every query
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      if constexpr (!MX) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+          sacc[kb] = mfma32(tile_row_op<D>(Ks, kb * 32, s, lane), qop[s], sacc[kb]);
+      } else {
+        const int r = kb * 32 + l32;
+        const uint32_t kw = *(const GDPA_LDS uint32_t*)(Ks + BN * S::KMX_P + r * 4);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const i32x4 lo = *(const GDPA_LDS i32x4*)(Ks + r * S::KMX_P + 64 * s + 16 * g);
+          const i32x4 hi = *(const GDPA_LDS i32x4*)(Ks + r * S::KMX_P + 64 * s + 32 + 16 * g);
+          const i32x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          // this lane supplies the scale of its row for k block g of the instruction, which is
+          // the 32-element block 2s + g along D
+          const int sa = (int)((kw >> (8 * (2 * s + g))) & 0xFFu);
+          const int sb = (int)((qsc >> (8 * (2 * s + g))) & 0xFFu);
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, q8[s], sacc[kb], 0, 0, 0,
+                                                                     sa, 0, sb);
+        }
+      }
+    }
+
+    // ---- scores -> probabilities (register r of block kb is key k0 + kb*32 + (r/4)*8 + 4g + r%4)
+    const bool need_mask = (k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow);
+    float p[2][16];
+    if (ACT == ACT_SOFTMAX) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
+          float x = sacc[kb][r] * sl2;
+          if (BIAS) x += bias_h[clampi(iq - j, 0, a.nb - 1)] * LOG2E;
+          if (need_mask && (j >= Lk || (CAUSAL && j > iq))) x = -INFINITY;
+          p[kb][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = half_max(mt);
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[kb][r] = fast_exp2(p[kb][r] - m_use);
+          ls += p[kb][r];
+        }
+      }
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) o[n] *= alpha;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
+          float x = sacc[kb][r] * a.scale;
+          if (BIAS) x += bias_h[clampi(iq - j, 0, a.nb - 1)];
+          float y = act_fwd(ACT, x);
+          if (need_mask && (j >= Lk || (CAUSAL && j > iq))) y = 0.0f;
+          p[kb][r] = y;
+        }
+      }
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pb = pack8(&p[kb][8 * s2]);
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+          o[n] = mfma32(tile_tr_op<D>(Vs, kb * 32 + 16 * s2, n, lane), pb, o[n]);
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  // ---- epilogue: lane owns query iq; register r of block n is d = n*32 + (r/4)*8 + 4g + r%4
+  float inv = 1.0f;
+  if (ACT == ACT_SOFTMAX) {
+    const float lt = half_sum(l_run);
+    inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (qv && g == 0 && a.lse != nullptr)
+      a.lse[qrow] = lt > 0.0f ? (m_run + log2f(lt)) * LN2 : -INFINITY;
+  }
+  if (!qv) return;
+  __bf16* orow = (__bf16*)a.O + qrow * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(orow, o[n], n, g, inv);
+}
+
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX>
+hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
+  prof_before(PROF_FWD, s);
+  hipLaunchKernelGGL((fwd_kernel<D, ACT, CAUSAL, BIAS, MX>), dim3(grid), dim3(NT), 0, s, a);
+  prof_after(PROF_FWD, s);
+  return hipGetLastError();
+}
+
+template <int D, int ACT, bool MX>
+hipError_t launch_cb(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
+  const bool bias = p.nb > 0;
+  if (p.causal)
+    return bias ? launch_t<D, ACT, true, true, MX>(a, grid, s) : launch_t<D, ACT, true, false, MX>(a, grid, s);
+  return bias ? launch_t<D, ACT, false, true, MX>(a, grid, s) : launch_t<D, ACT, false, false, MX>(a, grid, s);
+}
+
+template <int D, bool MX>
+hipError_t launch_d(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
+  switch (p.act) {
+    case ACT_SOFTMAX: return launch_cb<D, ACT_SOFTMAX, MX>(p, a, grid, s);
+    case ACT_GELU_TANH: return launch_cb<D, ACT_GELU_TANH, MX>(p, a, grid, s);
+    default: return launch_cb<D, ACT_SILU, MX>(p, a, grid, s);
+  }
+}
+
+}  // namespace fwdk
+}  // namespace gdpa

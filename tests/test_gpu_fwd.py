@@ -134,3 +134,48 @@ def test_bad_offsets_set_device_error():
     assert gdpa.read_device_error(ws) == 1
     gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], act="silu", workspace=ws)
     assert gdpa.read_device_error(ws) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# MX-fp8 (e4m3 data, e8m0 scales per 32 elements along D), forward only, D = 128
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu", "gelu_tanh"])
+@pytest.mark.parametrize("causal,nb", [(True, 0), (False, 0), (True, 64)])
+def test_mx_small(act, causal, nb):
+    check_fwd(small(300, 128, act, causal, nb, dtype="mxfp8", B=4))
+
+
+def test_mx_edges():
+    lq = np.array([1, 63, 64, 65, 127, 128, 129, 0, 5, 200])
+    lk = np.array([1, 63, 64, 65, 127, 128, 129, 7, 0, 3])
+    for act in ("softmax", "silu"):
+        p = inputs.make_problem("mx-edges", seed=31, H=2, D=128, lq=lq, lk=lk, dtype="mxfp8",
+                                act=act, causal=False, with_grad=False)
+        check_fwd(p)
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_config5_reduced(act):
+    check_fwd(inputs.config_problem(5, act=act, B=6, seed=2005))
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_config5_full_sampled(act):
+    """Full-size MX workload in one launch; the oracle recomputes a few whole samples of up to
+    4096 tokens (the shortest, one near the median, and the longest such sample)."""
+    p = inputs.config_problem(5, act=act)
+    O, lse = run_fwd(p)
+    Og = O.float().cpu().numpy()
+    lseg = lse.cpu().numpy() if lse is not None else None
+    L = p.lq
+    ok = np.where(L <= 4096)[0]
+    picks = sorted({int(ok[np.argmin(L[ok])]), int(ok[np.argmax(L[ok])]),
+                    int(ok[np.argsort(L[ok])[len(ok) // 2]])})
+    for b in picks:
+        sp = subproblem(p, b)
+        Or, lser = oracle_fwd(sp)
+        rows = slice(int(p.q_off[b]), int(p.q_off[b + 1]))
+        assert_close(Og[rows].astype(np.float64), Or, sp.q_off, "mxfp8", f"config5 sample {b}")
+        if lseg is not None:
+            assert_lse_close(lseg[rows], lser, f"config5 sample {b} lse")
