@@ -65,7 +65,7 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
 }
 
 struct BwdLayout {
-  size_t header, items_q, items_k, dvec, tile_base, part, total;
+  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, total;
   int64_t max_q_items, max_k_items, max_qtiles;
 };
 
@@ -81,9 +81,14 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   L.dvec = L.items_k + align_up((size_t)L.max_k_items * sizeof(Item));
   L.tile_base = L.dvec + align_up((size_t)p->total_q * p->H * sizeof(float));
   L.part = L.tile_base + align_up((size_t)(p->B + 1) * sizeof(int32_t));
+  L.part_bh = L.part;
   L.total = L.part;
-  if (p->bias_buckets > 0)
-    L.total += align_up((size_t)L.max_qtiles * p->H * p->bias_buckets * sizeof(float));
+  if (p->bias_buckets > 0) {
+    // one partial row per 32-query row block and head, then one per sample and head
+    const size_t rows = (size_t)L.max_qtiles * (tq / 32);
+    L.part_bh = L.part + align_up(rows * p->H * p->bias_buckets * sizeof(float));
+    L.total = L.part_bh + align_up((size_t)p->B * p->H * p->bias_buckets * sizeof(float));
+  }
   return L;
 }
 
@@ -259,17 +264,15 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
   sa.ws_header = ws + L.header;
-  // query-tile items (dQ, D, bias partials)
-  sa.mode = SCHED_QTILES; sa.tile_item = tq; sa.tile_loop = bwd_k_loop(p->dtype);
-  sa.max_items = (int)L.max_q_items; sa.list = 0;
-  sa.tile_base = (int32_t*)(ws + L.tile_base); sa.items = ws + L.items_q;
-  hipError_t e = launch_sched(sa, s);
-  if (e != hipSuccess) return map_hip(e);
-  // key-tile items (dK, dV)
-  sa.mode = SCHED_KTILES; sa.tile_item = tk; sa.tile_loop = bwd_q_loop(p->dtype);
-  sa.max_items = (int)L.max_k_items; sa.list = 1;
-  sa.tile_base = nullptr; sa.items = ws + L.items_k;
-  e = launch_sched(sa, s);
+  // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
+  SchedArgs sq = sa, sk = sa;
+  sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
+  sq.max_items = (int)L.max_q_items; sq.list = 0;
+  sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
+  sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
+  sk.max_items = (int)L.max_k_items; sk.list = 1;
+  sk.tile_base = nullptr; sk.items = ws + L.items_k;
+  hipError_t e = launch_sched2(sq, sk, s);
   if (e != hipSuccess) return map_hip(e);
 
   BwdArgs ba;
@@ -287,8 +290,9 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   if (p->bias_buckets > 0) {
     DbiasArgs da;
     da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
-    da.part = ba.dbias_part; da.dbias = dbias; da.hdr = ws + L.header;
-    da.B = p->B; da.H = p->H; da.nb = p->bias_buckets; da.tile_rows = tq;
+    da.part = ba.dbias_part; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
+    da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
+    da.causal = p->causal; da.tile_rows = tq; da.loop_rows = bwd_k_loop(p->dtype);
     e = launch_dbias_reduce(da, s);
   }
   return map_hip(e);

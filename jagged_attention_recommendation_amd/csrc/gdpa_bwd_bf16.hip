@@ -52,14 +52,27 @@ __device__ __forceinline__ float dscore(float s2, float s, float lse2, float Di,
 
 // ------------------------------------------------------------------------------------------
 // dQ
+//
+// Bias gradient inside this kernel. A wave's 32 x 64 block of dS (queries a, keys c) has 95
+// diagonals d = a - c in [-63, 31]. The wave writes the block to its own LDS buffer, then every
+// lane sums exactly 32 elements: lane 31 + t (t = 0..32) the full diagonal d = t - 32, and lane
+// t < 31 the two short diagonals d = t - 63 and d = t + 1. A diagonal with d < -32 continues in
+// the next key tile as d + 64 - the same lane's second diagonal - so lane t keeps it in a
+// register and adds it there. After each tile the 64 diagonals that no later tile reaches are
+// complete and are written once to the wave's partial row in global memory. Every sum is formed
+// in a fixed order; diagonals that clamp to the table's ends are combined by a fixed-order wave
+// reduction.
+constexpr int DSP = 68;  // floats per row of a wave's dS buffer (16-byte aligned rows)
+
 template <int D, int ACT, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   using T = Tile<D>;
-  constexpr int DSP = KL + 1;  // dS staging pitch (floats)
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + (BIAS ? QI * DSP * 4 : 0)];
+  constexpr int BIAS_BYTES = BIAS ? BIAS_WMAX * 4 + 4 * 32 * DSP * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + BIAS_BYTES];
   GDPA_LDS char* Ks = (GDPA_LDS char*)smem;
   GDPA_LDS char* Vs = Ks + T::BYTES;
-  GDPA_LDS float* dSs = (GDPA_LDS float*)(Vs + T::BYTES);
+  GDPA_LDS float* bwin = (GDPA_LDS float*)(Vs + T::BYTES);
+  GDPA_LDS float* dsbuf_all = bwin + BIAS_WMAX;  // [wave][32][DSP]
 
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
@@ -67,7 +80,8 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   const int b = it.b, h = it.h, H = a.H, nb = a.nb;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int i0 = it.tile * QI;
   const int wrow = i0 + w * 32;
   const int iq = wrow + l32;
@@ -107,22 +121,48 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
   if (i0 >= Lq) nkt = 0;
 
-  float* part = nullptr;
-  if (BIAS) {
-    part = a.dbias_part + ((int64_t)it.aux * H + h) * nb;
-    if (Lk > 0 && i0 < Lq) {
-      const int c_lo = clampi(i0 - (Lk - 1), 0, nb - 1);
-      const int c_hi = clampi(min(Lq, i0 + QI) - 1, 0, nb - 1);
-      for (int c = c_lo + ((tid - c_lo % NT) % NT + NT) % NT; c <= c_hi; c += NT) part[c] = 0.0f;
-    }
-  }
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  const float bmul = ACT == ACT_SOFTMAX ? LOG2E : 1.0f;
+  int w_hi = 0;
+  bool win_ok = false;
+  GDPA_LDS float* dsbuf = dsbuf_all + w * 32 * DSP;
+  float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
+  float* part = nullptr;
+  float e_lo = 0.0f, e_hi = 0.0f;
+  bool has_lo = false, has_hi = false;
+  if (BIAS) {
+    part = a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb;
+  }
+  // Writes the complete diagonal d of this wave (value v) to its partial row; the ends of the
+  // table collect every diagonal that clamps to them, summed over the wave in a fixed order.
+  // Under causal masking diagonals d < 0 hold only masked (zero) entries and are skipped.
+  auto emit = [&](int d, float v, bool valid) {
+    if (CAUSAL && d < 0) valid = false;
+    const bool lo = valid && d <= 0;
+    const bool hi = valid && !lo && d >= nb - 1;
+    if (valid && !lo && !hi) part[d] = v;
+    const uint64_t blo = __builtin_amdgcn_ballot_w64(lo), bhi = __builtin_amdgcn_ballot_w64(hi);
+    if (blo != 0) {
+      e_lo += wave_sum(lo ? v : 0.0f);
+      has_lo = true;
+    }
+    if (bhi != 0) {
+      e_hi += wave_sum(hi ? v : 0.0f);
+      has_hi = true;
+    }
+  };
+  int k0_last = -1;
 
   TileLoader<D, NT> lk_, lv_;
   if (nkt > 0) {
     lk_.load((const __bf16*)a.K, 0, Lk, kv0, H, h, tid);
     lv_.load((const __bf16*)a.V, 0, Lk, kv0, H, h, tid);
+  }
+  if (BIAS && nkt > 0) {  // staged while the first tile's loads are in flight
+    w_hi = i0 + QI - 1;  // raw diagonals iq - j: iq in [i0, i0 + QI), j in [0, nkt * KL)
+    win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
+                 bwin, bias_h, nb, i0 - (nkt * KL - 1), w_hi, true, bmul, tid, NT)) != 0;
   }
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
@@ -134,78 +174,128 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
       lv_.load((const __bf16*)a.V, (kt + 1) * KL, Lk, kv0, H, h, tid);
     }
     const int k0 = kt * KL;
-    const bool skip = !wave_active || (CAUSAL && k0 > wrow + 31);
-    f32x16 ds_acc[2];
-    if (!skip) {
-      f32x16 dp_acc[2];
+    if (!wave_active || (CAUSAL && k0 > wrow + 31)) continue;
+    k0_last = k0;
+    f32x16 ds_acc[2], dp_acc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        ds_acc[kb] = f32x16{};
-        dp_acc[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      ds_acc[kb] = f32x16{};
+      dp_acc[kb] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          ds_acc[kb] = mfma32(tile_row_op<D>(Ks, kb * 32, s, lane), qop[s], ds_acc[kb]);
-          dp_acc[kb] = mfma32(tile_row_op<D>(Vs, kb * 32, s, lane), doop[s], dp_acc[kb]);
-        }
+      for (int s = 0; s < D / 16; ++s) {
+        ds_acc[kb] = mfma32(tile_row_op<D>(Ks, kb * 32, s, lane), qop[s], ds_acc[kb]);
+        dp_acc[kb] = mfma32(tile_row_op<D>(Vs, kb * 32, s, lane), doop[s], dp_acc[kb]);
       }
-      const bool need_mask = (k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow);
+    }
+    const bool need_mask = (k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow);
+    // scores in place: x = s * scale (* log2 e for softmax) + bias of diagonal iq - j
+    const float sc = ACT == ACT_SOFTMAX ? sl2 : a.scale;
+    if (BIAS) {
+      if (win_ok) {
+        const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + 4 * g);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-          float bij = 0.0f;
-          if (BIAS) bij = bias_h[clampi(iq - j, 0, nb - 1)];
-          const float sraw = ds_acc[kb][r];
-          float p;
-          float ds = dscore<ACT>(sraw * sl2 + bij * LOG2E, sraw * a.scale + bij, lse2, Di,
-                                 dp_acc[kb][r], p);
-          if (!qv || (need_mask && (j >= Lk || (CAUSAL && j > iq)))) ds = 0.0f;
-          ds_acc[kb][r] = ds;
-        }
+          for (int r = 0; r < 16; ++r) ds_acc[kb][r] = ds_acc[kb][r] * sc + bp[kb * 32 + (r >> 2) * 8 + (r & 3)];
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            ds_acc[kb][r] = ds_acc[kb][r] * sc +
+                            bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, nb - 1)] * bmul;
       }
-      // dQ^T += K^T dS^T
+    } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) ds_acc[kb] *= sc;
+    }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float tmp[8];
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) tmp[e] = ds_acc[kb][8 * s2 + e];
-          const bf16x8 dsb = pack8(tmp);
-#pragma unroll
-          for (int n = 0; n < D / 32; ++n)
-            dq[n] = mfma32(tile_tr_op<D>(Ks, kb * 32 + 16 * s2, n, lane), dsb, dq[n]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
+        const float x = ds_acc[kb][r];
+        float p;
+        float ds = dscore<ACT>(x, x, lse2, Di, dp_acc[kb][r], p);
+        if (!qv || (need_mask && (j >= Lk || (CAUSAL && j > iq)))) ds = 0.0f;
+        ds_acc[kb][r] = ds;
       }
     }
     if (BIAS) {
-      // stage dS (fp32) of the whole 128 x 64 tile; rows of idle waves are zero
+      // dS block -> LDS (row = query a, column = key c; registers 4m..4m+3 are 4 consecutive keys)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          dSs[(w * 32 + l32) * DSP + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)] =
-              skip ? 0.0f : ds_acc[kb][r];
-      __syncthreads();
-      // owner thread of clamped diagonal c is c % NT; it sums every raw diagonal rr = i - j of
-      // the tile that clamps to c, in a fixed order
-      int rr_lo = i0 - (k0 + KL - 1);
-      const int rr_hi = i0 + QI - 1 - k0;
-      if (CAUSAL) rr_lo = max(rr_lo, 0);
-      if (rr_lo <= rr_hi) {
-        const int c_lo = clampi(rr_lo, 0, nb - 1), c_hi = clampi(rr_hi, 0, nb - 1);
-        for (int c = c_lo + ((tid - c_lo % NT) % NT + NT) % NT; c <= c_hi; c += NT) {
-          const int a_lo = c == 0 ? rr_lo : c;
-          const int a_hi = c == nb - 1 ? rr_hi : c;
-          float acc = 0.0f;
-          for (int rr = max(a_lo, rr_lo); rr <= min(a_hi, rr_hi); ++rr) {
-            const int d0 = rr - (i0 - k0);  // ii - jj
-            const int ii_lo = max(0, d0), ii_hi = min(QI - 1, KL - 1 + d0);
-            for (int ii = ii_lo; ii <= ii_hi; ++ii) acc += dSs[ii * DSP + (ii - d0)];
-          }
-          part[c] += acc;
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 v4 = {ds_acc[kb][4 * m], ds_acc[kb][4 * m + 1], ds_acc[kb][4 * m + 2],
+                            ds_acc[kb][4 * m + 3]};
+          *(GDPA_LDS f32x4*)(dsbuf + l32 * DSP + kb * 32 + m * 8 + 4 * g) = v4;
         }
+    }
+    // dS^T as bf16 B operands (registers 8*s2..8*s2+7 of block kb), then dQ^T += K^T dS^T
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float tmp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmp[e] = ds_acc[kb][8 * s2 + e];
+        dsb[kb][s2] = pack8(tmp);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+          dq[n] = mfma32(tile_tr_op<D>(Ks, kb * 32 + 16 * s2, n, lane), dsb[kb][s2], dq[n]);
+    if (BIAS) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Lane 31 + t sums diagonal t - 32 (rows 0..31); lane t < 31 sums diagonal t - 63 (rows
+      // 0..t) and then diagonal t + 1 (rows t + 1..31). In both cases step s reads row s,
+      // column (s + 63 - lane) mod 64, and the second diagonal starts where the column wraps.
+      // All 64 lanes read one row at distinct columns: no bank conflicts.
+      float s_a = 0.0f, s_b = 0.0f;
+#pragma unroll
+      for (int a8 = 0; a8 < 32; a8 += 8) {  // 8 reads in flight, then their sums
+        float vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (a8 + e + 63 - lane < 64) s_a += vv[e]; else s_b += vv[e];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // complete after this tile: lanes t < 31 emit d = t + 1 (with the carried part), the
+      // others emit d = lane - 63; absolute diagonal = wrow - k0 + d
+      float v;
+      int dabs;
+      if (lane < 31) {
+        v = carry + s_b;
+        carry = s_a;
+        dabs = wrow - k0 + lane + 1;
+      } else {
+        v = s_a;
+        dabs = wrow - k0 + lane - 63;
+      }
+      emit(dabs, v, true);
+    }
+  }
+  if (BIAS && k0_last >= 0) {
+    // the 31 carried diagonals d = t - 63 of the last tile
+    emit(wrow - k0_last + lane - 63, carry, lane < 31);
+    if (lane == 0) {
+      if (nb == 1) {
+        if (has_lo || has_hi) part[0] = e_lo + e_hi;
+      } else {
+        if (has_lo) part[0] = e_lo;
+        if (has_hi) part[nb - 1] = e_hi;
       }
     }
   }
@@ -220,11 +310,12 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
 template <int D, int ACT, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + 2 * QL * 4];
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + 2 * QL * 4 + (BIAS ? BIAS_WMAX * 4 : 0)];
   GDPA_LDS char* Qs = (GDPA_LDS char*)smem;
   GDPA_LDS char* dOs = Qs + T::BYTES;
   GDPA_LDS float* lse_s = (GDPA_LDS float*)(dOs + T::BYTES);
   GDPA_LDS float* D_s = lse_s + QL;
+  GDPA_LDS float* bwin = D_s + QL;
 
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items2) return;
@@ -232,7 +323,8 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
   const int b = it.b, h = it.h, H = a.H, nb = a.nb;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int j0 = it.tile * KI;
   const int wkey = j0 + w * 32;
   const int jk = wkey + l32;
@@ -256,6 +348,11 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
   const int qt0 = CAUSAL ? j0 / QL : 0;
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  // bias window in natural order (bwin[t] = bias[w_lo + t]), pre-multiplied by log2(e) for
+  // softmax: a lane's 16 lookups are one base address plus constant offsets
+  const float bmul = ACT == ACT_SOFTMAX ? LOG2E : 1.0f;
+  int w_lo = 0;
+  bool win_ok = false;
 
   TileLoader<D, NT> lq_, ldo_;
   float st_lse = 0.0f, st_d = 0.0f;
@@ -273,6 +370,12 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
     }
   };
   if (qt0 < nqt && j0 < Lk) load_q(qt0);
+  if (BIAS && qt0 < nqt && j0 < Lk) {  // staged while the first tile's loads are in flight
+    // raw diagonals i - jk: i in [qt0 * QL, nqt * QL), jk in [j0, j0 + KI)
+    w_lo = qt0 * QL - (j0 + KI - 1);
+    win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
+                 bwin, bias_h, nb, w_lo, nqt * QL - 1 - j0, false, bmul, tid, NT)) != 0;
+  }
   for (int qt = qt0; qt < nqt && j0 < Lk; ++qt) {
     __syncthreads();
     lq_.store(Qs, tid);
@@ -287,42 +390,59 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
     if (!wave_active) continue;
     if (CAUSAL && i0 + QL - 1 < wkey) continue;  // every query of the tile precedes every key
     const bool need_mask = (i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31);
-#pragma unroll
+#pragma unroll 1  // rolled: unrolling makes the register allocator spill
     for (int qb = 0; qb < 2; ++qb) {
+      __builtin_amdgcn_sched_barrier(0);  // keep each 32-query block's loads inside its block
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
         sacc = mfma32(tile_row_op<D>(Qs, qb * 32, s, lane), kop[s], sacc);
         dpacc = mfma32(tile_row_op<D>(dOs, qb * 32, s, lane), vop[s], dpacc);
       }
-      // register r holds query i0 + qb*32 + (r/4)*8 + 4g + r%4 for this lane's key jk
-      float pv[16], dsv[16];
+      // scores in place: x = s * scale (* log2 e for softmax) + bias of diagonal i - jk, query
+      // i = i0 + qb*32 + (r/4)*8 + 4g + r%4 for register r
+      const float sc = ACT == ACT_SOFTMAX ? sl2 : a.scale;
+      if (BIAS) {
+        if (win_ok) {
+          const GDPA_LDS float* bp = bwin + (i0 + qb * 32 + 4 * g - jk - w_lo);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int ql = qb * 32 + r4 * 8 + 4 * g;
-        const f32x4 l4 = *(const GDPA_LDS f32x4*)(lse_s + ql);
-        const f32x4 d4 = *(const GDPA_LDS f32x4*)(D_s + ql);
+          for (int r = 0; r < 16; ++r) sacc[r] = sacc[r] * sc + bp[(r >> 2) * 8 + (r & 3)];
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const int i = i0 + ql + e;
-          float bij = 0.0f;
-          if (BIAS) bij = bias_h[clampi(i - jk, 0, nb - 1)];
-          float p;
-          float ds = dscore<ACT>(sacc[r] * sl2 + bij * LOG2E, sacc[r] * a.scale + bij, l4[e], d4[e],
-                                 dpacc[r], p);
-          if (need_mask && (i >= Lq || !kvalid || (CAUSAL && jk > i))) {
-            p = 0.0f;
-            ds = 0.0f;
-          }
-          pv[r] = p;
-          dsv[r] = ds;
+          for (int r = 0; r < 16; ++r)
+            sacc[r] = sacc[r] * sc +
+                      bias_h[clampi(i0 + qb * 32 + (r >> 2) * 8 + 4 * g + (r & 3) - jk, 0, nb - 1)] * bmul;
         }
+      } else {
+        sacc *= sc;
       }
-#pragma unroll
+      // 8 queries at a time: probabilities and score gradients, then their two products
+#pragma unroll 1  // rolled: unrolling makes the register allocator spill
       for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 pb = pack8(&pv[8 * s2]);
-        const bf16x8 dsb = pack8(&dsv[8 * s2]);
+        __builtin_amdgcn_sched_barrier(0);
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int h4 = 0; h4 < 2; ++h4) {
+          const int r4 = 2 * s2 + h4;
+          const int ql = qb * 32 + r4 * 8 + 4 * g;
+          const f32x4 l4 = *(const GDPA_LDS f32x4*)(lse_s + ql);
+          const f32x4 d4 = *(const GDPA_LDS f32x4*)(D_s + ql);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            const int i = i0 + ql + e;
+            float p;
+            float ds = dscore<ACT>(sacc[r], sacc[r], l4[e], d4[e], dpacc[r], p);
+            if (need_mask && (i >= Lq || !kvalid || (CAUSAL && jk > i))) {
+              p = 0.0f;
+              ds = 0.0f;
+            }
+            pv[4 * h4 + e] = p;
+            dsv[4 * h4 + e] = ds;
+          }
+        }
+        const bf16x8 pb = pack8(pv);
+        const bf16x8 dsb = pack8(dsv);
 #pragma unroll
         for (int n = 0; n < D / 32; ++n) {
           dv[n] = mfma32(tile_tr_op<D>(dOs, qb * 32 + 16 * s2, n, lane), pb, dv[n]);

@@ -141,16 +141,25 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
   }
   int nkt = (Lk + TN - 1) / TN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + TM) - 1) / TN + 1);
-  // Bias gradient: this item owns the row part[tile, h, :] (tile = canonical query-tile index in
-  // it.aux). Diagonal c of that row belongs to thread c % 64, which zeroes it here and later adds
-  // every contribution to it in a fixed order.
+  // Bias gradient: the item's two 32-query row blocks own the partial rows
+  // part[2 * tile + q, h, :] (tile = canonical query-tile index in it.aux). Diagonal c of a row
+  // belongs to thread c % 64, which zeroes it here and later adds every contribution to it in a
+  // fixed order. A row block's written range is the clamp of its raw diagonal range
+  // [32rb - (k_end - 1), 32rb + 31], k_end = keys up to the last tile it can see.
   const int nb = a.nb;
-  float* part = nullptr;
+  float* part[2] = {nullptr, nullptr};
   if (BIAS) {
-    part = a.dbias_part + ((int64_t)it.aux * H + h) * nb;
-    if (Lk > 0 && i0 < Lq) {
-      const int c_lo = clampi(i0 - (Lk - 1), 0, nb - 1), c_hi = clampi(min(Lq, i0 + TM) - 1, 0, nb - 1);
-      for (int c = c_lo + ((tid - c_lo % 64) + 64) % 64; c <= c_hi; c += 64) part[c] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      part[q] = a.dbias_part + ((int64_t)(it.aux * 2 + q) * H + h) * nb;
+      const int wr = i0 + 32 * q;
+      if (Lk > 0 && wr < Lq) {
+        int last = nkt - 1;
+        if (CAUSAL) last = min(last, (wr + 31) / TN);
+        const int c_lo = clampi(wr - (last + 1) * TN + 1, 0, nb - 1);
+        const int c_hi = clampi(wr + 31, 0, nb - 1);
+        for (int c = c_lo + ((tid - c_lo % 64) + 64) % 64; c <= c_hi; c += 64) part[q][c] = 0.0f;
+      }
     }
   }
   for (int kt = 0; kt < nkt; ++kt) {
@@ -179,22 +188,28 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
     }
     if (BIAS) {
       __syncthreads();
-      // Owner thread of clamped diagonal c is c % 64; each owner sums, in a fixed order, every
-      // raw diagonal rr = i - j of this 64x64 tile that clamps to c.
+      // Owner thread of clamped diagonal c is c % 64; per row block it sums, in a fixed order,
+      // every raw diagonal rr = i - j of its 32 x 64 part of the tile that clamps to c.
       const int j0 = kt * TN;
-      const int rr_lo = i0 - (j0 + TN - 1), rr_hi = i0 + TM - 1 - j0;
-      const int c_lo = clampi(rr_lo, 0, nb - 1), c_hi = clampi(rr_hi, 0, nb - 1);
-      for (int c = c_lo + ((tid - c_lo % 64) + 64) % 64; c <= c_hi; c += 64) {
-        const int a_lo = c == 0 ? rr_lo : c;                 // raw diagonals mapping to c
-        const int a_hi = c == nb - 1 ? rr_hi : c;
-        float acc = 0.0f;
-        for (int rr = max(a_lo, rr_lo); rr <= min(a_hi, rr_hi); ++rr) {
-          // elements (ii, jj) with (i0 + ii) - (j0 + jj) = rr
-          const int d0 = rr - (i0 - j0);  // ii - jj
-          const int ii_lo = max(0, d0), ii_hi = min(TM - 1, TN - 1 + d0);
-          for (int ii = ii_lo; ii <= ii_hi; ++ii) acc += dS[ii][ii - d0];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int wr = i0 + 32 * q;
+        if (wr >= Lq) continue;
+        if (CAUSAL && j0 > wr + 31) continue;
+        const int rr_lo = wr - (j0 + TN - 1), rr_hi = wr + 31 - j0;
+        const int c_lo = clampi(rr_lo, 0, nb - 1), c_hi = clampi(rr_hi, 0, nb - 1);
+        for (int c = c_lo + ((tid - c_lo % 64) + 64) % 64; c <= c_hi; c += 64) {
+          const int a_lo = c == 0 ? rr_lo : c;  // raw diagonals mapping to c
+          const int a_hi = c == nb - 1 ? rr_hi : c;
+          float acc = 0.0f;
+          for (int rr = max(a_lo, rr_lo); rr <= min(a_hi, rr_hi); ++rr) {
+            // elements (ii, jj), ii in this row block, with (i0 + ii) - (j0 + jj) = rr
+            const int d0 = rr - (i0 - j0);  // ii - jj
+            const int ii_lo = max(32 * q, d0), ii_hi = min(32 * q + 31, TN - 1 + d0);
+            for (int ii = ii_lo; ii <= ii_hi; ++ii) acc += dS[ii][ii - d0];
+          }
+          part[q][c] += acc;
         }
-        part[c] += acc;
       }
     }
   }

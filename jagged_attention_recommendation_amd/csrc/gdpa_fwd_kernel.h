@@ -61,15 +61,17 @@ struct Smem {
   static constexpr int KMX_P = 144;
   static constexpr int K_BYTES = MX ? BN * KMX_P + BN * 4 : Tile<D>::BYTES;
   static constexpr int V_BYTES = Tile<D>::BYTES;
+  static constexpr int BIAS_BYTES = BIAS_WMAX * 4;
 };
 
 template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   static_assert(!MX || D == 128, "MX path is for D = 128");
   using S = Smem<D, MX>;
-  __shared__ __attribute__((aligned(16))) char smem[S::K_BYTES + S::V_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[S::K_BYTES + S::V_BYTES + (BIAS ? S::BIAS_BYTES : 0)];
   GDPA_LDS char* Ks = (GDPA_LDS char*)smem;
   GDPA_LDS char* Vs = Ks + S::K_BYTES;
+  GDPA_LDS float* bwin = (GDPA_LDS float*)(Vs + S::V_BYTES);
 
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   const int b = it.b, h = it.h, H = a.H;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
   const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int row_blk = it.tile * BM;   // first query of the item (local index)
   const int wrow = row_blk + w * 32;  // first query of this wave
   const int iq = wrow + l32;          // this lane's query
@@ -120,6 +123,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
+  // Bias window for this item, reversed (bwin[t] = bias[w_hi - t]) and pre-multiplied by log2(e)
+  // for softmax, so that the 16 lookups of a lane are one base address plus constant offsets.
+  const float bmul = ACT == ACT_SOFTMAX ? LOG2E : 1.0f;
+  int w_hi = 0;
+  bool win_ok = false;
 
   // ---- global -> register staging of one K/V tile
   TileLoader<D, NT> lk_, lv_;           // bf16 path
@@ -176,6 +184,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   };
 
   if (nkt > 0) load_tile(0);
+  if (BIAS && nkt > 0) {  // staged while the first tile's loads are in flight
+    // raw diagonals iq - j of the item: iq in [row_blk, row_blk + BM), j in [0, nkt * BN)
+    w_hi = row_blk + BM - 1;
+    win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
+                 bwin, bias_h, a.nb, row_blk - (nkt * BN - 1), w_hi, true, bmul, tid, NT)) != 0;
+  }
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
     store_tile();
@@ -214,6 +228,29 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
 
     // ---- scores -> probabilities (register r of block kb is key k0 + kb*32 + (r/4)*8 + 4g + r%4)
     const bool need_mask = (k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow);
+    __builtin_amdgcn_sched_barrier(0);  // bias lookups after the products
+    // scores in place: x = s * scale (* log2 e for softmax) + bias of diagonal iq - j,
+    // j = k0 + kb*32 + (r/4)*8 + 4g + r%4 for register r of block kb
+    const float sc = ACT == ACT_SOFTMAX ? sl2 : a.scale;
+    if (BIAS) {
+      if (win_ok) {
+        const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + 4 * g);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = sacc[kb][r] * sc + bp[kb * 32 + (r >> 2) * 8 + (r & 3)];
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = sacc[kb][r] * sc +
+                          bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, a.nb - 1)] * bmul;
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] *= sc;
+    }
     float p[2][16];
     if (ACT == ACT_SOFTMAX) {
       float mt = -INFINITY;
@@ -222,8 +259,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-          float x = sacc[kb][r] * sl2;
-          if (BIAS) x += bias_h[clampi(iq - j, 0, a.nb - 1)] * LOG2E;
+          float x = sacc[kb][r];
           if (need_mask && (j >= Lk || (CAUSAL && j > iq))) x = -INFINITY;
           p[kb][r] = x;
           mt = fmaxf(mt, x);
@@ -252,9 +288,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-          float x = sacc[kb][r] * a.scale;
-          if (BIAS) x += bias_h[clampi(iq - j, 0, a.nb - 1)];
-          float y = act_fwd(ACT, x);
+          float y = act_fwd(ACT, sacc[kb][r]);
           if (need_mask && (j >= Lk || (CAUSAL && j > iq))) y = 0.0f;
           p[kb][r] = y;
         }

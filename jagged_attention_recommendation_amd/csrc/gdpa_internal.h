@@ -34,17 +34,23 @@ struct SchedArgs {
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);
 
-// dbias[h, r] = sum over samples b and their query tiles t (canonical order) of the tile's
-// partial row, for every r the tile can reach. tile_rows = query rows per tile.
+// Bias gradient reduction. The dQ kernels write, per (32-query row block, head), the diagonal
+// sums of dS its queries produced (one row of NB floats, canonical row order); the reduction sums
+// them per sample in row-block order (stage A, into part_bh [B, H, NB]) and then over samples in
+// order (stage B).
 struct DbiasArgs {
   const int32_t* q_off;
   const int32_t* kv_off;
   const int32_t* tile_base;
   const float* part;
+  float* part_bh;
   float* dbias;
   const void* hdr;
-  int B, H, nb, tile_rows;
+  int B, H, nb, causal;
+  int tile_rows;  // queries per dQ item
+  int loop_rows;  // keys per dQ loop tile
 };
 hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s);
 
@@ -77,6 +83,9 @@ constexpr int FWD_BN_BF16 = 64;
 constexpr int F32_BM = 64;
 constexpr int F32_BN = 64;
 
+// Largest bias window (floats) a kernel stages in LDS; wider windows are read from global memory.
+constexpr int BIAS_WMAX = 4096;
+
 hipError_t launch_fwd_bf16(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_fwd_mx(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_fwd_f32(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
@@ -99,7 +108,7 @@ struct BwdArgs {
   const void* hdr;
   const void* items_q;   // query-tile items (dQ)
   const void* items_k;   // key-tile items (dK/dV)
-  float* dbias_part;     // [n_qtiles, H, NB] per query-tile diagonal sums of dS (canonical order)
+  float* dbias_part;     // [n_rowblocks, H, NB] per 32-query row block diagonal sums of dS
   const int32_t* tile_base;  // [B + 1] canonical index of each sample's first query tile
   int H, nb;
   float scale;

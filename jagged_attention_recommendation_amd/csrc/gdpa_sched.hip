@@ -1,23 +1,26 @@
-// Jagged work scheduler.
+// Jagged work scheduler and the bias-gradient reduction.
 //
 // Short sequences must not leave compute units idle while long ones finish (page "GEM Training:
 // How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA paragraph; the GDPA
 // paragraph adds that short or asymmetric K/V and large batches break occupancy assumptions and
-// that scheduling was redesigned). This kernel turns the offsets into a list of equal-shaped work
-// items, one per (sample, head, tile), sorted by decreasing cost: the cost of an item is the
-// number of inner-loop tiles it visits (all key tiles, or only those with j <= i under causal
-// masking). Workgroups are handed out by the hardware in index order, so the longest items start
-// first and short ones fill the gaps at the end (longest-processing-time-first list scheduling).
+// that scheduling was redesigned). The scheduler turns the offsets into a list of equal-shaped
+// work items, one per (sample, head, tile), sorted by decreasing cost: the cost of an item is the
+// number of inner-loop tiles it visits (all tiles, or only those allowed by causal masking).
+// Workgroups are handed out by the hardware in index order, so the longest items start first
+// and short ones fill the gaps at the end (longest-processing-time-first list scheduling).
 //
-// One workgroup of 1024 threads: validate offsets, histogram costs, scan, scatter. The relative
-// order of equal-cost items is not fixed, which cannot change results: every item computes its
-// outputs on its own.
+// One workgroup of 1024 threads per list (the backward builds its query-tile and key-tile lists
+// in one launch). Samples are walked in chunks of 1024: a scan of their tile counts gives each
+// tile a canonical index, threads then take tiles (not samples) so long samples do not serialise.
+// The relative order of equal-cost items is not fixed, which cannot change results: every item
+// computes its outputs on its own.
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
 
 namespace gdpa {
 
 constexpr int NBUCKET = 1024;
+constexpr int SNT = 1024;
 
 __device__ __forceinline__ int item_cost(int mode, int causal, int Lq, int Lk, int t, int ti,
                                          int tl) {
@@ -36,16 +39,29 @@ __device__ __forceinline__ int item_cost(int mode, int causal, int Lq, int Lk, i
   return nq - j0 / tl;
 }
 
-__global__ __launch_bounds__(1024) void sched_kernel(SchedArgs a) {
+// In-place inclusive scan of SNT ints in LDS (all threads participate).
+__device__ __forceinline__ void block_scan(int* buf, int tid) {
+  for (int off = 1; off < SNT; off <<= 1) {
+    __syncthreads();
+    int add = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += add;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) {
+  const SchedArgs& a = blockIdx.x == 0 ? a0 : a1;
   __shared__ int bucket[NBUCKET];
-  __shared__ int err;
+  __shared__ int cnt[SNT];  // inclusive scan of the chunk's per-sample tile counts
+  __shared__ int err, carry;
   const int tid = threadIdx.x;
   WsHeader* hdr = (WsHeader*)a.ws_header;
   Item* items = (Item*)a.items;
-  for (int i = tid; i < NBUCKET; i += blockDim.x) bucket[i] = 0;
+  for (int i = tid; i < NBUCKET; i += SNT) bucket[i] = 0;
   if (tid == 0) err = 0;
   __syncthreads();
-  for (int b = tid; b < a.B; b += blockDim.x) {
+  for (int b = tid; b < a.B; b += SNT) {
     if (a.q_off[b + 1] < a.q_off[b]) atomicOr(&err, 1);
     if (a.kv_off[b + 1] < a.kv_off[b]) atomicOr(&err, 2);
   }
@@ -62,119 +78,153 @@ __global__ __launch_bounds__(1024) void sched_kernel(SchedArgs a) {
     return;
   }
   const int ti = a.tile_item, tl = a.tile_loop;
-  // 1. histogram of costs; bucket index NBUCKET-1-cost puts expensive items first
-  for (int b = tid; b < a.B; b += blockDim.x) {
-    int Lq = a.q_off[b + 1] - a.q_off[b];
-    int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    int n = a.mode == SCHED_QTILES ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
-    for (int t = 0; t < n; ++t) {
-      int c = min(item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl), NBUCKET - 1);
-      atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
+  auto ntiles = [&](int b) {
+    const int Lq = a.q_off[b + 1] - a.q_off[b];
+    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+    return a.mode == SCHED_QTILES ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
+  };
+  // Walk the samples chunk by chunk; for every tile of the chunk call f(b, t, canonical index).
+  auto for_each_tile = [&](auto&& f) {
+    if (tid == 0) carry = 0;
+    for (int base = 0; base < a.B; base += SNT) {
+      const int b = base + tid;
+      const int n = b < a.B ? ntiles(b) : 0;
+      __syncthreads();
+      cnt[tid] = n;
+      block_scan(cnt, tid);
+      const int total = cnt[SNT - 1];
+      const int first = carry;
+      for (int u = tid; u < total; u += SNT) {
+        // sample of tile u: first index k with cnt[k] > u
+        int lo = 0, hi = SNT - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (cnt[mid] > u) hi = mid; else lo = mid + 1;
+        }
+        const int t = u - (lo > 0 ? cnt[lo - 1] : 0);
+        f(base + lo, t, first + u);
+      }
+      if (a.tile_base != nullptr && b < a.B) a.tile_base[b] = first + cnt[tid] - n;
+      __syncthreads();
+      if (tid == 0) carry = first + total;
+      __syncthreads();
     }
-  }
+  };
+  // 1. histogram of costs; bucket NBUCKET-1-cost puts expensive items first
+  for_each_tile([&](int b, int t, int) {
+    const int Lq = a.q_off[b + 1] - a.q_off[b];
+    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+    const int c = min(item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl), NBUCKET - 1);
+    atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
+  });
   __syncthreads();
-  // 2. exclusive scan over the buckets (NBUCKET == blockDim.x)
-  int own = bucket[tid];
-  for (int off = 1; off < NBUCKET; off <<= 1) {
-    __syncthreads();
-    int add = tid >= off ? bucket[tid - off] : 0;
-    __syncthreads();
-    bucket[tid] += add;
-  }
-  __syncthreads();
-  int total = bucket[NBUCKET - 1];
+  // 2. exclusive scan over the buckets (NBUCKET == SNT)
+  const int own = bucket[tid];
+  block_scan(bucket, tid);
+  const int total_items = bucket[NBUCKET - 1];
   __syncthreads();
   bucket[tid] -= own;
   __syncthreads();
-  // 3. scatter (b, tile, h) records. Samples are walked in chunks of blockDim.x; a scan of the
-  //    per-sample tile counts gives each sample's canonical first-tile index (tile_base), which
-  //    items carry in .aux.
-  __shared__ int cnt[NBUCKET];
-  __shared__ int carry;
-  if (tid == 0) carry = 0;
-  for (int base = 0; base < a.B; base += blockDim.x) {
-    const int b = base + tid;
-    int Lq = 0, Lk = 0, n = 0;
-    if (b < a.B) {
-      Lq = a.q_off[b + 1] - a.q_off[b];
-      Lk = a.kv_off[b + 1] - a.kv_off[b];
-      n = a.mode == SCHED_QTILES ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
-    }
-    __syncthreads();
-    cnt[tid] = n;
-    for (int off = 1; off < NBUCKET; off <<= 1) {
-      __syncthreads();
-      int add = tid >= off ? cnt[tid - off] : 0;
-      __syncthreads();
-      cnt[tid] += add;
-    }
-    __syncthreads();
-    const int first = carry + cnt[tid] - n;
-    if (b < a.B) {
-      if (a.tile_base != nullptr) a.tile_base[b] = first;
-      for (int t = 0; t < n; ++t) {
-        int cost = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
-        int c = min(cost, NBUCKET - 1);
-        int pos = atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
-        for (int h = 0; h < a.H; ++h) {
-          if (pos + h < a.max_items) {
-            Item it;
-            it.b = b; it.tile = t; it.h = h; it.aux = first + t;
-            items[pos + h] = it;
-          }
-        }
+  // 3. scatter (b, tile, h, canonical tile index)
+  for_each_tile([&](int b, int t, int canon) {
+    const int Lq = a.q_off[b + 1] - a.q_off[b];
+    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+    const int c = min(item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl), NBUCKET - 1);
+    const int pos = atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
+    for (int h = 0; h < a.H; ++h) {
+      if (pos + h < a.max_items) {
+        Item it;
+        it.b = b; it.tile = t; it.h = h; it.aux = canon;
+        items[pos + h] = it;
       }
     }
-    __syncthreads();
-    if (tid == blockDim.x - 1) carry += cnt[tid];
-  }
-  __syncthreads();
+  });
   if (tid == 0) {
     if (a.tile_base != nullptr) a.tile_base[a.B] = carry;
     hdr->error = 0;
-    int n = min(total, a.max_items);
+    const int n = min(total_items, a.max_items);
     if (a.list == 0) hdr->n_items = n; else hdr->n_items2 = n;
   }
 }
 
-// One thread per (h, r): walks samples and their query tiles in canonical order and adds every
-// partial row entry that tile wrote for diagonal r.
-__global__ __launch_bounds__(256) void dbias_reduce_kernel(DbiasArgs a) {
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
+  prof_before(PROF_SCHED, s);
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SNT), 0, s, a, a);
+  prof_after(PROF_SCHED, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) {
+  prof_before(PROF_SCHED, s);
+  hipLaunchKernelGGL(sched_kernel, dim3(2), dim3(SNT), 0, s, a, b);
+  prof_after(PROF_SCHED, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Bias gradient, stage A: one thread per (sample, head, diagonal c) sums the partial rows of the
+// sample's 32-query row blocks in block order. Row block rb of sample b (queries 32rb..32rb+31)
+// is stored at canonical row (tile_base[b] + rb / R) * R + rb % R, R = row blocks per dQ item,
+// and wrote exactly the clamped
+// diagonals of its raw range [32rb - (k_end - 1), 32rb + 31], k_end = keys it visited; the edge
+// entries 0 and NB-1 collect every raw diagonal that clamps to them.
+__device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causal, int qi, int kl,
+                                               int& d_lo, int& d_hi) {
+  const int wrow = rb * 32;
+  if (wrow >= Lq || Lk <= 0) return false;
+  const int t = wrow / qi;  // item (query tile) of this row block
+  int nkt = (Lk + kl - 1) / kl;
+  if (causal) nkt = min(nkt, (min(Lq, (t + 1) * qi) - 1) / kl + 1);
+  int last = nkt - 1;
+  if (causal) last = min(last, (wrow + 31) / kl);  // tiles after the block's last query skipped
+  d_lo = wrow - (last + 1) * kl + 1;
+  d_hi = wrow + 31;
+  return true;
+}
+
+__global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= a.nb) return;
   const WsHeader* hdr = (const WsHeader*)a.hdr;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)a.H * a.nb) return;
-  const int h = (int)(idx / a.nb), r = (int)(idx % a.nb);
   float acc = 0.0f;
   if (hdr->error == 0) {
-    const int TMr = a.tile_rows, nb = a.nb;
-    for (int b = 0; b < a.B; ++b) {
-      const int Lq = a.q_off[b + 1] - a.q_off[b];
-      const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-      if (Lk <= 0) continue;
-      const int nt = (Lq + TMr - 1) / TMr;
-      const int tb = a.tile_base[b];
-      for (int t = 0; t < nt; ++t) {
-        const int i0 = t * TMr;
-        const int c_lo = clampi(i0 - (Lk - 1), 0, nb - 1);
-        const int c_hi = clampi(min(Lq, i0 + TMr) - 1, 0, nb - 1);
-        if (r >= c_lo && r <= c_hi) acc += a.part[((int64_t)(tb + t) * a.H + h) * nb + r];
-      }
+    const int Lq = a.q_off[b + 1] - a.q_off[b];
+    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+    const int nrb = (Lq + 31) / 32;
+    const int tb = a.tile_base[b];
+    const int nb = a.nb;
+    for (int rb = 0; rb < nrb; ++rb) {
+      int d_lo, d_hi;
+      if (!rowblock_range(rb, Lq, Lk, a.causal, a.tile_rows, a.loop_rows, d_lo, d_hi)) continue;
+      const int c_lo = clampi(d_lo, 0, nb - 1), c_hi = clampi(d_hi, 0, nb - 1);
+      if (c < c_lo || c > c_hi) continue;
+      const int per = a.tile_rows / 32;
+      const int64_t row = (int64_t)(tb + rb / per) * per + rb % per;
+      acc += a.part[(row * a.H + h) * nb + c];
     }
   }
+  a.part_bh[((int64_t)b * a.H + h) * a.nb + c] = acc;
+}
+
+// Stage B: dbias[h, c] = sum over samples in order.
+__global__ __launch_bounds__(256) void dbias_stage_b(DbiasArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.H * a.nb) return;
+  float acc = 0.0f;
+  for (int b = 0; b < a.B; ++b) acc += a.part_bh[(int64_t)b * a.H * a.nb + idx];
   a.dbias[idx] = acc;
 }
 
 hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.H * a.nb;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dbias_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
-  prof_before(PROF_SCHED, s);
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(NBUCKET), 0, s, a);
-  prof_after(PROF_SCHED, s);
+  if (a.B > 0) {
+    hipLaunchKernelGGL(dbias_stage_a, dim3(a.B * a.H, (a.nb + 255) / 256), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(dbias_stage_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #pragma once
 
 #include "gdpa_common.h"
+#include "gdpa_internal.h"
 
 namespace gdpa {
 
@@ -88,6 +89,20 @@ __device__ __forceinline__ void store_acc_row_bf16(__bf16* row, const f32x16& ac
     bf16x4 v4 = {lo[0], lo[1], hi[0], hi[1]};
     *(bf16x4*)(row + n * 32 + r4 * 8 + 4 * g) = v4;
   }
+}
+
+// Stage the bias of raw diagonals lo..hi (inclusive, unclamped: entry d holds
+// bias[h][clamp(d, 0, nb - 1)]) in LDS, multiplied by mul, reversed (win[t] = entry hi - t) or in
+// order (win[t] = entry lo + t), so lookups need no clamping. Returns false and stages nothing
+// when the window is empty or wider than BIAS_WMAX (the caller then reads the table from global
+// memory). The caller synchronises before reading.
+__device__ __forceinline__ bool stage_bias_window(GDPA_LDS float* win, const float* bias_h, int nb,
+                                                  int lo, int hi, bool reversed, float mul,
+                                                  int tid, int nt) {
+  const int n = hi - lo + 1;
+  if (n <= 0 || n > BIAS_WMAX) return false;
+  for (int t = tid; t < n; t += nt) win[t] = bias_h[clampi(reversed ? hi - t : lo + t, 0, nb - 1)] * mul;
+  return true;
 }
 
 }  // namespace gdpa
