@@ -61,7 +61,8 @@ typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1, GDPA_MXFP8_E4M3 = 2 } gdpa_dtype;
 typedef enum {
   GDPA_OK = 0,
   GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
-  GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX backward, ... */
+  GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX backward,
+                          scale <= 0 outside fp32, ... */
   GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
   GDPA_EHIP = 4        /* the HIP runtime refused a launch */
 } gdpa_status;
@@ -78,7 +79,7 @@ typedef struct {
   int32_t max_kv;       /* an upper bound on any Lk_b, or 0 if unknown; only tunes scheduling */
   int32_t act;          /* gdpa_act */
   int32_t causal;       /* 0 or 1: keep j <= i on local positions (top-left aligned) */
-  float scale;          /* s = scale * q.k (+ bias) */
+  float scale;          /* s = scale * q.k (+ bias); must be > 0 for GDPA_BF16 / GDPA_MXFP8_E4M3 */
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
 } gdpa_problem;
 

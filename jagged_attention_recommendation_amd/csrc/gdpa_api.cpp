@@ -28,6 +28,8 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->causal != 0 && p->causal != 1) return GDPA_EINVAL;
   if (p->bias_buckets < 0 || p->max_q < 0 || p->max_kv < 0) return GDPA_EINVAL;
   if (!isfinite(p->scale)) return GDPA_EINVAL;
+  // the bf16 and MX kernels take row maxima on unscaled scores, which needs scale > 0
+  if (p->dtype != GDPA_F32 && !(p->scale > 0.0f)) return GDPA_ENOTSUP;
   if (p->D != 32 && p->D != 64 && p->D != 128) return GDPA_ENOTSUP;
   if (p->dtype == GDPA_MXFP8_E4M3 && p->D != 128) return GDPA_ENOTSUP;
   // element counts must fit the kernels' 64-bit addressing and the scheduler's int32 counters

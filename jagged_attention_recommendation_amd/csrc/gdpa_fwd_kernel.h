@@ -123,9 +123,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
-  // Bias window for this item, reversed (bwin[t] = bias[w_hi - t]) and pre-multiplied by log2(e)
-  // for softmax, so that the 16 lookups of a lane are one base address plus constant offsets.
-  const float bmul = ACT == ACT_SOFTMAX ? LOG2E : 1.0f;
+  // Bias window for this item over raw diagonals, reversed (bwin[t] = bias[clamp(w_hi - t)]) and
+  // divided by scale, so that the 16 lookups of a lane are one base address plus constant
+  // offsets and can seed the score accumulators.
+  const float inv_scale = 1.0f / a.scale;  // the window holds bias / scale (see S^T below)
   int w_hi = 0;
   bool win_ok = false;
 
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     // raw diagonals iq - j of the item: iq in [row_blk, row_blk + BM), j in [0, nkt * BN)
     w_hi = row_blk + BM - 1;
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
-                 bwin, bias_h, a.nb, row_blk - (nkt * BN - 1), w_hi, true, bmul, tid, NT)) != 0;
+                 bwin, bias_h, a.nb, row_blk - (nkt * BN - 1), w_hi, true, inv_scale, tid, NT)) != 0;
   }
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
@@ -199,11 +200,28 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     if (!wave_active) continue;
     if (CAUSAL && k0 > wrow + 31) continue;  // every key of the tile is after every query
 
-    // ---- S^T = K Q^T for two 32-key blocks
+    // ---- S^T = K Q^T for two 32-key blocks. With a bias the accumulators start from
+    // bias / scale read straight from the LDS window (register r of block kb is key
+    // j = k0 + kb*32 + (r/4)*8 + 4g + r%4, diagonal iq - j), so the products land on top of it.
     f32x16 sacc[2];
+    if (BIAS && win_ok) {
+      const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = bp[kb * 32 + (r >> 2) * 8 + (r & 3)];
+    } else if (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, a.nb - 1)] * inv_scale;
+    } else {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
       if constexpr (!MX) {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
@@ -226,72 +244,68 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    // ---- scores -> probabilities (register r of block kb is key k0 + kb*32 + (r/4)*8 + 4g + r%4)
-    const bool need_mask = (k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow);
-    __builtin_amdgcn_sched_barrier(0);  // bias lookups after the products
-    // scores in place: x = s * scale (* log2 e for softmax) + bias of diagonal iq - j,
-    // j = k0 + kb*32 + (r/4)*8 + 4g + r%4 for register r of block kb
-    const float sc = ACT == ACT_SOFTMAX ? sl2 : a.scale;
-    if (BIAS) {
-      if (win_ok) {
-        const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + 4 * g);
+    // ---- scores -> probabilities. Masking is needed only on tiles that reach past the keys or
+    // past the wave's first query (causal); valid keys of block kb satisfy
+    // (r/4)*8 + 4g + r%4 < lim_kb.
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow))) != 0;
+    int lim[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = sacc[kb][r] * sc + bp[kb * 32 + (r >> 2) * 8 + (r & 3)];
-      } else {
+    for (int kb = 0; kb < 2; ++kb) {
+      int l = Lk - (k0 + kb * 32);
+      if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
+      lim[kb] = l - 4 * g;
+    }
+    float p[2][16];
+    if (ACT == ACT_SOFTMAX) {
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            sacc[kb][r] = sacc[kb][r] * sc +
-                          bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, a.nb - 1)] * bmul;
+            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) sacc[kb][r] = -INFINITY;
       }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] *= sc;
-    }
-    float p[2][16];
-    if (ACT == ACT_SOFTMAX) {
+      // row max on the raw accumulators (scale > 0 preserves order), then one fma + exp2
       float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-          float x = sacc[kb][r];
-          if (need_mask && (j >= Lk || (CAUSAL && j > iq))) x = -INFINITY;
-          p[kb][r] = x;
-          mt = fmaxf(mt, x);
-        }
+        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+      mt = half_max(mt) * sl2;
+      // The reference maximum m_run moves only when a row's maximum exceeds it by more than 8
+      // (log2 units), so probabilities stay below 2^8 and the running output is rescaled
+      // rarely; the final normalisation uses the same reference, so the result is unchanged.
+      const bool grow = mt > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) o[n] *= alpha;
+        m_run = m_new;
       }
-      mt = half_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
       float ls = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[kb][r] = fast_exp2(p[kb][r] - m_use);
+          p[kb][r] = fast_exp2(fmaf(sacc[kb][r], sl2, -m_use));
           ls += p[kb][r];
         }
       }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) o[n] *= alpha;
+      l_run += ls;
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3);
-          float y = act_fwd(ACT, sacc[kb][r]);
-          if (need_mask && (j >= Lk || (CAUSAL && j > iq))) y = 0.0f;
-          p[kb][r] = y;
-        }
+        for (int r = 0; r < 16; ++r) p[kb][r] = act_fwd(ACT, sacc[kb][r] * a.scale);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) p[kb][r] = 0.0f;
       }
     }
 
