@@ -1,4 +1,6 @@
-// Forward launches for bf16 inputs (kernel template in gdpa_fwd_kernel.h).
+// Forward launches for bf16 inputs: D = 128 uses the direct-load kernel (gdpa_fwd_dl.h), D = 32
+// and 64 the register-staged one (gdpa_fwd_kernel.h).
+#include "gdpa_fwd_dl.h"
 #include "gdpa_fwd_kernel.h"
 
 namespace gdpa {
@@ -8,7 +10,7 @@ hipError_t launch_fwd_bf16(const Prob& p, const FwdArgs& a, int grid, hipStream_
   switch (p.D) {
     case 32: return fwdk::launch_d<32, false>(p, a, grid, s);
     case 64: return fwdk::launch_d<64, false>(p, a, grid, s);
-    default: return fwdk::launch_d<128, false>(p, a, grid, s);
+    default: return fwddl::launch(p, a, grid, s);
   }
 }
 

@@ -1,0 +1,283 @@
+// Forward kernel for D = 128 bf16 with direct global -> LDS tile loads and a two-stage LDS ring.
+//
+// Same method and operand orientation as gdpa_fwd_kernel.h (JFA softmax / GDPA activation on
+// jagged tensors, page "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
+// Foundation Model", JFA and GDPA paragraphs). What differs is the data movement:
+//   * K and V tiles (64 keys x 256 bytes) are fetched with global_load_lds_dwordx4, which writes
+//     each lane's 16 bytes straight into LDS at base + 16 * lane: no staging registers and no
+//     LDS store instructions. While a tile is computed, the next one streams into the other
+//     stage; one barrier per tile.
+//   * Rows are 256 bytes with no padding; the 16-byte chunk c of row r is stored at chunk
+//     c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3). A direct load fills four consecutive rows
+//     per instruction, and each lane simply fetches the global chunk that belongs at its slot.
+//     Row reads (16 rows, one chunk) and transposed reads (4 rows x 4 chunks per half-wave) both
+//     hit 16 distinct 16-byte bank groups.
+//   * Rows past the sample's last key are fetched from its first key instead: finite values
+//     whose scores are masked, so no tile ever needs zero filling.
+#pragma once
+
+#include <math.h>
+
+#include "gdpa_common.h"
+#include "gdpa_internal.h"
+#include "gdpa_tiles.h"
+
+namespace gdpa {
+namespace fwddl {
+
+constexpr int BM = FWD_BM_BF16;  // queries per item (4 waves x 32)
+constexpr int BN = FWD_BN_BF16;  // keys per tile
+constexpr int NT = 256;
+constexpr int D = 128;
+constexpr int ROWB = 256;         // bytes per tile row
+constexpr int TILE = BN * ROWB;   // 16 KiB
+constexpr int WMAX = 3072;        // bias window (floats) staged in LDS
+
+__device__ __forceinline__ int xf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int xoff(int r, int chunk) { return r * ROWB + ((chunk ^ xf(r)) << 4); }
+
+// A operand, rows rbase + l%32, k-step s (chunk 2s + l/32)
+__device__ __forceinline__ bf16x8 row_op(const GDPA_LDS char* t, int rbase, int s, int lane) {
+  return *(const GDPA_LDS bf16x8*)(t + xoff(rbase + (lane & 31), 2 * s + (lane >> 5)));
+}
+
+// Transposed A operand: rows key0 + 4g + {0..3} and key0 + 8 + 4g + {0..3}, D index
+// n*32 + l%32 (see tile_tr_op in gdpa_tiles.h for the k order).
+__device__ __forceinline__ bf16x8 tr_op(const GDPA_LDS char* t, int key0, int n, int lane) {
+  const int i16 = lane & 15, q = i16 & 3;
+  const int rr = key0 + 4 * (lane >> 5) + (i16 >> 2);
+  const int c = 4 * n + 2 * ((lane >> 4) & 1) + (q >> 1);
+  const int within = 8 * (q & 1);
+  const i16x4 lo = lds_read_tr(t + xoff(rr, c) + within);
+  const i16x4 hi = lds_read_tr(t + xoff(rr + 8, c) + within);
+  return cat_tr(lo, hi);
+}
+
+// Issue the direct loads of one 64-key tile of K (or V) into an LDS stage. Thread (wave w,
+// lane l) fills, for u = 0..3, physical row 16u + 4w + l/16 at chunk l%16.
+__device__ __forceinline__ void issue_tile(GDPA_LDS char* __restrict__ stage, const __bf16* src, int k0, int Lk,
+                                           int kv0, int H, int h, int w, int lane) {
+  const int rsub = 4 * w + (lane >> 4);
+  const int c = (lane & 15) ^ xf(rsub);  // xf depends on the row only through r mod 16
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int row = k0 + 16 * u + rsub;
+    row = row < Lk ? row : 0;
+    const __bf16* g = src + ((int64_t)(kv0 + row) * H + h) * D + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (GDPA_LDS void*)(stage + (16 * u + 4 * w) * ROWB), 16, 0, 0);
+  }
+}
+
+template <int ACT, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char sk0_[TILE];
+  __shared__ __attribute__((aligned(16))) char sv0_[TILE];
+  __shared__ __attribute__((aligned(16))) char sk1_[TILE];
+  __shared__ __attribute__((aligned(16))) char sv1_[TILE];
+  __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? WMAX : 1];
+  GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
+  GDPA_LDS char* sv0 = (GDPA_LDS char*)sv0_;
+  GDPA_LDS char* sk1 = (GDPA_LDS char*)sk1_;
+  GDPA_LDS char* sv1 = (GDPA_LDS char*)sv1_;
+  GDPA_LDS float* bwin = (GDPA_LDS float*)bwin_;
+
+  const WsHeader* hdr = (const WsHeader*)a.hdr;
+  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
+  const Item it = ((const Item*)a.items)[blockIdx.x];
+  const int b = it.b, h = it.h, H = a.H;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row_blk = it.tile * BM;
+  const int wrow = row_blk + w * 32;
+  const int iq = wrow + l32;
+  const bool wave_active = wrow < Lq;
+  const bool qv = iq < Lq;
+  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+
+  int nkt = (Lk + BN - 1) / BN;
+  if (CAUSAL) nkt = min(nkt, (min(Lq, row_blk + BM) - 1) / BN + 1);
+
+  const __bf16* K = (const __bf16*)a.K;
+  const __bf16* V = (const __bf16*)a.V;
+  if (nkt > 0) {
+    issue_tile(sk0, K, 0, Lk, kv0, H, h, w, lane);
+    issue_tile(sv0, V, 0, Lk, kv0, H, h, w, lane);
+  }
+
+  bf16x8 qop[D / 16];
+  {
+    const __bf16* Q = (const __bf16*)a.Q;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qop[s] = qv ? *(const bf16x8*)(Q + qrow * D + 16 * s + 8 * g) : zero_bf16x8();
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float sl2 = a.scale * LOG2E;
+  const float inv_scale = 1.0f / a.scale;
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
+  int w_hi = 0;
+  bool win_ok = false;
+  if (BIAS && nkt > 0) {
+    w_hi = row_blk + BM - 1;
+    const int lo = row_blk - (nkt * BN - 1);
+    bool ok = w_hi - lo + 1 <= WMAX;
+    if (ok)
+      for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, a.nb - 1)] * inv_scale;
+    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  }
+
+  // one key tile: scores, probabilities, output update (stage buffers passed in)
+  auto tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+    f32x16 sacc[2];
+    if (BIAS && win_ok) {
+      const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + 4 * g);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = bp[kb * 32 + (r >> 2) * 8 + (r & 3)];
+    } else if (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, a.nb - 1)] * inv_scale;
+    } else {
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) sacc[kb] = mfma32(row_op(Ks, kb * 32, s, lane), qop[s], sacc[kb]);
+
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow))) != 0;
+    int lim[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int l = Lk - (k0 + kb * 32);
+      if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
+      lim[kb] = l - 4 * g;
+    }
+    float p[2][16];
+    if (ACT == ACT_SOFTMAX) {
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) sacc[kb][r] = -INFINITY;
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+      mt = half_max(mt) * sl2;
+      const bool grow = mt > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) o[n] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[kb][r] = fast_exp2(fmaf(sacc[kb][r], sl2, -m_use));
+          ls += p[kb][r];
+        }
+      l_run += ls;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[kb][r] = act_fwd(ACT, sacc[kb][r] * a.scale);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) p[kb][r] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 pb = pack8(&p[kb][8 * s2]);
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) o[n] = mfma32(tr_op(Vs, kb * 32 + 16 * s2, n, lane), pb, o[n]);
+      }
+  };
+
+  // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
+  // into one stage can then stay in flight while the other stage is read.
+  for (int kt = 0; kt < nkt; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads for tile kt have landed
+    __syncthreads();                // ... and everyone else's; tile kt - 1 is done with stage 1
+    if (kt + 1 < nkt) {
+      issue_tile(sk1, K, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
+      issue_tile(sv1, V, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
+    }
+    if (wave_active && !(CAUSAL && kt * BN > wrow + 31)) tile(sk0, sv0, kt * BN);
+    if (kt + 1 >= nkt) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < nkt) {
+      issue_tile(sk0, K, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
+      issue_tile(sv0, V, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
+    }
+    if (wave_active && !(CAUSAL && (kt + 1) * BN > wrow + 31)) tile(sk1, sv1, (kt + 1) * BN);
+  }
+
+  if (!wave_active) return;
+  float inv = 1.0f;
+  if (ACT == ACT_SOFTMAX) {
+    const float lt = half_sum(l_run);
+    inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (qv && g == 0 && a.lse != nullptr)
+      a.lse[qrow] = lt > 0.0f ? (m_run + log2f(lt)) * LN2 : -INFINITY;
+  }
+  if (!qv) return;
+  __bf16* orow = (__bf16*)a.O + qrow * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(orow, o[n], n, g, inv);
+}
+
+template <int ACT, bool CAUSAL, bool BIAS>
+hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
+  prof_before(PROF_FWD, s);
+  hipLaunchKernelGGL((fwd_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  prof_after(PROF_FWD, s);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_cb(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
+  const bool bias = p.nb > 0;
+  if (p.causal) return bias ? launch_t<ACT, true, true>(a, grid, s) : launch_t<ACT, true, false>(a, grid, s);
+  return bias ? launch_t<ACT, false, true>(a, grid, s) : launch_t<ACT, false, false>(a, grid, s);
+}
+
+inline hipError_t launch(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
+  switch (p.act) {
+    case ACT_SOFTMAX: return launch_cb<ACT_SOFTMAX>(p, a, grid, s);
+    case ACT_GELU_TANH: return launch_cb<ACT_GELU_TANH>(p, a, grid, s);
+    default: return launch_cb<ACT_SILU>(p, a, grid, s);
+  }
+}
+
+}  // namespace fwddl
+}  // namespace gdpa
