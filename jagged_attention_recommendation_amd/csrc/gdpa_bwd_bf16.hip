@@ -22,6 +22,7 @@
 //               dO^T and Q^T read transposed from the query tiles.
 #include <math.h>
 
+#include "gdpa_bwd_dl.h"
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
 #include "gdpa_tiles.h"
@@ -494,13 +495,22 @@ hipError_t launch_d(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t
   }
 }
 
+// D = 128: the direct-load dQ kernel of gdpa_bwd_dl.h, then the dK/dV kernel above.
+hipError_t launch_d128(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t s) {
+  if (gq > 0) {
+    const hipError_t e = bwddl::launch_dq(p, a, gq, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_d<128>(p, a, 0, gk, s);
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_d<32>(p, a, grid_q, grid_k, s);
     case 64: return launch_d<64>(p, a, grid_q, grid_k, s);
-    default: return launch_d<128>(p, a, grid_q, grid_k, s);
+    default: return launch_d128(p, a, grid_q, grid_k, s);
   }
 }
 

@@ -1,0 +1,337 @@
+// Backward kernels for D = 128 bf16 with direct global -> LDS tile loads and a two-stage LDS ring.
+//
+// Same method, work split and operand orientation as the register-staged kernels in
+// gdpa_bwd_bf16.hip (recomputed scores, dQ and dK/dV in separate kernels with no atomics; page
+// "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA,
+// GDPA and block-attention paragraphs). What differs:
+//   * the streamed tiles (K and V for dQ, Q and dO for dK/dV) come in by direct loads (layout in
+//     gdpa_dl.h) into one stage while the other stage is computed: no staging registers;
+//   * each 64-row tile is processed in two 32-row halves, and the operands of a half are read
+//     from LDS before its products are issued, so the products do not wait on one read each;
+//   * the bias and the scale seed the score accumulators (acc = b / scale + q.k, then
+//     x = acc * scale (* log2 e)), and masking runs only on tiles that reach a boundary.
+#pragma once
+
+#include <math.h>
+
+#include "gdpa_common.h"
+#include "gdpa_dl.h"
+#include "gdpa_internal.h"
+#include "gdpa_tiles.h"  // store_acc_row_bf16
+
+namespace gdpa {
+namespace bwddl {
+
+using namespace dl;
+
+constexpr int NT = 256;         // threads per workgroup (4 waves)
+constexpr int QI = BWD_Q_ITEM;  // queries per dQ item
+constexpr int KL = BWD_K_LOOP;  // keys per tile in the dQ loop
+constexpr int KI = BWD_K_ITEM;  // keys per dK/dV item
+constexpr int QL = BWD_Q_LOOP;  // queries per tile in the dK/dV loop
+static_assert(QI == 128 && KI == 128 && KL == ROWS && QL == ROWS, "kernels assume these tiles");
+constexpr int DSP = 68;         // floats per row of a wave's dS buffer (16-byte aligned rows)
+
+template <int ACT>
+__device__ __forceinline__ float dscore(float x, float lse2, float Di, float dp, float& p) {
+  // x: score in log2 units (softmax) or natural units (GDPA)
+  if (ACT == ACT_SOFTMAX) {
+    p = fast_exp2(x - lse2);
+    return p * (dp - Di);
+  }
+  float y, dy;
+  act_fwd_bwd(ACT, x, y, dy);
+  p = y;
+  return dp * dy;
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ: item = 128 queries of one (sample, head), 4 waves x 32 queries; loop over 64-key tiles.
+// S^T = K Q^T and dP^T = V dO^T with lane = query, dQ^T += K^T dS^T with K^T read transposed.
+// Bias gradient: the paired-diagonal sums of gdpa_bwd_bf16.hip over the wave's 32 x 64 block of
+// dS, staged in a per-wave LDS buffer; every partial-row entry is written once.
+template <int ACT, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char sk0_[TILE];
+  __shared__ __attribute__((aligned(16))) char sv0_[TILE];
+  __shared__ __attribute__((aligned(16))) char sk1_[TILE];
+  __shared__ __attribute__((aligned(16))) char sv1_[TILE];
+  __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
+  __shared__ __attribute__((aligned(16))) float dsbuf_[BIAS ? 4 * 32 * DSP : 1];
+  GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
+  GDPA_LDS char* sv0 = (GDPA_LDS char*)sv0_;
+  GDPA_LDS char* sk1 = (GDPA_LDS char*)sk1_;
+  GDPA_LDS char* sv1 = (GDPA_LDS char*)sv1_;
+  GDPA_LDS float* bwin = (GDPA_LDS float*)bwin_;
+
+  const WsHeader* hdr = (const WsHeader*)a.hdr;
+  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
+  const Item it = ((const Item*)a.items_q)[blockIdx.x];
+  const int b = it.b, h = it.h, H = a.H, nb = a.nb;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i0 = it.tile * QI;
+  const int wrow = i0 + w * 32;
+  const int iq = wrow + l32;
+  const bool qv = iq < Lq;
+  const bool wave_active = wrow < Lq;
+  const int64_t row = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+
+  int nkt = (Lk + KL - 1) / KL;
+  if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
+  if (i0 >= Lq) nkt = 0;
+
+  const __bf16* K = (const __bf16*)a.K;
+  const __bf16* V = (const __bf16*)a.V;
+  if (nkt > 0) {
+    issue_tile(sk0, K, 0, Lk, kv0, H, h, w, lane);
+    issue_tile(sv0, V, 0, Lk, kv0, H, h, w, lane);
+  }
+
+  const __bf16* Q = (const __bf16*)a.Q;
+  const __bf16* dO = (const __bf16*)a.dO;
+  bf16x8 qop[D / 16], doop[D / 16];
+  float part_d = 0.0f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qop[s] = qv ? *(const bf16x8*)(Q + row * D + 16 * s + 8 * g) : zero_bf16x8();
+    doop[s] = qv ? *(const bf16x8*)(dO + row * D + 16 * s + 8 * g) : zero_bf16x8();
+    if (ACT == ACT_SOFTMAX && qv) {
+      const bf16x8 ov = *(const bf16x8*)((const __bf16*)a.O + row * D + 16 * s + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part_d += (float)doop[s][e] * (float)ov[e];
+    }
+  }
+  float Di = 0.0f, lse2 = 0.0f;
+  if (ACT == ACT_SOFTMAX) {
+    Di = half_sum(part_d);
+    if (qv) {
+      lse2 = a.lse[row] * LOG2E;
+      if (g == 0) a.Dvec[row] = Di;
+    }
+  }
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) dq[n] = f32x16{};
+
+  const float sc = ACT == ACT_SOFTMAX ? a.scale * LOG2E : a.scale;
+  const float inv_scale = 1.0f / a.scale;
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  int w_hi = 0;
+  bool win_ok = false;
+  if (BIAS && nkt > 0) {  // raw diagonals iq - j: iq in [i0, i0 + QI), j in [0, nkt * KL)
+    w_hi = i0 + QI - 1;
+    const int lo = i0 - (nkt * KL - 1);
+    const bool ok = w_hi - lo + 1 <= BIAS_WMAX;
+    if (ok)
+      for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, nb - 1)] * inv_scale;
+    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  }
+  GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * 32 * DSP;
+  float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
+  float* part = BIAS ? a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb : nullptr;
+  float e_lo = 0.0f, e_hi = 0.0f;
+  bool has_lo = false, has_hi = false;
+  // Writes the complete diagonal d of this wave (value v) to its partial row; the ends of the
+  // table collect every diagonal that clamps to them, summed over the wave in a fixed order.
+  // Under causal masking diagonals d < 0 hold only masked (zero) entries and are skipped.
+  auto emit = [&](int d, float v, bool valid) {
+    if (CAUSAL && d < 0) valid = false;
+    const bool lo = valid && d <= 0;
+    const bool hi = valid && !lo && d >= nb - 1;
+    if (valid && !lo && !hi) part[d] = v;
+    const uint64_t blo = __builtin_amdgcn_ballot_w64(lo), bhi = __builtin_amdgcn_ballot_w64(hi);
+    if (blo != 0) {
+      e_lo += wave_sum(lo ? v : 0.0f);
+      has_lo = true;
+    }
+    if (bhi != 0) {
+      e_hi += wave_sum(hi ? v : 0.0f);
+      has_hi = true;
+    }
+  };
+  int k0_last = -1;
+
+  auto tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+    k0_last = k0;
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+        (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq))) != 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc, dpacc = f32x16{};
+      if (BIAS && win_ok) {
+        const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + kb * 32 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = bp[(r >> 2) * 8 + (r & 3)];
+      } else if (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[r] = bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, nb - 1)] * inv_scale;
+      } else {
+        sacc = f32x16{};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 kr[D / 16], vr[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        kr[s] = row_op(Ks, kb * 32, s, lane);
+        vr[s] = row_op(Vs, kb * 32, s, lane);
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sacc = mfma32(kr[s], qop[s], sacc);
+        dpacc = mfma32(vr[s], doop[s], dpacc);
+      }
+      // all 16 operand reads first, then the 16 products (each waits only for its own operand)
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p;
+        dsv[r] = dscore<ACT>(sacc[r] * sc, lse2, Di, dpacc[r], p);
+      }
+      if (need_mask) {
+        int lim = Lk - (k0 + kb * 32);
+        if (CAUSAL) lim = min(lim, iq - (k0 + kb * 32) + 1);
+        lim = qv ? lim - 4 * g : -64;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((r >> 2) * 8 + (r & 3) >= lim) dsv[r] = 0.0f;
+      }
+      if (BIAS) {
+        // dS block -> LDS (row = query, column = key; registers 4m..4m+3 are 4 consecutive keys)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 v4 = {dsv[4 * m], dsv[4 * m + 1], dsv[4 * m + 2], dsv[4 * m + 3]};
+          *(GDPA_LDS f32x4*)(dsbuf + l32 * DSP + kb * 32 + m * 8 + 4 * g) = v4;
+        }
+      }
+      const bf16x8 dsb0 = pack8(&dsv[0]);
+      const bf16x8 dsb1 = pack8(&dsv[8]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 kt0[D / 32], kt1[D / 32];
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        kt0[n] = tr_op(Ks, kb * 32, n, lane);
+        kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
+      }
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        dq[n] = mfma32(kt0[n], dsb0, dq[n]);
+        dq[n] = mfma32(kt1[n], dsb1, dq[n]);
+      }
+      // the 16 transposed reads first, then the 8 products
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (BIAS) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Lane 31 + t sums diagonal t - 32 (rows 0..31); lane t < 31 sums diagonal t - 63 (rows
+      // 0..t) and then diagonal t + 1 (rows t + 1..31). In both cases step s reads row s,
+      // column (s + 63 - lane) mod 64, and the second diagonal starts where the column wraps.
+      // All 64 lanes read one row at distinct columns: no bank conflicts.
+      float s_a = 0.0f, s_b = 0.0f;
+#pragma unroll
+      for (int a8 = 0; a8 < 32; a8 += 8) {  // 8 reads in flight, then their sums
+        float vv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (a8 + e + 63 - lane < 64) s_a += vv[e]; else s_b += vv[e];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // complete after this tile: lanes t < 31 emit d = t + 1 (with the carried part), the
+      // others emit d = lane - 63; absolute diagonal = wrow - k0 + d
+      float v;
+      int dabs;
+      if (lane < 31) {
+        v = carry + s_b;
+        carry = s_a;
+        dabs = wrow - k0 + lane + 1;
+      } else {
+        v = s_a;
+        dabs = wrow - k0 + lane - 63;
+      }
+      emit(dabs, v, true);
+    }
+  };
+
+  // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
+  // into one stage stay in flight while the other stage is read.
+  for (int kt = 0; kt < nkt; kt += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads for tile kt have landed
+    __syncthreads();                // ... and everyone else's; tile kt - 1 is done with stage 1
+    if (kt + 1 < nkt) {
+      issue_tile(sk1, K, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
+      issue_tile(sv1, V, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
+    }
+    if (wave_active && !(CAUSAL && kt * KL > wrow + 31)) tile(sk0, sv0, kt * KL);
+    if (kt + 1 >= nkt) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 2 < nkt) {
+      issue_tile(sk0, K, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
+      issue_tile(sv0, V, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
+    }
+    if (wave_active && !(CAUSAL && (kt + 1) * KL > wrow + 31)) tile(sk1, sv1, (kt + 1) * KL);
+  }
+
+  if (BIAS && k0_last >= 0) {
+    // the 31 carried diagonals d = t - 63 of the last tile
+    emit(wrow - k0_last + lane - 63, carry, lane < 31);
+    if (lane == 0) {
+      if (nb == 1) {
+        if (has_lo || has_hi) part[0] = e_lo + e_hi;
+      } else {
+        if (has_lo) part[0] = e_lo;
+        if (has_hi) part[nb - 1] = e_hi;
+      }
+    }
+  }
+  if (!qv) return;
+  __bf16* dqrow = (__bf16*)a.dQ + row * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(dqrow, dq[n], n, g, a.scale);
+}
+
+template <int ACT, bool CAUSAL, bool BIAS>
+hipError_t launch_dq_t(const BwdArgs& a, int grid, hipStream_t s) {
+  prof_before(PROF_DQ, s);
+  hipLaunchKernelGGL((dq_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  prof_after(PROF_DQ, s);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_dq_cb(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
+  const bool bias = p.nb > 0;
+  if (p.causal) return bias ? launch_dq_t<ACT, true, true>(a, grid, s) : launch_dq_t<ACT, true, false>(a, grid, s);
+  return bias ? launch_dq_t<ACT, false, true>(a, grid, s) : launch_dq_t<ACT, false, false>(a, grid, s);
+}
+
+inline hipError_t launch_dq(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
+  switch (p.act) {
+    case ACT_SOFTMAX: return launch_dq_cb<ACT_SOFTMAX>(p, a, grid, s);
+    case ACT_GELU_TANH: return launch_dq_cb<ACT_GELU_TANH>(p, a, grid, s);
+    default: return launch_dq_cb<ACT_SILU>(p, a, grid, s);
+  }
+}
+
+}  // namespace bwddl
+}  // namespace gdpa

@@ -2,72 +2,28 @@
 //
 // Same method and operand orientation as gdpa_fwd_kernel.h (JFA softmax / GDPA activation on
 // jagged tensors, page "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
-// Foundation Model", JFA and GDPA paragraphs). What differs is the data movement:
-//   * K and V tiles (64 keys x 256 bytes) are fetched with global_load_lds_dwordx4, which writes
-//     each lane's 16 bytes straight into LDS at base + 16 * lane: no staging registers and no
-//     LDS store instructions. While a tile is computed, the next one streams into the other
-//     stage; one barrier per tile.
-//   * Rows are 256 bytes with no padding; the 16-byte chunk c of row r is stored at chunk
-//     c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3). A direct load fills four consecutive rows
-//     per instruction, and each lane simply fetches the global chunk that belongs at its slot.
-//     Row reads (16 rows, one chunk) and transposed reads (4 rows x 4 chunks per half-wave) both
-//     hit 16 distinct 16-byte bank groups.
-//   * Rows past the sample's last key are fetched from its first key instead: finite values
-//     whose scores are masked, so no tile ever needs zero filling.
+// Foundation Model", JFA and GDPA paragraphs). What differs is the data movement: K and V tiles
+// (64 keys x 256 bytes, layout in gdpa_dl.h) are fetched with direct loads, and while a tile is
+// computed the next one streams into the other stage; one barrier per tile.
 #pragma once
 
 #include <math.h>
 
 #include "gdpa_common.h"
+#include "gdpa_dl.h"
 #include "gdpa_internal.h"
-#include "gdpa_tiles.h"
+#include "gdpa_tiles.h"  // store_acc_row_bf16
 
 namespace gdpa {
 namespace fwddl {
 
+using namespace dl;
+
 constexpr int BM = FWD_BM_BF16;  // queries per item (4 waves x 32)
 constexpr int BN = FWD_BN_BF16;  // keys per tile
+static_assert(BN == ROWS, "one key tile is one direct-load tile");
 constexpr int NT = 256;
-constexpr int D = 128;
-constexpr int ROWB = 256;         // bytes per tile row
-constexpr int TILE = BN * ROWB;   // 16 KiB
 constexpr int WMAX = 3072;        // bias window (floats) staged in LDS
-
-__device__ __forceinline__ int xf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int xoff(int r, int chunk) { return r * ROWB + ((chunk ^ xf(r)) << 4); }
-
-// A operand, rows rbase + l%32, k-step s (chunk 2s + l/32)
-__device__ __forceinline__ bf16x8 row_op(const GDPA_LDS char* t, int rbase, int s, int lane) {
-  return *(const GDPA_LDS bf16x8*)(t + xoff(rbase + (lane & 31), 2 * s + (lane >> 5)));
-}
-
-// Transposed A operand: rows key0 + 4g + {0..3} and key0 + 8 + 4g + {0..3}, D index
-// n*32 + l%32 (see tile_tr_op in gdpa_tiles.h for the k order).
-__device__ __forceinline__ bf16x8 tr_op(const GDPA_LDS char* t, int key0, int n, int lane) {
-  const int i16 = lane & 15, q = i16 & 3;
-  const int rr = key0 + 4 * (lane >> 5) + (i16 >> 2);
-  const int c = 4 * n + 2 * ((lane >> 4) & 1) + (q >> 1);
-  const int within = 8 * (q & 1);
-  const i16x4 lo = lds_read_tr(t + xoff(rr, c) + within);
-  const i16x4 hi = lds_read_tr(t + xoff(rr + 8, c) + within);
-  return cat_tr(lo, hi);
-}
-
-// Issue the direct loads of one 64-key tile of K (or V) into an LDS stage. Thread (wave w,
-// lane l) fills, for u = 0..3, physical row 16u + 4w + l/16 at chunk l%16.
-__device__ __forceinline__ void issue_tile(GDPA_LDS char* __restrict__ stage, const __bf16* src, int k0, int Lk,
-                                           int kv0, int H, int h, int w, int lane) {
-  const int rsub = 4 * w + (lane >> 4);
-  const int c = (lane & 15) ^ xf(rsub);  // xf depends on the row only through r mod 16
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    int row = k0 + 16 * u + rsub;
-    row = row < Lk ? row : 0;
-    const __bf16* g = src + ((int64_t)(kv0 + row) * H + h) * D + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g,
-                                     (GDPA_LDS void*)(stage + (16 * u + 4 * w) * ROWB), 16, 0, 0);
-  }
-}
 
 template <int ACT, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {

@@ -182,6 +182,10 @@ __device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causa
   return true;
 }
 
+// Loads are issued in batches of 8 row blocks before any of them is added, so a thread waits on
+// one memory round trip per batch rather than per row block. A row block whose range misses
+// entry c contributes +0.0, which leaves the running sum unchanged: the summation order, and so
+// the result bits, are those of the plain loop over rb.
 __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int c = blockIdx.y * 256 + threadIdx.x;
@@ -194,25 +198,42 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     const int nrb = (Lq + 31) / 32;
     const int tb = a.tile_base[b];
     const int nb = a.nb;
-    for (int rb = 0; rb < nrb; ++rb) {
-      int d_lo, d_hi;
-      if (!rowblock_range(rb, Lq, Lk, a.causal, a.tile_rows, a.loop_rows, d_lo, d_hi)) continue;
-      const int c_lo = clampi(d_lo, 0, nb - 1), c_hi = clampi(d_hi, 0, nb - 1);
-      if (c < c_lo || c > c_hi) continue;
-      const int per = a.tile_rows / 32;
-      const int64_t row = (int64_t)(tb + rb / per) * per + rb % per;
-      acc += a.part[(row * a.H + h) * nb + c];
+    const int per = a.tile_rows / 32;
+    constexpr int BATCH = 8;
+    for (int rb0 = 0; rb0 < nrb; rb0 += BATCH) {
+      float v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int rb = rb0 + u;
+        int d_lo, d_hi;
+        v[u] = 0.0f;
+        if (rb < nrb && rowblock_range(rb, Lq, Lk, a.causal, a.tile_rows, a.loop_rows, d_lo, d_hi) &&
+            c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1)) {
+          const int64_t row = (int64_t)(tb + rb / per) * per + rb % per;
+          v[u] = a.part[(row * a.H + h) * nb + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) acc += v[u];
     }
   }
   a.part_bh[((int64_t)b * a.H + h) * a.nb + c] = acc;
 }
 
-// Stage B: dbias[h, c] = sum over samples in order.
+// Stage B: dbias[h, c] = sum over samples in order (loads batched as in stage A).
 __global__ __launch_bounds__(256) void dbias_stage_b(DbiasArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.H * a.nb) return;
+  const int64_t stride = (int64_t)a.H * a.nb;
+  constexpr int BATCH = 16;
   float acc = 0.0f;
-  for (int b = 0; b < a.B; ++b) acc += a.part_bh[(int64_t)b * a.H * a.nb + idx];
+  for (int b0 = 0; b0 < a.B; b0 += BATCH) {
+    float v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) v[u] = b0 + u < a.B ? a.part_bh[(b0 + u) * stride + idx] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) acc += v[u];
+  }
   a.dbias[idx] = acc;
 }
 
