@@ -495,13 +495,13 @@ hipError_t launch_d(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t
   }
 }
 
-// D = 128: the direct-load dQ kernel of gdpa_bwd_dl.h, then the dK/dV kernel above.
+// D = 128: the direct-load kernels of gdpa_bwd_dl.h.
 hipError_t launch_d128(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t s) {
   if (gq > 0) {
     const hipError_t e = bwddl::launch_dq(p, a, gq, s);
     if (e != hipSuccess) return e;
   }
-  return launch_d<128>(p, a, 0, gk, s);
+  return gk > 0 ? bwddl::launch_dkdv(p, a, gk, s) : hipSuccess;
 }
 
 }  // namespace

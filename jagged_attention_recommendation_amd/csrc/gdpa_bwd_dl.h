@@ -310,6 +310,226 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(dqrow, dq[n], n, g, a.scale);
 }
 
+// ------------------------------------------------------------------------------------------
+// dK, dV: item = 128 keys of one (sample, head), 4 waves x 32 keys; loop over 64-query tiles.
+// S = Q K^T and dP = dO V^T with lane = key; dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
+// read transposed from the query tiles. The softmax row terms (lse, D) of a query tile come in
+// by 4-byte direct loads beside the tile itself.
+template <int ACT, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
+  constexpr bool SM = ACT == ACT_SOFTMAX;
+  __shared__ __attribute__((aligned(16))) char sq0_[TILE];
+  __shared__ __attribute__((aligned(16))) char so0_[TILE];
+  __shared__ __attribute__((aligned(16))) char sq1_[TILE];
+  __shared__ __attribute__((aligned(16))) char so1_[TILE];
+  __shared__ __attribute__((aligned(16))) float rt_[SM ? 2 * 2 * QL : 1];  // [stage][lse, D][QL]
+  __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
+  GDPA_LDS char* sq0 = (GDPA_LDS char*)sq0_;
+  GDPA_LDS char* so0 = (GDPA_LDS char*)so0_;
+  GDPA_LDS char* sq1 = (GDPA_LDS char*)sq1_;
+  GDPA_LDS char* so1 = (GDPA_LDS char*)so1_;
+  GDPA_LDS float* rt = (GDPA_LDS float*)rt_;
+  GDPA_LDS float* bwin = (GDPA_LDS float*)bwin_;
+
+  const WsHeader* hdr = (const WsHeader*)a.hdr;
+  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items2) return;
+  const Item it = ((const Item*)a.items_k)[blockIdx.x];
+  const int b = it.b, h = it.h, H = a.H, nb = a.nb;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j0 = it.tile * KI;
+  const int wkey = j0 + w * 32;
+  const int jk = wkey + l32;
+  const bool kvalid = jk < Lk;
+  const bool wave_active = wkey < Lk;
+  const int64_t krow = (int64_t)(kv0 + (kvalid ? jk : 0)) * H + h;
+
+  const int nqt = (Lq + QL - 1) / QL;
+  const int qt0 = CAUSAL ? j0 / QL : 0;
+  const int nt = j0 < Lk && qt0 < nqt ? nqt - qt0 : 0;  // query tiles this item visits
+
+  const __bf16* Q = (const __bf16*)a.Q;
+  const __bf16* dO = (const __bf16*)a.dO;
+  // Direct loads of query tile qt (Q, dO and, for softmax, its lse and D entries) into a stage.
+  // Waves 0 and 1 fetch the 64 lse / D values (one 4-byte load per lane, rows past the end
+  // repeat the tile's first row).
+  auto issue = [&](GDPA_LDS char* sq, GDPA_LDS char* so, GDPA_LDS float* srt, int qt) {
+    issue_tile(sq, Q, qt * QL, Lq, q0, H, h, w, lane);
+    issue_tile(so, dO, qt * QL, Lq, q0, H, h, w, lane);
+    if (SM && w < 2) {
+      const int r0 = qt * QL, n = min(QL, Lq - r0);
+      const float* src = (w == 0 ? a.lse : a.Dvec) + ((int64_t)(q0 + r0) * H + h);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, ((n - 1) * H + 1) * 4, 0x00020000);
+      const int r = lane < n ? lane : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)(srt + w * QL), 4, r * H * 4, 0, 0, 0);
+    }
+  };
+  if (nt > 0) issue(sq0, so0, rt, qt0);
+
+  bf16x8 kop[D / 16], vop[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.K + krow * D + 16 * s + 8 * g) : zero_bf16x8();
+    vop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.V + krow * D + 16 * s + 8 * g) : zero_bf16x8();
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
+  const float sc = SM ? a.scale * LOG2E : a.scale;
+  const float inv_scale = 1.0f / a.scale;
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  // bias window in natural order (bwin[t] = bias[clamp(w_lo + t)] / scale): a lane's 16 lookups
+  // are one base address plus constant offsets
+  int w_lo = 0;
+  bool win_ok = false;
+  if (BIAS && nt > 0) {  // raw diagonals i - jk: i in [qt0 * QL, nqt * QL), jk in [j0, j0 + KI)
+    w_lo = qt0 * QL - (j0 + KI - 1);
+    const int w_hi = nqt * QL - 1 - j0;
+    const bool ok = w_hi - w_lo + 1 <= BIAS_WMAX;
+    if (ok)
+      for (int t = tid; t <= w_hi - w_lo; t += NT) bwin[t] = bias_h[clampi(w_lo + t, 0, nb - 1)] * inv_scale;
+    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  }
+
+  auto tile = [&](const GDPA_LDS char* __restrict__ Qs, const GDPA_LDS char* __restrict__ dOs,
+                  const GDPA_LDS float* srt, int i0) {
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+        (int)((i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31))) != 0;
+#pragma unroll 1  // rolled: one 32-query half at a time keeps the register count in bounds
+    for (int qb = 0; qb < 2; ++qb) {
+      const int ib = i0 + qb * 32 + 4 * g;  // query of register r: ib + (r / 4) * 8 + r % 4
+      f32x16 sacc, dpacc = f32x16{};
+      if (BIAS && win_ok) {
+        const GDPA_LDS float* bp = bwin + (ib - jk - w_lo);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = bp[(r >> 2) * 8 + (r & 3)];
+      } else if (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[r] = bias_h[clampi(ib + (r >> 2) * 8 + (r & 3) - jk, 0, nb - 1)] * inv_scale;
+      } else {
+        sacc = f32x16{};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 qr[D / 16], dr[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        qr[s] = row_op(Qs, qb * 32, s, lane);
+        dr[s] = row_op(dOs, qb * 32, s, lane);
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sacc = mfma32(qr[s], kop[s], sacc);
+        dpacc = mfma32(dr[s], vop[s], dpacc);
+      }
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 l4 = {}, d4 = {};
+        if (SM) {
+          l4 = *(const GDPA_LDS f32x4*)(srt + qb * 32 + m * 8 + 4 * g);
+          d4 = *(const GDPA_LDS f32x4*)(srt + QL + qb * 32 + m * 8 + 4 * g);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e;
+          float p;
+          dsv[r] = dscore<ACT>(sacc[r] * sc, l4[e] * LOG2E, d4[e], dpacc[r], p);
+          pv[r] = p;
+        }
+      }
+      if (need_mask) {
+        int hi = kvalid ? Lq - ib : -64;    // query offsets at or past hi are invalid
+        const int lo = CAUSAL ? jk - ib : -64;  // query offsets below lo precede the key
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = (r >> 2) * 8 + (r & 3);
+          if (off >= hi || off < lo) {
+            pv[r] = 0.0f;
+            dsv[r] = 0.0f;
+          }
+        }
+      }
+      const bf16x8 pb0 = pack8(&pv[0]), pb1 = pack8(&pv[8]);
+      const bf16x8 db0 = pack8(&dsv[0]), db1 = pack8(&dsv[8]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 ot[2][D / 32], qt[2][D / 32];
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        ot[0][n] = tr_op(dOs, qb * 32, n, lane);
+        ot[1][n] = tr_op(dOs, qb * 32 + 16, n, lane);
+      }
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        qt[0][n] = tr_op(Qs, qb * 32, n, lane);
+        qt[1][n] = tr_op(Qs, qb * 32 + 16, n, lane);
+      }
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        dv[n] = mfma32(ot[0][n], pb0, dv[n]);
+        dv[n] = mfma32(ot[1][n], pb1, dv[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        dk[n] = mfma32(qt[0][n], db0, dk[n]);
+        dk[n] = mfma32(qt[1][n], db1, dk[n]);
+      }
+      // dO^T reads, then the dV products interleaved with the Q^T reads, then the dK products
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two stages, as in the dQ kernel.
+  GDPA_LDS float* rt0 = rt;
+  GDPA_LDS float* rt1 = rt + (SM ? 2 * QL : 0);
+  for (int t = 0; t < nt; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < nt) issue(sq1, so1, rt1, qt0 + t + 1);
+    {
+      const int i0 = (qt0 + t) * QL;
+      if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq0, so0, rt0, i0);
+    }
+    if (t + 1 >= nt) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < nt) issue(sq0, so0, rt0, qt0 + t + 2);
+    {
+      const int i0 = (qt0 + t + 1) * QL;
+      if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq1, so1, rt1, i0);
+    }
+  }
+  if (!kvalid) return;
+  __bf16* dkrow = (__bf16*)a.dK + krow * D;
+  __bf16* dvrow = (__bf16*)a.dV + krow * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    store_acc_row_bf16(dkrow, dk[n], n, g, a.scale);
+    store_acc_row_bf16(dvrow, dv[n], n, g, 1.0f);
+  }
+}
+
 template <int ACT, bool CAUSAL, bool BIAS>
 hipError_t launch_dq_t(const BwdArgs& a, int grid, hipStream_t s) {
   prof_before(PROF_DQ, s);
@@ -323,6 +543,29 @@ hipError_t launch_dq_cb(const Prob& p, const BwdArgs& a, int grid, hipStream_t s
   const bool bias = p.nb > 0;
   if (p.causal) return bias ? launch_dq_t<ACT, true, true>(a, grid, s) : launch_dq_t<ACT, true, false>(a, grid, s);
   return bias ? launch_dq_t<ACT, false, true>(a, grid, s) : launch_dq_t<ACT, false, false>(a, grid, s);
+}
+
+template <int ACT, bool CAUSAL, bool BIAS>
+hipError_t launch_dkdv_t(const BwdArgs& a, int grid, hipStream_t s) {
+  prof_before(PROF_DKDV, s);
+  hipLaunchKernelGGL((dkdv_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  prof_after(PROF_DKDV, s);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_dkdv_cb(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
+  const bool bias = p.nb > 0;
+  if (p.causal) return bias ? launch_dkdv_t<ACT, true, true>(a, grid, s) : launch_dkdv_t<ACT, true, false>(a, grid, s);
+  return bias ? launch_dkdv_t<ACT, false, true>(a, grid, s) : launch_dkdv_t<ACT, false, false>(a, grid, s);
+}
+
+inline hipError_t launch_dkdv(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
+  switch (p.act) {
+    case ACT_SOFTMAX: return launch_dkdv_cb<ACT_SOFTMAX>(p, a, grid, s);
+    case ACT_GELU_TANH: return launch_dkdv_cb<ACT_GELU_TANH>(p, a, grid, s);
+    default: return launch_dkdv_cb<ACT_SILU>(p, a, grid, s);
+  }
 }
 
 inline hipError_t launch_dq(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
