@@ -242,7 +242,9 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       // 0..t) and then diagonal t + 1 (rows t + 1..31). In both cases step s reads row s,
       // column (s + 63 - lane) mod 64, and the second diagonal starts where the column wraps.
       // All 64 lanes read one row at distinct columns: no bank conflicts.
-      float s_a = 0.0f, s_b = 0.0f;
+      // One running sum over the 32 steps; lane t < 31 captures it after step t (its first
+      // diagonal) and takes the second diagonal as the rest.
+      float run = 0.0f, s_a = 0.0f;
 #pragma unroll
       for (int a8 = 0; a8 < 32; a8 += 8) {  // 8 reads in flight, then their sums
         float vv[8];
@@ -250,9 +252,12 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
         for (int e = 0; e < 8; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          if (a8 + e + 63 - lane < 64) s_a += vv[e]; else s_b += vv[e];
+          run += vv[e];
+          if (a8 + e == lane) s_a = run;
         }
       }
+      if (lane > 31) s_a = run;
+      const float s_b = run - s_a;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

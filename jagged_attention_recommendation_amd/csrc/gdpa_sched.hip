@@ -39,14 +39,29 @@ __device__ __forceinline__ int item_cost(int mode, int causal, int Lq, int Lk, i
   return nq - j0 / tl;
 }
 
-// In-place inclusive scan of SNT ints in LDS (all threads participate).
-__device__ __forceinline__ void block_scan(int* buf, int tid) {
-  for (int off = 1; off < SNT; off <<= 1) {
-    __syncthreads();
-    int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
+  return x;
+}
+
+// In-place inclusive scan of SNT ints in LDS (all threads participate): a scan inside each wave,
+// then a scan of the 16 wave totals by wave 0.
+__device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
+  const int lane = tid & 63, w = tid >> 6;
+  __syncthreads();
+  int x = wave_incl_scan(buf[tid], lane);
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    const int v = wave_incl_scan(lane < SNT / 64 ? wsum[lane] : 0, lane);
+    if (lane < SNT / 64) wsum[lane] = v;
+  }
+  __syncthreads();
+  buf[tid] = x + (w > 0 ? wsum[w - 1] : 0);
   __syncthreads();
 }
 
@@ -54,6 +69,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   const SchedArgs& a = blockIdx.x == 0 ? a0 : a1;
   __shared__ int bucket[NBUCKET];
   __shared__ int cnt[SNT];  // inclusive scan of the chunk's per-sample tile counts
+  __shared__ int wsum[SNT / 64];
   __shared__ int err, carry;
   const int tid = threadIdx.x;
   WsHeader* hdr = (WsHeader*)a.ws_header;
@@ -91,7 +107,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       const int n = b < a.B ? ntiles(b) : 0;
       __syncthreads();
       cnt[tid] = n;
-      block_scan(cnt, tid);
+      block_scan(cnt, wsum, tid);
       const int total = cnt[SNT - 1];
       const int first = carry;
       for (int u = tid; u < total; u += SNT) {
@@ -120,7 +136,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   __syncthreads();
   // 2. exclusive scan over the buckets (NBUCKET == SNT)
   const int own = bucket[tid];
-  block_scan(bucket, tid);
+  block_scan(bucket, wsum, tid);
   const int total_items = bucket[NBUCKET - 1];
   __syncthreads();
   bucket[tid] -= own;
@@ -168,16 +184,16 @@ hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) 
 // and wrote exactly the clamped
 // diagonals of its raw range [32rb - (k_end - 1), 32rb + 31], k_end = keys it visited; the edge
 // entries 0 and NB-1 collect every raw diagonal that clamps to them.
-__device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causal, int qi, int kl,
-                                               int& d_lo, int& d_hi) {
+template <int QI, int KL>
+__device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causal, int& d_lo, int& d_hi) {
   const int wrow = rb * 32;
   if (wrow >= Lq || Lk <= 0) return false;
-  const int t = wrow / qi;  // item (query tile) of this row block
-  int nkt = (Lk + kl - 1) / kl;
-  if (causal) nkt = min(nkt, (min(Lq, (t + 1) * qi) - 1) / kl + 1);
+  const int t = wrow / QI;  // item (query tile) of this row block
+  int nkt = (Lk + KL - 1) / KL;
+  if (causal) nkt = min(nkt, (min(Lq, (t + 1) * QI) - 1) / KL + 1);
   int last = nkt - 1;
-  if (causal) last = min(last, (wrow + 31) / kl);  // tiles after the block's last query skipped
-  d_lo = wrow - (last + 1) * kl + 1;
+  if (causal) last = min(last, (wrow + 31) / KL);  // tiles after the block's last query skipped
+  d_lo = wrow - (last + 1) * KL + 1;
   d_hi = wrow + 31;
   return true;
 }
@@ -186,6 +202,9 @@ __device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causa
 // one memory round trip per batch rather than per row block. A row block whose range misses
 // entry c contributes +0.0, which leaves the running sum unchanged: the summation order, and so
 // the result bits, are those of the plain loop over rb.
+// The tile sizes are template parameters so that the per-row-block range arithmetic divides by
+// constants.
+template <int QI, int KL>
 __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int c = blockIdx.y * 256 + threadIdx.x;
@@ -198,18 +217,23 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     const int nrb = (Lq + 31) / 32;
     const int tb = a.tile_base[b];
     const int nb = a.nb;
-    const int per = a.tile_rows / 32;
+    constexpr int PER = QI / 32;
     constexpr int BATCH = 8;
-    for (int rb0 = 0; rb0 < nrb; rb0 += BATCH) {
+    // Row block rb reaches diagonals up to 32 rb + 31 (clamped), so entry c sees only row blocks
+    // rb >= (c - 31) / 32: the loop starts at the wave's first such block (its lowest c) and is
+    // empty past the last row block. Blocks it skips would each have added +0.0.
+    const int c_first = __builtin_amdgcn_readfirstlane(c);
+    const int rb_begin = c_first > 32 * nrb - 1 ? nrb : max(0, (c_first - 31) / 32);
+    for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
       float v[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int rb = rb0 + u;
         int d_lo, d_hi;
         v[u] = 0.0f;
-        if (rb < nrb && rowblock_range(rb, Lq, Lk, a.causal, a.tile_rows, a.loop_rows, d_lo, d_hi) &&
+        if (rb < nrb && rowblock_range<QI, KL>(rb, Lq, Lk, a.causal, d_lo, d_hi) &&
             c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1)) {
-          const int64_t row = (int64_t)(tb + rb / per) * per + rb % per;
+          const int64_t row = (int64_t)(tb + rb / PER) * PER + rb % PER;
           v[u] = a.part[(row * a.H + h) * nb + c];
         }
       }
@@ -241,7 +265,14 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.H * a.nb;
   if (n <= 0) return hipSuccess;
   if (a.B > 0) {
-    hipLaunchKernelGGL(dbias_stage_a, dim3(a.B * a.H, (a.nb + 255) / 256), dim3(256), 0, s, a);
+    const dim3 grid(a.B * a.H, (a.nb + 255) / 256);
+    if (a.tile_rows == 128 && a.loop_rows == 64) {
+      hipLaunchKernelGGL((dbias_stage_a<128, 64>), grid, dim3(256), 0, s, a);
+    } else if (a.tile_rows == 64 && a.loop_rows == 64) {
+      hipLaunchKernelGGL((dbias_stage_a<64, 64>), grid, dim3(256), 0, s, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
