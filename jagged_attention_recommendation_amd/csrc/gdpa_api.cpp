@@ -53,29 +53,41 @@ int bwd_k_item(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_K_ITEM; }
 int bwd_q_loop(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_Q_LOOP; }
 
 struct FwdLayout {
-  size_t header, items, total;
+  size_t header, items, splits, part_o, part_ml, total;
   int64_t max_items;
+  bool split;
 };
 
 FwdLayout fwd_layout(const gdpa_problem* p) {
   FwdLayout L;
-  L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype));
+  L.split = split_supported(to_prob(p));
+  L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype), L.split);
   L.header = 0;
   L.items = ALIGN;
-  L.total = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.splits = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.part_o = L.part_ml = L.total = L.splits;
+  if (L.split) {
+    const size_t rows = (size_t)SPLIT_SLOTS * fwd_tile_rows(p->dtype);
+    L.part_o = L.splits + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
+    L.part_ml = L.part_o + align_up(rows * p->D * sizeof(float));
+    L.total = L.part_ml + align_up(rows * 2 * sizeof(float));
+  }
   return L;
 }
 
 struct BwdLayout {
-  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, total;
+  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, splits_q, splits_k, split_slot,
+      part_dq, part_dk, part_dv, part_x, total;
   int64_t max_q_items, max_k_items, max_qtiles;
+  bool split;
 };
 
 BwdLayout bwd_layout(const gdpa_problem* p) {
   BwdLayout L;
+  L.split = split_supported(to_prob(p));
   const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
-  L.max_q_items = items_bound(p->total_q, p->B, p->H, tq);
-  L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk);
+  L.max_q_items = items_bound(p->total_q, p->B, p->H, tq, L.split);
+  L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk, L.split);
   L.max_qtiles = (p->total_q + tq - 1) / tq + p->B;
   L.header = 0;
   L.items_q = ALIGN;
@@ -84,13 +96,27 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   L.tile_base = L.dvec + align_up((size_t)p->total_q * p->H * sizeof(float));
   L.part = L.tile_base + align_up((size_t)(p->B + 1) * sizeof(int32_t));
   L.part_bh = L.part;
-  L.total = L.part;
+  size_t end = L.part;
   if (p->bias_buckets > 0) {
     // one partial row per 32-query row block and head, then one per sample and head
     const size_t rows = (size_t)L.max_qtiles * (tq / 32);
     L.part_bh = L.part + align_up(rows * p->H * p->bias_buckets * sizeof(float));
-    L.total = L.part_bh + align_up((size_t)p->B * p->H * p->bias_buckets * sizeof(float));
+    end = L.part_bh + align_up((size_t)p->B * p->H * p->bias_buckets * sizeof(float));
   }
+  L.splits_q = L.splits_k = L.split_slot = L.part_dq = L.part_dk = L.part_dv = L.part_x = end;
+  if (L.split) {
+    // split lists, the per-(tile, head) slot table, and the chunks' partial rows
+    L.splits_q = end;
+    L.splits_k = L.splits_q + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
+    L.split_slot = L.splits_k + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
+    L.part_dq = L.split_slot + align_up((size_t)L.max_qtiles * p->H * sizeof(int32_t));
+    L.part_dk = L.part_dq + align_up((size_t)SPLIT_SLOTS * tq * p->D * sizeof(float));
+    L.part_dv = L.part_dk + align_up((size_t)SPLIT_SLOTS * tk * p->D * sizeof(float));
+    L.part_x = L.part_dv + align_up((size_t)SPLIT_SLOTS * tk * p->D * sizeof(float));
+    end = L.part_x;
+    if (p->bias_buckets > 0) end += align_up((size_t)SPLIT_SLOTS * (tq / 32) * p->bias_buckets * sizeof(float));
+  }
+  L.total = end;
   return L;
 }
 
@@ -216,7 +242,8 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
   sa.causal = p->causal; sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
-  sa.tile_base = nullptr; sa.ws_header = ws + L.header; sa.items = ws + L.items;
+  sa.split = L.split ? 1 : 0; sa.tile_base = nullptr; sa.split_slot = nullptr;
+  sa.ws_header = ws + L.header; sa.items = ws + L.items; sa.splits = ws + L.splits;
   hipError_t e = launch_sched(sa, s);
   if (e != hipSuccess) return map_hip(e);
 
@@ -225,11 +252,13 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
   fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
   fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
-  fa.scale = p->scale;
+  fa.scale = p->scale; fa.splits = ws + L.splits;
+  fa.part_o = (float*)(ws + L.part_o); fa.part_ml = (float*)(ws + L.part_ml);
   const int grid = (int)L.max_items;
   if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
   else if (p->dtype == GDPA_BF16) e = launch_fwd_bf16(pr, fa, grid, s);
   else e = launch_fwd_mx(pr, fa, grid, s);
+  if (e == hipSuccess && L.split) e = launch_combine_fwd(pr, fa, s);
   return map_hip(e);
 }
 
@@ -267,13 +296,17 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
   sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
+  sa.split = L.split ? 1 : 0;
   SchedArgs sq = sa, sk = sa;
   sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
   sq.max_items = (int)L.max_q_items; sq.list = 0;
   sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
+  sq.splits = ws + L.splits_q;
+  sq.split_slot = L.split && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
   sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
   sk.max_items = (int)L.max_k_items; sk.list = 1;
-  sk.tile_base = nullptr; sk.items = ws + L.items_k;
+  sk.tile_base = nullptr; sk.items = ws + L.items_k; sk.splits = ws + L.splits_k;
+  sk.split_slot = nullptr;
   hipError_t e = launch_sched2(sq, sk, s);
   if (e != hipSuccess) return map_hip(e);
 
@@ -285,13 +318,20 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.items_q = ws + L.items_q; ba.items_k = ws + L.items_k;
   ba.dbias_part = p->bias_buckets > 0 ? (float*)(ws + L.part) : nullptr;
   ba.tile_base = (const int32_t*)(ws + L.tile_base);
+  ba.dbias_part_x = (float*)(ws + L.part_x);
+  ba.splits_q = ws + L.splits_q; ba.splits_k = ws + L.splits_k;
+  ba.part_dq = (float*)(ws + L.part_dq); ba.part_dk = (float*)(ws + L.part_dk);
+  ba.part_dv = (float*)(ws + L.part_dv);
   ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale;
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
+  if (e == hipSuccess && L.split) e = launch_combine_dq(pr, ba, s);
+  if (e == hipSuccess && L.split) e = launch_combine_dkdv(pr, ba, s);
   if (e != hipSuccess) return map_hip(e);
   if (p->bias_buckets > 0) {
     DbiasArgs da;
     da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
+    da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
     da.part = ba.dbias_part; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
     da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
     da.causal = p->causal; da.tile_rows = tq; da.loop_rows = bwd_k_loop(p->dtype);

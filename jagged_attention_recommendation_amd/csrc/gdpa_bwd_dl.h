@@ -82,12 +82,14 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   int nkt = (Lk + KL - 1) / KL;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
   if (i0 >= Lq) nkt = 0;
+  // key tiles of this item: all of them, or one chunk of a split tile
+  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
 
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
-  if (nkt > 0) {
-    issue_tile(sk0, K, 0, Lk, kv0, H, h, w, lane);
-    issue_tile(sv0, V, 0, Lk, kv0, H, h, w, lane);
+  if (kt_lo < kt_hi) {
+    issue_tile(sk0, K, kt_lo * KL, Lk, kv0, H, h, w, lane);
+    issue_tile(sv0, V, kt_lo * KL, Lk, kv0, H, h, w, lane);
   }
 
   const __bf16* Q = (const __bf16*)a.Q;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     Di = half_sum(part_d);
     if (qv) {
       lse2 = a.lse[row] * LOG2E;
-      if (g == 0) a.Dvec[row] = Di;
+      if (g == 0 && it.chunk == 0) a.Dvec[row] = Di;  // every chunk computes it; one writes it
     }
   }
 
@@ -122,9 +124,9 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
   int w_hi = 0;
   bool win_ok = false;
-  if (BIAS && nkt > 0) {  // raw diagonals iq - j: iq in [i0, i0 + QI), j in [0, nkt * KL)
-    w_hi = i0 + QI - 1;
-    const int lo = i0 - (nkt * KL - 1);
+  if (BIAS && kt_lo < kt_hi) {  // raw diagonals iq - j: iq in [i0, i0 + QI), j in the item's tiles
+    w_hi = i0 + QI - 1 - kt_lo * KL;
+    const int lo = i0 - (kt_hi * KL - 1);
     const bool ok = w_hi - lo + 1 <= BIAS_WMAX;
     if (ok)
       for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, nb - 1)] * inv_scale;
@@ -132,7 +134,10 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   }
   GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * 32 * DSP;
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
-  float* part = BIAS ? a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb : nullptr;
+  // partial row of this row block: canonical, or the chunk's slot row for a split tile
+  float* part = !BIAS ? nullptr
+                : it.slot < 0 ? a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb
+                              : a.dbias_part_x + ((int64_t)it.slot * (QI / 32) + w) * nb;
   float e_lo = 0.0f, e_hi = 0.0f;
   bool has_lo = false, has_hi = false;
   // Writes the complete diagonal d of this wave (value v) to its partial row; the ends of the
@@ -279,18 +284,18 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
 
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage stay in flight while the other stage is read.
-  for (int kt = 0; kt < nkt; kt += 2) {
+  for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads for tile kt have landed
     __syncthreads();                // ... and everyone else's; tile kt - 1 is done with stage 1
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kt_hi) {
       issue_tile(sk1, K, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
     }
     if (wave_active && !(CAUSAL && kt * KL > wrow + 31)) tile(sk0, sv0, kt * KL);
-    if (kt + 1 >= nkt) break;
+    if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < nkt) {
+    if (kt + 2 < kt_hi) {
       issue_tile(sk0, K, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
     }
@@ -308,6 +313,17 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
         if (has_hi) part[nb - 1] = e_hi;
       }
     }
+  }
+  if (it.slot >= 0) {  // chunk of a split tile: fp32 partial rows, summed later in chunk order
+    if (!wave_active) return;
+    float* pq = a.part_dq + ((int64_t)it.slot * QI + w * 32 + l32) * D;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(f32x4*)(pq + n * 32 + r4 * 8 + 4 * g) =
+            f32x4{dq[n][4 * r4], dq[n][4 * r4 + 1], dq[n][4 * r4 + 2], dq[n][4 * r4 + 3]};
+    return;
   }
   if (!qv) return;
   __bf16* dqrow = (__bf16*)a.dQ + row * D;
@@ -353,7 +369,9 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
 
   const int nqt = (Lq + QL - 1) / QL;
   const int qt0 = CAUSAL ? j0 / QL : 0;
-  const int nt = j0 < Lk && qt0 < nqt ? nqt - qt0 : 0;  // query tiles this item visits
+  const int nt = j0 < Lk && qt0 < nqt ? nqt - qt0 : 0;  // query tiles this key tile visits
+  // the item's query tiles qt0 + [t_lo, t_hi): all of them, or one chunk of a split tile
+  const int t_lo = it.lo, t_hi = min(it.hi, nt);
 
   const __bf16* Q = (const __bf16*)a.Q;
   const __bf16* dO = (const __bf16*)a.dO;
@@ -372,7 +390,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)(srt + w * QL), 4, r * H * 4, 0, 0, 0);
     }
   };
-  if (nt > 0) issue(sq0, so0, rt, qt0);
+  if (t_lo < t_hi) issue(sq0, so0, rt, qt0 + t_lo);
 
   bf16x8 kop[D / 16], vop[D / 16];
 #pragma unroll
@@ -393,9 +411,9 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   // are one base address plus constant offsets
   int w_lo = 0;
   bool win_ok = false;
-  if (BIAS && nt > 0) {  // raw diagonals i - jk: i in [qt0 * QL, nqt * QL), jk in [j0, j0 + KI)
-    w_lo = qt0 * QL - (j0 + KI - 1);
-    const int w_hi = nqt * QL - 1 - j0;
+  if (BIAS && t_lo < t_hi) {  // raw diagonals i - jk: i in the item's query tiles, jk in [j0, j0 + KI)
+    w_lo = (qt0 + t_lo) * QL - (j0 + KI - 1);
+    const int w_hi = (qt0 + t_hi) * QL - 1 - j0;
     const bool ok = w_hi - w_lo + 1 <= BIAS_WMAX;
     if (ok)
       for (int t = tid; t <= w_hi - w_lo; t += NT) bwin[t] = bias_h[clampi(w_lo + t, 0, nb - 1)] * inv_scale;
@@ -508,22 +526,36 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   // Two stages, as in the dQ kernel.
   GDPA_LDS float* rt0 = rt;
   GDPA_LDS float* rt1 = rt + (SM ? 2 * QL : 0);
-  for (int t = 0; t < nt; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < nt) issue(sq1, so1, rt1, qt0 + t + 1);
+    if (t + 1 < t_hi) issue(sq1, so1, rt1, qt0 + t + 1);
     {
       const int i0 = (qt0 + t) * QL;
       if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq0, so0, rt0, i0);
     }
-    if (t + 1 >= nt) break;
+    if (t + 1 >= t_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < nt) issue(sq0, so0, rt0, qt0 + t + 2);
+    if (t + 2 < t_hi) issue(sq0, so0, rt0, qt0 + t + 2);
     {
       const int i0 = (qt0 + t + 1) * QL;
       if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq1, so1, rt1, i0);
     }
+  }
+  if (it.slot >= 0) {  // chunk of a split tile: fp32 partial rows, summed later in chunk order
+    if (!wave_active) return;
+    const int64_t prow = ((int64_t)it.slot * KI + w * 32 + l32) * D;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        *(f32x4*)(a.part_dk + prow + n * 32 + r4 * 8 + 4 * g) =
+            f32x4{dk[n][4 * r4], dk[n][4 * r4 + 1], dk[n][4 * r4 + 2], dk[n][4 * r4 + 3]};
+        *(f32x4*)(a.part_dv + prow + n * 32 + r4 * 8 + 4 * g) =
+            f32x4{dv[n][4 * r4], dv[n][4 * r4 + 1], dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]};
+      }
+    return;
   }
   if (!kvalid) return;
   __bf16* dkrow = (__bf16*)a.dK + krow * D;

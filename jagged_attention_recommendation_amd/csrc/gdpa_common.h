@@ -33,9 +33,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define GDPA_LDS __attribute__((address_space(3)))
 
 // Work item of the jagged scheduler: sample, tile index (of queries for forward / dQ, of keys
-// for dK/dV), head, and a spare word.
+// for dK/dV), head, the canonical index of the (sample, tile), and the range [lo, hi) of
+// inner-loop tiles the item covers (counted from the first tile the tile visits). A long tile
+// split into chunks has one item per chunk: slot is the chunk's partial-result slot and chunk its
+// index; an unsplit item has slot -1 and chunk 0.
 struct Item {
   int b, tile, h, aux;
+  int lo, hi, slot, chunk;
+};
+
+// A split tile: its n chunks wrote partial results to slots slot .. slot + n - 1.
+struct Split {
+  int b, tile, h, n, slot, aux, pad0, pad1;
 };
 
 // Workspace header (first 256 bytes of every workspace).
@@ -43,7 +52,11 @@ struct WsHeader {
   int error;      // 0 ok, 1 bad q_offsets, 2 bad kv_offsets
   int n_items;    // items written by the scheduler
   int n_items2;   // second list (backward: key-tile items)
-  int pad[61];
+  int n_split;    // split tiles of the first list
+  int n_split2;   // split tiles of the second list
+  int chunk;      // inner tiles per chunk, first list (0: no splitting)
+  int chunk2;     // inner tiles per chunk, second list
+  int pad[57];
 };
 
 constexpr float LOG2E = 1.4426950408889634f;

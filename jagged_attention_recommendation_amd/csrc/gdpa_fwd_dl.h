@@ -55,12 +55,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
 
   int nkt = (Lk + BN - 1) / BN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, row_blk + BM) - 1) / BN + 1);
+  // key tiles of this item: all of them, or one chunk of a split tile
+  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
 
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
-  if (nkt > 0) {
-    issue_tile(sk0, K, 0, Lk, kv0, H, h, w, lane);
-    issue_tile(sv0, V, 0, Lk, kv0, H, h, w, lane);
+  if (kt_lo < kt_hi) {
+    issue_tile(sk0, K, kt_lo * BN, Lk, kv0, H, h, w, lane);
+    issue_tile(sv0, V, kt_lo * BN, Lk, kv0, H, h, w, lane);
   }
 
   bf16x8 qop[D / 16];
@@ -79,9 +81,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
   int w_hi = 0;
   bool win_ok = false;
-  if (BIAS && nkt > 0) {
-    w_hi = row_blk + BM - 1;
-    const int lo = row_blk - (nkt * BN - 1);
+  if (BIAS && kt_lo < kt_hi) {  // raw diagonals iq - j: iq in the item, j in its key tiles
+    w_hi = row_blk + BM - 1 - kt_lo * BN;
+    const int lo = row_blk - (kt_hi * BN - 1);
     bool ok = w_hi - lo + 1 <= WMAX;
     if (ok)
       for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, a.nb - 1)] * inv_scale;
@@ -180,18 +182,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
 
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage can then stay in flight while the other stage is read.
-  for (int kt = 0; kt < nkt; kt += 2) {
+  for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads for tile kt have landed
     __syncthreads();                // ... and everyone else's; tile kt - 1 is done with stage 1
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kt_hi) {
       issue_tile(sk1, K, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
     }
     if (wave_active && !(CAUSAL && kt * BN > wrow + 31)) tile(sk0, sv0, kt * BN);
-    if (kt + 1 >= nkt) break;
+    if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 2 < nkt) {
+    if (kt + 2 < kt_hi) {
       issue_tile(sk0, K, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
     }
@@ -199,6 +201,26 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   }
 
   if (!wave_active) return;
+  if (it.slot >= 0) {
+    // chunk of a split tile: unnormalised output rows and, for softmax, the running max (log2
+    // units) and sum, combined later in chunk order
+    float* po = a.part_o + ((int64_t)it.slot * BM + w * 32 + l32) * D;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(f32x4*)(po + n * 32 + r4 * 8 + 4 * g) =
+            f32x4{o[n][4 * r4], o[n][4 * r4 + 1], o[n][4 * r4 + 2], o[n][4 * r4 + 3]};
+    if (ACT == ACT_SOFTMAX) {
+      const float lt = half_sum(l_run);
+      if (g == 0) {
+        float* pml = a.part_ml + (int64_t)it.slot * 2 * BM;
+        pml[w * 32 + l32] = m_run;
+        pml[BM + w * 32 + l32] = lt;
+      }
+    }
+    return;
+  }
   float inv = 1.0f;
   if (ACT == ACT_SOFTMAX) {
     const float lt = half_sum(l_run);

@@ -19,6 +19,15 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_MX = 2 };
 // Scheduler modes: items over query tiles (forward, dQ) or over key tiles (dK/dV).
 enum { SCHED_QTILES = 0, SCHED_KTILES = 1 };
 
+// Long tiles are split into chunks of inner tiles when splitting is on: the chunk length is
+// T = max(SPLIT_MIN_TILES, ceil(total cost / SPLIT_NSLOT)), the mean load of SPLIT_NSLOT
+// concurrent workgroups, and a tile of cost c > T becomes ceil(c / T) chunks. Split tiles each
+// cost more than T, so there are at most total / T <= SPLIT_NSLOT of them and at most
+// 2 * SPLIT_NSLOT chunks among them: the partial-result storage has a fixed size.
+constexpr int SPLIT_NSLOT = 256;
+constexpr int SPLIT_SLOTS = 2 * SPLIT_NSLOT;
+constexpr int SPLIT_MIN_TILES = 8;
+
 struct SchedArgs {
   const int32_t* q_off;
   const int32_t* kv_off;
@@ -27,10 +36,13 @@ struct SchedArgs {
   int mode, causal;
   int tile_item, tile_loop;  // rows per item tile / rows per inner-loop tile
   int max_items;
-  int list;                  // 0: header.n_items, 1: header.n_items2
+  int list;                  // 0: first list of the header, 1: second list
+  int split;                 // 1: split long tiles into chunks
   int32_t* tile_base;        // optional [B + 1]: canonical index of each sample's first tile
+  int32_t* split_slot;       // optional [canonical tiles * H]: first slot of a split tile, or -1
   void* ws_header;
   void* items;
+  void* splits;              // [SPLIT_NSLOT] split tiles (when split)
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
@@ -40,11 +52,15 @@ hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);
 // sums of dS its queries produced (one row of NB floats, canonical row order); the reduction sums
 // them per sample in row-block order (stage A, into part_bh [B, H, NB]) and then over samples in
 // order (stage B).
+// Rows of split dQ tiles go to the slot rows part_x[(slot * R + rb % R) * NB], one per chunk,
+// and are summed in chunk order.
 struct DbiasArgs {
   const int32_t* q_off;
   const int32_t* kv_off;
   const int32_t* tile_base;
+  const int32_t* split_slot;  // [canonical tiles * H] or null
   const float* part;
+  const float* part_x;
   float* part_bh;
   float* dbias;
   const void* hdr;
@@ -55,8 +71,8 @@ struct DbiasArgs {
 hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s);
 
 // Upper bound on the number of items the scheduler can emit.
-inline int64_t items_bound(int64_t total_rows, int B, int H, int tile) {
-  return (int64_t)H * ((total_rows + tile - 1) / tile + (int64_t)B);
+inline int64_t items_bound(int64_t total_rows, int B, int H, int tile, bool split) {
+  return (int64_t)H * ((total_rows + tile - 1) / tile + (int64_t)B) + (split ? SPLIT_SLOTS : 0);
 }
 
 struct FwdArgs {
@@ -73,6 +89,9 @@ struct FwdArgs {
   float* lse;
   const void* hdr;
   const void* items;
+  const void* splits;  // split tiles of the item list
+  float* part_o;   // split chunks: [SPLIT_SLOTS][BM][D] fp32 unnormalised output
+  float* part_ml;  // split chunks (softmax): [SPLIT_SLOTS][2][BM] running max (log2 units), sum
   int H, nb;
   float scale;
 };
@@ -109,7 +128,13 @@ struct BwdArgs {
   const void* items_q;   // query-tile items (dQ)
   const void* items_k;   // key-tile items (dK/dV)
   float* dbias_part;     // [n_rowblocks, H, NB] per 32-query row block diagonal sums of dS
+  float* dbias_part_x;   // split chunks: [SPLIT_SLOTS * QI / 32, NB]
+  const void* splits_q;  // split tiles of the query-tile list
+  const void* splits_k;  // split tiles of the key-tile list
   const int32_t* tile_base;  // [B + 1] canonical index of each sample's first query tile
+  float* part_dq;        // split chunks: [SPLIT_SLOTS][QI][D] fp32
+  float* part_dk;        // split chunks: [SPLIT_SLOTS][KI][D] fp32
+  float* part_dv;
   int H, nb;
   float scale;
 };
@@ -120,6 +145,13 @@ constexpr int BWD_K_ITEM = 128;  // keys per dK/dV work item (bf16)
 constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
+
+// Fixed-order combines of split chunks (D = 128 bf16 path).
+hipError_t launch_combine_fwd(const Prob& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_combine_dq(const Prob& p, const BwdArgs& a, hipStream_t s);
+hipError_t launch_combine_dkdv(const Prob& p, const BwdArgs& a, hipStream_t s);
+// Whether the kernels for this problem take split items.
+inline bool split_supported(const Prob& p) { return p.dtype == DT_BF16 && p.D == 128; }
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
 // Profiling hook: brackets launches of one kernel with HIP events (see gdpa_profile_start).

@@ -70,7 +70,9 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   __shared__ int bucket[NBUCKET];
   __shared__ int cnt[SNT];  // inclusive scan of the chunk's per-sample tile counts
   __shared__ int wsum[SNT / 64];
-  __shared__ int err, carry;
+  __shared__ int err, carry, split_count, slot_count;
+  __shared__ unsigned long long wtot[SNT / 64];
+  __shared__ int wmax[SNT / 64];
   const int tid = threadIdx.x;
   WsHeader* hdr = (WsHeader*)a.ws_header;
   Item* items = (Item*)a.items;
@@ -89,7 +91,11 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   if (err != 0) {
     if (tid == 0) {
       hdr->error = err;
-      if (a.list == 0) hdr->n_items = 0; else hdr->n_items2 = 0;
+      if (a.list == 0) {
+        hdr->n_items = 0; hdr->n_split = 0;
+      } else {
+        hdr->n_items2 = 0; hdr->n_split2 = 0;
+      }
     }
     return;
   }
@@ -126,13 +132,63 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       __syncthreads();
     }
   };
-  // 1. histogram of costs; bucket NBUCKET-1-cost puts expensive items first
+  // 1. histogram of tile costs (bucket NBUCKET-1-cost puts expensive items first), and with
+  //    splitting the total cost (all heads) and the largest tile cost, reduced over the block
+  unsigned long long tot = 0;
+  int mx = 0;
   for_each_tile([&](int b, int t, int) {
     const int Lq = a.q_off[b + 1] - a.q_off[b];
     const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = min(item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl), NBUCKET - 1);
-    atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
+    const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+    atomicAdd(&bucket[NBUCKET - 1 - min(c, NBUCKET - 1)], a.H);
+    tot += (unsigned long long)c;
+    mx = max(mx, c);
   });
+  int T = 0x7fffffff;  // chunk length; no splitting unless a tile costs more
+  if (a.split) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      tot += __shfl_xor(tot, off, 64);
+      mx = max(mx, __shfl_xor(mx, off, 64));
+    }
+    if ((tid & 63) == 0) {
+      wtot[tid >> 6] = tot;
+      wmax[tid >> 6] = mx;
+    }
+    __syncthreads();
+    unsigned long long total = 0;
+    int biggest = 0;
+    for (int w = 0; w < SNT / 64; ++w) {
+      total += wtot[w];
+      biggest = max(biggest, wmax[w]);
+    }
+    total *= (unsigned long long)a.H;
+    const unsigned long long tpc = (total + SPLIT_NSLOT - 1) / SPLIT_NSLOT;
+    const int t_mean = (int)min(max(tpc, (unsigned long long)SPLIT_MIN_TILES), (unsigned long long)0x7fffffff);
+    if (biggest > t_mean) {
+      T = t_mean;
+      // some tiles are split: the histogram counts chunks instead
+      __syncthreads();
+      bucket[tid] = 0;
+      __syncthreads();
+      for_each_tile([&](int b, int t, int) {
+        const int Lq = a.q_off[b + 1] - a.q_off[b];
+        const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+        const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+        const int n = c > T ? (c + T - 1) / T : 1;
+        for (int k = 0; k < n; ++k) {
+          const int cc = n == 1 ? c : min(T, c - k * T);
+          atomicAdd(&bucket[NBUCKET - 1 - min(cc, NBUCKET - 1)], a.H);
+        }
+      });
+    }
+  }
+  if (tid == 0) {
+    split_count = 0;
+    slot_count = 0;
+  }
+  // chunks of a tile of cost c: ceil(c / T) when c > T (the last one may be shorter), else one
+  auto chunks = [&](int c) { return c > T ? (c + T - 1) / T : 1; };
   __syncthreads();
   // 2. exclusive scan over the buckets (NBUCKET == SNT)
   const int own = bucket[tid];
@@ -141,25 +197,62 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   __syncthreads();
   bucket[tid] -= own;
   __syncthreads();
-  // 3. scatter (b, tile, h, canonical tile index)
+  // 3. scatter the chunks (b, tile, h, canonical tile index, inner range, slot, chunk); a split
+  //    tile takes n consecutive slots per head and one entry per head in the split list
   for_each_tile([&](int b, int t, int canon) {
     const int Lq = a.q_off[b + 1] - a.q_off[b];
     const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = min(item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl), NBUCKET - 1);
-    const int pos = atomicAdd(&bucket[NBUCKET - 1 - c], a.H);
-    for (int h = 0; h < a.H; ++h) {
-      if (pos + h < a.max_items) {
-        Item it;
-        it.b = b; it.tile = t; it.h = h; it.aux = canon;
-        items[pos + h] = it;
+    const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+    const int n = chunks(c);
+    int sbase = -1;
+    if (n > 1) {
+      sbase = atomicAdd(&slot_count, n * a.H);
+      const int si = atomicAdd(&split_count, a.H);
+      if (sbase + n * a.H > SPLIT_SLOTS || si + a.H > SPLIT_NSLOT) {
+        atomicOr(&err, 4);  // cannot happen: the chunk length bounds both counts
+        sbase = -1;
+      } else {
+        Split* sp = (Split*)a.splits;
+        for (int h = 0; h < a.H; ++h) {
+          Split e;
+          e.b = b; e.tile = t; e.h = h; e.n = n; e.slot = sbase + h * n; e.aux = canon;
+          e.pad0 = 0; e.pad1 = 0;
+          sp[si + h] = e;
+        }
+      }
+    }
+    if (a.split_slot != nullptr)
+      for (int h = 0; h < a.H; ++h) a.split_slot[(int64_t)canon * a.H + h] = sbase < 0 ? -1 : sbase + h * n;
+    for (int k = 0; k < n; ++k) {
+      const int cc = n == 1 ? c : min(T, c - k * T);
+      const int pos = atomicAdd(&bucket[NBUCKET - 1 - min(cc, NBUCKET - 1)], a.H);
+      for (int h = 0; h < a.H; ++h) {
+        if (pos + h < a.max_items) {
+          Item it;
+          it.b = b; it.tile = t; it.h = h; it.aux = canon;
+          it.lo = n == 1 ? 0 : k * T;
+          it.hi = n == 1 ? c : min(c, (k + 1) * T);
+          it.slot = sbase < 0 ? -1 : sbase + h * n + k;
+          it.chunk = k;
+          items[pos + h] = it;
+        }
       }
     }
   });
+  __syncthreads();
   if (tid == 0) {
+    // Only the first list writes the error word (both lists see the same offsets); a list that
+    // failed on its own is left empty.
     if (a.tile_base != nullptr) a.tile_base[a.B] = carry;
-    hdr->error = 0;
-    const int n = min(total_items, a.max_items);
-    if (a.list == 0) hdr->n_items = n; else hdr->n_items2 = n;
+    const int n = err != 0 ? 0 : min(total_items, a.max_items);
+    const int ns = err != 0 ? 0 : split_count;
+    const int chunk = a.split && T != 0x7fffffff ? T : 0;
+    if (a.list == 0) {
+      hdr->error = err;
+      hdr->n_items = n; hdr->n_split = ns; hdr->chunk = chunk;
+    } else {
+      hdr->n_items2 = n; hdr->n_split2 = ns; hdr->chunk2 = chunk;
+    }
   }
 }
 
@@ -184,17 +277,27 @@ hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) 
 // and wrote exactly the clamped
 // diagonals of its raw range [32rb - (k_end - 1), 32rb + 31], k_end = keys it visited; the edge
 // entries 0 and NB-1 collect every raw diagonal that clamps to them.
+// Inner tiles a dQ item of query tile t visits (all key tiles, or those up to the causal limit).
 template <int QI, int KL>
-__device__ __forceinline__ bool rowblock_range(int rb, int Lq, int Lk, int causal, int& d_lo, int& d_hi) {
-  const int wrow = rb * 32;
-  if (wrow >= Lq || Lk <= 0) return false;
-  const int t = wrow / QI;  // item (query tile) of this row block
+__device__ __forceinline__ int qtile_cost(int t, int Lq, int Lk, int causal) {
+  if (Lk <= 0) return 0;
   int nkt = (Lk + KL - 1) / KL;
   if (causal) nkt = min(nkt, (min(Lq, (t + 1) * QI) - 1) / KL + 1);
-  int last = nkt - 1;
+  return nkt;
+}
+
+// Raw diagonal range [d_lo, d_hi] that row block rb wrote while its item (or chunk) visited key
+// tiles [lo, hi): the wave stops after its causal limit; false if it visited none.
+template <int KL>
+__device__ __forceinline__ bool chunk_range(int rb, int Lq, int causal, int lo, int hi, int& d_lo,
+                                            int& d_hi) {
+  const int wrow = rb * 32;
+  if (wrow >= Lq) return false;
+  int last = hi - 1;
   if (causal) last = min(last, (wrow + 31) / KL);  // tiles after the block's last query skipped
+  if (lo > last) return false;
   d_lo = wrow - (last + 1) * KL + 1;
-  d_hi = wrow + 31;
+  d_hi = wrow + 31 - lo * KL;
   return true;
 }
 
@@ -231,10 +334,27 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
         const int rb = rb0 + u;
         int d_lo, d_hi;
         v[u] = 0.0f;
-        if (rb < nrb && rowblock_range<QI, KL>(rb, Lq, Lk, a.causal, d_lo, d_hi) &&
-            c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1)) {
-          const int64_t row = (int64_t)(tb + rb / PER) * PER + rb % PER;
-          v[u] = a.part[(row * a.H + h) * nb + c];
+        if (rb >= nrb) continue;
+        const int t = rb / PER;
+        const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal);
+        const int sb = a.split_slot != nullptr ? a.split_slot[(int64_t)(tb + t) * a.H + h] : -1;
+        if (sb < 0) {
+          if (chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi) && c >= clampi(d_lo, 0, nb - 1) &&
+              c <= clampi(d_hi, 0, nb - 1)) {
+            const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
+            v[u] = a.part[(row * a.H + h) * nb + c];
+          }
+        } else {
+          // split tile: its chunks' rows, in chunk order
+          const int T = hdr->chunk;
+          const int n = (nkt + T - 1) / T;
+          float sv = 0.0f;
+          for (int k = 0; k < n; ++k) {
+            if (chunk_range<KL>(rb, Lq, a.causal, k * T, min(nkt, (k + 1) * T), d_lo, d_hi) &&
+                c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1))
+              sv += a.part_x[((int64_t)(sb + k) * PER + rb % PER) * nb + c];
+          }
+          v[u] = sv;
         }
       }
 #pragma unroll

@@ -189,6 +189,17 @@ def read_device_error(workspace, stream=None):
     return int(err.value)
 
 
+def workspace_header(workspace):
+    """Scheduler counters of the last call that used this workspace (diagnostics; synchronises).
+
+    Keys: error, items, items2 (forward / dQ list, dK/dV list), split, split2 (tiles split into
+    chunks), chunk, chunk2 (inner tiles per chunk; 0 when splitting is off).
+    """
+    torch.cuda.synchronize(workspace.device)
+    w = workspace[:28].view(torch.int32).cpu().tolist()
+    return dict(zip(["error", "items", "items2", "split", "split2", "chunk", "chunk2"], w))
+
+
 def profile_start(kernels):
     """Bracket every launch of the given kernels ("fwd", "dq", "dkdv", "sched") with HIP events."""
     mask = 0

@@ -51,7 +51,7 @@ def _load():
                                     c_int, c_double, dp, dp, c_int]
     lib.gdpa_oracle_fwd.restype = c_int
     lib.gdpa_oracle_bwd.argtypes = [c_int, c_int, c_int, ip, ip, dp, dp, dp, dp, dp, c_int, c_int,
-                                    c_int, c_double, dp, dp, dp, dp, dp, c_int]
+                                    c_int, c_double, dp, dp, dp, dp, dp, dp, c_int]
     lib.gdpa_oracle_bwd.restype = c_int
     lib.gdpa_oracle_act.argtypes = [c_int, dp, c_long, dp, dp]
     lib.gdpa_oracle_act.restype = None
@@ -123,11 +123,13 @@ def fwd(q_off, kv_off, Q, K, V, *, act="softmax", causal=False, scale=None, bias
 
 
 def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, bias=None,
-        nthreads=None):
+        nthreads=None, error_scale=False):
     """Backward pass of the loss sum(dO * O).
 
-    Returns dict with dQ, dK, dV (fp64, same layouts as Q/K/V), dbias ([H, NB] or None) and
-    D ([total_q, H], the softmax row term sum_j p_ij dp_ij; 0 for GDPA).
+    Returns dict with dQ, dK, dV (fp64, same layouts as Q/K/V), dbias ([H, NB] or None),
+    dbias_scale ([H, NB] or None: the error scale of each bias bucket under a rounded forward
+    output, see the C source; computed when error_scale) and D ([total_q, H], the softmax row term sum_j p_ij dp_ij; 0 for
+    GDPA).
     """
     lib = _load()
     q_off, kv_off = _i32(q_off), _i32(kv_off)
@@ -140,10 +142,12 @@ def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, 
     nb = 0
     bias_arr = np.zeros(1)
     dbias = np.zeros(1)
+    dscale = np.zeros(1)
     if bias is not None:
         bias_arr = _f64(bias)
         nb = bias_arr.shape[1]
         dbias = np.empty((H, nb), dtype=np.float64)
+        dscale = np.empty((H, nb), dtype=np.float64)
     dQ = np.empty((total_q, H, D))
     dK = np.empty((total_kv, H, D))
     dV = np.empty((total_kv, H, D))
@@ -155,10 +159,12 @@ def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, 
                              int(bool(causal)), float(scale), _ptr(dQ, ctypes.c_double),
                              _ptr(dK, ctypes.c_double), _ptr(dV, ctypes.c_double),
                              _ptr(dbias, ctypes.c_double), _ptr(Dv, ctypes.c_double),
+                             _ptr(dscale, ctypes.c_double) if error_scale and nb > 0 else None,
                              nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle bwd rejected its arguments (rc={rc})")
-    return {"dQ": dQ, "dK": dK, "dV": dV, "dbias": dbias if nb > 0 else None, "D": Dv}
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dbias": dbias if nb > 0 else None,
+            "dbias_scale": dscale if error_scale and nb > 0 else None, "D": Dv}
 
 
 def act(name, x, derivative=False):

@@ -29,6 +29,15 @@
  *     GDPA:    ds_ij = dp_ij act'(s_ij)
  *     dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij do_i
  *     dbias[h,r] = sum over b and valid (i,j) with clamp(i-j,0,NB-1) = r of ds_ij
+ *   error scale of dbias (optional output, not a result): a low-precision softmax backward forms
+ *   D_i from a forward output whose element o_ic carries independent rounding errors: one per
+ *   probability in sum_j p_ij v_jc and one when o_ic is stored. With errors of relative size eps
+ *   and unit variance per |x|^2, D_i moves with variance eps^2 w_i,
+ *     w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2),
+ *   and bucket r, which takes m_ir = sum of p_ij over the row's pairs in r, moves with variance
+ *   eps^2 sum_i m_ir^2 w_i. dbias_scale[h,r] = sqrt(sum over b, i of m_ir^2 w_i) (0 for GDPA,
+ *   which has no D_i). Buckets that sum whole rows cancel (softmax rows of ds sum to 0), so this
+ *   term, not |dbias|, sets how close a rounded backward can come there.
  *   gelu_tanh(x) = x/2 (1 + tanh(c (x + a x^3))), c = sqrt(2/pi), a = 0.044715
  *   silu(x)      = x sigmoid(x)
  *
@@ -203,7 +212,8 @@ int gdpa_oracle_fwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
 int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv_off,
                     const double* Q, const double* K, const double* V, const double* dO,
                     const double* bias, int nb, int act, int causal, double scale, double* dQ,
-                    double* dK, double* dV, double* dbias, double* Dvec, int nthreads) {
+                    double* dK, double* dV, double* dbias, double* Dvec, double* dbias_scale,
+                    int nthreads) {
   if (B < 0 || H <= 0 || D <= 0 || nb < 0) return 1;
   if (act < 0 || act > 2) return 1;
   if (check_offsets(B, q_off) || check_offsets(B, kv_off)) return 1;
@@ -218,9 +228,17 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
   memset(dV, 0, sizeof(double) * (size_t)total_kv * H * D);
   /* one dbias partial per (sample, head) task, reduced over samples in order afterwards */
   double* dbias_part = NULL;
+  double* scale_part = NULL;
   if (nb > 0 && dbias) {
     dbias_part = (double*)calloc((size_t)(ntask > 0 ? ntask : 1) * nb, sizeof(double));
     if (!dbias_part) return 2;
+  }
+  if (nb > 0 && dbias_scale && act == ORACLE_ACT_SOFTMAX) {
+    scale_part = (double*)calloc((size_t)(ntask > 0 ? ntask : 1) * nb, sizeof(double));
+    if (!scale_part) {
+      free(dbias_part);
+      return 2;
+    }
   }
   int bad = 0;
 #pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
@@ -230,7 +248,9 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
     double* dp = (double*)malloc(sizeof(double) * (size_t)(maxk + 1));
     double* ds = (double*)malloc(sizeof(double) * (size_t)(maxk + 1));
     unsigned char* valid = (unsigned char*)malloc((size_t)(maxk + 1));
-    if (!s || !p || !dp || !ds || !valid) {
+    double* pv = (double*)malloc(sizeof(double) * (size_t)D * 2);
+    double* mr = (double*)calloc((size_t)(nb > 0 ? nb : 1), sizeof(double));
+    if (!s || !p || !dp || !ds || !valid || !pv || !mr) {
 #pragma omp atomic write
       bad = 1;
     } else {
@@ -243,6 +263,7 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
         const double* Vb = V + (size_t)k0 * H * D;
         const double* bias_h = nb > 0 ? bias + (size_t)h * nb : NULL;
         double* part = dbias_part ? dbias_part + (size_t)t * nb : NULL;
+        double* spart = scale_part ? scale_part + (size_t)t * nb : NULL;
         for (long i = 0; i < Lq; ++i) {
           size_t row = ((size_t)(q0 + i) * H + h);
           const double* qi = Q + row * D;
@@ -279,9 +300,34 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
             }
             if (part) part[bias_index(i, j, nb)] += ds[j];
           }
+          if (spart) {
+            /* w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2); m_ir per bucket of the row */
+            double* o2 = pv;
+            double* pv2 = pv + D;
+            for (int c = 0; c < D; ++c) o2[c] = pv2[c] = 0.0;
+            for (long j = 0; j < Lk; ++j) {
+              if (!valid[j]) continue;
+              const double* vj = Vb + (size_t)j * H * D + (size_t)h * D;
+              for (int c = 0; c < D; ++c) {
+                o2[c] += p[j] * vj[c];
+                pv2[c] += p[j] * p[j] * vj[c] * vj[c];
+              }
+            }
+            double wi = 0.0;
+            for (int c = 0; c < D; ++c) wi += doi[c] * doi[c] * (o2[c] * o2[c] + pv2[c]);
+            for (long j = 0; j < Lk; ++j)
+              if (valid[j]) mr[bias_index(i, j, nb)] += p[j];
+            /* the row's buckets are bias_index(i, Lk - 1) .. bias_index(i, 0) */
+            for (int r = bias_index(i, Lk - 1, nb); r <= bias_index(i, 0, nb); ++r) {
+              spart[r] += mr[r] * mr[r] * wi;
+              mr[r] = 0.0;
+            }
+          }
         }
       }
     }
+    free(pv);
+    free(mr);
     free(s);
     free(p);
     free(dp);
@@ -299,6 +345,16 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
   } else if (dbias && nb > 0) {
     memset(dbias, 0, sizeof(double) * (size_t)H * nb);
   }
+  if (dbias_scale && nb > 0) {
+    for (int h = 0; h < H; ++h)
+      for (int r = 0; r < nb; ++r) {
+        double acc = 0.0;
+        if (scale_part)
+          for (int b = 0; b < B; ++b) acc += scale_part[((size_t)b * H + h) * nb + r];
+        dbias_scale[(size_t)h * nb + r] = sqrt(acc);
+      }
+  }
+  free(scale_part);
   return bad ? 2 : 0;
 }
 

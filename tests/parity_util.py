@@ -61,7 +61,8 @@ def oracle_fwd(p, nthreads=None):
 def oracle_bwd(p, nthreads=None):
     return oracle.bwd(p.q_off, p.kv_off, host_f64(p, "Q"), host_f64(p, "K"), host_f64(p, "V"),
                       host_f64(p, "dO"), act=p.act, causal=p.causal, scale=p.scale,
-                      bias=None if p.bias is None else p.bias.astype(np.float64), nthreads=nthreads)
+                      bias=None if p.bias is None else p.bias.astype(np.float64), nthreads=nthreads,
+                      error_scale=True)
 
 
 def block_scale(r, off):

@@ -28,12 +28,21 @@ def run_fwd_bwd(p):
     return dq, dk, dv, dbias
 
 
-def assert_dbias_close(g, r, name):
+def assert_dbias_close(g, r, name, err_scale=None):
+    """Bias gradient: the bf16 tolerance on the table's rms and each entry, plus 8 standard
+    deviations of the error a bf16 forward output puts into the bucket. The softmax backward
+    forms D_i from the forward output O, whose elements carry two bf16 roundings (P rounded for
+    P V, then O stored), each of standard deviation 2^-9 |x| / sqrt(3); a bucket that sums whole
+    rows of dS cancels (the rows sum to zero) and keeps that error. err_scale is the oracle's
+    square root of the bucket's error variance in units of those roundings."""
     g = g.detach().double().cpu().numpy()
     atol, rtol = TOL["bf16"]
     s = max(1.0, float(np.sqrt((r ** 2).mean())))
     err = np.abs(g - r)
-    bad = err > atol * s + rtol * np.abs(r)
+    tol = atol * s + rtol * np.abs(r)
+    if err_scale is not None:
+        tol = tol + 8.0 * 2.0 ** -9 / np.sqrt(3.0) * err_scale
+    bad = err > tol
     assert not bad.any(), f"{name}: {bad.sum()} bad, max err {err.max():.3e}, rms {s:.3e}"
 
 
@@ -45,7 +54,7 @@ def check_bwd(p):
     assert_close(dk, ref["dK"], p.kv_off, kind, f"{p.name} dK")
     assert_close(dv, ref["dV"], p.kv_off, kind, f"{p.name} dV")
     if p.bias is not None:
-        assert_dbias_close(dbias, ref["dbias"], f"{p.name} dbias")
+        assert_dbias_close(dbias, ref["dbias"], f"{p.name} dbias", ref["dbias_scale"])
 
 
 def small(seed, D, act, causal, nb, dtype="bf16", B=5, H=2, lo=1, hi=300, same=True):

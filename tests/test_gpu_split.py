@@ -1,0 +1,103 @@
+"""Parity of split tiles: long tiles cut into chunks of inner tiles, combined in chunk order.
+
+The scheduler splits a tile when its inner-tile count exceeds T = max(8, ceil(total / 256)), so
+one or two long samples with few heads are split; the combined outputs must match the fp64 oracle
+to the same tolerance as unsplit ones, and repeated runs must give identical bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+from jagged_attention_recommendation_amd import inputs
+from parity_util import assert_close, assert_lse_close, oracle_bwd, oracle_fwd, to_device
+from test_gpu_bwd import assert_dbias_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from jagged_attention_recommendation_amd import gdpa
+    gdpa.load()
+
+
+def run(p):
+    """Forward and backward with caller-owned workspaces; returns outputs and scheduler headers."""
+    from jagged_attention_recommendation_amd import gdpa
+    d = to_device(p)
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"])
+    B, H, D = p.B, p.H, p.D
+    tq, tk = int(p.q_off[-1]), int(p.kv_off[-1])
+    prob = gdpa.problem(B, H, D, tq, tk, dtype="bf16", act=p.act, causal=p.causal, scale=p.scale,
+                        bias_buckets=0 if p.bias is None else p.bias.shape[1])
+    wf = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, **kw)
+    hf = gdpa.workspace_header(wf)
+    dq, dk, dv, dbias = gdpa.bwd(d["Q"], d["K"], d["V"], O, d["dO"], lse, d["q_off"], d["kv_off"],
+                                 workspace=wb, **kw)
+    hb = gdpa.workspace_header(wb)
+    return (O, lse, dq, dk, dv, dbias), hf, hb
+
+
+def check(p, expect_fwd_split, expect_q_split, expect_k_split):
+    (O, lse, dq, dk, dv, dbias), hf, hb = run(p)
+    assert hf["error"] == 0 and hb["error"] == 0
+    assert (hf["split"] > 0) == expect_fwd_split, hf
+    assert (hb["split"] > 0) == expect_q_split, hb
+    assert (hb["split2"] > 0) == expect_k_split, hb
+    O_ref, lse_ref = oracle_fwd(p)
+    assert_close(O, O_ref, p.q_off, "bf16", f"{p.name} O")
+    if p.act == "softmax":
+        assert_lse_close(lse, lse_ref, f"{p.name} lse")
+    rb = oracle_bwd(p)
+    assert_close(dq, rb["dQ"], p.q_off, "bf16", f"{p.name} dQ")
+    assert_close(dk, rb["dK"], p.kv_off, "bf16", f"{p.name} dK")
+    assert_close(dv, rb["dV"], p.kv_off, "bf16", f"{p.name} dV")
+    if p.bias is not None:
+        assert_dbias_close(dbias, rb["dbias"], f"{p.name} dbias", rb["dbias_scale"])
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_long_causal_self(act):
+    # one long sample and two short ones, one head: the long sample's late query tiles (up to 24
+    # key tiles) and early key tiles are split; the short ones are not
+    lq = np.array([1500, 70, 5])
+    p = inputs.make_problem(f"split-self-{act}", seed=71, H=1, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act=act, causal=True, bias_buckets=600)
+    check(p, True, True, True)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "softmax"])
+def test_long_cross(act):
+    # long keys for short query sets (dQ / forward chunks over keys) and long queries for short
+    # key sets (dK/dV chunks over queries)
+    lq = np.array([200, 2100, 33])
+    lk = np.array([2500, 90, 700])
+    p = inputs.make_problem(f"split-cross-{act}", seed=72, H=2, D=128, lq=lq, lk=lk, dtype="bf16",
+                            act=act, causal=False, bias_buckets=64)
+    check(p, True, True, True)
+
+
+def test_no_split_when_balanced():
+    # many samples of moderate length: every tile is cheaper than the mean per-slot load
+    rng = np.random.default_rng(73)
+    lq = rng.integers(1, 400, size=48)
+    p = inputs.make_problem("split-none", seed=73, H=4, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=0)
+    (O, *_), hf, hb = run(p)
+    assert hf["split"] == 0 and hb["split"] == 0 and hb["split2"] == 0
+    assert hf["chunk"] == 0  # nothing split: the header reports no chunk length
+
+
+def test_split_bitwise_repeatable():
+    lq = np.array([1300, 40])
+    p = inputs.make_problem("split-repeat", seed=74, H=1, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=300)
+    a, hf, hb = run(p)
+    assert hf["split"] > 0 and hb["split"] > 0
+    b, _, _ = run(p)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

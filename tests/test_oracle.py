@@ -100,7 +100,7 @@ def run_oracle_fwd(pb, act, causal, scale):
 
 def run_oracle_bwd(pb, act, causal, scale):
     return oracle.bwd(pb["qo"], pb["ko"], pb["Q"], pb["K"], pb["V"], pb["dO"], act=act,
-                      causal=causal, scale=scale, bias=pb["bias"], nthreads=2)
+                      causal=causal, scale=scale, bias=pb["bias"], nthreads=2, error_scale=True)
 
 
 CASES = [
@@ -174,6 +174,44 @@ def test_brute_force_pure_python_tiny():
                          for x in s]
                 ref = [sum(w[j] * vs[j][c] for j in range(len(w))) for c in range(3)]
                 np.testing.assert_allclose(O[pb["qo"][b] + i, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_dbias_error_scale_brute_force_tiny():
+    """The bias buckets' error scale (a tolerance input, not a result) by a loop-only evaluation:
+    scale[h, r]^2 = sum over rows i of m_ir^2 w_i, m_ir = sum of p_ij over the row's pairs in
+    bucket r, w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2), for softmax; zero for GDPA,
+    which has no row term D_i."""
+    pb = rand_problem(8, B=2, H=2, D=3, lq=[4, 2], lk=[3, 5], nb=3)
+    scale = 0.8
+    for causal in (False, True):
+        g = run_oracle_bwd(pb, "softmax", causal, scale)
+        ref = np.zeros((2, 3))
+        for h in range(2):
+            for b in range(2):
+                q0, k0 = pb["qo"][b], pb["ko"][b]
+                for i in range(pb["qo"][b + 1] - q0):
+                    js = [j for j in range(pb["ko"][b + 1] - k0) if not causal or j <= i]
+                    if not js:
+                        continue
+                    s = {j: scale * sum(pb["Q"][q0 + i, h, c] * pb["K"][k0 + j, h, c] for c in range(3))
+                         + pb["bias"][h][min(max(i - j, 0), 2)] for j in js}
+                    mx = max(s.values())
+                    w = {j: math.exp(s[j] - mx) for j in js}
+                    tot = sum(w.values())
+                    pr = {j: w[j] / tot for j in js}
+                    wi = 0.0
+                    for c in range(3):
+                        oc = sum(pr[j] * pb["V"][k0 + j, h, c] for j in js)
+                        e2 = sum(pr[j] ** 2 * pb["V"][k0 + j, h, c] ** 2 for j in js)
+                        wi += pb["dO"][q0 + i, h, c] ** 2 * (oc * oc + e2)
+                    m = [0.0, 0.0, 0.0]
+                    for j in js:
+                        m[min(max(i - j, 0), 2)] += pr[j]
+                    for r in range(3):
+                        ref[h][r] += m[r] ** 2 * wi
+        np.testing.assert_allclose(g["dbias_scale"], np.sqrt(ref), rtol=1e-12, atol=1e-14)
+        gd = run_oracle_bwd(pb, "gelu_tanh", causal, scale)
+        assert np.array_equal(gd["dbias_scale"], np.zeros((2, 3)))
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
