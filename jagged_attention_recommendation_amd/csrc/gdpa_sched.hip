@@ -321,30 +321,29 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     const int tb = a.tile_base[b];
     const int nb = a.nb;
     constexpr int PER = QI / 32;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 16;
     // Row block rb reaches diagonals up to 32 rb + 31 (clamped), so entry c sees only row blocks
     // rb >= (c - 31) / 32: the loop starts at the wave's first such block (its lowest c) and is
-    // empty past the last row block. Blocks it skips would each have added +0.0.
+    // empty past the last row block. Blocks it skips would each have added +0.0. The range
+    // arithmetic is uniform across the wave; every lane loads its entry of the row (in bounds,
+    // and the wave's 64 entries overlap the row's range anyway) and keeps it only inside the
+    // range, so the loads carry no branches.
     const int c_first = __builtin_amdgcn_readfirstlane(c);
     const int rb_begin = c_first > 32 * nrb - 1 ? nrb : max(0, (c_first - 31) / 32);
     for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
       float v[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const int rb = rb0 + u;
-        int d_lo, d_hi;
-        v[u] = 0.0f;
-        if (rb >= nrb) continue;
+        const int rb = min(rb0 + u, nrb - 1);
         const int t = rb / PER;
         const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal);
         const int sb = a.split_slot != nullptr ? a.split_slot[(int64_t)(tb + t) * a.H + h] : -1;
-        if (sb < 0) {
-          if (chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi) && c >= clampi(d_lo, 0, nb - 1) &&
-              c <= clampi(d_hi, 0, nb - 1)) {
-            const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
-            v[u] = a.part[(row * a.H + h) * nb + c];
-          }
-        } else {
+        int d_lo = 1, d_hi = 0;
+        const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi);
+        const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
+        const float x = a.part[(row * a.H + h) * nb + c];
+        v[u] = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1) ? x : 0.0f;
+        if (sb >= 0 && rb0 + u < nrb) {
           // split tile: its chunks' rows, in chunk order
           const int T = hdr->chunk;
           const int n = (nkt + T - 1) / T;
