@@ -424,8 +424,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
                   const GDPA_LDS float* srt, int i0) {
     const bool need_mask = __builtin_amdgcn_readfirstlane(
         (int)((i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31))) != 0;
-#pragma unroll 1  // rolled: one 32-query half at a time keeps the register count in bounds
-    for (int qb = 0; qb < 2; ++qb) {
+    auto half = [&](int qb) {
       const int ib = i0 + qb * 32 + 4 * g;  // query of register r: ib + (r / 4) * 8 + r % 4
       f32x16 sacc, dpacc = f32x16{};
       if (BIAS && win_ok) {
@@ -520,6 +519,16 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // The two halves straight-line when a bias is present; without one the unrolled form runs
+    // out of registers, so the halves stay in a loop there (whose back edge copies the dK/dV
+    // accumulators).
+    if constexpr (BIAS) {
+      half(0);
+      half(1);
+    } else {
+#pragma unroll 1
+      for (int qb = 0; qb < 2; ++qb) half(qb);
     }
   };
 
