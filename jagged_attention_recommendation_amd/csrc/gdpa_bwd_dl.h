@@ -190,11 +190,22 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
         sacc = mfma32(kr[s], qop[s], sacc);
         dpacc = mfma32(vr[s], doop[s], dpacc);
       }
-      // all 16 operand reads first, then the 16 products (each waits only for its own operand)
+      // the transposed K^T operands of this half's dQ products, read now so they arrive during
+      // the gradient arithmetic
+      bf16x8 kt0[D / 32], kt1[D / 32];
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        kt0[n] = tr_op(Ks, kb * 32, n, lane);
+        kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
+      }
+      // the 16 operand reads, then the 16 products each followed by one transposed read
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       float dsv[16];
 #pragma unroll
@@ -221,22 +232,11 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       const bf16x8 dsb0 = pack8(&dsv[0]);
       const bf16x8 dsb1 = pack8(&dsv[8]);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 kt0[D / 32], kt1[D / 32];
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        kt0[n] = tr_op(Ks, kb * 32, n, lane);
-        kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
-      }
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) {
         dq[n] = mfma32(kt0[n], dsb0, dq[n]);
         dq[n] = mfma32(kt1[n], dsb1, dq[n]);
       }
-      // the 16 transposed reads first, then the 8 products
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (BIAS) {
@@ -251,12 +251,12 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       // diagonal) and takes the second diagonal as the rest.
       float run = 0.0f, s_a = 0.0f;
 #pragma unroll
-      for (int a8 = 0; a8 < 32; a8 += 8) {  // 8 reads in flight, then their sums
-        float vv[8];
+      for (int a8 = 0; a8 < 32; a8 += 32) {  // all 32 reads in flight, then their sums
+        float vv[32];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
+        for (int e = 0; e < 32; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 32; ++e) {
           run += vv[e];
           if (a8 + e == lane) s_a = run;
         }
@@ -450,10 +450,22 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
         sacc = mfma32(qr[s], kop[s], sacc);
         dpacc = mfma32(dr[s], vop[s], dpacc);
       }
+      // the transposed dO^T operands of this half's dV products, read now so they arrive during
+      // the gradient arithmetic
+      bf16x8 ot[2][D / 32];
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        ot[0][n] = tr_op(dOs, qb * 32, n, lane);
+        ot[1][n] = tr_op(dOs, qb * 32 + 16, n, lane);
+      }
+      // the 16 operand reads, then the 16 products each followed by one transposed read
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
 
       float pv[16], dsv[16];
@@ -487,12 +499,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
       const bf16x8 pb0 = pack8(&pv[0]), pb1 = pack8(&pv[8]);
       const bf16x8 db0 = pack8(&dsv[0]), db1 = pack8(&dsv[8]);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 ot[2][D / 32], qt[2][D / 32];
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        ot[0][n] = tr_op(dOs, qb * 32, n, lane);
-        ot[1][n] = tr_op(dOs, qb * 32 + 16, n, lane);
-      }
+      bf16x8 qt[2][D / 32];
 #pragma unroll
       for (int n = 0; n < D / 32; ++n) {
         qt[0][n] = tr_op(Qs, qb * 32, n, lane);
@@ -508,9 +515,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
         dk[n] = mfma32(qt[0][n], db0, dk[n]);
         dk[n] = mfma32(qt[1][n], db1, dk[n]);
       }
-      // dO^T reads, then the dV products interleaved with the Q^T reads, then the dK products
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      // the dV products interleaved with the Q^T reads, then the dK products
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
