@@ -330,14 +330,36 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     // range, so the loads carry no branches.
     const int c_first = __builtin_amdgcn_readfirstlane(c);
     const int rb_begin = c_first > 32 * nrb - 1 ? nrb : max(0, (c_first - 31) / 32);
-    for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
+    if (a.split_slot == nullptr || hdr->n_split == 0) {
+      // no split tiles: one row per row block. All loads of a batch first (in bounds, no
+      // branches), then the range tests; an entry outside its row block's range is cleared by a
+      // bit mask (stale bits there may be anything, even NaN), which also keeps every load used.
+      for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
+        int xi[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int rb = min(rb0 + u, nrb - 1);
+          const int64_t row = (int64_t)(tb + rb / PER) * PER + rb % PER;
+          xi[u] = __float_as_int(a.part[(row * a.H + h) * nb + c]);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int rb = min(rb0 + u, nrb - 1);
+          const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal);
+          int d_lo = 1, d_hi = 0;
+          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi);
+          const bool keep = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1);
+          acc += __int_as_float(xi[u] & (keep ? -1 : 0));
+        }
+      }
+    } else for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
       float v[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
         const int rb = min(rb0 + u, nrb - 1);
         const int t = rb / PER;
         const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal);
-        const int sb = a.split_slot != nullptr ? a.split_slot[(int64_t)(tb + t) * a.H + h] : -1;
+        const int sb = a.split_slot[(int64_t)(tb + t) * a.H + h];
         int d_lo = 1, d_hi = 0;
         const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi);
         const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
