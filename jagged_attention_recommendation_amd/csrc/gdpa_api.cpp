@@ -53,7 +53,7 @@ int bwd_k_item(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_K_ITEM; }
 int bwd_q_loop(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_Q_LOOP; }
 
 struct FwdLayout {
-  size_t header, items, splits, part_o, part_ml, total;
+  size_t header, items, split_cnt, part_o, part_ml, total;
   int64_t max_items;
   bool split;
 };
@@ -64,11 +64,11 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
   L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype), L.split);
   L.header = 0;
   L.items = ALIGN;
-  L.splits = L.items + align_up((size_t)L.max_items * sizeof(Item));
-  L.part_o = L.part_ml = L.total = L.splits;
+  L.split_cnt = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.part_o = L.part_ml = L.total = L.split_cnt;
   if (L.split) {
     const size_t rows = (size_t)SPLIT_SLOTS * fwd_tile_rows(p->dtype);
-    L.part_o = L.splits + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
+    L.part_o = L.split_cnt + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
     L.part_ml = L.part_o + align_up(rows * p->D * sizeof(float));
     L.total = L.part_ml + align_up(rows * 2 * sizeof(float));
   }
@@ -76,8 +76,8 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
 }
 
 struct BwdLayout {
-  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, splits_q, splits_k, split_slot,
-      part_dq, part_dk, part_dv, part_x, total;
+  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, split_cnt_q, split_cnt_k,
+      split_slot, part_dq, part_dk, part_dv, part_x, total;
   int64_t max_q_items, max_k_items, max_qtiles;
   bool split;
 };
@@ -103,12 +103,12 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
     L.part_bh = L.part + align_up(rows * p->H * p->bias_buckets * sizeof(float));
     end = L.part_bh + align_up((size_t)p->B * p->H * p->bias_buckets * sizeof(float));
   }
-  L.splits_q = L.splits_k = L.split_slot = L.part_dq = L.part_dk = L.part_dv = L.part_x = end;
+  L.split_cnt_q = L.split_cnt_k = L.split_slot = L.part_dq = L.part_dk = L.part_dv = L.part_x = end;
   if (L.split) {
-    // split lists, the per-(tile, head) slot table, and the chunks' partial rows
-    L.splits_q = end;
-    L.splits_k = L.splits_q + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
-    L.split_slot = L.splits_k + align_up((size_t)SPLIT_NSLOT * sizeof(Split));
+    // chunk counters of both lists, the per-(tile, head) slot table, the chunks' partial rows
+    L.split_cnt_q = end;
+    L.split_cnt_k = L.split_cnt_q + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
+    L.split_slot = L.split_cnt_k + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
     L.part_dq = L.split_slot + align_up((size_t)L.max_qtiles * p->H * sizeof(int32_t));
     L.part_dk = L.part_dq + align_up((size_t)SPLIT_SLOTS * tq * p->D * sizeof(float));
     L.part_dv = L.part_dk + align_up((size_t)SPLIT_SLOTS * tk * p->D * sizeof(float));
@@ -243,7 +243,8 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.causal = p->causal; sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
   sa.split = L.split ? 1 : 0; sa.tile_base = nullptr; sa.split_slot = nullptr;
-  sa.ws_header = ws + L.header; sa.items = ws + L.items; sa.splits = ws + L.splits;
+  sa.ws_header = ws + L.header; sa.items = ws + L.items;
+  sa.split_cnt = (int32_t*)(ws + L.split_cnt);
   hipError_t e = launch_sched(sa, s);
   if (e != hipSuccess) return map_hip(e);
 
@@ -252,13 +253,12 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
   fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
   fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
-  fa.scale = p->scale; fa.splits = ws + L.splits;
+  fa.scale = p->scale; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
   fa.part_o = (float*)(ws + L.part_o); fa.part_ml = (float*)(ws + L.part_ml);
   const int grid = (int)L.max_items;
   if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
   else if (p->dtype == GDPA_BF16) e = launch_fwd_bf16(pr, fa, grid, s);
   else e = launch_fwd_mx(pr, fa, grid, s);
-  if (e == hipSuccess && L.split) e = launch_combine_fwd(pr, fa, s);
   return map_hip(e);
 }
 
@@ -301,11 +301,12 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
   sq.max_items = (int)L.max_q_items; sq.list = 0;
   sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
-  sq.splits = ws + L.splits_q;
+  sq.split_cnt = (int32_t*)(ws + L.split_cnt_q);
   sq.split_slot = L.split && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
   sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
   sk.max_items = (int)L.max_k_items; sk.list = 1;
-  sk.tile_base = nullptr; sk.items = ws + L.items_k; sk.splits = ws + L.splits_k;
+  sk.tile_base = nullptr; sk.items = ws + L.items_k;
+  sk.split_cnt = (int32_t*)(ws + L.split_cnt_k);
   sk.split_slot = nullptr;
   hipError_t e = launch_sched2(sq, sk, s);
   if (e != hipSuccess) return map_hip(e);
@@ -319,14 +320,12 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.dbias_part = p->bias_buckets > 0 ? (float*)(ws + L.part) : nullptr;
   ba.tile_base = (const int32_t*)(ws + L.tile_base);
   ba.dbias_part_x = (float*)(ws + L.part_x);
-  ba.splits_q = ws + L.splits_q; ba.splits_k = ws + L.splits_k;
+  ba.split_cnt_q = (int32_t*)(ws + L.split_cnt_q); ba.split_cnt_k = (int32_t*)(ws + L.split_cnt_k);
   ba.part_dq = (float*)(ws + L.part_dq); ba.part_dk = (float*)(ws + L.part_dk);
   ba.part_dv = (float*)(ws + L.part_dv);
   ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale;
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
-  if (e == hipSuccess && L.split) e = launch_combine_dq(pr, ba, s);
-  if (e == hipSuccess && L.split) e = launch_combine_dkdv(pr, ba, s);
   if (e != hipSuccess) return map_hip(e);
   if (p->bias_buckets > 0) {
     DbiasArgs da;

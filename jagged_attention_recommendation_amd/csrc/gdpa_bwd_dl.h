@@ -17,6 +17,7 @@
 #include "gdpa_common.h"
 #include "gdpa_dl.h"
 #include "gdpa_internal.h"
+#include "gdpa_split.h"
 #include "gdpa_tiles.h"  // store_acc_row_bf16
 
 namespace gdpa {
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sv1_[TILE];
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
   __shared__ __attribute__((aligned(16))) float dsbuf_[BIAS ? 4 * 32 * DSP : 1];
+  __shared__ int flag_;
   GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
   GDPA_LDS char* sv0 = (GDPA_LDS char*)sv0_;
   GDPA_LDS char* sk1 = (GDPA_LDS char*)sk1_;
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     Di = half_sum(part_d);
     if (qv) {
       lse2 = a.lse[row] * LOG2E;
-      if (g == 0 && it.chunk == 0) a.Dvec[row] = Di;  // every chunk computes it; one writes it
+      // every chunk computes it; the first writes it
+      if (g == 0 && split::chunk_index(it.chunk) == 0) a.Dvec[row] = Di;
     }
   }
 
@@ -314,15 +317,21 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       }
     }
   }
-  if (it.slot >= 0) {  // chunk of a split tile: fp32 partial rows, summed later in chunk order
-    if (!wave_active) return;
-    float* pq = a.part_dq + ((int64_t)it.slot * QI + w * 32 + l32) * D;
+  if (it.slot >= 0) {
+    // chunk of a split tile: fp32 partial rows; the workgroup that completes the tile combines
+    // its chunks in order
+    if (wave_active) {
+      float* pq = a.part_dq + ((int64_t)it.slot * QI + w * 32 + l32) * D;
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n)
+      for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *(f32x4*)(pq + n * 32 + r4 * 8 + 4 * g) =
-            f32x4{dq[n][4 * r4], dq[n][4 * r4 + 1], dq[n][4 * r4 + 2], dq[n][4 * r4 + 3]};
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(pq + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{dq[n][4 * r4], dq[n][4 * r4 + 1], dq[n][4 * r4 + 2], dq[n][4 * r4 + 3]};
+    }
+    const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
+    if (split::chunk_done(a.split_cnt_q + first, n, (GDPA_LDS int*)&flag_))
+      split::combine_dq_tile(a, b, it.tile, h, n, first);
     return;
   }
   if (!qv) return;
@@ -345,6 +354,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char so1_[TILE];
   __shared__ __attribute__((aligned(16))) float rt_[SM ? 2 * 2 * QL : 1];  // [stage][lse, D][QL]
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
+  __shared__ int flag_;
   GDPA_LDS char* sq0 = (GDPA_LDS char*)sq0_;
   GDPA_LDS char* so0 = (GDPA_LDS char*)so0_;
   GDPA_LDS char* sq1 = (GDPA_LDS char*)sq1_;
@@ -557,18 +567,24 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
       if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq1, so1, rt1, i0);
     }
   }
-  if (it.slot >= 0) {  // chunk of a split tile: fp32 partial rows, summed later in chunk order
-    if (!wave_active) return;
-    const int64_t prow = ((int64_t)it.slot * KI + w * 32 + l32) * D;
+  if (it.slot >= 0) {
+    // chunk of a split tile: fp32 partial rows; the workgroup that completes the tile combines
+    // its chunks in order
+    if (wave_active) {
+      const int64_t prow = ((int64_t)it.slot * KI + w * 32 + l32) * D;
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n)
+      for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        *(f32x4*)(a.part_dk + prow + n * 32 + r4 * 8 + 4 * g) =
-            f32x4{dk[n][4 * r4], dk[n][4 * r4 + 1], dk[n][4 * r4 + 2], dk[n][4 * r4 + 3]};
-        *(f32x4*)(a.part_dv + prow + n * 32 + r4 * 8 + 4 * g) =
-            f32x4{dv[n][4 * r4], dv[n][4 * r4 + 1], dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]};
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          *(f32x4*)(a.part_dk + prow + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{dk[n][4 * r4], dk[n][4 * r4 + 1], dk[n][4 * r4 + 2], dk[n][4 * r4 + 3]};
+          *(f32x4*)(a.part_dv + prow + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{dv[n][4 * r4], dv[n][4 * r4 + 1], dv[n][4 * r4 + 2], dv[n][4 * r4 + 3]};
+        }
+    }
+    const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
+    if (split::chunk_done(a.split_cnt_k + first, n, (GDPA_LDS int*)&flag_))
+      split::combine_dkdv_tile(a, b, it.tile, h, n, first);
     return;
   }
   if (!kvalid) return;

@@ -35,16 +35,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // Work item of the jagged scheduler: sample, tile index (of queries for forward / dQ, of keys
 // for dK/dV), head, the canonical index of the (sample, tile), and the range [lo, hi) of
 // inner-loop tiles the item covers (counted from the first tile the tile visits). A long tile
-// split into chunks has one item per chunk: slot is the chunk's partial-result slot and chunk its
-// index; an unsplit item has slot -1 and chunk 0.
+// split into n chunks has one item per chunk: slot is the chunk's partial-result slot (the
+// tile's chunks use consecutive slots) and chunk packs the chunk index (low 16 bits) with n; an
+// unsplit item has slot -1 and chunk 0.
 struct Item {
   int b, tile, h, aux;
   int lo, hi, slot, chunk;
-};
-
-// A split tile: its n chunks wrote partial results to slots slot .. slot + n - 1.
-struct Split {
-  int b, tile, h, n, slot, aux, pad0, pad1;
 };
 
 // Workspace header (first 256 bytes of every workspace).

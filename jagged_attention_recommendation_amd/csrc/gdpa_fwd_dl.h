@@ -12,6 +12,7 @@
 #include "gdpa_common.h"
 #include "gdpa_dl.h"
 #include "gdpa_internal.h"
+#include "gdpa_split.h"
 #include "gdpa_tiles.h"  // store_acc_row_bf16
 
 namespace gdpa {
@@ -32,6 +33,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sk1_[TILE];
   __shared__ __attribute__((aligned(16))) char sv1_[TILE];
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? WMAX : 1];
+  __shared__ int flag_;
   GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
   GDPA_LDS char* sv0 = (GDPA_LDS char*)sv0_;
   GDPA_LDS char* sk1 = (GDPA_LDS char*)sk1_;
@@ -200,27 +202,32 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
     if (wave_active && !(CAUSAL && (kt + 1) * BN > wrow + 31)) tile(sk1, sv1, (kt + 1) * BN);
   }
 
-  if (!wave_active) return;
   if (it.slot >= 0) {
     // chunk of a split tile: unnormalised output rows and, for softmax, the running max (log2
-    // units) and sum, combined later in chunk order
-    float* po = a.part_o + ((int64_t)it.slot * BM + w * 32 + l32) * D;
+    // units) and sum; the workgroup that completes the tile combines its chunks in order
+    if (wave_active) {
+      float* po = a.part_o + ((int64_t)it.slot * BM + w * 32 + l32) * D;
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n)
+      for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *(f32x4*)(po + n * 32 + r4 * 8 + 4 * g) =
-            f32x4{o[n][4 * r4], o[n][4 * r4 + 1], o[n][4 * r4 + 2], o[n][4 * r4 + 3]};
-    if (ACT == ACT_SOFTMAX) {
-      const float lt = half_sum(l_run);
-      if (g == 0) {
-        float* pml = a.part_ml + (int64_t)it.slot * 2 * BM;
-        pml[w * 32 + l32] = m_run;
-        pml[BM + w * 32 + l32] = lt;
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(po + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{o[n][4 * r4], o[n][4 * r4 + 1], o[n][4 * r4 + 2], o[n][4 * r4 + 3]};
+      if (ACT == ACT_SOFTMAX) {
+        const float lt = half_sum(l_run);
+        if (g == 0) {
+          float* pml = a.part_ml + (int64_t)it.slot * 2 * BM;
+          pml[w * 32 + l32] = m_run;
+          pml[BM + w * 32 + l32] = lt;
+        }
       }
     }
+    const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
+    if (split::chunk_done(a.split_cnt + first, n, (GDPA_LDS int*)&flag_))
+      split::combine_fwd_tile<ACT == ACT_SOFTMAX>(a, b, it.tile, h, n, first);
     return;
   }
+  if (!wave_active) return;
   float inv = 1.0f;
   if (ACT == ACT_SOFTMAX) {
     const float lt = half_sum(l_run);

@@ -23,7 +23,9 @@ enum { SCHED_QTILES = 0, SCHED_KTILES = 1 };
 // T = max(SPLIT_MIN_TILES, ceil(total cost / SPLIT_NSLOT)), the mean load of SPLIT_NSLOT
 // concurrent workgroups, and a tile of cost c > T becomes ceil(c / T) chunks. Split tiles each
 // cost more than T, so there are at most total / T <= SPLIT_NSLOT of them and at most
-// 2 * SPLIT_NSLOT chunks among them: the partial-result storage has a fixed size.
+// 2 * SPLIT_NSLOT chunks among them: the partial-result storage has a fixed size. A tile's cost
+// is at most the total, so it has at most SPLIT_NSLOT chunks (Item::chunk keeps the count in 16
+// bits).
 constexpr int SPLIT_NSLOT = 256;
 constexpr int SPLIT_SLOTS = 2 * SPLIT_NSLOT;
 constexpr int SPLIT_MIN_TILES = 8;
@@ -40,9 +42,9 @@ struct SchedArgs {
   int split;                 // 1: split long tiles into chunks
   int32_t* tile_base;        // optional [B + 1]: canonical index of each sample's first tile
   int32_t* split_slot;       // optional [canonical tiles * H]: first slot of a split tile, or -1
+  int32_t* split_cnt;        // [SPLIT_SLOTS] chunk counters, indexed by a split tile's first slot
   void* ws_header;
   void* items;
-  void* splits;              // [SPLIT_NSLOT] split tiles (when split)
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
@@ -89,7 +91,7 @@ struct FwdArgs {
   float* lse;
   const void* hdr;
   const void* items;
-  const void* splits;  // split tiles of the item list
+  int32_t* split_cnt;  // chunk counters of split tiles
   float* part_o;   // split chunks: [SPLIT_SLOTS][BM][D] fp32 unnormalised output
   float* part_ml;  // split chunks (softmax): [SPLIT_SLOTS][2][BM] running max (log2 units), sum
   int H, nb;
@@ -129,8 +131,8 @@ struct BwdArgs {
   const void* items_k;   // key-tile items (dK/dV)
   float* dbias_part;     // [n_rowblocks, H, NB] per 32-query row block diagonal sums of dS
   float* dbias_part_x;   // split chunks: [SPLIT_SLOTS * QI / 32, NB]
-  const void* splits_q;  // split tiles of the query-tile list
-  const void* splits_k;  // split tiles of the key-tile list
+  int32_t* split_cnt_q;  // chunk counters of split query tiles
+  int32_t* split_cnt_k;  // chunk counters of split key tiles
   const int32_t* tile_base;  // [B + 1] canonical index of each sample's first query tile
   float* part_dq;        // split chunks: [SPLIT_SLOTS][QI][D] fp32
   float* part_dk;        // split chunks: [SPLIT_SLOTS][KI][D] fp32
@@ -146,11 +148,8 @@ constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
-// Fixed-order combines of split chunks (D = 128 bf16 path).
-hipError_t launch_combine_fwd(const Prob& p, const FwdArgs& a, hipStream_t s);
-hipError_t launch_combine_dq(const Prob& p, const BwdArgs& a, hipStream_t s);
-hipError_t launch_combine_dkdv(const Prob& p, const BwdArgs& a, hipStream_t s);
-// Whether the kernels for this problem take split items.
+// Whether the kernels for this problem take split items (D = 128 bf16 path; the last chunk of a
+// split tile combines the tile, see gdpa_split.h).
 inline bool split_supported(const Prob& p) { return p.dtype == DT_BF16 && p.D == 128; }
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   bucket[tid] -= own;
   __syncthreads();
   // 3. scatter the chunks (b, tile, h, canonical tile index, inner range, slot, chunk); a split
-  //    tile takes n consecutive slots per head and one entry per head in the split list
+  //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared
   for_each_tile([&](int b, int t, int canon) {
     const int Lq = a.q_off[b + 1] - a.q_off[b];
     const int Lk = a.kv_off[b + 1] - a.kv_off[b];
@@ -207,18 +207,12 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     int sbase = -1;
     if (n > 1) {
       sbase = atomicAdd(&slot_count, n * a.H);
-      const int si = atomicAdd(&split_count, a.H);
-      if (sbase + n * a.H > SPLIT_SLOTS || si + a.H > SPLIT_NSLOT) {
-        atomicOr(&err, 4);  // cannot happen: the chunk length bounds both counts
+      atomicAdd(&split_count, a.H);
+      if (sbase + n * a.H > SPLIT_SLOTS) {
+        atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
         sbase = -1;
       } else {
-        Split* sp = (Split*)a.splits;
-        for (int h = 0; h < a.H; ++h) {
-          Split e;
-          e.b = b; e.tile = t; e.h = h; e.n = n; e.slot = sbase + h * n; e.aux = canon;
-          e.pad0 = 0; e.pad1 = 0;
-          sp[si + h] = e;
-        }
+        for (int h = 0; h < a.H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
       }
     }
     if (a.split_slot != nullptr)
@@ -233,7 +227,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
           it.lo = n == 1 ? 0 : k * T;
           it.hi = n == 1 ? c : min(c, (k + 1) * T);
           it.slot = sbase < 0 ? -1 : sbase + h * n + k;
-          it.chunk = k;
+          it.chunk = sbase < 0 ? 0 : k | (n << 16);
           items[pos + h] = it;
         }
       }
