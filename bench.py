@@ -55,6 +55,25 @@ def dominant_kernel_flops(p, kernel):
     return float(per_pair) * pairs
 
 
+TRAFFIC_SUMMARY = {
+    2: "profiles/jfa_causal_bias_B64_H4_D128_fwd_dq_dkdv_hbm_traffic.txt",
+}
+
+
+def measured_traffic(config, kernel):
+    """HBM bytes per launch of the kernel from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs scaled by a plain copy), or None when there is none for this workload or the
+    kernel sources have changed since the counters were taken."""
+    from jagged_attention_recommendation_amd import counters
+    path = TRAFFIC_SUMMARY.get(config)
+    if path is None:
+        return None
+    s = counters.load_summary(os.path.join(os.path.dirname(os.path.abspath(__file__)), path))
+    if s is None or s.get("csrc_sha256") != counters.csrc_digest() or kernel not in s["kernels"]:
+        return None
+    return s["kernels"][kernel]["bytes"]
+
+
 def prefix_problem(p, n):
     """The first n samples of p as a problem of their own (same bits)."""
     import copy
@@ -203,7 +222,8 @@ def main():
     achieved = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(args.config, dom),
                 "avg_launch_ms": round(kern_ms[dom], 4),
                 "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()}}
 

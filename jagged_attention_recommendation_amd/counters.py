@@ -1,0 +1,99 @@
+"""HBM traffic per kernel launch from rocprofv3 counter runs (profiling support, not the path).
+
+Two `rocprofv3 --pmc` runs of `bench.py --copy-calibration`, one with FETCH_SIZE and one with
+WRITE_SIZE, give KiB per dispatch for every kernel. The benchmark's plain 256 MiB device copy has
+known traffic (256 MiB read, 256 MiB written), so each counter is scaled by what it reads for that
+copy. The summary records a digest of the kernel sources: the benchmark reports the traffic only
+while the sources are unchanged.
+
+    python -m jagged_attention_recommendation_amd.counters FETCH_DIR WRITE_DIR > summary.txt
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+COPY_BYTES = 256 << 20
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNELS = {"fwd": "fwd_dl_kernel", "dq": "dq_dl_kernel", "dkdv": "dkdv_dl_kernel"}
+
+
+def csrc_digest() -> str:
+    """sha256 over the kernel sources (names and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def per_dispatch(run_dir):
+    """{dispatch id: (kernel name, grid size, summed counter value in KiB)}"""
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "*counter_collection.csv")):
+        rows += list(csv.DictReader(open(f)))
+    val = collections.defaultdict(float)
+    meta = {}
+    for r in rows:
+        val[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        meta[r["Dispatch_Id"]] = (r["Kernel_Name"], int(r["Grid_Size"]))
+    return {d: (meta[d][0], meta[d][1], v) for d, v in val.items()}
+
+
+def summarize(fetch_dir, write_dir):
+    fetch, write = per_dispatch(fetch_dir), per_dispatch(write_dir)
+
+    def copy_kib(d):
+        # the largest copyBuffer dispatches are the 256 MiB calibration copies
+        vals = sorted((v for k, g, v in d.values() if "copyBuffer" in k), reverse=True)[:3]
+        return sum(vals) / len(vals)
+
+    f_scale = (COPY_BYTES / 1024) / copy_kib(fetch)
+    w_scale = (COPY_BYTES / 1024) / copy_kib(write)
+    out = {"copy_fetch_kib": round(copy_kib(fetch), 1), "copy_write_kib": round(copy_kib(write), 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for short, sub in KERNELS.items():
+        fv = [v for k, g, v in fetch.values() if sub in k]
+        wv = [v for k, g, v in write.values() if sub in k]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        out["kernels"][short] = {"dispatches": len(fv), "fetch_kib": round(fk, 1),
+                                 "write_kib": round(wk, 1),
+                                 "bytes": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
+    out["csrc_sha256"] = csrc_digest()
+    return out
+
+
+def load_summary(path):
+    """The json record of a summary file, or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("json: "):
+                    return json.loads(line[len("json: "):])
+    except OSError:
+        return None
+    return None
+
+
+def main(argv):
+    fetch_dir, write_dir = argv[1], argv[2]
+    s = summarize(fetch_dir, write_dir)
+    print(f"# calibration: the 256 MiB copy reads as {s['copy_fetch_kib']} KiB FETCH_SIZE "
+          f"(scale {s['fetch_scale']}) and {s['copy_write_kib']} KiB WRITE_SIZE (scale {s['write_scale']})")
+    print(f"{'kernel':8} {'dispatches':>10} {'FETCH_KiB':>12} {'WRITE_KiB':>12} {'scaled_MB':>10}")
+    for k, v in s["kernels"].items():
+        print(f"{k:8} {v['dispatches']:>10} {v['fetch_kib']:>12} {v['write_kib']:>12} {v['bytes'] / 1e6:>10.1f}")
+    print("json: " + json.dumps(s))
+
+
+if __name__ == "__main__":
+    main(sys.argv)

@@ -1,0 +1,38 @@
+"""Host logic of the HBM traffic summary: copy calibration and per-kernel scaling."""
+import csv
+import json
+
+from jagged_attention_recommendation_amd import counters
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+
+
+def write_run(path, counter, rows):
+    path.mkdir()
+    with open(path / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, (k, v) in enumerate(rows, 1):
+            # two dimension rows per dispatch, summed by the reader
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Grid_Size": 1, "Counter_Name": counter,
+                        "Counter_Value": v / 2})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Grid_Size": 1, "Counter_Name": counter,
+                        "Counter_Value": v / 2})
+
+
+def test_summary_scales_by_the_copy(tmp_path):
+    kib = (256 << 20) / 1024
+    write_run(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 1.0)] +
+              [("__amd_rocclr_copyBuffer", kib / 2)] * 3 +
+              [("void gdpa::bwddl::dq_dl_kernel<0, true, true>(gdpa::BwdArgs)", 1000.0)] * 2)
+    write_run(tmp_path / "w", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 0.0)] +
+              [("__amd_rocclr_copyBuffer", kib)] * 3 +
+              [("void gdpa::bwddl::dq_dl_kernel<0, true, true>(gdpa::BwdArgs)", 300.0)] * 2)
+    s = counters.summarize(tmp_path / "f", tmp_path / "w")
+    assert s["fetch_scale"] == 2.0 and s["write_scale"] == 1.0
+    assert s["kernels"]["dq"] == {"dispatches": 2, "fetch_kib": 1000.0, "write_kib": 300.0,
+                                  "bytes": 1000 * 1024 * 2 + 300 * 1024}
+    assert s["csrc_sha256"] == counters.csrc_digest()
+    p = tmp_path / "summary.txt"
+    p.write_text("# header\njson: " + json.dumps(s) + "\n")
+    assert counters.load_summary(p) == s
