@@ -31,7 +31,7 @@ constexpr int KL = BWD_K_LOOP;  // keys per tile in the dQ loop
 constexpr int KI = BWD_K_ITEM;  // keys per dK/dV item
 constexpr int QL = BWD_Q_LOOP;  // queries per tile in the dK/dV loop
 static_assert(QI == 128 && KI == 128 && KL == ROWS && QL == ROWS, "kernels assume these tiles");
-constexpr int DSP = 68;         // floats per row of a wave's dS buffer (16-byte aligned rows)
+constexpr int DSP = 128;        // floats per row of a wave's skewed dS buffer
 
 template <int ACT>
 __device__ __forceinline__ float dscore(float x, float lse2, float Di, float dp, float& p) {
@@ -136,6 +136,22 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
   }
   GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * 32 * DSP;
+  // Bias gradient: diagonal sums of each tile's 32 x 64 dS block. The block is stored skewed:
+  // entry (row s, key j) at column j - s + 64 of row s, so a diagonal (fixed j - s) is one column,
+  // and the columns a tile does not write stay zero. Lane t reads column 127 - t (diagonal
+  // t - 63: rows 0..t, zeros below) and column 63 - t (diagonal t + 1: rows t + 1..31, zeros
+  // above); for t >= 31 the first is the full diagonal t - 63 and the second is all zeros. Each
+  // row read is one ds_read2st64 (the two columns are 64 floats apart), every lane reads its own
+  // column (no bank conflicts), and the two sums need no selects. A tile's sums are taken during
+  // the next tile's score products (or after the loop), so the reads overlap matrix work and the
+  // partial-row store is not waited for at once.
+  const GDPA_LDS float* dsrd = dsbuf + (63 - lane);
+  GDPA_LDS float* dswr = dsbuf + l32 * (DSP - 1) + 64 + 4 * g;  // row l32, key 4g at column 4g - l32 + 64
+  if (BIAS) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      *(GDPA_LDS f32x4*)(dsbuf + (lane >> 1) * DSP + (lane & 1) * 64 + 4 * u) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
   // partial row of this row block: canonical, or the chunk's slot row for a split tile
   float* part = !BIAS ? nullptr
@@ -161,9 +177,42 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       has_hi = true;
     }
   };
+  // the diagonals completed by the tile at key offset kp (s_a, s_b: its two column sums); pend =
+  // a tile of this wave has been reduced
+  auto finish = [&](int kp, float s_a, float s_b, bool pend) {
+    // lanes t < 31 emit d = t + 1 (with the carried part), the others emit d = lane - 63;
+    // absolute diagonal = wrow - kp + d
+    float v;
+    int dabs;
+    if (lane < 31) {
+      v = carry + s_b;
+      carry = s_a;
+      dabs = wrow - kp + lane + 1;
+    } else {
+      v = s_a;
+      dabs = wrow - kp + lane - 63;
+    }
+    emit(dabs, v, pend);
+  };
+  auto col_sums = [&](float& s_a, float& s_b) {
+    float va[32], vb[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      va[e] = dsrd[e * DSP + 64];
+      vb[e] = dsrd[e * DSP];
+    }
+    s_a = 0.0f;
+    s_b = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      s_a += va[e];
+      s_b += vb[e];
+    }
+  };
   int k0_last = -1;
 
   auto tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+    const int kp = k0_last;
     k0_last = k0;
     const bool need_mask = __builtin_amdgcn_readfirstlane(
         (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq))) != 0;
@@ -182,34 +231,72 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
         sacc = f32x16{};
       }
       __builtin_amdgcn_sched_barrier(0);
+      constexpr bool DEFER = BIAS;  // the previous tile's diagonal sums ride along with kb = 0
+      const bool red = DEFER && kb == 0;
       bf16x8 kr[D / 16], vr[D / 16];
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
+      for (int s = 0; s < (red ? 2 : D / 16); ++s) {
         kr[s] = row_op(Ks, kb * 32, s, lane);
         vr[s] = row_op(Vs, kb * 32, s, lane);
       }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        sacc = mfma32(kr[s], qop[s], sacc);
-        dpacc = mfma32(vr[s], doop[s], dpacc);
-      }
-      // the transposed K^T operands of this half's dQ products, read now so they arrive during
-      // the gradient arithmetic
+      // the transposed K^T operands of this half's dQ products, read during the score products
+      // so they arrive during the gradient arithmetic
       bf16x8 kt0[D / 32], kt1[D / 32];
+      float s_a = 0.0f, s_b = 0.0f;
+      if (red) {
+        f32x2 sab = {0.0f, 0.0f};  // both sums advance together
+        // the previous tile's column sums ride along: per pair of products, the operands of the
+        // pair two steps ahead, the reads of four rows, one transposed operand, and the sums of
+        // the rows read two steps earlier
+        float va[32], vb[32];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        kt0[n] = tr_op(Ks, kb * 32, n, lane);
-        kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
-      }
-      // the 16 operand reads, then the 16 products each followed by one transposed read
+        for (int s = 0; s < D / 16; ++s) {
+          if (s + 2 < D / 16) {
+            kr[s + 2] = row_op(Ks, kb * 32, s + 2, lane);
+            vr[s + 2] = row_op(Vs, kb * 32, s + 2, lane);
+          }
+          sacc = mfma32(kr[s], qop[s], sacc);
+          dpacc = mfma32(vr[s], doop[s], dpacc);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int e = 4 * s; e < 4 * s + 4; ++e) {
+            va[e] = dsrd[e * DSP + 64];
+            vb[e] = dsrd[e * DSP];
+          }
+          if (s & 1) kt1[s >> 1] = tr_op(Ks, kb * 32 + 16, s >> 1, lane);
+          else kt0[s >> 1] = tr_op(Ks, kb * 32, s >> 1, lane);
+          if (s >= 2) {
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int e = 4 * s - 8; e < 4 * s - 4; ++e) sab += f32x2{va[e], vb[e]};
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 24; e < 32; ++e) sab += f32x2{va[e], vb[e]};
+        s_a = sab[0];
+        s_b = sab[1];
+      } else {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          sacc = mfma32(kr[s], qop[s], sacc);
+          dpacc = mfma32(vr[s], doop[s], dpacc);
+        }
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) {
+          kt0[n] = tr_op(Ks, kb * 32, n, lane);
+          kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
+        }
+        // the 16 operand reads, then the 16 products each followed by one transposed read
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (red) finish(kp, s_a, s_b, kp >= 0);
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -225,12 +312,14 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
           if ((r >> 2) * 8 + (r & 3) >= lim) dsv[r] = 0.0f;
       }
       if (BIAS) {
-        // dS block -> LDS (row = query, column = key; registers 4m..4m+3 are 4 consecutive keys)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 v4 = {dsv[4 * m], dsv[4 * m + 1], dsv[4 * m + 2], dsv[4 * m + 3]};
-          *(GDPA_LDS f32x4*)(dsbuf + l32 * DSP + kb * 32 + m * 8 + 4 * g) = v4;
+        if (kb == 0) {  // the diagonal reads above are done before the buffer is rewritten
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+        // dS block -> the skewed buffer (register r holds key kb*32 + 8(r/4) + 4g + r%4)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dswr[kb * 32 + (r >> 2) * 8 + (r & 3)] = dsv[r];
       }
       const bf16x8 dsb0 = pack8(&dsv[0]);
       const bf16x8 dsb1 = pack8(&dsv[8]);
@@ -241,47 +330,6 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
         dq[n] = mfma32(kt1[n], dsb1, dq[n]);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (BIAS) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Lane 31 + t sums diagonal t - 32 (rows 0..31); lane t < 31 sums diagonal t - 63 (rows
-      // 0..t) and then diagonal t + 1 (rows t + 1..31). In both cases step s reads row s,
-      // column (s + 63 - lane) mod 64, and the second diagonal starts where the column wraps.
-      // All 64 lanes read one row at distinct columns: no bank conflicts.
-      // One running sum over the 32 steps; lane t < 31 captures it after step t (its first
-      // diagonal) and takes the second diagonal as the rest.
-      float run = 0.0f, s_a = 0.0f;
-#pragma unroll
-      for (int a8 = 0; a8 < 32; a8 += 32) {  // all 32 reads in flight, then their sums
-        float vv[32];
-#pragma unroll
-        for (int e = 0; e < 32; ++e) vv[e] = dsbuf[(a8 + e) * DSP + ((a8 + e + 63 - lane) & 63)];
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          run += vv[e];
-          if (a8 + e == lane) s_a = run;
-        }
-      }
-      if (lane > 31) s_a = run;
-      const float s_b = run - s_a;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // complete after this tile: lanes t < 31 emit d = t + 1 (with the carried part), the
-      // others emit d = lane - 63; absolute diagonal = wrow - k0 + d
-      float v;
-      int dabs;
-      if (lane < 31) {
-        v = carry + s_b;
-        carry = s_a;
-        dabs = wrow - k0 + lane + 1;
-      } else {
-        v = s_a;
-        dabs = wrow - k0 + lane - 63;
-      }
-      emit(dabs, v, true);
     }
   };
 
@@ -306,7 +354,13 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   }
 
   if (BIAS && k0_last >= 0) {
-    // the 31 carried diagonals d = t - 63 of the last tile
+    // the sums of this wave's last tile, then its 31 carried diagonals d = t - 63
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float s_a, s_b;
+    col_sums(s_a, s_b);
+    finish(k0_last, s_a, s_b, true);
     emit(wrow - k0_last + lane - 63, carry, lane < 31);
     if (lane == 0) {
       if (nb == 1) {
