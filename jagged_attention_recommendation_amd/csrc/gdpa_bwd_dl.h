@@ -33,6 +33,15 @@ constexpr int QL = BWD_Q_LOOP;  // queries per tile in the dK/dV loop
 static_assert(QI == 128 && KI == 128 && KL == ROWS && QL == ROWS, "kernels assume these tiles");
 constexpr int DSP = 128;        // floats per row of a wave's skewed dS buffer
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// Ties a value to its place in the instruction stream: the computation of x stays before this
+// point (an empty volatile asm is ordered with the scheduling barriers around it).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 template <int ACT>
 __device__ __forceinline__ float dscore(float x, float lse2, float Di, float dp, float& p) {
   // x: score in log2 units (softmax) or natural units (GDPA)
@@ -147,10 +156,9 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   // partial-row store is not waited for at once.
   const GDPA_LDS float* dsrd = dsbuf + (63 - lane);
   GDPA_LDS float* dswr = dsbuf + l32 * (DSP - 1) + 64 + 4 * g;  // row l32, key 4g at column 4g - l32 + 64
-  if (BIAS) {
+  if (BIAS) {  // each store covers 1 KiB of the buffer: 64 lanes on distinct banks
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      *(GDPA_LDS f32x4*)(dsbuf + (lane >> 1) * DSP + (lane & 1) * 64 + 4 * u) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < 16; ++u) *(GDPA_LDS f32x4*)(dsbuf + 256 * u + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
   // partial row of this row block: canonical, or the chunk's slot row for a split tile
@@ -211,126 +219,155 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   };
   int k0_last = -1;
 
-  auto tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+  // score accumulators of half kb of the tile at key offset k0, seeded with the bias / scale
+  auto seed = [&](f32x16& sacc, int k0, int kb) {
+    if (BIAS && win_ok) {
+      const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + kb * 32 + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = bp[(r >> 2) * 8 + (r & 3)];
+    } else if (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sacc[r] = bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, nb - 1)] * inv_scale;
+    } else {
+      sacc = f32x16{};
+    }
+  };
+
+  // One key tile in four sections, each a run of matrix products with independent vector work
+  // laid between them (a wave issues in order, so work placed between products runs while they
+  // execute):
+  //   A  scores S^T, dP^T of keys 0..31, with the previous tile's column sums (bias) and the
+  //      transposed K^T operands of keys 0..31;
+  //   B  scores of keys 32..63, with the gradient dS^T of keys 0..31 and the K^T operands of
+  //      keys 32..63;
+  //   C  dQ^T += K^T dS^T for keys 0..31, with the gradient of keys 32..63;
+  //   D  dQ^T += K^T dS^T for keys 32..63.
+  // MASK: the tile reaches the end of the keys, the causal diagonal or the end of the queries.
+  auto tile = [&](auto mask_c, const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int kp = k0_last;
     k0_last = k0;
-    const bool need_mask = __builtin_amdgcn_readfirstlane(
-        (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq))) != 0;
+    int lim[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 sacc, dpacc = f32x16{};
-      if (BIAS && win_ok) {
-        const GDPA_LDS float* bp = bwin + (w_hi - iq + k0 + kb * 32 + 4 * g);
+      int l = Lk - (k0 + kb * 32);
+      if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
+      lim[kb] = qv ? l - 4 * g : -64;
+    }
+    // gradient of element r of half kb (register r holds key kb*32 + 8(r/4) + 4g + r%4)
+    auto grad = [&](int kb, int r, float sv, float dpv) {
+      float p;
+      float v = dscore<ACT>(sv * sc, lse2, Di, dpv, p);
+      if (MASK && (r >> 2) * 8 + (r & 3) >= lim[kb]) v = 0.0f;
+      return v;
+    };
+    f32x16 sacc0, sacc1, dpacc0 = f32x16{}, dpacc1 = f32x16{};
+    seed(sacc0, k0, 0);
+    bf16x8 kr[D / 16], vr[D / 16], kr1[D / 16], vr1[D / 16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = bp[(r >> 2) * 8 + (r & 3)];
-      } else if (BIAS) {
+    for (int s = 0; s < 2; ++s) {
+      kr[s] = row_op(Ks, 0, s, lane);
+      vr[s] = row_op(Vs, 0, s, lane);
+    }
+    bf16x8 kt0[D / 32], kt1[D / 32], ku0[D / 32], ku1[D / 32];
+    f32x2 sab = {0.0f, 0.0f};  // the two column sums advance together
+    float va[32], vb[32];
+    __builtin_amdgcn_sched_barrier(0);
+    // A: per pair of products, the operands two steps ahead, the column reads of four rows, one
+    // transposed operand, and the sums of the rows read two steps earlier
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sacc[r] = bias_h[clampi(iq - (k0 + kb * 32 + (r >> 2) * 8 + 4 * g + (r & 3)), 0, nb - 1)] * inv_scale;
+    for (int s = 0; s < D / 16; ++s) {
+      if (s + 2 < D / 16) {
+        kr[s + 2] = row_op(Ks, 0, s + 2, lane);
+        vr[s + 2] = row_op(Vs, 0, s + 2, lane);
       } else {
-        sacc = f32x16{};
+        kr1[s - 6] = row_op(Ks, 32, s - 6, lane);
+        vr1[s - 6] = row_op(Vs, 32, s - 6, lane);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      constexpr bool DEFER = BIAS;  // the previous tile's diagonal sums ride along with kb = 0
-      const bool red = DEFER && kb == 0;
-      bf16x8 kr[D / 16], vr[D / 16];
-#pragma unroll
-      for (int s = 0; s < (red ? 2 : D / 16); ++s) {
-        kr[s] = row_op(Ks, kb * 32, s, lane);
-        vr[s] = row_op(Vs, kb * 32, s, lane);
-      }
-      // the transposed K^T operands of this half's dQ products, read during the score products
-      // so they arrive during the gradient arithmetic
-      bf16x8 kt0[D / 32], kt1[D / 32];
-      float s_a = 0.0f, s_b = 0.0f;
-      if (red) {
-        f32x2 sab = {0.0f, 0.0f};  // both sums advance together
-        // the previous tile's column sums ride along: per pair of products, the operands of the
-        // pair two steps ahead, the reads of four rows, one transposed operand, and the sums of
-        // the rows read two steps earlier
-        float va[32], vb[32];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          if (s + 2 < D / 16) {
-            kr[s + 2] = row_op(Ks, kb * 32, s + 2, lane);
-            vr[s + 2] = row_op(Vs, kb * 32, s + 2, lane);
-          }
-          sacc = mfma32(kr[s], qop[s], sacc);
-          dpacc = mfma32(vr[s], doop[s], dpacc);
-#pragma unroll
-          for (int e = 4 * s; e < 4 * s + 4; ++e) {
-            va[e] = dsrd[e * DSP + 64];
-            vb[e] = dsrd[e * DSP];
-          }
-          if (s & 1) kt1[s >> 1] = tr_op(Ks, kb * 32 + 16, s >> 1, lane);
-          else kt0[s >> 1] = tr_op(Ks, kb * 32, s >> 1, lane);
-          if (s >= 2) {
-#pragma unroll
-            for (int e = 4 * s - 8; e < 4 * s - 4; ++e) sab += f32x2{va[e], vb[e]};
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int e = 24; e < 32; ++e) sab += f32x2{va[e], vb[e]};
-        s_a = sab[0];
-        s_b = sab[1];
-      } else {
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sacc = mfma32(kr[s], qop[s], sacc);
-          dpacc = mfma32(vr[s], doop[s], dpacc);
-        }
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) {
-          kt0[n] = tr_op(Ks, kb * 32, n, lane);
-          kt1[n] = tr_op(Ks, kb * 32 + 16, n, lane);
-        }
-        // the 16 operand reads, then the 16 products each followed by one transposed read
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (red) finish(kp, s_a, s_b, kp >= 0);
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p;
-        dsv[r] = dscore<ACT>(sacc[r] * sc, lse2, Di, dpacc[r], p);
-      }
-      if (need_mask) {
-        int lim = Lk - (k0 + kb * 32);
-        if (CAUSAL) lim = min(lim, iq - (k0 + kb * 32) + 1);
-        lim = qv ? lim - 4 * g : -64;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((r >> 2) * 8 + (r & 3) >= lim) dsv[r] = 0.0f;
-      }
+      sacc0 = mfma32(kr[s], qop[s], sacc0);
+      dpacc0 = mfma32(vr[s], doop[s], dpacc0);
       if (BIAS) {
-        if (kb == 0) {  // the diagonal reads above are done before the buffer is rewritten
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int e = 4 * s; e < 4 * s + 4; ++e) {
+          va[e] = dsrd[e * DSP + 64];
+          vb[e] = dsrd[e * DSP];
         }
-        // dS block -> the skewed buffer (register r holds key kb*32 + 8(r/4) + 4g + r%4)
+        if (s >= 2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dswr[kb * 32 + (r >> 2) * 8 + (r & 3)] = dsv[r];
+          for (int e = 4 * s - 8; e < 4 * s - 4; ++e) sab += f32x2{va[e], vb[e]};
+        }
       }
-      const bf16x8 dsb0 = pack8(&dsv[0]);
-      const bf16x8 dsb1 = pack8(&dsv[8]);
+      if (s & 1) kt1[s >> 1] = tr_op(Ks, 16, s >> 1, lane);
+      else kt0[s >> 1] = tr_op(Ks, 0, s >> 1, lane);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (BIAS) {
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        dq[n] = mfma32(kt0[n], dsb0, dq[n]);
-        dq[n] = mfma32(kt1[n], dsb1, dq[n]);
+      for (int e = 24; e < 32; ++e) sab += f32x2{va[e], vb[e]};
+      finish(kp, sab[0], sab[1], kp >= 0);
+    }
+    seed(sacc1, k0, 1);  // (read here rather than with the first seed: measured faster)
+    __builtin_amdgcn_sched_barrier(0);
+    // B: per pair of products, the operands two steps ahead, the gradient of two elements of
+    // half 0 and one transposed operand of half 1
+    float ds0[16], ds1[16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      if (s + 2 < D / 16) {
+        kr1[s + 2] = row_op(Ks, 32, s + 2, lane);
+        vr1[s + 2] = row_op(Vs, 32, s + 2, lane);
+      }
+      sacc1 = mfma32(kr1[s], qop[s], sacc1);
+      dpacc1 = mfma32(vr1[s], doop[s], dpacc1);
+      ds0[2 * s] = grad(0, 2 * s, sacc0[2 * s], dpacc0[2 * s]);
+      ds0[2 * s + 1] = grad(0, 2 * s + 1, sacc0[2 * s + 1], dpacc0[2 * s + 1]);
+      pin(ds0[2 * s]);
+      pin(ds0[2 * s + 1]);
+      if (s & 1) ku1[s >> 1] = tr_op(Ks, 48, s >> 1, lane);
+      else ku0[s >> 1] = tr_op(Ks, 32, s >> 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (BIAS) {  // the column reads of section A are done before the buffer is rewritten
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dswr[(r >> 2) * 8 + (r & 3)] = ds0[r];
+    }
+    const bf16x8 d00 = pack8(&ds0[0]), d01 = pack8(&ds0[8]);
+    __builtin_amdgcn_sched_barrier(0);
+    // C: per pair of products, the gradient of four elements of half 1
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      dq[n] = mfma32(kt0[n], d00, dq[n]);
+      dq[n] = mfma32(kt1[n], d01, dq[n]);
+#pragma unroll
+      for (int r = 4 * n; r < 4 * n + 4; ++r) {
+        ds1[r] = grad(1, r, sacc1[r], dpacc1[r]);
+        pin(ds1[r]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dswr[32 + (r >> 2) * 8 + (r & 3)] = ds1[r];
+    }
+    const bf16x8 d10 = pack8(&ds1[0]), d11 = pack8(&ds1[8]);
+    __builtin_amdgcn_sched_barrier(0);
+    // D
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      dq[n] = mfma32(ku0[n], d10, dq[n]);
+      dq[n] = mfma32(ku1[n], d11, dq[n]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto run_tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
+    const bool need_mask = __builtin_amdgcn_readfirstlane(
+        (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq))) != 0;
+    if (need_mask) tile(BoolC<true>{}, Ks, Vs, k0);
+    else tile(BoolC<false>{}, Ks, Vs, k0);
   };
 
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
@@ -342,7 +379,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       issue_tile(sk1, K, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && kt * KL > wrow + 31)) tile(sk0, sv0, kt * KL);
+    if (wave_active && !(CAUSAL && kt * KL > wrow + 31)) run_tile(sk0, sv0, kt * KL);
     if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -350,7 +387,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       issue_tile(sk0, K, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && (kt + 1) * KL > wrow + 31)) tile(sk1, sv1, (kt + 1) * KL);
+    if (wave_active && !(CAUSAL && (kt + 1) * KL > wrow + 31)) run_tile(sk1, sv1, (kt + 1) * KL);
   }
 
   if (BIAS && k0_last >= 0) {
