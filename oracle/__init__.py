@@ -48,10 +48,10 @@ def _load():
     up = ctypes.POINTER(ctypes.c_uint8)
     c_int, c_long, c_double = ctypes.c_int, ctypes.c_long, ctypes.c_double
     lib.gdpa_oracle_fwd.argtypes = [c_int, c_int, c_int, ip, ip, dp, dp, dp, dp, c_int, c_int,
-                                    c_int, c_double, dp, dp, c_int]
+                                    c_int, c_int, c_double, dp, dp, c_int]
     lib.gdpa_oracle_fwd.restype = c_int
     lib.gdpa_oracle_bwd.argtypes = [c_int, c_int, c_int, ip, ip, dp, dp, dp, dp, dp, c_int, c_int,
-                                    c_int, c_double, dp, dp, dp, dp, dp, dp, c_int]
+                                    c_int, c_int, c_double, dp, dp, dp, dp, dp, dp, c_int]
     lib.gdpa_oracle_bwd.restype = c_int
     lib.gdpa_oracle_act.argtypes = [c_int, dp, c_long, dp, dp]
     lib.gdpa_oracle_act.restype = None
@@ -89,8 +89,9 @@ def _act_code(act):
 
 
 def fwd(q_off, kv_off, Q, K, V, *, act="softmax", causal=False, scale=None, bias=None,
-        nthreads=None):
+        nthreads=None, window=0):
     """Forward pass. Q: [total_q, H, D], K/V: [total_kv, H, D] (any float dtype, upcast exactly).
+    window W >= 1 also drops keys j <= i - W (sliding window).
 
     Returns (O [total_q, H, D] fp64, lse [total_q, H] fp64; lse is 0 for GDPA).
     """
@@ -114,7 +115,7 @@ def fwd(q_off, kv_off, Q, K, V, *, act="softmax", causal=False, scale=None, bias
     rc = lib.gdpa_oracle_fwd(B, H, D, _ptr(q_off, ctypes.c_int32), _ptr(kv_off, ctypes.c_int32),
                              _ptr(Q, ctypes.c_double), _ptr(K, ctypes.c_double),
                              _ptr(V, ctypes.c_double), _ptr(bias_arr, ctypes.c_double), nb,
-                             _act_code(act), int(bool(causal)), float(scale),
+                             _act_code(act), int(bool(causal)), int(window), float(scale),
                              _ptr(O, ctypes.c_double), _ptr(lse, ctypes.c_double),
                              nthreads or default_threads())
     if rc != 0:
@@ -123,7 +124,7 @@ def fwd(q_off, kv_off, Q, K, V, *, act="softmax", causal=False, scale=None, bias
 
 
 def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, bias=None,
-        nthreads=None, error_scale=False):
+        nthreads=None, error_scale=False, window=0):
     """Backward pass of the loss sum(dO * O).
 
     Returns dict with dQ, dK, dV (fp64, same layouts as Q/K/V), dbias ([H, NB] or None),
@@ -156,7 +157,7 @@ def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, 
                              _ptr(Q, ctypes.c_double), _ptr(K, ctypes.c_double),
                              _ptr(V, ctypes.c_double), _ptr(dO, ctypes.c_double),
                              _ptr(bias_arr, ctypes.c_double), nb, _act_code(act),
-                             int(bool(causal)), float(scale), _ptr(dQ, ctypes.c_double),
+                             int(bool(causal)), int(window), float(scale), _ptr(dQ, ctypes.c_double),
                              _ptr(dK, ctypes.c_double), _ptr(dV, ctypes.c_double),
                              _ptr(dbias, ctypes.c_double), _ptr(Dv, ctypes.c_double),
                              _ptr(dscale, ctypes.c_double) if error_scale and nb > 0 else None,

@@ -18,7 +18,10 @@
  *     backward; lse_i = m_i + ln l_i and D_i = sum_j p_ij dp_ij are those quantities.
  *
  * Definition, per sample b and head h, local query i in [0,Lq) and key j in [0,Lk):
- *   valid(i,j) = !causal || j <= i
+ *   valid(i,j) = (!causal || j <= i) && (W == 0 || j > i - W)
+ *     W >= 1 is a sliding window (same page, self-attention paragraph on sliding-window
+ *     attention: each token attends only to nearby events; read as the W most recent keys,
+ *     itself included); the library takes it with causal = 1
  *   s_ij = scale * <q_i,k_j> + bias[h, clamp(i-j, 0, NB-1)]        (bias term absent if NB = 0)
  *   softmax: p_ij = exp(s_ij - m_i) / l_i over valid j, o_i = sum_j p_ij v_j, lse_i = m_i + ln l_i
  *            a row with no valid key gives o_i = 0, lse_i = -inf
@@ -118,11 +121,11 @@ static int check_offsets(int B, const int32_t* off) {
 /* Scores of one query row against every key of its sample. valid[j] marks the unmasked keys.
  * Returns the number of valid keys. */
 static long row_scores(int D, int H, int h, long i, long Lk, const double* qi, const double* Kb,
-                       const double* bias_h, int nb, int causal, double scale, double* s,
-                       unsigned char* valid) {
+                       const double* bias_h, int nb, int causal, int window, double scale,
+                       double* s, unsigned char* valid) {
   long nvalid = 0;
   for (long j = 0; j < Lk; ++j) {
-    valid[j] = (unsigned char)(!causal || j <= i);
+    valid[j] = (unsigned char)((!causal || j <= i) && (window <= 0 || j > i - window));
     if (!valid[j]) continue;
     double v = scale * dot(qi, Kb + (size_t)j * H * D + (size_t)h * D, D);
     if (nb > 0) v += bias_h[bias_index(i, j, nb)];
@@ -158,8 +161,9 @@ static double row_probs(int act, long Lk, const double* s, const unsigned char* 
 
 int gdpa_oracle_fwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv_off,
                     const double* Q, const double* K, const double* V, const double* bias, int nb,
-                    int act, int causal, double scale, double* O, double* lse, int nthreads) {
-  if (B < 0 || H <= 0 || D <= 0 || nb < 0) return 1;
+                    int act, int causal, int window, double scale, double* O, double* lse,
+                    int nthreads) {
+  if (B < 0 || H <= 0 || D <= 0 || nb < 0 || window < 0) return 1;
   if (act < 0 || act > 2) return 1;
   if (check_offsets(B, q_off) || check_offsets(B, kv_off)) return 1;
   long ntask = (long)B * H;
@@ -189,7 +193,7 @@ int gdpa_oracle_fwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
         for (long i = 0; i < Lq; ++i) {
           size_t row = ((size_t)(q0 + i) * H + h);
           const double* qi = Q + row * D;
-          long nvalid = row_scores(D, H, h, i, Lk, qi, Kb, bias_h, nb, causal, scale, s, valid);
+          long nvalid = row_scores(D, H, h, i, Lk, qi, Kb, bias_h, nb, causal, window, scale, s, valid);
           double li = row_probs(act, Lk, s, valid, nvalid, p);
           double* oi = O + row * D;
           for (int c = 0; c < D; ++c) oi[c] = 0.0;
@@ -211,10 +215,10 @@ int gdpa_oracle_fwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
 
 int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv_off,
                     const double* Q, const double* K, const double* V, const double* dO,
-                    const double* bias, int nb, int act, int causal, double scale, double* dQ,
-                    double* dK, double* dV, double* dbias, double* Dvec, double* dbias_scale,
-                    int nthreads) {
-  if (B < 0 || H <= 0 || D <= 0 || nb < 0) return 1;
+                    const double* bias, int nb, int act, int causal, int window, double scale,
+                    double* dQ, double* dK, double* dV, double* dbias, double* Dvec,
+                    double* dbias_scale, int nthreads) {
+  if (B < 0 || H <= 0 || D <= 0 || nb < 0 || window < 0) return 1;
   if (act < 0 || act > 2) return 1;
   if (check_offsets(B, q_off) || check_offsets(B, kv_off)) return 1;
   long ntask = (long)B * H;
@@ -268,7 +272,7 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
           size_t row = ((size_t)(q0 + i) * H + h);
           const double* qi = Q + row * D;
           const double* doi = dO + row * D;
-          long nvalid = row_scores(D, H, h, i, Lk, qi, Kb, bias_h, nb, causal, scale, s, valid);
+          long nvalid = row_scores(D, H, h, i, Lk, qi, Kb, bias_h, nb, causal, window, scale, s, valid);
           row_probs(act, Lk, s, valid, nvalid, p);
           double Di = 0.0;
           for (long j = 0; j < Lk; ++j) {

@@ -40,8 +40,8 @@ def rand_problem(seed, B=3, H=2, D=4, lq=None, lk=None, maxlen=6, nb=0, same=Tru
     return dict(qo=qo, ko=ko, Q=Q, K=K, V=V, dO=dO, bias=bias)
 
 
-def padded_torch(pb, act, causal, scale, requires_grad=False):
-    """Dense padded reference: [B, H, Lmax, D] tensors, mask carries lengths/causality/bias."""
+def padded_torch(pb, act, causal, scale, requires_grad=False, window=0):
+    """Dense padded reference: [B, H, Lmax, D] tensors, mask carries lengths/causality/window/bias."""
     qo, ko = pb["qo"], pb["ko"]
     B = len(qo) - 1
     H, D = pb["Q"].shape[1:]
@@ -70,6 +70,8 @@ def padded_torch(pb, act, causal, scale, requires_grad=False):
         m = (i < int(lq[b])) & (j < int(lk[b]))
         if causal:
             m = m & (j <= i)
+        if window > 0:
+            m = m & (j > i - window)
         valid[b, 0] = m
     add = torch.zeros(B, H, Lq, Lk, dtype=torch.float64)
     if bt is not None:
@@ -93,14 +95,15 @@ def padded_torch(pb, act, causal, scale, requires_grad=False):
     return O, (Qt, Kt, Vt, bt)
 
 
-def run_oracle_fwd(pb, act, causal, scale):
+def run_oracle_fwd(pb, act, causal, scale, window=0):
     return oracle.fwd(pb["qo"], pb["ko"], pb["Q"], pb["K"], pb["V"], act=act, causal=causal,
-                      scale=scale, bias=pb["bias"], nthreads=2)
+                      scale=scale, bias=pb["bias"], nthreads=2, window=window)
 
 
-def run_oracle_bwd(pb, act, causal, scale):
+def run_oracle_bwd(pb, act, causal, scale, window=0):
     return oracle.bwd(pb["qo"], pb["ko"], pb["Q"], pb["K"], pb["V"], pb["dO"], act=act,
-                      causal=causal, scale=scale, bias=pb["bias"], nthreads=2, error_scale=True)
+                      causal=causal, scale=scale, bias=pb["bias"], nthreads=2, error_scale=True,
+                      window=window)
 
 
 CASES = [
@@ -412,6 +415,110 @@ def test_softmax_backward_invariants():
             sdv = g["dV"][pb["ko"][b]:pb["ko"][b + 1]].sum(axis=0)
             sdo = pb["dO"][pb["qo"][b]:pb["qo"][b + 1]].sum(axis=0)
             np.testing.assert_allclose(sdv, sdo, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# sliding window (causal, W most recent keys)
+
+WINDOW_CASES = [("softmax", 3, 2), ("softmax", 0, 1), ("gelu_tanh", 4, 3), ("silu", 0, 2)]
+
+
+@pytest.mark.parametrize("act,nb,window", WINDOW_CASES)
+def test_window_fwd_bwd_match_padded_library_attention(act, nb, window):
+    """The window is one more mask term of the padded library reference (forward and autograd)."""
+    pb = rand_problem(51, B=3, H=2, D=4, maxlen=9, nb=nb, same=False)
+    scale = 0.8
+    O, _ = run_oracle_fwd(pb, act, True, scale, window)
+    Oref, (Qt, Kt, Vt, bt) = padded_torch(pb, act, True, scale, requires_grad=True, window=window)
+    np.testing.assert_allclose(O, Oref.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (Oref * torch.tensor(pb["dO"])).sum().backward()
+    g = run_oracle_bwd(pb, act, True, scale, window)
+    np.testing.assert_allclose(g["dQ"], Qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g["dK"], Kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g["dV"], Vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    if nb > 0:
+        np.testing.assert_allclose(g["dbias"], bt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
+def test_window_one_keeps_only_the_diagonal(act):
+    """W = 1: query i sees key i alone, so softmax gives o_i = v_i and lse_i = s_ii, and GDPA
+    gives o_i = act(s_ii) v_i (rows past the keys see nothing)."""
+    pb = rand_problem(52, B=3, H=2, D=5, lq=[4, 6, 3], lk=[4, 5, 3], nb=3)
+    scale = 0.6
+    O, lse = run_oracle_fwd(pb, act, True, scale, 1)
+    for b in range(3):
+        for i in range(pb["qo"][b + 1] - pb["qo"][b]):
+            q = pb["Q"][pb["qo"][b] + i]
+            if i >= pb["ko"][b + 1] - pb["ko"][b]:
+                np.testing.assert_array_equal(O[pb["qo"][b] + i], 0.0)
+                continue
+            k, v = pb["K"][pb["ko"][b] + i], pb["V"][pb["ko"][b] + i]
+            s = scale * (q * k).sum(axis=1) + pb["bias"][:, 0]  # i - j = 0: bucket 0
+            if act == "softmax":
+                np.testing.assert_array_equal(O[pb["qo"][b] + i], v)
+                np.testing.assert_allclose(lse[pb["qo"][b] + i], s, rtol=1e-14, atol=1e-14)
+            else:
+                a = oracle.act(act, s)
+                np.testing.assert_allclose(O[pb["qo"][b] + i], a[:, None] * v, rtol=1e-13, atol=1e-14)
+
+
+def test_window_covering_every_key_is_plain_causal():
+    pb = rand_problem(53, B=4, H=2, D=3, maxlen=7, nb=4, same=False)
+    for act in ("softmax", "silu"):
+        O0, l0 = run_oracle_fwd(pb, act, True, 0.7)
+        O1, l1 = run_oracle_fwd(pb, act, True, 0.7, 7)
+        np.testing.assert_array_equal(O0, O1)
+        np.testing.assert_array_equal(l0, l1)
+        g0, g1 = run_oracle_bwd(pb, act, True, 0.7), run_oracle_bwd(pb, act, True, 0.7, 7)
+        for k in ("dQ", "dK", "dV", "dbias"):
+            np.testing.assert_array_equal(g0[k], g1[k])
+
+
+def test_window_equals_attention_over_the_key_slice():
+    """Without a bias, query i under window W is non-causal attention of that one query over keys
+    max(0, i - W + 1) .. i: rebuild every query as its own sample with that key slice, and sum
+    the slices' key gradients back (a different evaluation order of the same terms)."""
+    W = 3
+    pb = rand_problem(54, B=2, H=2, D=4, lq=[7, 5], lk=[7, 5])
+    scale = 0.9
+    for act in ("softmax", "gelu_tanh"):
+        O, _ = run_oracle_fwd(pb, act, True, scale, W)
+        g = run_oracle_bwd(pb, act, True, scale, W)
+        qs, ks, rows = [], [], []
+        for b in range(2):
+            for i in range(pb["qo"][b + 1] - pb["qo"][b]):
+                lo = max(0, i - W + 1)
+                rows.append((pb["qo"][b] + i, pb["ko"][b] + lo, pb["ko"][b] + i + 1))
+        qo = inputs.offsets_from_lengths(np.ones(len(rows), dtype=np.int64))
+        ko = inputs.offsets_from_lengths(np.array([e - s for _, s, e in rows]))
+        Qs = np.stack([pb["Q"][r] for r, _, _ in rows])
+        dOs = np.stack([pb["dO"][r] for r, _, _ in rows])
+        Ks = np.concatenate([pb["K"][s:e] for _, s, e in rows])
+        Vs = np.concatenate([pb["V"][s:e] for _, s, e in rows])
+        Os, _ = oracle.fwd(qo, ko, Qs, Ks, Vs, act=act, causal=False, scale=scale, nthreads=2)
+        gs = oracle.bwd(qo, ko, Qs, Ks, Vs, dOs, act=act, causal=False, scale=scale, nthreads=2)
+        idx = [r for r, _, _ in rows]
+        np.testing.assert_allclose(O[idx], Os, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(g["dQ"][idx], gs["dQ"], rtol=1e-12, atol=1e-13)
+        dK = np.zeros_like(pb["K"])
+        dV = np.zeros_like(pb["V"])
+        for n, (_, s, e) in enumerate(rows):
+            dK[s:e] += gs["dK"][ko[n]:ko[n + 1]]
+            dV[s:e] += gs["dV"][ko[n]:ko[n + 1]]
+        np.testing.assert_allclose(g["dK"], dK, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(g["dV"], dV, rtol=1e-12, atol=1e-13)
+
+
+def test_window_bias_gradient_invariants():
+    """Valid pairs have 0 <= i - j < W, so buckets W and above get nothing; softmax gradient
+    rows sum to zero, so every head's buckets sum to zero."""
+    W = 3
+    pb = rand_problem(55, B=3, H=2, D=4, maxlen=9, nb=6, same=False)
+    g = run_oracle_bwd(pb, "softmax", True, 0.7, W)
+    np.testing.assert_array_equal(g["dbias"][:, W:], 0.0)
+    np.testing.assert_allclose(g["dbias"].sum(axis=1), 0.0, atol=1e-12)
+    assert np.abs(g["dbias"][:, :W]).min() > 0.0
 
 
 # ----------------------------------------------------------------------------------------------
