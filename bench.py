@@ -29,7 +29,10 @@ WORKLOADS = {
     2: "jfa_softmax_causal_bias_B64_H4_D128_L1-2048_bf16",
     3: "gdpa_cross_gelu_B256_H4_D128_Lq64-4096_Lk8-64_bf16",
     4: "gdpa_pma_silu_B512_H8_D64_Lq32_Lk_lognormal_bf16",
+    5: "mxfp8_causal_softmax_and_silu_fwd_B128_H8_D128_L_lognormal",
 }
+# Workloads bound by HBM bandwidth (short key or query sequences): their roofline is in GB/s.
+HBM_BOUND = (3, 4)
 
 
 def parse():
@@ -141,6 +144,8 @@ def main():
         sys.exit(1)
     gdpa.load()
     dev = torch.device("cuda:0")
+    if args.config == 5:
+        return main_mx(args, torch, gdpa, inputs, workload, dev)
     p = inputs.config_problem(args.config)
 
     def up_bf16(a):
@@ -218,14 +223,21 @@ def main():
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
     dom = max(kern_ms, key=kern_ms.get)
-    dom_flops = dominant_kernel_flops(p, dom)
-    achieved = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, dom),
-                "avg_launch_ms": round(kern_ms[dom], 4),
-                "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()}}
+    if args.config in HBM_BOUND:
+        # short keys (cross) or short queries (PMA): the kernels stream the long side once
+        achieved = workload.kernel_bytes(p, dom) / (kern_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = dominant_kernel_flops(p, dom) / (kern_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roofline.update({"traffic": measured_traffic(args.config, dom),
+                     "avg_launch_ms": round(kern_ms[dom], 4),
+                     "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+                     "kernel_gbs": {k: round(workload.kernel_bytes(p, k) / (v * 1e-3) / 1e9, 1)
+                                    for k, v in kern_ms.items()}})
 
     out = {
         "metric": "useful (unpadded) TFLOPS fwd+bwd, jagged sparsity 0.5, and % of MFMA peak",
@@ -253,6 +265,65 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def main_mx(args, torch, gdpa, inputs, workload, dev):
+    """MX-fp8 forward workload: one step = the causal forward with softmax and with SiLU on the
+    same e4m3 + e8m0 inputs (scaled fp8 products for Q.K^T, bf16 for P.V, fp32 accumulation)."""
+    p = inputs.config_problem(5)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    Q, K, V = u8(p.Q), u8(p.K), u8(p.V)
+    qs, ks, vs = u8(p.q_scale), u8(p.k_scale), u8(p.v_scale)
+    q_off = torch.from_numpy(p.q_off).to(dev)
+    kv_off = torch.from_numpy(p.kv_off).to(dev)
+    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
+    acts = ("softmax", "silu")
+    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, dtype="mxfp8", act="softmax",
+                        causal=True, scale=p.scale, bias_buckets=0, max_q=max_q, max_kv=max_kv)
+    ws = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
+    O = {a: torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev) for a in acts}
+    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev)
+
+    def step():
+        for a in acts:
+            gdpa.fwd(Q, K, V, q_off, kv_off, act=a, causal=True, scale=p.scale, q_scale=qs,
+                     k_scale=ks, v_scale=vs, max_q=max_q, max_kv=max_kv, out=O[a],
+                     lse=lse if a == "softmax" else None, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdpa.profile_start(("fwd",))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdpa.profile_stop()
+    n, ms = gdpa.profile_read("fwd")
+    kern_ms = ms / max(n, 1)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    for a in acts:
+        if not torch.isfinite(O[a].float()).all():
+            raise RuntimeError("non-finite output")
+    f_fwd = workload.useful_flops(p, "fwd")
+    value = len(acts) * f_fwd / (ms_step * 1e-3) / 1e12
+    achieved = f_fwd / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": "useful (unpadded) TFLOPS fwd, MX-fp8 (softmax + SiLU), and % of fp8 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
+        "config": {"workload": WORKLOADS[5], "B": p.B, "H": p.H, "D": p.D,
+                   "total_tokens": p.total_q, "causal": True, "acts": list(acts)},
+        "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "fwd", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(kern_ms, 4),
+                     "hbm_gbs": round(workload.fwd_bytes(p) / (kern_ms * 1e-3) / 1e9, 1)},
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -61,3 +61,30 @@ def bwd_bytes(p):
     if p.bias is not None:
         b += 2 * p.bias.size * 4
     return float(b)
+
+
+def kernel_bytes(p, kernel):
+    """Algorithmic HBM bytes of one launch of a kernel: every operand it must read and every
+    result it must write, each once.
+
+    fwd: Q, K, V read, O (+ lse) written. dq: Q, dO, K, V (+ O and lse for softmax, whose
+    prologue forms D) read, dQ (+ D) written. dkdv: Q, dO, K, V (+ lse, D) read, dK, dV written.
+    """
+    if kernel == "fwd":
+        return fwd_bytes(p)
+    e = elem_bytes(p)
+    H, D = p.H, p.D
+    tq, tk = p.total_q, p.total_kv
+    b = (2 * tq + 2 * tk) * H * D * e
+    sm = p.act == "softmax"
+    if kernel == "dq":
+        b += tq * H * D * e
+        if sm:
+            b += tq * H * D * e + tq * H * 4 + tq * H * 4
+    elif kernel == "dkdv":
+        b += 2 * tk * H * D * e
+        if sm:
+            b += 2 * tq * H * 4
+    else:
+        raise ValueError(kernel)
+    return float(b)

@@ -36,3 +36,22 @@ def test_summary_scales_by_the_copy(tmp_path):
     p = tmp_path / "summary.txt"
     p.write_text("# header\njson: " + json.dumps(s) + "\n")
     assert counters.load_summary(p) == s
+
+
+def test_kernel_bytes_count_each_operand_once():
+    """Per-kernel algorithmic bytes: the tensors each kernel reads and writes, counted by hand."""
+    from jagged_attention_recommendation_amd import inputs, workload
+    import numpy as np
+    lq, lk = np.array([5, 9]), np.array([3, 7])
+    for act in ("softmax", "silu"):
+        p = inputs.make_problem("kb", seed=1, H=2, D=32, lq=lq, lk=lk, dtype="bf16", act=act,
+                                causal=False, bias_buckets=0)
+        tq, tk, row = 14, 10, 2 * 32 * 2  # rows of Q and of K; bytes of one row (H x D bf16)
+        sm = act == "softmax"
+        assert workload.kernel_bytes(p, "fwd") == workload.fwd_bytes(p)
+        # dQ: Q, dO, K, V read, dQ written; softmax adds O (for D), lse, and the D vector written
+        dq = (2 * tq + 2 * tk) * row + tq * row + (tq * row + 2 * tq * 2 * 4 if sm else 0)
+        # dK/dV: Q, dO, K, V read, dK, dV written; softmax adds lse and D read
+        dkdv = (2 * tq + 2 * tk) * row + 2 * tk * row + (2 * tq * 2 * 4 if sm else 0)
+        assert workload.kernel_bytes(p, "dq") == dq
+        assert workload.kernel_bytes(p, "dkdv") == dkdv
