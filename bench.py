@@ -45,15 +45,17 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of W keys on the causal JFA workload (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
 
 
-def dominant_kernel_flops(p, kernel):
+def dominant_kernel_flops(p, kernel, window=0):
     """Algorithmic flops one launch of the kernel must do: pairs x flops-per-pair."""
     from jagged_attention_recommendation_amd import workload
-    pairs = int(workload.pairs_per_sample(p.lq, p.lk, p.causal).sum()) * p.H
+    pairs = int(workload.pairs_per_sample(p.lq, p.lk, p.causal, window).sum()) * p.H
     per_pair = {"fwd": 4, "dq": 6, "dkdv": 8}[kernel] * p.D  # products: 2 / 3 / 4
     return float(per_pair) * pairs
 
@@ -146,6 +148,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.config == 5:
         return main_mx(args, torch, gdpa, inputs, workload, dev)
+    if args.window and args.config != 2:
+        print("--window applies to the causal JFA workload (--config 2)", file=sys.stderr)
+        sys.exit(2)
+    win = args.window
     p = inputs.config_problem(args.config)
 
     def up_bf16(a):
@@ -158,14 +164,15 @@ def main():
     nb = 0 if bias is None else bias.shape[1]
     max_q, max_kv = int(p.lq.max()), int(p.lk.max())
     prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, act=p.act, causal=p.causal,
-                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv)
+                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=win)
     ws_f = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
     O = torch.empty_like(Q)
     lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if p.act == "softmax" else None
     grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
              torch.empty_like(bias) if bias is not None else None)
-    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv)
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv,
+              window=win)
 
     def step():
         gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
@@ -218,8 +225,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    f_fwd = workload.useful_flops(p, "fwd")
-    f_bwd = workload.useful_flops(p, "bwd")
+    f_fwd = workload.useful_flops(p, "fwd", win)
+    f_bwd = workload.useful_flops(p, "bwd", win)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
     dom = max(kern_ms, key=kern_ms.get)
@@ -229,11 +236,11 @@ def main():
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
-        achieved = dominant_kernel_flops(p, dom) / (kern_ms[dom] * 1e-3) / 1e12
+        achieved = dominant_kernel_flops(p, dom, win) / (kern_ms[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roofline.update({"traffic": measured_traffic(args.config, dom),
+    roofline.update({"traffic": None if win else measured_traffic(args.config, dom),
                      "avg_launch_ms": round(kern_ms[dom], 4),
                      "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()},
                      "kernel_gbs": {k: round(workload.kernel_bytes(p, k) / (v * 1e-3) / 1e9, 1)
@@ -252,7 +259,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "B": p.B, "H": p.H, "D": p.D,
+        "config": {"workload": WORKLOADS[args.config] + (f"_window{win}" if win else ""),
+                   "B": p.B, "H": p.H, "D": p.D, "window": win,
                    "total_tokens": p.total_q, "causal": p.causal, "act": p.act,
                    "bias_buckets": nb,
                    "token_sparsity": round(1 - p.total_q / (p.B * max(max_q, 1)), 4)},
@@ -263,7 +271,7 @@ def main():
         "bwd_ms": round(bwd_ms, 4),
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not win:
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -12,7 +12,7 @@
  *     multiplications with an element-wise activation in between).
  *
  * Math, per sample b, head h, local query i in [0, Lq_b) and key j in [0, Lk_b):
- *   valid(i,j) = !causal || j <= i
+ *   valid(i,j) = (!causal || j <= i) && (window == 0 || j > i - window)
  *   s_ij = scale * <q_i, k_j> + bias[h, clamp(i - j, 0, NB - 1)]   (no bias term if NB == 0)
  *   softmax: o_i = sum_j softmax_j(s_i.) v_j over valid j; lse_i = ln sum_j exp(s_ij)
  *            (a row with no valid key: o_i = 0, lse_i = -inf)
@@ -29,6 +29,9 @@
  * consecutive elements along D ([rows, H, D/32] arrays q_scale/k_scale/v_scale), O is bf16.
  * This MX encoding follows the OCP Microscaling Formats v1.0 (same page, low-precision part:
  * MXFP8 block-scaled matrix products).
+ * Sliding-window attention (same page, the paragraph on sliding-window attention): with
+ * causal = 1 and window = W >= 1, query i attends to keys i - W + 1 .. i only; tiles wholly
+ * outside the window are neither scheduled nor loaded.
  *
  * Ownership and synchronisation. Every pointer except `p` is device memory owned by the caller and
  * must stay valid until the work enqueued on `stream` (a hipStream_t; NULL = the null stream)
@@ -62,7 +65,7 @@ typedef enum {
   GDPA_OK = 0,
   GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
   GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX backward,
-                          scale <= 0 outside fp32, ... */
+                          scale <= 0 outside fp32, a window outside causal bf16 D = 128, ... */
   GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
   GDPA_EHIP = 4        /* the HIP runtime refused a launch */
 } gdpa_status;
@@ -81,10 +84,12 @@ typedef struct {
   int32_t causal;       /* 0 or 1: keep j <= i on local positions (top-left aligned) */
   float scale;          /* s = scale * q.k (+ bias); must be > 0 for GDPA_BF16 / GDPA_MXFP8_E4M3 */
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
+  int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1,
+                           GDPA_BF16 and D = 128 (otherwise GDPA_ENOTSUP) */
 } gdpa_problem;
 
 /* ABI version of this header (checked by bindings). */
-#define GDPA_ABI_VERSION 1
+#define GDPA_ABI_VERSION 2
 int32_t gdpa_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */

@@ -32,6 +32,9 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->dtype != GDPA_F32 && !(p->scale > 0.0f)) return GDPA_ENOTSUP;
   if (p->D != 32 && p->D != 64 && p->D != 128) return GDPA_ENOTSUP;
   if (p->dtype == GDPA_MXFP8_E4M3 && p->D != 128) return GDPA_ENOTSUP;
+  if (p->window < 0) return GDPA_EINVAL;
+  // sliding windows: causal self-attention on the bf16 D = 128 kernels
+  if (p->window > 0 && (p->causal != 1 || p->dtype != GDPA_BF16 || p->D != 128)) return GDPA_ENOTSUP;
   // element counts must fit the kernels' 64-bit addressing and the scheduler's int32 counters
   if ((int64_t)p->H * p->D > (1 << 20)) return GDPA_ENOTSUP;
   return GDPA_OK;
@@ -41,7 +44,7 @@ Prob to_prob(const gdpa_problem* p) {
   Prob r;
   r.B = p->B; r.H = p->H; r.D = p->D; r.dtype = p->dtype; r.act = p->act; r.causal = p->causal;
   r.nb = p->bias_buckets; r.total_q = p->total_q; r.total_kv = p->total_kv;
-  r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale;
+  r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale; r.win = p->window;
   return r;
 }
 
@@ -240,7 +243,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
-  sa.causal = p->causal; sa.tile_item = fwd_tile_rows(p->dtype);
+  sa.causal = p->causal; sa.win = p->window; sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
   sa.split = L.split ? 1 : 0; sa.tile_base = nullptr; sa.split_slot = nullptr;
   sa.ws_header = ws + L.header; sa.items = ws + L.items;
@@ -253,7 +256,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
   fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
   fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
-  fa.scale = p->scale; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
+  fa.scale = p->scale; fa.win = p->window; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
   fa.part_o = (float*)(ws + L.part_o); fa.part_ml = (float*)(ws + L.part_ml);
   const int grid = (int)L.max_items;
   if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
@@ -294,7 +297,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
-  sa.ws_header = ws + L.header;
+  sa.win = p->window; sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
   sa.split = L.split ? 1 : 0;
   SchedArgs sq = sa, sk = sa;
@@ -323,7 +326,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.split_cnt_q = (int32_t*)(ws + L.split_cnt_q); ba.split_cnt_k = (int32_t*)(ws + L.split_cnt_k);
   ba.part_dq = (float*)(ws + L.part_dq); ba.part_dk = (float*)(ws + L.part_dk);
   ba.part_dv = (float*)(ws + L.part_dv);
-  ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale;
+  ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale; ba.win = p->window;
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   if (e != hipSuccess) return map_hip(e);
@@ -333,7 +336,8 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
     da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
     da.part = ba.dbias_part; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
     da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
-    da.causal = p->causal; da.tile_rows = tq; da.loop_rows = bwd_k_loop(p->dtype);
+    da.causal = p->causal; da.win = p->window; da.tile_rows = tq;
+    da.loop_rows = bwd_k_loop(p->dtype);
     e = launch_dbias_reduce(da, s);
   }
   return map_hip(e);

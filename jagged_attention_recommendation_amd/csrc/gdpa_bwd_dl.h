@@ -60,7 +60,8 @@ __device__ __forceinline__ float dscore(float x, float lse2, float Di, float dp,
 // S^T = K Q^T and dP^T = V dO^T with lane = query, dQ^T += K^T dS^T with K^T read transposed.
 // Bias gradient: the paired-diagonal sums of gdpa_bwd_bf16.hip over the wave's 32 x 64 block of
 // dS, staged in a per-wave LDS buffer; every partial-row entry is written once.
-template <int ACT, bool CAUSAL, bool BIAS>
+// WIN: causal sliding window of a.win keys (query i sees keys i - win + 1 .. i).
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sk0_[TILE];
   __shared__ __attribute__((aligned(16))) char sv0_[TILE];
@@ -93,8 +94,10 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   int nkt = (Lk + KL - 1) / KL;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
   if (i0 >= Lq) nkt = 0;
-  // key tiles of this item: all of them, or one chunk of a split tile
-  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
+  // key tiles of this item: all of them, or one chunk of a split tile, counted from the first
+  // tile the item's sliding window reaches
+  const int kt_first = WIN ? win_first_ktile(i0, a.win, KL) : 0;
+  const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
 
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
@@ -248,18 +251,19 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     constexpr bool MASK = decltype(mask_c)::value;
     const int kp = k0_last;
     k0_last = k0;
-    int lim[2];
+    int lim[2], lo[2];  // key offset o of register r (8 (r / 4) + r % 4) valid for lo <= o < lim
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int l = Lk - (k0 + kb * 32);
       if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
       lim[kb] = qv ? l - 4 * g : -64;
+      lo[kb] = WIN ? iq - a.win + 1 - (k0 + kb * 32) - 4 * g : -64;
     }
     // gradient of element r of half kb (register r holds key kb*32 + 8(r/4) + 4g + r%4)
     auto grad = [&](int kb, int r, float sv, float dpv) {
       float p;
       float v = dscore<ACT>(sv * sc, lse2, Di, dpv, p);
-      if (MASK && (r >> 2) * 8 + (r & 3) >= lim[kb]) v = 0.0f;
+      if (MASK && ((r >> 2) * 8 + (r & 3) >= lim[kb] || (WIN && (r >> 2) * 8 + (r & 3) < lo[kb]))) v = 0.0f;
       return v;
     };
     f32x16 sacc0, sacc1, dpacc0 = f32x16{}, dpacc1 = f32x16{};
@@ -365,11 +369,17 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   };
   auto run_tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
     const bool need_mask = __builtin_amdgcn_readfirstlane(
-        (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq))) != 0;
+        (int)((k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (wrow + 32 > Lq) ||
+              (WIN && k0 < wrow + 32 - a.win))) != 0;
     if (need_mask) tile(BoolC<true>{}, Ks, Vs, k0);
     else tile(BoolC<false>{}, Ks, Vs, k0);
   };
 
+  // whether this wave computes key tile kt: not wholly after its last query (causal) nor wholly
+  // before its first query's window (the bias-gradient reduction assumes the same range)
+  auto wave_needs = [&](int kt) {
+    return wave_active && !(CAUSAL && kt * KL > wrow + 31) && !(WIN && (kt + 1) * KL <= wrow - a.win + 1);
+  };
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage stay in flight while the other stage is read.
   for (int kt = kt_lo; kt < kt_hi; kt += 2) {
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       issue_tile(sk1, K, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && kt * KL > wrow + 31)) run_tile(sk0, sv0, kt * KL);
+    if (wave_needs(kt)) run_tile(sk0, sv0, kt * KL);
     if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       issue_tile(sk0, K, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && (kt + 1) * KL > wrow + 31)) run_tile(sk1, sv1, (kt + 1) * KL);
+    if (wave_needs(kt + 1)) run_tile(sk1, sv1, (kt + 1) * KL);
   }
 
   if (BIAS && k0_last >= 0) {
@@ -436,7 +446,8 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
 // S = Q K^T and dP = dO V^T with lane = key; dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
 // read transposed from the query tiles. The softmax row terms (lse, D) of a query tile come in
 // by 4-byte direct loads beside the tile itself.
-template <int ACT, bool CAUSAL, bool BIAS>
+// WIN: causal sliding window of a.win keys (key j is seen by queries j .. j + win - 1).
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   constexpr bool SM = ACT == ACT_SOFTMAX;
   __shared__ __attribute__((aligned(16))) char sq0_[TILE];
@@ -470,7 +481,9 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
 
   const int nqt = (Lq + QL - 1) / QL;
   const int qt0 = CAUSAL ? j0 / QL : 0;
-  const int nt = j0 < Lk && qt0 < nqt ? nqt - qt0 : 0;  // query tiles this key tile visits
+  // one past the last query tile whose window reaches this key tile
+  const int qend = WIN ? win_end_qtile(min(Lk, j0 + KI) - 1, a.win, QL, nqt) : nqt;
+  const int nt = j0 < Lk && qt0 < qend ? qend - qt0 : 0;  // query tiles this key tile visits
   // the item's query tiles qt0 + [t_lo, t_hi): all of them, or one chunk of a split tile
   const int t_lo = it.lo, t_hi = min(it.hi, nt);
 
@@ -524,7 +537,8 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   auto tile = [&](const GDPA_LDS char* __restrict__ Qs, const GDPA_LDS char* __restrict__ dOs,
                   const GDPA_LDS float* srt, int i0) {
     const bool need_mask = __builtin_amdgcn_readfirstlane(
-        (int)((i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31))) != 0;
+        (int)((i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31) ||
+              (WIN && i0 + QL - 1 > wkey + a.win - 1))) != 0;
     auto half = [&](int qb) {
       const int ib = i0 + qb * 32 + 4 * g;  // query of register r: ib + (r / 4) * 8 + r % 4
       f32x16 sacc, dpacc = f32x16{};
@@ -587,6 +601,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
       }
       if (need_mask) {
         int hi = kvalid ? Lq - ib : -64;    // query offsets at or past hi are invalid
+        if (WIN) hi = min(hi, jk + a.win - ib);  // ... and those past the key's window
         const int lo = CAUSAL ? jk - ib : -64;  // query offsets below lo precede the key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -638,6 +653,11 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     }
   };
 
+  // whether this wave computes the query tile at i0: not wholly before its first key (causal)
+  // nor wholly after the window of its last key
+  auto wave_needs = [&](int i0) {
+    return wave_active && !(CAUSAL && i0 + QL - 1 < wkey) && !(WIN && i0 > min(wkey + 31, Lk - 1) + a.win - 1);
+  };
   // Two stages, as in the dQ kernel.
   GDPA_LDS float* rt0 = rt;
   GDPA_LDS float* rt1 = rt + (SM ? 2 * QL : 0);
@@ -647,7 +667,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     if (t + 1 < t_hi) issue(sq1, so1, rt1, qt0 + t + 1);
     {
       const int i0 = (qt0 + t) * QL;
-      if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq0, so0, rt0, i0);
+      if (wave_needs(i0)) tile(sq0, so0, rt0, i0);
     }
     if (t + 1 >= t_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -655,7 +675,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     if (t + 2 < t_hi) issue(sq0, so0, rt0, qt0 + t + 2);
     {
       const int i0 = (qt0 + t + 1) * QL;
-      if (wave_active && !(CAUSAL && i0 + QL - 1 < wkey)) tile(sq1, so1, rt1, i0);
+      if (wave_needs(i0)) tile(sq1, so1, rt1, i0);
     }
   }
   if (it.slot >= 0) {
@@ -688,10 +708,10 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   }
 }
 
-template <int ACT, bool CAUSAL, bool BIAS>
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 hipError_t launch_dq_t(const BwdArgs& a, int grid, hipStream_t s) {
   prof_before(PROF_DQ, s);
-  hipLaunchKernelGGL((dq_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((dq_dl_kernel<ACT, CAUSAL, BIAS, WIN>), dim3(grid), dim3(NT), 0, s, a);
   prof_after(PROF_DQ, s);
   return hipGetLastError();
 }
@@ -699,14 +719,15 @@ hipError_t launch_dq_t(const BwdArgs& a, int grid, hipStream_t s) {
 template <int ACT>
 hipError_t launch_dq_cb(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
   const bool bias = p.nb > 0;
+  if (p.win > 0) return bias ? launch_dq_t<ACT, true, true, true>(a, grid, s) : launch_dq_t<ACT, true, false, true>(a, grid, s);
   if (p.causal) return bias ? launch_dq_t<ACT, true, true>(a, grid, s) : launch_dq_t<ACT, true, false>(a, grid, s);
   return bias ? launch_dq_t<ACT, false, true>(a, grid, s) : launch_dq_t<ACT, false, false>(a, grid, s);
 }
 
-template <int ACT, bool CAUSAL, bool BIAS>
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 hipError_t launch_dkdv_t(const BwdArgs& a, int grid, hipStream_t s) {
   prof_before(PROF_DKDV, s);
-  hipLaunchKernelGGL((dkdv_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((dkdv_dl_kernel<ACT, CAUSAL, BIAS, WIN>), dim3(grid), dim3(NT), 0, s, a);
   prof_after(PROF_DKDV, s);
   return hipGetLastError();
 }
@@ -714,6 +735,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a, int grid, hipStream_t s) {
 template <int ACT>
 hipError_t launch_dkdv_cb(const Prob& p, const BwdArgs& a, int grid, hipStream_t s) {
   const bool bias = p.nb > 0;
+  if (p.win > 0) return bias ? launch_dkdv_t<ACT, true, true, true>(a, grid, s) : launch_dkdv_t<ACT, true, false, true>(a, grid, s);
   if (p.causal) return bias ? launch_dkdv_t<ACT, true, true>(a, grid, s) : launch_dkdv_t<ACT, true, false>(a, grid, s);
   return bias ? launch_dkdv_t<ACT, false, true>(a, grid, s) : launch_dkdv_t<ACT, false, false>(a, grid, s);
 }

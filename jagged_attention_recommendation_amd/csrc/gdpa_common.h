@@ -154,4 +154,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Sliding window of W keys (key j is valid for query i when j > i - W; W = 0: no window).
+// First key tile (tiles of kl keys) that queries from q_lo on can reach.
+__device__ __forceinline__ int win_first_ktile(int q_lo, int win, int kl) {
+  return win > 0 ? max(0, q_lo - win + 1) / kl : 0;
+}
+// One past the last query tile (tiles of ql queries, nq of them) whose window reaches key k_hi.
+__device__ __forceinline__ int win_end_qtile(int k_hi, int win, int ql, int nq) {
+  return win > 0 ? min(nq, (k_hi + win - 1) / ql + 1) : nq;
+}
+
 }  // namespace gdpa

@@ -26,7 +26,8 @@ static_assert(BN == ROWS, "one key tile is one direct-load tile");
 constexpr int NT = 256;
 constexpr int WMAX = 3072;        // bias window (floats) staged in LDS
 
-template <int ACT, bool CAUSAL, bool BIAS>
+// WIN: causal sliding window of a.win keys (query i sees keys i - win + 1 .. i).
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sk0_[TILE];
   __shared__ __attribute__((aligned(16))) char sv0_[TILE];
@@ -57,8 +58,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
 
   int nkt = (Lk + BN - 1) / BN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, row_blk + BM) - 1) / BN + 1);
-  // key tiles of this item: all of them, or one chunk of a split tile
-  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
+  // key tiles of this item: all of them, or one chunk of a split tile, counted from the first
+  // tile the item's sliding window reaches
+  const int kt_first = WIN ? win_first_ktile(row_blk, a.win, BN) : 0;
+  const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
 
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
@@ -117,14 +120,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
       for (int s = 0; s < D / 16; ++s) sacc[kb] = mfma32(row_op(Ks, kb * 32, s, lane), qop[s], sacc[kb]);
 
     const bool need_mask = __builtin_amdgcn_readfirstlane(
-        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow))) != 0;
-    int lim[2];
+        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow) || (WIN && k0 < wrow + 32 - a.win))) != 0;
+    // register r of half kb (key offset o = 8 (r / 4) + r % 4) is valid for lo[kb] <= o < lim[kb]
+    int lim[2], lo[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int l = Lk - (k0 + kb * 32);
       if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
       lim[kb] = l - 4 * g;
+      lo[kb] = WIN ? iq - a.win + 1 - (k0 + kb * 32) - 4 * g : -64;
     }
+    auto masked = [&](int kb, int r) {
+      const int o = (r >> 2) * 8 + (r & 3);
+      return o >= lim[kb] || (WIN && o < lo[kb]);
+    };
     float p[2][16];
     if (ACT == ACT_SOFTMAX) {
       if (need_mask) {
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) sacc[kb][r] = -INFINITY;
+            if (masked(kb, r)) sacc[kb][r] = -INFINITY;
       }
       float mt = -INFINITY;
 #pragma unroll
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) p[kb][r] = 0.0f;
+            if (masked(kb, r)) p[kb][r] = 0.0f;
       }
     }
 #pragma unroll
@@ -182,6 +191,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
       }
   };
 
+  // whether this wave computes key tile kt: not wholly after its last query (causal) nor wholly
+  // before its first query's window
+  auto wave_needs = [&](int kt) {
+    return wave_active && !(CAUSAL && kt * BN > wrow + 31) && !(WIN && (kt + 1) * BN <= wrow - a.win + 1);
+  };
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage can then stay in flight while the other stage is read.
   for (int kt = kt_lo; kt < kt_hi; kt += 2) {
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
       issue_tile(sk1, K, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * BN, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && kt * BN > wrow + 31)) tile(sk0, sv0, kt * BN);
+    if (wave_needs(kt)) tile(sk0, sv0, kt * BN);
     if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
       issue_tile(sk0, K, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * BN, Lk, kv0, H, h, w, lane);
     }
-    if (wave_active && !(CAUSAL && (kt + 1) * BN > wrow + 31)) tile(sk1, sv1, (kt + 1) * BN);
+    if (wave_needs(kt + 1)) tile(sk1, sv1, (kt + 1) * BN);
   }
 
   if (it.slot >= 0) {
@@ -241,10 +255,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(orow, o[n], n, g, inv);
 }
 
-template <int ACT, bool CAUSAL, bool BIAS>
+template <int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
   prof_before(PROF_FWD, s);
-  hipLaunchKernelGGL((fwd_dl_kernel<ACT, CAUSAL, BIAS>), dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((fwd_dl_kernel<ACT, CAUSAL, BIAS, WIN>), dim3(grid), dim3(NT), 0, s, a);
   prof_after(PROF_FWD, s);
   return hipGetLastError();
 }
@@ -252,6 +266,7 @@ hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
 template <int ACT>
 hipError_t launch_cb(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
   const bool bias = p.nb > 0;
+  if (p.win > 0) return bias ? launch_t<ACT, true, true, true>(a, grid, s) : launch_t<ACT, true, false, true>(a, grid, s);
   if (p.causal) return bias ? launch_t<ACT, true, true>(a, grid, s) : launch_t<ACT, true, false>(a, grid, s);
   return bias ? launch_t<ACT, false, true>(a, grid, s) : launch_t<ACT, false, false>(a, grid, s);
 }

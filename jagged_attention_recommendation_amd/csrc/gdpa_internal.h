@@ -9,6 +9,7 @@ namespace gdpa {
 
 struct Prob {
   int B, H, D, dtype, act, causal, nb;
+  int win;  // sliding window W (0: none); only with causal bf16 D = 128
   int64_t total_q, total_kv;
   int max_q, max_kv;
   float scale;
@@ -36,6 +37,7 @@ struct SchedArgs {
   int B, H;
   int64_t total_q, total_kv;
   int mode, causal;
+  int win;                   // sliding window W (0: none)
   int tile_item, tile_loop;  // rows per item tile / rows per inner-loop tile
   int max_items;
   int list;                  // 0: first list of the header, 1: second list
@@ -67,6 +69,7 @@ struct DbiasArgs {
   float* dbias;
   const void* hdr;
   int B, H, nb, causal;
+  int win;        // sliding window W (0: none)
   int tile_rows;  // queries per dQ item
   int loop_rows;  // keys per dQ loop tile
 };
@@ -95,6 +98,7 @@ struct FwdArgs {
   float* part_o;   // split chunks: [SPLIT_SLOTS][BM][D] fp32 unnormalised output
   float* part_ml;  // split chunks (softmax): [SPLIT_SLOTS][2][BM] running max (log2 units), sum
   int H, nb;
+  int win;         // sliding window W (0: none)
   float scale;
 };
 
@@ -138,6 +142,7 @@ struct BwdArgs {
   float* part_dk;        // split chunks: [SPLIT_SLOTS][KI][D] fp32
   float* part_dv;
   int H, nb;
+  int win;               // sliding window W (0: none)
   float scale;
 };
 

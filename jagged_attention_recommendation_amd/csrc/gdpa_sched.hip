@@ -22,21 +22,32 @@ namespace gdpa {
 constexpr int NBUCKET = 1024;
 constexpr int SNT = 1024;
 
-__device__ __forceinline__ int item_cost(int mode, int causal, int Lq, int Lk, int t, int ti,
-                                         int tl) {
+// Inner tiles an item visits. Query-tile items (forward, dQ) visit key tiles
+// [first, last): all of them, or up to the causal limit, and with a sliding window of W keys
+// from the tile holding key t*ti - W + 1 (win_first_ktile); key-tile items (dK/dV) visit query
+// tiles from the causal start to the last query whose window reaches the item's last key. Item
+// ranges [lo, hi) count from the first visited tile.
+__device__ __forceinline__ int item_cost(int mode, int causal, int win, int Lq, int Lk, int t,
+                                         int ti, int tl) {
   if (mode == SCHED_QTILES) {
     if (Lk <= 0) return 0;
     int nk = (Lk + tl - 1) / tl;
-    if (!causal) return nk;
-    int i_max = min(Lq, (t + 1) * ti) - 1;
-    return min(nk, i_max / tl + 1);
+    if (causal) {
+      int i_max = min(Lq, (t + 1) * ti) - 1;
+      nk = min(nk, i_max / tl + 1);
+    }
+    return max(0, nk - win_first_ktile(t * ti, win, tl));
   }
   if (Lq <= 0) return 0;
   int nq = (Lq + tl - 1) / tl;
-  if (!causal) return nq;
-  int j0 = t * ti;
-  if (j0 >= Lq) return 0;
-  return nq - j0 / tl;
+  const int j0 = t * ti;
+  int first = 0;
+  if (causal) {
+    if (j0 >= Lq) return 0;
+    first = j0 / tl;
+  }
+  nq = win_end_qtile(min(Lk, (t + 1) * ti) - 1, win, tl, nq);
+  return max(0, nq - first);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   for_each_tile([&](int b, int t, int) {
     const int Lq = a.q_off[b + 1] - a.q_off[b];
     const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+    const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
     atomicAdd(&bucket[NBUCKET - 1 - min(c, NBUCKET - 1)], a.H);
     tot += (unsigned long long)c;
     mx = max(mx, c);
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       for_each_tile([&](int b, int t, int) {
         const int Lq = a.q_off[b + 1] - a.q_off[b];
         const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-        const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+        const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
         const int n = c > T ? (c + T - 1) / T : 1;
         for (int k = 0; k < n; ++k) {
           const int cc = n == 1 ? c : min(T, c - k * T);
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   for_each_tile([&](int b, int t, int canon) {
     const int Lq = a.q_off[b + 1] - a.q_off[b];
     const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = item_cost(a.mode, a.causal, Lq, Lk, t, ti, tl);
+    const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
     const int n = chunks(c);
     int sbase = -1;
     if (n > 1) {
@@ -271,24 +282,28 @@ hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) 
 // and wrote exactly the clamped
 // diagonals of its raw range [32rb - (k_end - 1), 32rb + 31], k_end = keys it visited; the edge
 // entries 0 and NB-1 collect every raw diagonal that clamps to them.
-// Inner tiles a dQ item of query tile t visits (all key tiles, or those up to the causal limit).
+// Inner tiles a dQ item of query tile t visits: key tiles [first, first + count) (all key tiles,
+// or those up to the causal limit, from the first one its sliding window reaches).
 template <int QI, int KL>
-__device__ __forceinline__ int qtile_cost(int t, int Lq, int Lk, int causal) {
+__device__ __forceinline__ int qtile_cost(int t, int Lq, int Lk, int causal, int win, int& first) {
+  first = win_first_ktile(t * QI, win, KL);
   if (Lk <= 0) return 0;
   int nkt = (Lk + KL - 1) / KL;
   if (causal) nkt = min(nkt, (min(Lq, (t + 1) * QI) - 1) / KL + 1);
-  return nkt;
+  return max(0, nkt - first);
 }
 
 // Raw diagonal range [d_lo, d_hi] that row block rb wrote while its item (or chunk) visited key
-// tiles [lo, hi): the wave stops after its causal limit; false if it visited none.
+// tiles [lo, hi): the wave starts at the first tile its window reaches and stops after its
+// causal limit; false if it visited none.
 template <int KL>
-__device__ __forceinline__ bool chunk_range(int rb, int Lq, int causal, int lo, int hi, int& d_lo,
-                                            int& d_hi) {
+__device__ __forceinline__ bool chunk_range(int rb, int Lq, int causal, int win, int lo, int hi,
+                                            int& d_lo, int& d_hi) {
   const int wrow = rb * 32;
   if (wrow >= Lq) return false;
   int last = hi - 1;
   if (causal) last = min(last, (wrow + 31) / KL);  // tiles after the block's last query skipped
+  lo = max(lo, win_first_ktile(wrow, win, KL));    // tiles before its window skipped
   if (lo > last) return false;
   d_lo = wrow - (last + 1) * KL + 1;
   d_hi = wrow + 31 - lo * KL;
@@ -339,9 +354,10 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
           const int rb = min(rb0 + u, nrb - 1);
-          const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal);
+          int kf;
+          const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal, a.win, kf);
           int d_lo = 1, d_hi = 0;
-          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi);
+          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, a.win, kf, kf + nkt, d_lo, d_hi);
           const bool keep = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1);
           acc += __int_as_float(xi[u] & (keep ? -1 : 0));
         }
@@ -352,10 +368,11 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
       for (int u = 0; u < BATCH; ++u) {
         const int rb = min(rb0 + u, nrb - 1);
         const int t = rb / PER;
-        const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal);
+        int kf;
+        const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal, a.win, kf);
         const int sb = a.split_slot[(int64_t)(tb + t) * a.H + h];
         int d_lo = 1, d_hi = 0;
-        const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, 0, nkt, d_lo, d_hi);
+        const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, a.win, kf, kf + nkt, d_lo, d_hi);
         const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
         const float x = a.part[(row * a.H + h) * nb + c];
         v[u] = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1) ? x : 0.0f;
@@ -365,7 +382,7 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
           const int n = (nkt + T - 1) / T;
           float sv = 0.0f;
           for (int k = 0; k < n; ++k) {
-            if (chunk_range<KL>(rb, Lq, a.causal, k * T, min(nkt, (k + 1) * T), d_lo, d_hi) &&
+            if (chunk_range<KL>(rb, Lq, a.causal, a.win, kf + k * T, kf + min(nkt, (k + 1) * T), d_lo, d_hi) &&
                 c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1))
               sv += a.part_x[((int64_t)(sb + k) * PER + rb % PER) * nb + c];
           }

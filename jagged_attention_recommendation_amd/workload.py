@@ -11,21 +11,34 @@ from __future__ import annotations
 import numpy as np
 
 
-def pairs_per_sample(lq, lk, causal):
-    """Unmasked (i, j) pairs per sample. Causal keeps j <= i on local positions."""
+def pairs_per_sample(lq, lk, causal, window=0):
+    """Unmasked (i, j) pairs per sample. Causal keeps j <= i on local positions; a sliding window
+    W >= 1 (with causal) also drops keys j <= i - W."""
     lq = np.asarray(lq, dtype=np.int64)
     lk = np.asarray(lk, dtype=np.int64)
     if not causal:
         return lq * lk
-    # sum_{i < Lq} min(i + 1, Lk)
     m = np.minimum(lq, lk)
-    full = m * (m + 1) // 2                 # rows i < m see i + 1 keys
-    rest = np.maximum(lq - lk, 0) * lk      # rows i >= Lk see all Lk keys
-    return full + rest
+    if window <= 0:
+        # sum_{i < Lq} min(i + 1, Lk)
+        full = m * (m + 1) // 2                 # rows i < m see i + 1 keys
+        rest = np.maximum(lq - lk, 0) * lk      # rows i >= Lk see all Lk keys
+        return full + rest
+    W = int(window)
+    # rows i < m see min(i + 1, W) keys
+    head = np.where(m <= W, m * (m + 1) // 2, W * (W + 1) // 2 + (m - W) * W)
+    # rows i = Lk + t (t < Lq - Lk) see keys max(0, i - W + 1) .. Lk - 1: min(Lk, max(0, W - 1 - t))
+    # of them, i.e. g(W - 1) - g(W - 1 - Lk) with g(a) = sum_t max(0, a - t)
+    n = np.maximum(lq - lk, 0)
+
+    def g(a):
+        a = np.maximum(a, 0)
+        return np.where(n >= a, a * (a + 1) // 2, n * a - n * (n - 1) // 2)
+    return head + g(W - 1 + 0 * lk) - g(W - 1 - lk)
 
 
-def useful_flops(p, direction="fwd"):
-    pairs = int(pairs_per_sample(p.lq, p.lk, p.causal).sum())
+def useful_flops(p, direction="fwd", window=0):
+    pairs = int(pairs_per_sample(p.lq, p.lk, p.causal, window).sum())
     per = {"fwd": 4, "bwd": 10, "fwdbwd": 14}[direction]
     return float(per) * p.D * p.H * pairs
 

@@ -24,14 +24,15 @@ def test_library_exports_every_symbol():
     lib = gdpa.load()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.gdpa_abi_version() == 1
+    assert lib.gdpa_abi_version() == 2
     assert lib.gdpa_status_string(0) == b"ok"
 
 
 def test_problem_struct_layout():
-    assert ctypes.sizeof(gdpa.GdpaProblem) == 56
+    assert ctypes.sizeof(gdpa.GdpaProblem) == 64
     assert gdpa.GdpaProblem.total_q.offset == 16
     assert gdpa.GdpaProblem.scale.offset == 48
+    assert gdpa.GdpaProblem.window.offset == 56
 
 
 def test_workspace_size_validation():
@@ -48,6 +49,21 @@ def test_workspace_size_validation():
     with pytest.raises(gdpa.GdpaError) as e:
         gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100, dtype="mxfp8"), True)
     assert e.value.status == 2  # MX backward not provided
+
+
+def test_window_validation():
+    """A sliding window needs causal bf16 D = 128; a negative window is an argument error."""
+    ok = gdpa.problem(4, 2, 128, 100, 100, causal=True, window=33)
+    assert gdpa.workspace_size(ok) >= 256 and gdpa.workspace_size(ok, True) >= 256
+    for kw, status in [(dict(D=128, causal=True, window=-1), 1),
+                       (dict(D=128, causal=False, window=8), 2),
+                       (dict(D=64, causal=True, window=8), 2),
+                       (dict(D=128, causal=True, window=8, dtype="f32"), 2),
+                       (dict(D=128, causal=True, window=8, dtype="mxfp8"), 2)]:
+        D = kw.pop("D")
+        with pytest.raises(gdpa.GdpaError) as e:
+            gdpa.workspace_size(gdpa.problem(4, 2, D, 100, 100, **kw))
+        assert e.value.status == status, kw
 
 
 def test_fwd_rejects_host_checkable_errors_without_launching():

@@ -1,0 +1,123 @@
+"""Sliding-window attention (causal; query i sees keys i - W + 1 .. i) on the bf16 D = 128 path.
+
+The window is the attention variant of page "GEM Training: How Meta Doubled the Efficiency of Its
+LLM-Scale Ads Foundation Model" (sliding-window attention paragraph). The fp64 oracle applies it
+as one more term of the validity mask; the GPU path also skips the tiles wholly outside the
+window (scheduler costs, per-wave tile ranges, the bias-gradient reduction's diagonal ranges), so
+these tests compare every output and gradient with the oracle on ragged batches, at window sizes
+around the tile edges (32 / 64 / 128), below and above the sample lengths, with and without a
+bias table, and on split tiles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from jagged_attention_recommendation_amd import inputs
+from parity_util import assert_close, assert_lse_close, host_f64, to_device
+from test_gpu_bwd import assert_dbias_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from jagged_attention_recommendation_amd import gdpa
+    gdpa.load()
+
+
+def oracle_args(p):
+    return (p.q_off, p.kv_off, host_f64(p, "Q"), host_f64(p, "K"), host_f64(p, "V"))
+
+
+def run(p, W):
+    from jagged_attention_recommendation_amd import gdpa
+    d = to_device(p)
+    nb = 0 if p.bias is None else p.bias.shape[1]
+    prob = gdpa.problem(p.B, p.H, p.D, int(p.q_off[-1]), int(p.kv_off[-1]), act=p.act,
+                        causal=True, scale=p.scale, bias_buckets=nb, window=W)
+    wf = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    kw = dict(act=p.act, causal=True, scale=p.scale, bias=d["bias"], window=W)
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, **kw)
+    hf = gdpa.workspace_header(wf)
+    grads = gdpa.bwd(d["Q"], d["K"], d["V"], O, d["dO"], lse, d["q_off"], d["kv_off"],
+                     workspace=wb, **kw)
+    hb = gdpa.workspace_header(wb)
+    torch.cuda.synchronize()
+    return O, lse, grads, hf, hb
+
+
+def check(p, W, nthreads=None):
+    O, lse, (dq, dk, dv, dbias), hf, hb = run(p, W)
+    assert hf["error"] == 0 and hb["error"] == 0
+    bias = None if p.bias is None else p.bias.astype(np.float64)
+    Or, lser = oracle.fwd(*oracle_args(p), act=p.act, causal=True, scale=p.scale, bias=bias,
+                          nthreads=nthreads, window=W)
+    tag = f"{p.name} W={W}"
+    assert_close(O, Or, p.q_off, "bf16", f"{tag} O")
+    if p.act == "softmax":
+        assert_lse_close(lse, lser, f"{tag} lse")
+    g = oracle.bwd(*oracle_args(p), host_f64(p, "dO"), act=p.act, causal=True, scale=p.scale,
+                   bias=bias, nthreads=nthreads, error_scale=True, window=W)
+    assert_close(dq, g["dQ"], p.q_off, "bf16", f"{tag} dQ")
+    assert_close(dk, g["dK"], p.kv_off, "bf16", f"{tag} dK")
+    assert_close(dv, g["dV"], p.kv_off, "bf16", f"{tag} dV")
+    if p.bias is not None:
+        assert_dbias_close(dbias, g["dbias"], f"{tag} dbias", g["dbias_scale"])
+    return hf, hb
+
+
+def ragged(seed, act, nb, B=5, H=2, hi=300):
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(1, hi + 1, size=B)
+    return inputs.make_problem(f"win-{seed}", seed=seed, H=H, D=128, lq=lq, lk=lq, dtype="bf16",
+                               act=act, causal=True, bias_buckets=nb)
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
+@pytest.mark.parametrize("nb", [0, 48])
+@pytest.mark.parametrize("W", [1, 31, 32, 33, 64, 100, 129, 400])
+def test_window_ragged(act, nb, W):
+    check(ragged(300 + W, act, nb), W)
+
+
+def test_window_edge_lengths():
+    """Lengths at the tile edges, an empty query block, and windows at the tile edges."""
+    lq = np.array([1, 63, 64, 65, 127, 128, 129, 0, 200])
+    for W in (63, 64, 65, 128):
+        p = inputs.make_problem("win-edges", seed=7, H=2, D=128, lq=lq, lk=lq, dtype="bf16",
+                                act="softmax", causal=True, bias_buckets=64)
+        check(p, W)
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+def test_window_split_tiles(act):
+    """One long sample among short ones: its tiles cost more than the split threshold, so they
+    are cut into chunks (forward, dQ and dK/dV), each starting inside the window."""
+    lq = np.array([2100, 40, 70, 9])
+    p = inputs.make_problem("win-split", seed=11, H=1, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act=act, causal=True, bias_buckets=96)
+    hf, hb = check(p, 900)
+    assert hf["split"] > 0 and hb["split"] > 0 and hb["split2"] > 0, (hf, hb)
+
+
+def test_window_wider_than_every_sample_is_causal():
+    """W >= every length: the same results as plain causal attention, to the oracle's tolerance,
+    and the windowed oracle equals the causal oracle exactly."""
+    p = ragged(77, "softmax", 32, hi=200)
+    check(p, 4096)
+    a = oracle.fwd(*oracle_args(p), act="softmax", causal=True, scale=p.scale,
+                   bias=p.bias.astype(np.float64), window=4096)
+    b = oracle.fwd(*oracle_args(p), act="softmax", causal=True, scale=p.scale,
+                   bias=p.bias.astype(np.float64))
+    assert np.array_equal(a[0], b[0])
+
+
+def test_window_workload_shape():
+    """The causal JFA workload's sample-length mix (lengths uniform in [1, 2048], a 4096-entry
+    bias table) on 8 samples with a 512-key window, checked on every sample and head."""
+    p = inputs.config_problem(2, B=8)
+    check(p, 512)

@@ -618,6 +618,10 @@ def test_pair_counter_brute_force():
         ref = [sum(1 for i in range(a) for j in range(b) if (not causal or j <= i))
                for a, b in zip(lq, lk)]
         assert list(got) == ref
+    for W in (1, 2, 5, 17, 39, 100):
+        got = workload.pairs_per_sample(lq, lk, True, W)
+        ref = [sum(1 for i in range(a) for j in range(b) if i - W < j <= i) for a, b in zip(lq, lk)]
+        assert list(got) == ref, W
 
 
 def test_config_generators_shapes():
