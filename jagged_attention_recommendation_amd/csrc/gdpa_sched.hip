@@ -316,8 +316,9 @@ __device__ __forceinline__ bool chunk_range(int rb, int Lq, int causal, int win,
 // the result bits, are those of the plain loop over rb.
 // The tile sizes are template parameters so that the per-row-block range arithmetic divides by
 // constants.
-template <int QI, int KL>
+template <int QI, int KL, bool WIN>
 __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
+  const int win = WIN ? a.win : 0;  // a compile-time zero without a window
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int c = blockIdx.y * 256 + threadIdx.x;
   if (c >= a.nb) return;
@@ -355,9 +356,9 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
         for (int u = 0; u < BATCH; ++u) {
           const int rb = min(rb0 + u, nrb - 1);
           int kf;
-          const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal, a.win, kf);
+          const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal, win, kf);
           int d_lo = 1, d_hi = 0;
-          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, a.win, kf, kf + nkt, d_lo, d_hi);
+          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, win, kf, kf + nkt, d_lo, d_hi);
           const bool keep = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1);
           acc += __int_as_float(xi[u] & (keep ? -1 : 0));
         }
@@ -369,10 +370,10 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
         const int rb = min(rb0 + u, nrb - 1);
         const int t = rb / PER;
         int kf;
-        const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal, a.win, kf);
+        const int nkt = qtile_cost<QI, KL>(t, Lq, Lk, a.causal, win, kf);
         const int sb = a.split_slot[(int64_t)(tb + t) * a.H + h];
         int d_lo = 1, d_hi = 0;
-        const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, a.win, kf, kf + nkt, d_lo, d_hi);
+        const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, win, kf, kf + nkt, d_lo, d_hi);
         const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
         const float x = a.part[(row * a.H + h) * nb + c];
         v[u] = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1) ? x : 0.0f;
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
           const int n = (nkt + T - 1) / T;
           float sv = 0.0f;
           for (int k = 0; k < n; ++k) {
-            if (chunk_range<KL>(rb, Lq, a.causal, a.win, kf + k * T, kf + min(nkt, (k + 1) * T), d_lo, d_hi) &&
+            if (chunk_range<KL>(rb, Lq, a.causal, win, kf + k * T, kf + min(nkt, (k + 1) * T), d_lo, d_hi) &&
                 c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1))
               sv += a.part_x[((int64_t)(sb + k) * PER + rb % PER) * nb + c];
           }
@@ -419,9 +420,10 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
   if (a.B > 0) {
     const dim3 grid(a.B * a.H, (a.nb + 255) / 256);
     if (a.tile_rows == 128 && a.loop_rows == 64) {
-      hipLaunchKernelGGL((dbias_stage_a<128, 64>), grid, dim3(256), 0, s, a);
+      if (a.win > 0) hipLaunchKernelGGL((dbias_stage_a<128, 64, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((dbias_stage_a<128, 64, false>), grid, dim3(256), 0, s, a);
     } else if (a.tile_rows == 64 && a.loop_rows == 64) {
-      hipLaunchKernelGGL((dbias_stage_a<64, 64>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((dbias_stage_a<64, 64, false>), grid, dim3(256), 0, s, a);
     } else {
       return hipErrorInvalidValue;
     }
