@@ -59,19 +59,22 @@ struct FwdLayout {
   size_t header, items, split_cnt, part_o, part_ml, total;
   int64_t max_items;
   bool split;
+  int slots;  // chunk slots (0 without splitting)
 };
 
 FwdLayout fwd_layout(const gdpa_problem* p) {
   FwdLayout L;
-  L.split = split_supported(to_prob(p));
-  L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype), L.split);
+  const Prob pr = to_prob(p);
+  L.split = split_fwd(pr);
+  L.slots = L.split ? split_slots(pr) : 0;
+  L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype), L.slots);
   L.header = 0;
   L.items = ALIGN;
   L.split_cnt = L.items + align_up((size_t)L.max_items * sizeof(Item));
   L.part_o = L.part_ml = L.total = L.split_cnt;
   if (L.split) {
-    const size_t rows = (size_t)SPLIT_SLOTS * fwd_tile_rows(p->dtype);
-    L.part_o = L.split_cnt + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
+    const size_t rows = (size_t)L.slots * fwd_tile_rows(p->dtype);
+    L.part_o = L.split_cnt + align_up((size_t)L.slots * sizeof(int32_t));
     L.part_ml = L.part_o + align_up(rows * p->D * sizeof(float));
     L.total = L.part_ml + align_up(rows * 2 * sizeof(float));
   }
@@ -82,15 +85,20 @@ struct BwdLayout {
   size_t header, items_q, items_k, dvec, tile_base, part, part_bh, split_cnt_q, split_cnt_k,
       split_slot, part_dq, part_dk, part_dv, part_x, total;
   int64_t max_q_items, max_k_items, max_qtiles;
-  bool split;
+  bool split, split_q, split_k;  // split storage present / per list
+  int slots;                     // chunk slots of each list (0 without splitting)
 };
 
 BwdLayout bwd_layout(const gdpa_problem* p) {
   BwdLayout L;
-  L.split = split_supported(to_prob(p));
+  const Prob pr = to_prob(p);
+  L.split_q = split_dq(pr);
+  L.split_k = split_dkdv(pr);
+  L.split = L.split_q || L.split_k;
+  L.slots = L.split ? split_slots(pr) : 0;
   const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
-  L.max_q_items = items_bound(p->total_q, p->B, p->H, tq, L.split);
-  L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk, L.split);
+  L.max_q_items = items_bound(p->total_q, p->B, p->H, tq, L.split_q ? L.slots : 0);
+  L.max_k_items = items_bound(p->total_kv, p->B, p->H, tk, L.split_k ? L.slots : 0);
   L.max_qtiles = (p->total_q + tq - 1) / tq + p->B;
   L.header = 0;
   L.items_q = ALIGN;
@@ -110,14 +118,16 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   if (L.split) {
     // chunk counters of both lists, the per-(tile, head) slot table, the chunks' partial rows
     L.split_cnt_q = end;
-    L.split_cnt_k = L.split_cnt_q + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
-    L.split_slot = L.split_cnt_k + align_up((size_t)SPLIT_SLOTS * sizeof(int32_t));
+    L.split_cnt_k = L.split_cnt_q + align_up((size_t)L.slots * sizeof(int32_t));
+    L.split_slot = L.split_cnt_k + align_up((size_t)L.slots * sizeof(int32_t));
     L.part_dq = L.split_slot + align_up((size_t)L.max_qtiles * p->H * sizeof(int32_t));
-    L.part_dk = L.part_dq + align_up((size_t)SPLIT_SLOTS * tq * p->D * sizeof(float));
-    L.part_dv = L.part_dk + align_up((size_t)SPLIT_SLOTS * tk * p->D * sizeof(float));
-    L.part_x = L.part_dv + align_up((size_t)SPLIT_SLOTS * tk * p->D * sizeof(float));
+    // partial rows only for the lists that split
+    const size_t nq = L.split_q ? L.slots : 0, nk = L.split_k ? L.slots : 0;
+    L.part_dk = L.part_dq + align_up(nq * tq * p->D * sizeof(float));
+    L.part_dv = L.part_dk + align_up(nk * tk * p->D * sizeof(float));
+    L.part_x = L.part_dv + align_up(nk * tk * p->D * sizeof(float));
     end = L.part_x;
-    if (p->bias_buckets > 0) end += align_up((size_t)SPLIT_SLOTS * (tq / 32) * p->bias_buckets * sizeof(float));
+    if (p->bias_buckets > 0) end += align_up(nq * (tq / 32) * p->bias_buckets * sizeof(float));
   }
   L.total = end;
   return L;
@@ -232,20 +242,21 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   if (((uintptr_t)lse & 3u) || ((uintptr_t)bias & 3u) || ((uintptr_t)q_offsets & 3u) ||
       ((uintptr_t)kv_offsets & 3u))
     return GDPA_EINVAL;
+  const Prob pr = to_prob(p);
   const FwdLayout L = fwd_layout(p);
   if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
   if (L.max_items > INT32_MAX) return GDPA_ENOTSUP;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const Prob pr = to_prob(p);
 
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
   sa.causal = p->causal; sa.win = p->window; sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
-  sa.split = L.split ? 1 : 0; sa.tile_base = nullptr; sa.split_slot = nullptr;
+  sa.split = L.split ? 1 : 0; sa.nslot = split_nslot(pr);
+  sa.tile_base = nullptr; sa.split_slot = nullptr;
   sa.ws_header = ws + L.header; sa.items = ws + L.items;
   sa.split_cnt = (int32_t*)(ws + L.split_cnt);
   hipError_t e = launch_sched(sa, s);
@@ -299,13 +310,15 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
   sa.win = p->window; sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
-  sa.split = L.split ? 1 : 0;
+  sa.nslot = split_nslot(pr);
   SchedArgs sq = sa, sk = sa;
+  sq.split = L.split_q ? 1 : 0;
+  sk.split = L.split_k ? 1 : 0;
   sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
   sq.max_items = (int)L.max_q_items; sq.list = 0;
   sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
   sq.split_cnt = (int32_t*)(ws + L.split_cnt_q);
-  sq.split_slot = L.split && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
+  sq.split_slot = L.split_q && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
   sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
   sk.max_items = (int)L.max_k_items; sk.list = 1;
   sk.tile_base = nullptr; sk.items = ws + L.items_k;

@@ -25,6 +25,7 @@
 #include "gdpa_bwd_dl.h"
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
+#include "gdpa_split.h"
 #include "gdpa_tiles.h"
 
 namespace gdpa {
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   GDPA_LDS char* Vs = Ks + T::BYTES;
   GDPA_LDS float* bwin = (GDPA_LDS float*)(Vs + T::BYTES);
   GDPA_LDS float* dsbuf_all = bwin + BIAS_WMAX;  // [wave][32][DSP]
+  __shared__ int flag_;
 
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
@@ -110,7 +112,8 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
     Di = half_sum(part_d);
     if (qv) {
       lse2 = a.lse[row] * LOG2E;
-      if (g == 0) a.Dvec[row] = Di;
+      // every chunk of a split tile computes it; the first writes it
+      if (g == 0 && split::chunk_index(it.chunk) == 0) a.Dvec[row] = Di;
     }
   }
 
@@ -121,6 +124,9 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   int nkt = (Lk + KL - 1) / KL;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
   if (i0 >= Lq) nkt = 0;
+  // key tiles of this item: all of them, or one chunk of a split tile (splitting is used only
+  // without a bias table, whose partial rows assume whole tiles)
+  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
 
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
@@ -156,21 +162,21 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   int k0_last = -1;
 
   TileLoader<D, NT> lk_, lv_;
-  if (nkt > 0) {
-    lk_.load((const __bf16*)a.K, 0, Lk, kv0, H, h, tid);
-    lv_.load((const __bf16*)a.V, 0, Lk, kv0, H, h, tid);
+  if (kt_lo < kt_hi) {
+    lk_.load((const __bf16*)a.K, kt_lo * KL, Lk, kv0, H, h, tid);
+    lv_.load((const __bf16*)a.V, kt_lo * KL, Lk, kv0, H, h, tid);
   }
   if (BIAS && nkt > 0) {  // staged while the first tile's loads are in flight
     w_hi = i0 + QI - 1;  // raw diagonals iq - j: iq in [i0, i0 + QI), j in [0, nkt * KL)
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
                  bwin, bias_h, nb, i0 - (nkt * KL - 1), w_hi, true, bmul, tid, NT)) != 0;
   }
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
     __syncthreads();
     lk_.store(Ks, tid);
     lv_.store(Vs, tid);
     __syncthreads();
-    if (kt + 1 < nkt) {
+    if (kt + 1 < kt_hi) {
       lk_.load((const __bf16*)a.K, (kt + 1) * KL, Lk, kv0, H, h, tid);
       lv_.load((const __bf16*)a.V, (kt + 1) * KL, Lk, kv0, H, h, tid);
     }
@@ -299,6 +305,23 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
         if (has_hi) part[nb - 1] = e_hi;
       }
     }
+  }
+  if (!BIAS && it.slot >= 0) {
+    // chunk of a split tile: fp32 partial rows; the workgroup that completes the tile combines
+    // its chunks in order
+    if (wave_active) {
+      float* pq = a.part_dq + ((int64_t)it.slot * QI + w * 32 + l32) * D;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(pq + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{dq[n][4 * r4], dq[n][4 * r4 + 1], dq[n][4 * r4 + 2], dq[n][4 * r4 + 3]};
+    }
+    const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
+    if (split::chunk_done(a.split_cnt_q + first, n, (GDPA_LDS int*)&flag_))
+      split::combine_dq_tile<D>(a, b, it.tile, h, n, first);
+    return;
   }
   if (!qv) return;
   __bf16* dqrow = (__bf16*)a.dQ + row * D;

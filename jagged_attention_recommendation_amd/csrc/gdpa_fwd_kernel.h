@@ -32,6 +32,7 @@
 
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
+#include "gdpa_split.h"
 #include "gdpa_tiles.h"
 
 namespace gdpa {
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   GDPA_LDS char* Ks = (GDPA_LDS char*)smem;
   GDPA_LDS char* Vs = Ks + S::K_BYTES;
   GDPA_LDS float* bwin = (GDPA_LDS float*)(Vs + S::V_BYTES);
+  __shared__ int flag_;
 
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
@@ -93,6 +95,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int i_max = min(Lq, row_blk + BM) - 1;
     nkt = min(nkt, i_max / BN + 1);
   }
+  // key tiles of this item: all of them, or one chunk of a split tile (bf16 only)
+  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
 
   // ---- Q^T operand: lane holds query iq
   bf16x8 qop[MX ? 1 : D / 16];
@@ -184,18 +188,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (nkt > 0) load_tile(0);
-  if (BIAS && nkt > 0) {  // staged while the first tile's loads are in flight
-    // raw diagonals iq - j of the item: iq in [row_blk, row_blk + BM), j in [0, nkt * BN)
-    w_hi = row_blk + BM - 1;
+  if (kt_lo < kt_hi) load_tile(kt_lo);
+  if (BIAS && kt_lo < kt_hi) {  // staged while the first tile's loads are in flight
+    // raw diagonals iq - j of the item: iq in [row_blk, row_blk + BM), j in its key tiles
+    w_hi = row_blk + BM - 1 - kt_lo * BN;
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
-                 bwin, bias_h, a.nb, row_blk - (nkt * BN - 1), w_hi, true, inv_scale, tid, NT)) != 0;
+                 bwin, bias_h, a.nb, row_blk - (kt_hi * BN - 1), w_hi, true, inv_scale, tid, NT)) != 0;
   }
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = kt_lo; kt < kt_hi; ++kt) {
     __syncthreads();
     store_tile();
     __syncthreads();
-    if (kt + 1 < nkt) load_tile(kt + 1);
+    if (kt + 1 < kt_hi) load_tile(kt + 1);
     const int k0 = kt * BN;
     if (!wave_active) continue;
     if (CAUSAL && k0 > wrow + 31) continue;  // every key of the tile is after every query
@@ -322,6 +326,31 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
+  if (!MX && it.slot >= 0) {
+    // chunk of a split tile: unnormalised output rows and, for softmax, the running max (log2
+    // units) and sum; the workgroup that completes the tile combines its chunks in order
+    if (wave_active) {
+      float* po = a.part_o + ((int64_t)it.slot * BM + w * 32 + l32) * D;
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(po + n * 32 + r4 * 8 + 4 * g) =
+              f32x4{o[n][4 * r4], o[n][4 * r4 + 1], o[n][4 * r4 + 2], o[n][4 * r4 + 3]};
+      if (ACT == ACT_SOFTMAX) {
+        const float lt = half_sum(l_run);
+        if (g == 0) {
+          float* pml = a.part_ml + (int64_t)it.slot * 2 * BM;
+          pml[w * 32 + l32] = m_run;
+          pml[BM + w * 32 + l32] = lt;
+        }
+      }
+    }
+    const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
+    if (split::chunk_done(a.split_cnt + first, n, (GDPA_LDS int*)&flag_))
+      split::combine_fwd_tile<ACT == ACT_SOFTMAX, D>(a, b, it.tile, h, n, first);
+    return;
+  }
   if (!wave_active) return;
   // ---- epilogue: lane owns query iq; register r of block n is d = n*32 + (r/4)*8 + 4g + r%4
   float inv = 1.0f;

@@ -21,14 +21,14 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_MX = 2 };
 enum { SCHED_QTILES = 0, SCHED_KTILES = 1 };
 
 // Long tiles are split into chunks of inner tiles when splitting is on: the chunk length is
-// T = max(SPLIT_MIN_TILES, ceil(total cost / SPLIT_NSLOT)), the mean load of SPLIT_NSLOT
-// concurrent workgroups, and a tile of cost c > T becomes ceil(c / T) chunks. Split tiles each
-// cost more than T, so there are at most total / T <= SPLIT_NSLOT of them and at most
-// 2 * SPLIT_NSLOT chunks among them: the partial-result storage has a fixed size. A tile's cost
-// is at most the total, so it has at most SPLIT_NSLOT chunks (Item::chunk keeps the count in 16
-// bits).
+// T = max(SPLIT_MIN_TILES, ceil(total cost / nslot)), the mean load of nslot concurrent
+// workgroups, and a tile of cost c > T becomes ceil(c / T) chunks. Split tiles each cost more
+// than T, so there are at most total / T <= nslot of them and at most 2 * nslot chunks among
+// them: the partial-result storage has a fixed size. A tile's cost is at most the total, so it
+// has at most nslot chunks (Item::chunk keeps the count in 16 bits). nslot is SPLIT_NSLOT for
+// the D = 128 kernels (two workgroups per compute unit) and twice that for D = 32 / 64, whose
+// smaller tiles leave room for more workgroups per compute unit.
 constexpr int SPLIT_NSLOT = 256;
-constexpr int SPLIT_SLOTS = 2 * SPLIT_NSLOT;
 constexpr int SPLIT_MIN_TILES = 8;
 
 struct SchedArgs {
@@ -42,9 +42,10 @@ struct SchedArgs {
   int max_items;
   int list;                  // 0: first list of the header, 1: second list
   int split;                 // 1: split long tiles into chunks
+  int nslot;                 // concurrent workgroups the chunk length aims at (see above)
   int32_t* tile_base;        // optional [B + 1]: canonical index of each sample's first tile
   int32_t* split_slot;       // optional [canonical tiles * H]: first slot of a split tile, or -1
-  int32_t* split_cnt;        // [SPLIT_SLOTS] chunk counters, indexed by a split tile's first slot
+  int32_t* split_cnt;        // [2 * nslot] chunk counters, indexed by a split tile's first slot
   void* ws_header;
   void* items;
 };
@@ -75,9 +76,10 @@ struct DbiasArgs {
 };
 hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s);
 
-// Upper bound on the number of items the scheduler can emit.
-inline int64_t items_bound(int64_t total_rows, int B, int H, int tile, bool split) {
-  return (int64_t)H * ((total_rows + tile - 1) / tile + (int64_t)B) + (split ? SPLIT_SLOTS : 0);
+// Upper bound on the number of items the scheduler can emit (slots: chunk slots of the list when
+// it splits, else 0).
+inline int64_t items_bound(int64_t total_rows, int B, int H, int tile, int slots) {
+  return (int64_t)H * ((total_rows + tile - 1) / tile + (int64_t)B) + slots;
 }
 
 struct FwdArgs {
@@ -95,8 +97,8 @@ struct FwdArgs {
   const void* hdr;
   const void* items;
   int32_t* split_cnt;  // chunk counters of split tiles
-  float* part_o;   // split chunks: [SPLIT_SLOTS][BM][D] fp32 unnormalised output
-  float* part_ml;  // split chunks (softmax): [SPLIT_SLOTS][2][BM] running max (log2 units), sum
+  float* part_o;   // split chunks: [2 * nslot][BM][D] fp32 unnormalised output
+  float* part_ml;  // split chunks (softmax): [2 * nslot][2][BM] running max (log2 units), sum
   int H, nb;
   int win;         // sliding window W (0: none)
   float scale;
@@ -134,12 +136,12 @@ struct BwdArgs {
   const void* items_q;   // query-tile items (dQ)
   const void* items_k;   // key-tile items (dK/dV)
   float* dbias_part;     // [n_rowblocks, H, NB] per 32-query row block diagonal sums of dS
-  float* dbias_part_x;   // split chunks: [SPLIT_SLOTS * QI / 32, NB]
+  float* dbias_part_x;   // split chunks: [2 * nslot * QI / 32, NB]
   int32_t* split_cnt_q;  // chunk counters of split query tiles
   int32_t* split_cnt_k;  // chunk counters of split key tiles
   const int32_t* tile_base;  // [B + 1] canonical index of each sample's first query tile
-  float* part_dq;        // split chunks: [SPLIT_SLOTS][QI][D] fp32
-  float* part_dk;        // split chunks: [SPLIT_SLOTS][KI][D] fp32
+  float* part_dq;        // split chunks: [2 * nslot][QI][D] fp32
+  float* part_dk;        // split chunks: [2 * nslot][KI][D] fp32
   float* part_dv;
   int H, nb;
   int win;               // sliding window W (0: none)
@@ -153,9 +155,14 @@ constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
-// Whether the kernels for this problem take split items (D = 128 bf16 path; the last chunk of a
-// split tile combines the tile, see gdpa_split.h).
-inline bool split_supported(const Prob& p) { return p.dtype == DT_BF16 && p.D == 128; }
+// Which lists of this problem take split items (the last chunk of a split tile combines the
+// tile, see gdpa_split.h): forward and dQ on every bf16 kernel (the D = 32 / 64 dQ kernel only
+// without a bias table), dK/dV on the D = 128 kernel.
+inline bool split_fwd(const Prob& p) { return p.dtype == DT_BF16; }
+inline bool split_dq(const Prob& p) { return p.dtype == DT_BF16 && (p.D == 128 || p.nb == 0); }
+inline bool split_dkdv(const Prob& p) { return p.dtype == DT_BF16 && p.D == 128; }
+inline int split_nslot(const Prob& p) { return p.D == 128 ? SPLIT_NSLOT : 2 * SPLIT_NSLOT; }
+inline int split_slots(const Prob& p) { return 2 * split_nslot(p); }
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
 // Profiling hook: brackets launches of one kernel with HIP events (see gdpa_profile_start).

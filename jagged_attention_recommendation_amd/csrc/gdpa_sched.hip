@@ -174,7 +174,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       biggest = max(biggest, wmax[w]);
     }
     total *= (unsigned long long)a.H;
-    const unsigned long long tpc = (total + SPLIT_NSLOT - 1) / SPLIT_NSLOT;
+    const unsigned long long tpc = (total + a.nslot - 1) / a.nslot;
     const int t_mean = (int)min(max(tpc, (unsigned long long)SPLIT_MIN_TILES), (unsigned long long)0x7fffffff);
     if (biggest > t_mean) {
       T = t_mean;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     if (n > 1) {
       sbase = atomicAdd(&slot_count, n * a.H);
       atomicAdd(&split_count, a.H);
-      if (sbase + n * a.H > SPLIT_SLOTS) {
+      if (sbase + n * a.H > 2 * a.nslot) {
         atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
         sbase = -1;
       } else {

@@ -1,4 +1,4 @@
-// Fixed-order combines of split tiles (D = 128 bf16 path).
+// Fixed-order combines of split tiles (bf16 paths).
 //
 // When a few long tiles would leave most compute units idle, the scheduler splits each of them
 // into chunks of inner tiles (page "GEM Training: How Meta Doubled the Efficiency of Its
@@ -12,7 +12,7 @@
 //     lse = (m + log2 l) ln 2  (the online-softmax rescaling, applied across chunks);
 //   GDPA forward: O = sum_c O_c;
 //   dQ = scale * sum_c dQ_c;  dK = scale * sum_c dK_c;  dV = sum_c dV_c.
-// Thread pair (2r, 2r + 1) of the 256-thread workgroup owns tile row r, 64 columns each.
+// Thread pair (2r, 2r + 1) of the 256-thread workgroup owns tile row r, D / 2 columns each.
 #pragma once
 
 #include <math.h>
@@ -23,7 +23,6 @@
 namespace gdpa {
 namespace split {
 
-constexpr int D = 128;
 constexpr int ROWS = 128;  // rows per tile in every split list
 static_assert(FWD_BM_BF16 == ROWS && BWD_Q_ITEM == ROWS && BWD_K_ITEM == ROWS, "tile rows");
 
@@ -43,20 +42,22 @@ __device__ __forceinline__ bool chunk_done(int* counter, int n, GDPA_LDS int* fl
   return last;
 }
 
-// acc[0..63] += w * src[0..63] (16-byte loads)
-__device__ __forceinline__ void axpy64(float* acc, float w, const float* src) {
+// acc[0..N) += w * src[0..N) (16-byte loads)
+template <int N>
+__device__ __forceinline__ void axpy(float* acc, float w, const float* src) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < N / 4; ++j) {
     const f32x4 v = *(const f32x4*)(src + 4 * j);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(w, v[e], acc[4 * j + e]);
   }
 }
 
-// dst[0..63] = bf16(acc * mul)
-__device__ __forceinline__ void store64(__bf16* dst, const float* acc, float mul) {
+// dst[0..N) = bf16(acc * mul)
+template <int N>
+__device__ __forceinline__ void store(__bf16* dst, const float* acc, float mul) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < N / 8; ++j) {
     float t[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = acc[8 * j + e] * mul;
@@ -64,18 +65,19 @@ __device__ __forceinline__ void store64(__bf16* dst, const float* acc, float mul
   }
 }
 
-template <bool SOFTMAX>
+template <bool SOFTMAX, int D = 128>
 __device__ void combine_fwd_tile(const FwdArgs& a, int b, int tile, int h, int n, int slot) {
+  constexpr int N = D / 2;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int r = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * 64;
+  const int r = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * N;
   const int iq = tile * ROWS + r;
   if (iq >= Lq) return;
   float m = -INFINITY, l = 0.0f;
   if (SOFTMAX)
     for (int k = 0; k < n; ++k) m = fmaxf(m, a.part_ml[(int64_t)(slot + k) * 2 * ROWS + r]);
-  float acc[64];
+  float acc[N];
 #pragma unroll
-  for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
+  for (int j = 0; j < N; ++j) acc[j] = 0.0f;
   for (int k = 0; k < n; ++k) {
     float wk = 1.0f;
     if (SOFTMAX) {
@@ -83,26 +85,29 @@ __device__ void combine_fwd_tile(const FwdArgs& a, int b, int tile, int h, int n
       wk = mk == -INFINITY ? 0.0f : fast_exp2(mk - m);
       l = fmaf(wk, a.part_ml[(int64_t)(slot + k) * 2 * ROWS + ROWS + r], l);
     }
-    axpy64(acc, wk, a.part_o + ((int64_t)(slot + k) * ROWS + r) * D + c0);
+    axpy<N>(acc, wk, a.part_o + ((int64_t)(slot + k) * ROWS + r) * D + c0);
   }
   const int64_t orow = (int64_t)(q0 + iq) * a.H + h;
-  store64((__bf16*)a.O + orow * D + c0, acc, SOFTMAX ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f);
+  store<N>((__bf16*)a.O + orow * D + c0, acc, SOFTMAX ? (l > 0.0f ? 1.0f / l : 0.0f) : 1.0f);
   if (SOFTMAX && c0 == 0 && a.lse != nullptr) a.lse[orow] = l > 0.0f ? (m + log2f(l)) * LN2 : -INFINITY;
 }
 
+template <int D = 128>
 __device__ inline void combine_dq_tile(const BwdArgs& a, int b, int tile, int h, int n, int slot) {
+  constexpr int N = D / 2;
   const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int r = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * 64;
+  const int r = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * N;
   const int iq = tile * ROWS + r;
   if (iq >= Lq) return;
-  float acc[64];
+  float acc[N];
 #pragma unroll
-  for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
-  for (int k = 0; k < n; ++k) axpy64(acc, 1.0f, a.part_dq + ((int64_t)(slot + k) * ROWS + r) * D + c0);
-  store64((__bf16*)a.dQ + ((int64_t)(q0 + iq) * a.H + h) * D + c0, acc, a.scale);
+  for (int j = 0; j < N; ++j) acc[j] = 0.0f;
+  for (int k = 0; k < n; ++k) axpy<N>(acc, 1.0f, a.part_dq + ((int64_t)(slot + k) * ROWS + r) * D + c0);
+  store<N>((__bf16*)a.dQ + ((int64_t)(q0 + iq) * a.H + h) * D + c0, acc, a.scale);
 }
 
 __device__ inline void combine_dkdv_tile(const BwdArgs& a, int b, int tile, int h, int n, int slot) {
+  constexpr int D = 128;
   const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
   const int r = threadIdx.x >> 1, c0 = (threadIdx.x & 1) * 64;
   const int jk = tile * ROWS + r;
@@ -111,12 +116,12 @@ __device__ inline void combine_dkdv_tile(const BwdArgs& a, int b, int tile, int 
   float acc[64];
 #pragma unroll
   for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
-  for (int k = 0; k < n; ++k) axpy64(acc, 1.0f, a.part_dk + ((int64_t)(slot + k) * ROWS + r) * D + c0);
-  store64((__bf16*)a.dK + krow, acc, a.scale);
+  for (int k = 0; k < n; ++k) axpy<64>(acc, 1.0f, a.part_dk + ((int64_t)(slot + k) * ROWS + r) * D + c0);
+  store<64>((__bf16*)a.dK + krow, acc, a.scale);
 #pragma unroll
   for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
-  for (int k = 0; k < n; ++k) axpy64(acc, 1.0f, a.part_dv + ((int64_t)(slot + k) * ROWS + r) * D + c0);
-  store64((__bf16*)a.dV + krow, acc, 1.0f);
+  for (int k = 0; k < n; ++k) axpy<64>(acc, 1.0f, a.part_dv + ((int64_t)(slot + k) * ROWS + r) * D + c0);
+  store<64>((__bf16*)a.dV + krow, acc, 1.0f);
 }
 
 }  // namespace split

@@ -38,8 +38,9 @@ def test_problem_struct_layout():
 def test_workspace_size_validation():
     ok = gdpa.problem(4, 2, 64, 100, 100)
     assert gdpa.workspace_size(ok) >= 256
-    assert gdpa.workspace_size(gdpa.problem(4, 2, 64, 100, 100, bias_buckets=16), True) > \
-        gdpa.workspace_size(gdpa.problem(4, 2, 64, 100, 100), True)
+    # a bias table adds its partial rows (D = 128: the same lists split with and without one)
+    assert gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100, bias_buckets=16), True) > \
+        gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100), True)
     with pytest.raises(gdpa.GdpaError) as e:
         gdpa.workspace_size(gdpa.problem(4, 2, 48, 100, 100))
     assert e.value.status == 2  # D = 48 unsupported

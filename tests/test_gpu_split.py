@@ -101,3 +101,27 @@ def test_split_bitwise_repeatable():
     b, _, _ = run(p)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("act", ["silu", "softmax"])
+def test_short_queries_long_keys_d64(act):
+    # PMA shape at D = 64: 32 queries per sample, one sample with thousands of keys among short
+    # ones; its forward and dQ tiles are split over keys (the D = 64 dK/dV list never splits)
+    lq = np.array([32, 32, 32, 32])
+    lk = np.array([6000, 50, 80, 20])
+    p = inputs.make_problem(f"split-pma-d64-{act}", seed=75, H=2, D=64, lq=lq, lk=lk, dtype="bf16",
+                            act=act, causal=False, bias_buckets=0)
+    check(p, True, True, False)
+
+
+@pytest.mark.parametrize("D", [32, 64])
+def test_long_causal_self_small_d(D):
+    # D = 32 / 64 causal self-attention: forward and dQ split without a bias table; with one, the
+    # dQ list is not split (its bias partial rows assume whole tiles) but the forward still is
+    lq = np.array([1500, 30, 40])
+    p = inputs.make_problem(f"split-self-d{D}", seed=76, H=1, D=D, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=0)
+    check(p, True, True, False)
+    pb = inputs.make_problem(f"split-self-d{D}-bias", seed=77, H=1, D=D, lq=lq, lk=lq,
+                             dtype="bf16", act="gelu_tanh", causal=True, bias_buckets=48)
+    check(pb, True, False, False)
