@@ -331,8 +331,10 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // dK, dV
+// Three workgroups per compute unit at D = 32 (their item count is large and each item short);
+// at D = 64 the third does not fit without spills.
 template <int D, int ACT, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + 2 * QL * 4 + (BIAS ? BIAS_WMAX * 4 : 0)];
   GDPA_LDS char* Qs = (GDPA_LDS char*)smem;
@@ -416,6 +418,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a) {
     const bool need_mask = (i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31);
 #pragma unroll 1  // rolled: unrolling makes the register allocator spill
     for (int qb = 0; qb < 2; ++qb) {
+      if (i0 + qb * 32 >= Lq) break;  // a half past the last query adds nothing (short queries)
       __builtin_amdgcn_sched_barrier(0);  // keep each 32-query block's loads inside its block
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
