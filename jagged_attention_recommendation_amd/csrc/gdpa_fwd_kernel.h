@@ -23,8 +23,9 @@
 //   O^T += V^T P^T: A = V^T read transposed from the row-major bf16 V tile (ds_read_b64_tr_b16),
 //                  B = P^T (bf16) straight from the S^T accumulator (the key order inside a
 //                  16-key k-step is permuted identically on both operands). For MX, V is
-//                  dequantised exactly into the bf16 tile: an e4m3 value times a power of two has
-//                  at most 4 significant bits. P is rounded to bf16 in both paths.
+//                  dequantised exactly into the bf16 tile by the scaled fp8 -> bf16 conversion
+//                  instruction: an e4m3 value times a power of two has at most 4 significant
+//                  bits. P is rounded to bf16 in both paths.
 // The exp of softmax uses exp2 with log2(e) folded into the score scale.
 #pragma once
 
@@ -41,14 +42,6 @@ namespace fwdk {
 constexpr int BM = FWD_BM_BF16;  // queries per item (4 waves x 32)
 constexpr int BN = FWD_BN_BF16;  // keys per tile
 constexpr int NT = 256;
-
-// e4m3 code (low byte of c) times the power of two sc, in fp32 (exact).
-__device__ __forceinline__ float e4m3_times(uint32_t c, float sc) {
-  const uint32_t em = c & 0x7Fu;
-  float mag = em >= 8u ? __builtin_bit_cast(float, (em + 960u) << 20) : (float)em * 0x1p-9f;
-  mag *= sc;
-  return (c & 0x80u) ? -mag : mag;
-}
 
 // 2^(X-127) for an e8m0 code X (0xFF, NaN in the format, is not produced by this path's inputs)
 __device__ __forceinline__ float e8m0_value(uint32_t X) {
@@ -176,13 +169,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
       for (int u = 0; u < MXC; ++u) {
         const int c = tid + NT * u, r = c >> 3, col = c & 7;
         *(GDPA_LDS i32x4*)(Ks + r * S::KMX_P + col * 16) = kc[u];
-        // dequantise 16 V codes into two 16-byte bf16 chunks
+        // dequantise 16 V codes into two 16-byte bf16 chunks: each conversion takes two e4m3
+        // bytes of a word (low or high half) times the block's power-of-two scale; the products
+        // have at most 4 significant bits, so bf16 holds them exactly
         const float sc = e8m0_value(vsb[u]);
-        float f[16];
+        bf16x2 pv[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) f[e] = e4m3_times((uint32_t)vc[u][e >> 2] >> (8 * (e & 3)), sc);
-        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16)) = pack8(&f[0]);
-        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16 + 8)) = pack8(&f[8]);
+        for (int wd = 0; wd < 4; ++wd) {
+          pv[2 * wd] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vc[u][wd], sc, false);
+          pv[2 * wd + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vc[u][wd], sc, true);
+        }
+        const bf16x8 lo8 = {pv[0][0], pv[0][1], pv[1][0], pv[1][1], pv[2][0], pv[2][1], pv[3][0], pv[3][1]};
+        const bf16x8 hi8 = {pv[4][0], pv[4][1], pv[5][0], pv[5][1], pv[6][0], pv[6][1], pv[7][0], pv[7][1]};
+        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16)) = lo8;
+        *(GDPA_LDS bf16x8*)(Vs + Tile<D>::off(r, col * 16 + 8)) = hi8;
       }
       if (tid < BN) *(GDPA_LDS uint32_t*)(Ks + BN * S::KMX_P + tid * 4) = ksw;
     }

@@ -339,7 +339,11 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     // and the wave's 64 entries overlap the row's range anyway) and keeps it only inside the
     // range, so the loads carry no branches.
     const int c_first = __builtin_amdgcn_readfirstlane(c);
-    const int rb_begin = c_first > 32 * nrb - 1 ? nrb : max(0, (c_first - 31) / 32);
+    // With a sliding window a row block's first visited key tile starts at most KL - 1 keys
+    // before its first query's window, so it wrote no diagonal above win + KL + 29: a wave whose
+    // entries all lie above that sums nothing.
+    const bool above_window = WIN && c_first > win + KL + 29;
+    const int rb_begin = c_first > 32 * nrb - 1 || above_window ? nrb : max(0, (c_first - 31) / 32);
     if (a.split_slot == nullptr || hdr->n_split == 0) {
       // no split tiles: one row per row block. All loads of a batch first (in bounds, no
       // branches), then the range tests; an entry outside its row block's range is cleared by a
