@@ -7,6 +7,10 @@ copy. The summary records a digest of the kernel sources: the benchmark reports 
 while the sources are unchanged.
 
     python -m jagged_attention_recommendation_amd.counters FETCH_DIR WRITE_DIR > summary.txt
+
+A second summary reads one run of shader-sequencer counters (`--sq DIR`): per kernel family the
+mean per dispatch of each counter and the MFMA busy fraction
+SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), the same ratio as rocprofv3's MfmaUtil.
 """
 from __future__ import annotations
 
@@ -20,7 +24,17 @@ import sys
 
 COPY_BYTES = 256 << 20
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNELS = {"fwd": "fwd_dl_kernel", "dq": "dq_dl_kernel", "dkdv": "dkdv_dl_kernel"}
+# kernel families: the D = 128 direct-load kernels and the D = 32 / 64 / MX kernels
+KERNELS = {"fwd": ("fwd_dl_kernel", "fwd_kernel"), "dq": ("dq_dl_kernel", "dq_kernel"),
+           "dkdv": ("dkdv_dl_kernel", "dkdv_kernel")}
+SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
+
+
+def family(kernel_name):
+    for short, subs in KERNELS.items():
+        if any(sub in kernel_name for sub in subs):
+            return short
+    return None
 
 
 def csrc_digest() -> str:
@@ -59,9 +73,9 @@ def summarize(fetch_dir, write_dir):
     w_scale = (COPY_BYTES / 1024) / copy_kib(write)
     out = {"copy_fetch_kib": round(copy_kib(fetch), 1), "copy_write_kib": round(copy_kib(write), 1),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
-    for short, sub in KERNELS.items():
-        fv = [v for k, g, v in fetch.values() if sub in k]
-        wv = [v for k, g, v in write.values() if sub in k]
+    for short in KERNELS:
+        fv = [v for k, g, v in fetch.values() if family(k) == short]
+        wv = [v for k, g, v in write.values() if family(k) == short]
         if not fv or not wv:
             continue
         fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
@@ -69,6 +83,35 @@ def summarize(fetch_dir, write_dir):
                                  "write_kib": round(wk, 1),
                                  "bytes": round(fk * 1024 * f_scale + wk * 1024 * w_scale)}
     out["csrc_sha256"] = csrc_digest()
+    return out
+
+
+def summarize_sq(run_dir):
+    """{family: {counter: mean per dispatch, ..., "dispatches": n, "mfma_busy_pct": x}}.
+    GRBM counters are per-instance copies of one clock (max taken), SQ counters are summed."""
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "*counter_collection.csv")):
+        rows += list(csv.DictReader(open(f)))
+    vals = collections.defaultdict(list)
+    names = {}
+    for r in rows:
+        vals[(r["Dispatch_Id"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    per = collections.defaultdict(dict)
+    for (d, c), v in vals.items():
+        per[d][c] = max(v) if c.startswith("GRBM") else sum(v)
+    out = {}
+    for short in KERNELS:
+        ds = [d for d in per if family(names[d]) == short]
+        if not ds:
+            continue
+        counters = sorted({c for d in ds for c in per[d]})
+        mean = {c: sum(per[d].get(c, 0.0) for d in ds) / len(ds) for c in counters}
+        mean["dispatches"] = len(ds)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE", 0) > 0:
+            mean["mfma_busy_pct"] = round(100.0 * mean["SQ_VALU_MFMA_BUSY_CYCLES"]
+                                          / (mean["GRBM_GUI_ACTIVE"] * SIMDS), 2)
+        out[short] = mean
     return out
 
 
@@ -85,6 +128,13 @@ def load_summary(path):
 
 
 def main(argv):
+    if argv[1] == "--sq":
+        s = summarize_sq(argv[2])
+        for k, v in s.items():
+            items = ", ".join(f"{c}={v[c]:.4g}" for c in sorted(v) if c not in ("dispatches",))
+            print(f"{k:5} dispatches={v['dispatches']}: {items}")
+        print("json: " + json.dumps(s))
+        return
     fetch_dir, write_dir = argv[1], argv[2]
     s = summarize(fetch_dir, write_dir)
     print(f"# calibration: the 256 MiB copy reads as {s['copy_fetch_kib']} KiB FETCH_SIZE "

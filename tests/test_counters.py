@@ -55,3 +55,26 @@ def test_kernel_bytes_count_each_operand_once():
         dkdv = (2 * tq + 2 * tk) * row + 2 * tk * row + (2 * tq * 2 * 4 if sm else 0)
         assert workload.kernel_bytes(p, "dq") == dq
         assert workload.kernel_bytes(p, "dkdv") == dkdv
+
+
+def test_sq_summary_mfma_busy(tmp_path):
+    """Shader-sequencer summary: SQ counters summed over instances, GRBM clock maxed, and the
+    MFMA busy fraction over all 1024 SIMDs."""
+    d = tmp_path / "sq"
+    d.mkdir()
+    rows = []
+    for disp, kern in ((1, "void gdpa::fwdk::fwd_kernel<64, 2, false, false, false>(gdpa::FwdArgs)"),
+                       (2, "void gdpa::fwdk::fwd_kernel<64, 2, false, false, false>(gdpa::FwdArgs)")):
+        for inst in range(2):
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": kern, "Grid_Size": 1,
+                         "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": 1024 * 50})
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": kern, "Grid_Size": 1,
+                         "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 1000})
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        w.writerows(rows)
+    s = counters.summarize_sq(d)
+    assert s["fwd"]["dispatches"] == 2
+    assert s["fwd"]["GRBM_GUI_ACTIVE"] == 1000 and s["fwd"]["SQ_VALU_MFMA_BUSY_CYCLES"] == 1024 * 100
+    assert s["fwd"]["mfma_busy_pct"] == 10.0
