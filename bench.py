@@ -62,6 +62,8 @@ def dominant_kernel_flops(p, kernel, window=0):
 
 TRAFFIC_SUMMARY = {
     2: "profiles/jfa_causal_bias_B64_H4_D128_fwd_dq_dkdv_hbm_traffic.txt",
+    3: "profiles/gdpa_cross_gelu_B256_H4_D128_fwd_dq_dkdv_hbm_traffic.txt",
+    4: "profiles/gdpa_pma_silu_B512_H8_D64_fwd_dq_dkdv_hbm_traffic.txt",
 }
 
 
