@@ -70,32 +70,39 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Element-wise activations of GDPA in fp32, built on exp2 and the hardware reciprocal.
-// tanh(u) = 1 - 2 / (1 + e^{2u}); at large |u| this saturates to +-1 without NaN.
+// GELU (tanh form): x/2 (1 + tanh(u)) with u = c (x + a x^3) equals x sigma(2u) =
+// x / (1 + e^{-2u}), since 1 + tanh(u) = 2 sigma(2u); written that way it takes one exp2 and one
+// reciprocal, and saturates without NaN (e^{-2u} = inf gives 0, e^{-2u} = 0 gives x).
+// Its derivative is sigma + x sigma (1 - sigma) 2c (1 + 3 a x^2).
+// SiLU: x sigma(x) = x / (1 + e^{-x}), derivative sigma (1 + x (1 - sigma)).
+constexpr float GELU_K = -2.0f * GELU_C * LOG2E;       // -2u log2(e) = x (GELU_K + GELU_KA x^2)
+constexpr float GELU_KA = GELU_K * GELU_A;
+constexpr float GELU_D1 = 2.0f * GELU_C;                // 2c (1 + 3 a x^2) = GELU_D1 + GELU_D3 x^2
+constexpr float GELU_D3 = 6.0f * GELU_C * GELU_A;
+
 __device__ __forceinline__ float act_fwd(int act, float x) {
   if (act == ACT_GELU_TANH) {
-    float u = GELU_C * (x + GELU_A * x * x * x);
-    float e = fast_exp2(2.0f * LOG2E * u);
-    float t = 1.0f - 2.0f * fast_rcp(1.0f + e);
-    return 0.5f * x * (1.0f + t);
+    const float x2 = x * x;
+    const float e = fast_exp2(x * fmaf(GELU_KA, x2, GELU_K));
+    return x * fast_rcp(1.0f + e);
   }
   // silu
-  float e = fast_exp2(-LOG2E * x);
+  const float e = fast_exp2(-LOG2E * x);
   return x * fast_rcp(1.0f + e);
 }
 
 // Value and derivative together (backward).
 __device__ __forceinline__ void act_fwd_bwd(int act, float x, float& y, float& dy) {
   if (act == ACT_GELU_TANH) {
-    float x2 = x * x;
-    float u = GELU_C * (x + GELU_A * x2 * x);
-    float e = fast_exp2(2.0f * LOG2E * u);
-    float t = 1.0f - 2.0f * fast_rcp(1.0f + e);
-    y = 0.5f * x * (1.0f + t);
-    dy = 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * GELU_C * (1.0f + 3.0f * GELU_A * x2);
+    const float x2 = x * x;
+    const float e = fast_exp2(x * fmaf(GELU_KA, x2, GELU_K));
+    const float sg = fast_rcp(1.0f + e);
+    y = x * sg;
+    dy = fmaf(y * (1.0f - sg), fmaf(GELU_D3, x2, GELU_D1), sg);
     return;
   }
-  float e = fast_exp2(-LOG2E * x);
-  float sg = fast_rcp(1.0f + e);
+  const float e = fast_exp2(-LOG2E * x);
+  const float sg = fast_rcp(1.0f + e);
   y = x * sg;
   dy = sg * (1.0f + x * (1.0f - sg));
 }
