@@ -168,6 +168,38 @@ def bwd(q_off, kv_off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, 
             "dbias_scale": dscale if error_scale and nb > 0 else None, "D": Dv}
 
 
+def shared_rows(q_off, seeds):
+    """Per-sample query rows of a shared query block: local query i of every sample is row i of
+    `seeds` [max_q, H, D] (PMA: one set of learned seed queries attends to each sample's keys;
+    page "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model",
+    GDPA paragraph). Returns the jagged [total_q, H, D] block."""
+    q_off = np.asarray(q_off, dtype=np.int64)
+    lens = np.diff(q_off)
+    assert (lens <= seeds.shape[0]).all(), "a sample is longer than the shared block"
+    idx = np.concatenate([np.arange(n) for n in lens]) if len(lens) else np.zeros(0, np.int64)
+    return np.asarray(seeds)[idx]
+
+
+def fwd_shared_q(q_off, kv_off, seeds, K, V, **kw):
+    """Forward with a shared query block (see shared_rows): the plain forward of the expanded
+    queries."""
+    return fwd(q_off, kv_off, shared_rows(q_off, seeds), K, V, **kw)
+
+
+def bwd_shared_q(q_off, kv_off, seeds, K, V, dO, **kw):
+    """Backward with a shared query block. The loss reaches seed row i through every sample that
+    reads it, so its gradient is the sum over those samples of their query gradients (chain rule);
+    summed here sample by sample in fp64. Other outputs as in bwd(); dQ is [max_q, H, D]."""
+    g = bwd(q_off, kv_off, shared_rows(q_off, seeds), K, V, dO, **kw)
+    dq = np.zeros(np.shape(seeds), dtype=np.float64)
+    q_off = np.asarray(q_off, dtype=np.int64)
+    for b in range(len(q_off) - 1):
+        lo, hi = int(q_off[b]), int(q_off[b + 1])
+        dq[:hi - lo] += g["dQ"][lo:hi]
+    g["dQ"] = dq
+    return g
+
+
 def act(name, x, derivative=False):
     """The oracle's own activation (or its derivative) on an array."""
     lib = _load()

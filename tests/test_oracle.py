@@ -401,6 +401,82 @@ def test_bwd_finite_differences(act, causal, nb):
         assert err.max() < 1e-6, (name, err.max())
 
 
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shared_query_gradient_finite_differences(act, causal):
+    """Shared query block (PMA seeds): central differences of sum(dO * O) with respect to each seed
+    element match the summed query gradient. Samples of different lengths, one empty and one
+    shorter than the block, so a seed row used by only some samples is covered."""
+    rng = np.random.default_rng(77)
+    H, D, max_q = 2, 3, 4
+    lq = np.array([4, 2, 0, 3])
+    lk = np.array([3, 5, 2, 1])
+    q_off, kv_off = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    seeds = rng.standard_normal((max_q, H, D))
+    K = rng.standard_normal((kv_off[-1], H, D))
+    V = rng.standard_normal((kv_off[-1], H, D))
+    dO = rng.standard_normal((q_off[-1], H, D))
+    bias = 0.3 * rng.standard_normal((H, 3))
+    kw = dict(act=act, causal=causal, scale=0.8, bias=bias)
+    g = oracle.bwd_shared_q(q_off, kv_off, seeds, K, V, dO, **kw)
+    assert g["dQ"].shape == seeds.shape
+
+    def loss(sd):
+        O, _ = oracle.fwd_shared_q(q_off, kv_off, sd, K, V, **kw)
+        return float((O * dO).sum())
+
+    h = 1e-6
+    fd = np.zeros_like(seeds)
+    for idx in np.ndindex(seeds.shape):
+        plus, minus = seeds.copy(), seeds.copy()
+        plus[idx] += h
+        minus[idx] -= h
+        fd[idx] = (loss(plus) - loss(minus)) / (2 * h)
+    err = np.abs(fd - g["dQ"]) / np.maximum(1.0, np.abs(g["dQ"]))
+    assert err.max() < 1e-6, err.max()
+
+
+def test_shared_query_identical_samples_scale_gradient():
+    """B samples with the same keys, values and output gradient: every sample's output is the
+    single-sample output, and the seed gradient is exactly B times the single-sample one (up to
+    rounding of the sum)."""
+    rng = np.random.default_rng(78)
+    H, D, Lq, Lk, B = 2, 8, 5, 7, 6
+    seeds = rng.standard_normal((Lq, H, D))
+    K1, V1 = rng.standard_normal((Lk, H, D)), rng.standard_normal((Lk, H, D))
+    dO1 = rng.standard_normal((Lq, H, D))
+    q1, k1 = np.array([0, Lq]), np.array([0, Lk])
+    qB, kB = np.arange(B + 1) * Lq, np.arange(B + 1) * Lk
+    for act in ("softmax", "silu"):
+        O1, _ = oracle.fwd(q1, k1, seeds, K1, V1, act=act)
+        g1 = oracle.bwd(q1, k1, seeds, K1, V1, dO1, act=act)
+        OB, _ = oracle.fwd_shared_q(qB, kB, seeds, np.tile(K1, (B, 1, 1)), np.tile(V1, (B, 1, 1)),
+                                    act=act)
+        gB = oracle.bwd_shared_q(qB, kB, seeds, np.tile(K1, (B, 1, 1)), np.tile(V1, (B, 1, 1)),
+                                 np.tile(dO1, (B, 1, 1)), act=act)
+        np.testing.assert_array_equal(OB, np.tile(O1, (B, 1, 1)))
+        np.testing.assert_allclose(gB["dQ"], B * g1["dQ"], rtol=1e-13, atol=1e-13)
+        np.testing.assert_array_equal(gB["dK"], np.tile(g1["dK"], (B, 1, 1)))
+
+
+def test_shared_query_unused_rows_have_zero_gradient():
+    """Seed rows that no sample reaches (every Lq_b shorter than the block) get a zero gradient;
+    a single sample that uses the whole block reproduces the plain backward."""
+    rng = np.random.default_rng(79)
+    H, D = 1, 4
+    seeds = rng.standard_normal((6, H, D))
+    q_off, kv_off = np.array([0, 2, 5]), np.array([0, 4, 9])
+    K, V = rng.standard_normal((9, H, D)), rng.standard_normal((9, H, D))
+    dO = rng.standard_normal((5, H, D))
+    g = oracle.bwd_shared_q(q_off, kv_off, seeds, K, V, dO, act="gelu_tanh")
+    assert (g["dQ"][3:] == 0).all() and (g["dQ"][:3] != 0).any()
+    dO6 = rng.standard_normal((6, H, D))
+    one = oracle.bwd_shared_q(np.array([0, 6]), np.array([0, 4]), seeds, K[:4], V[:4], dO6,
+                              act="softmax")
+    plain = oracle.bwd(np.array([0, 6]), np.array([0, 4]), seeds, K[:4], V[:4], dO6, act="softmax")
+    np.testing.assert_array_equal(one["dQ"], plain["dQ"])
+
+
 def test_softmax_backward_invariants():
     pb = rand_problem(41, B=4, H=3, D=5, maxlen=9, nb=6, same=False)
     for causal in (False, True):
