@@ -2,8 +2,10 @@
 
 Tolerance, stated before any kernel ran and never tuned to pass: an element g of a GPU output and
 the oracle's r agree when |g - r| <= atol * s + rtol * |r|, where s = max(1, rms of r over the
-output's (sample, head) block). The rms term keeps the check meaningful for GDPA, whose outputs
-are unnormalised sums of up to thousands of terms; for softmax outputs s is 1. bf16 results use
+output's (sample, head) block, taken over the rows that form a sum: rows whose oracle value is
+identically zero, such as keys that no query reaches under a causal mask when Lq < Lk, carry no
+rounding error and are left out of it). The rms term keeps the check meaningful for GDPA, whose
+outputs are unnormalised sums of up to thousands of terms; for softmax outputs s is 1. bf16 results use
 atol = rtol = 2e-2 (half a bf16 ulp is 2^-9 ~ 2e-3 per rounding, and P is rounded to bf16 before
 the second product), fp32 results 1e-4 / 1e-4, lse 1e-3 / 1e-4.
 """
@@ -66,14 +68,17 @@ def oracle_bwd(p, nthreads=None):
 
 
 def block_scale(r, off):
-    """s[row, h] = max(1, rms of r over the (sample, head) block containing that row)."""
+    """s[row, h] = max(1, rms of r over the nonzero rows of the (sample, head) block containing
+    that row)."""
     rows, H = r.shape[0], r.shape[1]
     s = np.ones((rows, H))
     for b in range(len(off) - 1):
         lo, hi = int(off[b]), int(off[b + 1])
         if hi > lo:
             blk = r[lo:hi].reshape(hi - lo, H, -1)
-            rms = np.sqrt((blk ** 2).mean(axis=(0, 2)))
+            sq = (blk ** 2).sum(axis=2)                  # [rows, H]
+            active = (blk != 0).any(axis=2).sum(axis=0)  # rows forming a sum, per head
+            rms = np.sqrt(sq.sum(axis=0) / np.maximum(active * blk.shape[2], 1))
             s[lo:hi] = np.maximum(1.0, rms)[None, :]
     return s
 
