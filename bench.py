@@ -159,22 +159,26 @@ def main():
     def up_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    Q, K, V, dO = up_bf16(p.Q), up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
+    # the PMA workload reads one shared block of seed queries (dQ is that block's gradient)
+    shared = p.seeds is not None
+    Q = up_bf16(p.seeds if shared else p.Q)
+    K, V, dO = up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
     q_off = torch.from_numpy(p.q_off).to(dev)
     kv_off = torch.from_numpy(p.kv_off).to(dev)
     bias = torch.from_numpy(p.bias).to(dev) if p.bias is not None else None
     nb = 0 if bias is None else bias.shape[1]
     max_q, max_kv = int(p.lq.max()), int(p.lk.max())
     prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, act=p.act, causal=p.causal,
-                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=win)
+                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=win,
+                        q_shared=shared)
     ws_f = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
-    O = torch.empty_like(Q)
+    O = torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if p.act == "softmax" else None
     grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
              torch.empty_like(bias) if bias is not None else None)
     kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv,
-              window=win)
+              window=win, q_shared=shared)
 
     def step():
         gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)

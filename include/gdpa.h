@@ -32,6 +32,11 @@
  * Sliding-window attention (same page, the paragraph on sliding-window attention): with
  * causal = 1 and window = W >= 1, query i attends to keys i - W + 1 .. i only; tiles wholly
  * outside the window are neither scheduled nor loaded.
+ * Shared queries (PMA, same page, GDPA paragraph: a fixed set of learned seed queries attends to
+ * every sample's keys): with q_shared = 1, Q and dQ are one block [max_q, H, D] used by every
+ * sample, whose local query i reads row i; O, dO and lse stay jagged over q_offsets. The
+ * backward returns dQ[i] = sum over samples b with Lq_b > i of the per-sample gradient, summed in
+ * fp32 in a fixed order and rounded once.
  *
  * Ownership and synchronisation. Every pointer except `p` is device memory owned by the caller and
  * must stay valid until the work enqueued on `stream` (a hipStream_t; NULL = the null stream)
@@ -41,8 +46,8 @@
  * overwritten, never accumulated. Base pointers must be 16-byte aligned.
  *
  * Errors. Host-checkable argument errors return a status and enqueue nothing. Data-dependent
- * errors (offsets not starting at 0, decreasing, or ending at a value other than total_q/total_kv)
- * are detected on the device: a device error word in the workspace is set, every kernel of the
+ * errors (offsets not starting at 0, decreasing, or ending at a value other than total_q/total_kv;
+ * with q_shared, a sample longer than max_q) are detected on the device: a device error word in the workspace is set, every kernel of the
  * call then skips its work and the outputs are left unspecified; gdpa_read_device_error() reads
  * that word. Nothing is printed and no C++ exception crosses this interface. Calls that share a
  * workspace must be ordered on one stream.
@@ -86,10 +91,13 @@ typedef struct {
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
   int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1,
                            GDPA_BF16 and D = 128 (otherwise GDPA_ENOTSUP) */
+  int32_t q_shared;     /* 0 or 1. 1: Q and dQ are [max_q, H, D], shared by all samples; needs
+                           GDPA_BF16 (else GDPA_ENOTSUP) and max_q >= 1 (else GDPA_EINVAL); a
+                           sample with Lq_b > max_q is a malformed q_offsets (device error 1) */
 } gdpa_problem;
 
 /* ABI version of this header (checked by bindings). */
-#define GDPA_ABI_VERSION 2
+#define GDPA_ABI_VERSION 3
 int32_t gdpa_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */

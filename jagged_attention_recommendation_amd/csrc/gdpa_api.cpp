@@ -35,6 +35,10 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->window < 0) return GDPA_EINVAL;
   // sliding windows: causal self-attention on the bf16 D = 128 kernels
   if (p->window > 0 && (p->causal != 1 || p->dtype != GDPA_BF16 || p->D != 128)) return GDPA_ENOTSUP;
+  // a shared query block: bf16 kernels, max_q rows
+  if (p->q_shared != 0 && p->q_shared != 1) return GDPA_EINVAL;
+  if (p->q_shared && p->max_q < 1) return GDPA_EINVAL;
+  if (p->q_shared && p->dtype != GDPA_BF16) return GDPA_ENOTSUP;
   // element counts must fit the kernels' 64-bit addressing and the scheduler's int32 counters
   if ((int64_t)p->H * p->D > (1 << 20)) return GDPA_ENOTSUP;
   return GDPA_OK;
@@ -45,6 +49,7 @@ Prob to_prob(const gdpa_problem* p) {
   r.B = p->B; r.H = p->H; r.D = p->D; r.dtype = p->dtype; r.act = p->act; r.causal = p->causal;
   r.nb = p->bias_buckets; r.total_q = p->total_q; r.total_kv = p->total_kv;
   r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale; r.win = p->window;
+  r.q_rows = p->q_shared ? p->max_q : 0;
   return r;
 }
 
@@ -83,7 +88,7 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
 
 struct BwdLayout {
   size_t header, items_q, items_k, dvec, tile_base, part, part_bh, split_cnt_q, split_cnt_k,
-      split_slot, part_dq, part_dk, part_dv, part_x, total;
+      split_slot, part_dq, part_dk, part_dv, part_x, dq_f32, total;
   int64_t max_q_items, max_k_items, max_qtiles;
   bool split, split_q, split_k;  // split storage present / per list
   int slots;                     // chunk slots of each list (0 without splitting)
@@ -129,6 +134,9 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
     end = L.part_x;
     if (p->bias_buckets > 0) end += align_up(nq * (tq / 32) * p->bias_buckets * sizeof(float));
   }
+  // shared query block: every sample's dQ in fp32 at O's rows, summed over samples afterwards
+  L.dq_f32 = end;
+  if (p->q_shared) end += align_up((size_t)p->total_q * p->H * p->D * sizeof(float));
   L.total = end;
   return L;
 }
@@ -253,7 +261,8 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
-  sa.causal = p->causal; sa.win = p->window; sa.tile_item = fwd_tile_rows(p->dtype);
+  sa.causal = p->causal; sa.win = p->window; sa.q_rows = pr.q_rows;
+  sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
   sa.split = L.split ? 1 : 0; sa.nslot = split_nslot(pr);
   sa.tile_base = nullptr; sa.split_slot = nullptr;
@@ -267,7 +276,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
   fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
   fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
-  fa.scale = p->scale; fa.win = p->window; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
+  fa.scale = p->scale; fa.win = p->window; fa.q_shared = p->q_shared; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
   fa.part_o = (float*)(ws + L.part_o); fa.part_ml = (float*)(ws + L.part_ml);
   const int grid = (int)L.max_items;
   if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
@@ -285,6 +294,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   if (p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
   if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
   if (p->total_q > 0 && (!Q || !dO || !dQ)) return GDPA_EINVAL;
+  if (p->q_shared && (!Q || !dQ)) return GDPA_EINVAL;  // dQ is written even with no queries
   if (p->total_kv > 0 && (!K || !V || !dK || !dV)) return GDPA_EINVAL;
   const bool softmax = p->act == GDPA_ACT_SOFTMAX;
   if (softmax && p->total_q > 0 && (!O || !lse)) return GDPA_EINVAL;
@@ -308,7 +318,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
-  sa.win = p->window; sa.ws_header = ws + L.header;
+  sa.win = p->window; sa.q_rows = pr.q_rows; sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
   sa.nslot = split_nslot(pr);
   SchedArgs sq = sa, sk = sa;
@@ -340,9 +350,18 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.part_dq = (float*)(ws + L.part_dq); ba.part_dk = (float*)(ws + L.part_dk);
   ba.part_dv = (float*)(ws + L.part_dv);
   ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale; ba.win = p->window;
+  ba.q_shared = p->q_shared;
+  ba.dq_f32 = p->q_shared ? (float*)(ws + L.dq_f32) : nullptr;
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   if (e != hipSuccess) return map_hip(e);
+  if (p->q_shared) {
+    DqSharedArgs qa;
+    qa.q_off = q_offsets; qa.part = ba.dq_f32; qa.dQ = dQ; qa.hdr = ws + L.header;
+    qa.B = p->B; qa.H = p->H; qa.D = p->D; qa.q_rows = pr.q_rows;
+    e = launch_dq_shared_reduce(qa, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
   if (p->bias_buckets > 0) {
     DbiasArgs da;
     da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;

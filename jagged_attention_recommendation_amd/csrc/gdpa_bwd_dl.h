@@ -89,7 +89,9 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   const int iq = wrow + l32;
   const bool qv = iq < Lq;
   const bool wave_active = wrow < Lq;
-  const int64_t row = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+  const int64_t row = (int64_t)(q0 + (qv ? iq : 0)) * H + h;  // O, dO, lse, D row
+  // Q row: in the sample's rows, or in the one block every sample shares
+  const int64_t qin = a.q_shared ? (int64_t)(qv ? iq : 0) * H + h : row;
 
   int nkt = (Lk + KL - 1) / KL;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   float part_d = 0.0f;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    qop[s] = qv ? *(const bf16x8*)(Q + row * D + 16 * s + 8 * g) : zero_bf16x8();
+    qop[s] = qv ? *(const bf16x8*)(Q + qin * D + 16 * s + 8 * g) : zero_bf16x8();
     doop[s] = qv ? *(const bf16x8*)(dO + row * D + 16 * s + 8 * g) : zero_bf16x8();
     if (ACT == ACT_SOFTMAX && qv) {
       const bf16x8 ov = *(const bf16x8*)((const __bf16*)a.O + row * D + 16 * s + 8 * g);
@@ -436,6 +438,11 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     return;
   }
   if (!qv) return;
+  if (a.dq_f32) {  // shared Q: this sample's gradient, summed over samples afterwards
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) store_acc_row_f32(a.dq_f32 + row * D, dq[n], n, g, a.scale);
+    return;
+  }
   __bf16* dqrow = (__bf16*)a.dQ + row * D;
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(dqrow, dq[n], n, g, a.scale);
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   // Waves 0 and 1 fetch the 64 lse / D values (one 4-byte load per lane, rows past the end
   // repeat the tile's first row).
   auto issue = [&](GDPA_LDS char* sq, GDPA_LDS char* so, GDPA_LDS float* srt, int qt) {
-    issue_tile(sq, Q, qt * QL, Lq, q0, H, h, w, lane);
+    issue_tile(sq, Q, qt * QL, Lq, a.q_shared ? 0 : q0, H, h, w, lane);
     issue_tile(so, dO, qt * QL, Lq, q0, H, h, w, lane);
     if (SM && w < 2) {
       const int r0 = qt * QL, n = min(QL, Lq - r0);

@@ -54,7 +54,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   const int iq = wrow + l32;
   const bool wave_active = wrow < Lq;
   const bool qv = iq < Lq;
-  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;  // O / lse row
+  // Q row: in the sample's rows, or in the one block every sample shares
+  const int64_t qin = a.q_shared ? (int64_t)(qv ? iq : 0) * H + h : qrow;
 
   int nkt = (Lk + BN - 1) / BN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, row_blk + BM) - 1) / BN + 1);
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
     const __bf16* Q = (const __bf16*)a.Q;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qop[s] = qv ? *(const bf16x8*)(Q + qrow * D + 16 * s + 8 * g) : zero_bf16x8();
+      qop[s] = qv ? *(const bf16x8*)(Q + qin * D + 16 * s + 8 * g) : zero_bf16x8();
   }
   f32x16 o[D / 32];
 #pragma unroll

@@ -81,7 +81,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   const int iq = wrow + l32;          // this lane's query
   const bool wave_active = wrow < Lq;
   const bool qv = iq < Lq;
-  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;
+  const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;  // O / lse row
+  // Q row: in the sample's rows, or in the one block every sample shares
+  const int64_t qin = a.q_shared ? (int64_t)(qv ? iq : 0) * H + h : qrow;
 
   int nkt = (Lk + BN - 1) / BN;
   if (CAUSAL) {
@@ -99,19 +101,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const __bf16* Q = (const __bf16*)a.Q;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
-      qop[s] = qv ? *(const bf16x8*)(Q + qrow * D + 16 * s + 8 * g) : zero_bf16x8();
+      qop[s] = qv ? *(const bf16x8*)(Q + qin * D + 16 * s + 8 * g) : zero_bf16x8();
   } else {
     const uint8_t* Q8 = (const uint8_t*)a.Q;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
       if (qv) {
-        lo = *(const i32x4*)(Q8 + qrow * D + 64 * s + 16 * g);
-        hi = *(const i32x4*)(Q8 + qrow * D + 64 * s + 32 + 16 * g);
+        lo = *(const i32x4*)(Q8 + qin * D + 64 * s + 16 * g);
+        hi = *(const i32x4*)(Q8 + qin * D + 64 * s + 32 + 16 * g);
       }
       q8[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    qsc = qv ? *(const uint32_t*)(a.qs + qrow * 4) : 0x7F7F7F7Fu;
+    qsc = qv ? *(const uint32_t*)(a.qs + qin * 4) : 0x7F7F7F7Fu;
   }
 
   f32x16 o[D / 32];

@@ -10,6 +10,7 @@ namespace gdpa {
 struct Prob {
   int B, H, D, dtype, act, causal, nb;
   int win;  // sliding window W (0: none); only with causal bf16 D = 128
+  int q_rows;  // shared query block: rows of Q / dQ (0: Q is jagged like O)
   int64_t total_q, total_kv;
   int max_q, max_kv;
   float scale;
@@ -38,6 +39,7 @@ struct SchedArgs {
   int64_t total_q, total_kv;
   int mode, causal;
   int win;                   // sliding window W (0: none)
+  int q_rows;                // shared query block: every Lq_b must be <= q_rows (0: no check)
   int tile_item, tile_loop;  // rows per item tile / rows per inner-loop tile
   int max_items;
   int list;                  // 0: first list of the header, 1: second list
@@ -101,6 +103,7 @@ struct FwdArgs {
   float* part_ml;  // split chunks (softmax): [2 * nslot][2][BM] running max (log2 units), sum
   int H, nb;
   int win;         // sliding window W (0: none)
+  int q_shared;    // 1: Q is one block read by every sample (local query i reads row i)
   float scale;
 };
 
@@ -145,8 +148,22 @@ struct BwdArgs {
   float* part_dv;
   int H, nb;
   int win;               // sliding window W (0: none)
+  int q_shared;          // 1: Q is one block read by every sample (local query i reads row i)
+  float* dq_f32;         // shared Q: per-sample dQ, fp32 scaled, at O's rows ([total_q, H, D]);
+                         // null: dQ is written in place in bf16
   float scale;
 };
+
+// Shared query block: dQ[i, h] = sum over samples b with Lq_b > i of dq_f32[q_off[b] + i, h],
+// summed in a fixed order, rounded once to bf16.
+struct DqSharedArgs {
+  const int32_t* q_off;
+  const float* part;
+  void* dQ;
+  const void* hdr;
+  int B, H, D, q_rows;
+};
+hipError_t launch_dq_shared_reduce(const DqSharedArgs& a, hipStream_t s);
 
 constexpr int BWD_Q_ITEM = 128;  // queries per dQ work item (bf16)
 constexpr int BWD_K_LOOP = 64;   // keys per tile in the dQ loop (bf16)

@@ -92,6 +92,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   __syncthreads();
   for (int b = tid; b < a.B; b += SNT) {
     if (a.q_off[b + 1] < a.q_off[b]) atomicOr(&err, 1);
+    if (a.q_rows > 0 && a.q_off[b + 1] - a.q_off[b] > a.q_rows) atomicOr(&err, 1);
     if (a.kv_off[b + 1] < a.kv_off[b]) atomicOr(&err, 2);
   }
   if (tid == 0) {
@@ -435,6 +436,56 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(dbias_stage_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Shared query block: dQ[i, h, :] = the sum of the samples' fp32 gradient rows for query i. A
+// workgroup owns one (i, h); each thread holds 4 columns of a row and takes the samples s,
+// s + S, s + 2S, ... (S = 256 / (D / 4) rows in flight), then one thread per 4 columns adds
+// the S partial sums in order. The order is fixed, so the result is bitwise reproducible.
+template <int D>
+__global__ __launch_bounds__(256) void dq_shared_reduce(DqSharedArgs a) {
+  constexpr int LPR = D / 4, S = 256 / LPR, U = 4;
+  __shared__ f32x4 red[256];
+  const WsHeader* hdr = (const WsHeader*)a.hdr;
+  if (hdr->error != 0) return;
+  const int i = blockIdx.x / a.H, h = blockIdx.x - i * a.H;
+  const int tid = threadIdx.x, c = tid % LPR, s = tid / LPR;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b0 = s; b0 < a.B; b0 += U * S) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = b0 + u * S;
+      v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (b < a.B) {
+        const int q0 = a.q_off[b];
+        if (i < a.q_off[b + 1] - q0)
+          v[u] = *(const f32x4*)(a.part + ((int64_t)(q0 + i) * a.H + h) * D + 4 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += v[u];
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < LPR) {
+    f32x4 t = red[c];
+    for (int k = 1; k < S; ++k) t += red[k * LPR + c];
+    const bf16x2 lo = pack_bf16(t[0], t[1]), hi = pack_bf16(t[2], t[3]);
+    *(bf16x4*)((__bf16*)a.dQ + ((int64_t)i * a.H + h) * D + 4 * c) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+hipError_t launch_dq_shared_reduce(const DqSharedArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.q_rows * a.H;
+  if (n <= 0) return hipSuccess;
+  if (n > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n);
+  if (a.D == 32) hipLaunchKernelGGL(dq_shared_reduce<32>, grid, dim3(256), 0, s, a);
+  else if (a.D == 64) hipLaunchKernelGGL(dq_shared_reduce<64>, grid, dim3(256), 0, s, a);
+  else if (a.D == 128) hipLaunchKernelGGL(dq_shared_reduce<128>, grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -103,7 +103,15 @@ __device__ inline void combine_dq_tile(const BwdArgs& a, int b, int tile, int h,
 #pragma unroll
   for (int j = 0; j < N; ++j) acc[j] = 0.0f;
   for (int k = 0; k < n; ++k) axpy<N>(acc, 1.0f, a.part_dq + ((int64_t)(slot + k) * ROWS + r) * D + c0);
-  store<N>((__bf16*)a.dQ + ((int64_t)(q0 + iq) * a.H + h) * D + c0, acc, a.scale);
+  const int64_t row = (int64_t)(q0 + iq) * a.H + h;
+  if (a.dq_f32) {  // shared Q: this sample's gradient, summed over samples afterwards
+#pragma unroll
+    for (int j = 0; j < N; j += 4)
+      *(f32x4*)(a.dq_f32 + row * D + c0 + j) =
+          f32x4{acc[j] * a.scale, acc[j + 1] * a.scale, acc[j + 2] * a.scale, acc[j + 3] * a.scale};
+    return;
+  }
+  store<N>((__bf16*)a.dQ + row * D + c0, acc, a.scale);
 }
 
 __device__ inline void combine_dkdv_tile(const BwdArgs& a, int b, int tile, int h, int n, int slot) {

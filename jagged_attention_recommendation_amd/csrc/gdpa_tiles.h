@@ -91,6 +91,15 @@ __device__ __forceinline__ void store_acc_row_bf16(__bf16* row, const f32x16& ac
   }
 }
 
+// Same as store_acc_row_bf16, in fp32.
+__device__ __forceinline__ void store_acc_row_f32(float* row, const f32x16& acc, int n, int g,
+                                                  float mul) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+    *(f32x4*)(row + n * 32 + r4 * 8 + 4 * g) =
+        f32x4{acc[4 * r4] * mul, acc[4 * r4 + 1] * mul, acc[4 * r4 + 2] * mul, acc[4 * r4 + 3] * mul};
+}
+
 // Stage the bias of raw diagonals lo..hi (inclusive, unclamped: entry d holds
 // bias[h][clamp(d, 0, nb - 1)]) in LDS, multiplied by mul, reversed (win[t] = entry hi - t) or in
 // order (win[t] = entry lo + t), so lookups need no clamping. Returns false and stages nothing

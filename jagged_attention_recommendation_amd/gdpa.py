@@ -33,7 +33,7 @@ class GdpaProblem(ctypes.Structure):
                 ("total_kv", ctypes.c_int64), ("max_q", ctypes.c_int32),
                 ("max_kv", ctypes.c_int32), ("act", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("bias_buckets", ctypes.c_int32),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("q_shared", ctypes.c_int32)]
 
 
 class GdpaError(RuntimeError):
@@ -74,19 +74,20 @@ def load():
                                       ctypes.POINTER(ctypes.c_double)]
     lib.gdpa_profile_stop.restype = ctypes.c_int32
     lib.gdpa_profile_stop.argtypes = []
-    if lib.gdpa_abi_version() != 2:
+    if lib.gdpa_abi_version() != 3:
         raise RuntimeError("libgdpa.so ABI version mismatch")
     _lib = lib
     return lib
 
 
 def problem(B, H, D, total_q, total_kv, *, dtype="bf16", act="softmax", causal=False,
-            scale=None, bias_buckets=0, max_q=0, max_kv=0, window=0):
+            scale=None, bias_buckets=0, max_q=0, max_kv=0, window=0, q_shared=False):
     if scale is None:
         scale = D ** -0.5
     return GdpaProblem(B=B, H=H, D=D, dtype=DTYPE[dtype], total_q=total_q, total_kv=total_kv,
                        max_q=max_q, max_kv=max_kv, act=ACT[act], causal=int(bool(causal)),
-                       scale=float(scale), bias_buckets=bias_buckets, window=int(window))
+                       scale=float(scale), bias_buckets=bias_buckets, window=int(window),
+                       q_shared=int(bool(q_shared)))
 
 
 def workspace_size(prob, for_bwd=False):
@@ -123,19 +124,29 @@ def _workspace(nbytes, device):
 
 def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None, bias=None,
         q_scale=None, k_scale=None, v_scale=None, max_q=0, max_kv=0, out=None, lse=None,
-        workspace=None, stream=None, return_lse=True, window=0):
+        workspace=None, stream=None, return_lse=True, window=0, q_shared=False, total_q=None):
     """Forward over jagged tensors q [total_q, H, D], k/v [total_kv, H, D].
 
     bf16 / fp32 tensors, or uint8 e4m3 codes with uint8 e8m0 scales [rows, H, D/32] (MX).
+    q_shared: q is one block [max_q, H, D] that every sample reads (local query i = row i); the
+    output row count total_q (= q_offsets[-1]) then comes from `total_q` or `out`.
     Returns (O, lse); lse is None for GDPA activations.
     """
     lib = load()
-    total_q, H, D = q.shape
+    rows, H, D = q.shape
+    if q_shared:
+        max_q = rows
+        if out is not None:
+            total_q = out.shape[0]
+        elif total_q is None:
+            raise ValueError("q_shared needs total_q or out")
+    else:
+        total_q = rows
     B = q_offsets.numel() - 1
     dt = _dtype_of(q)
     prob = problem(B, H, D, total_q, k.shape[0], dtype=dt, act=act, causal=causal, scale=scale,
                    bias_buckets=0 if bias is None else bias.shape[1], max_q=max_q, max_kv=max_kv,
-                   window=window)
+                   window=window, q_shared=q_shared)
     out_dtype = torch.float32 if dt == "f32" else torch.bfloat16
     if out is None:
         out = torch.empty((total_q, H, D), dtype=out_dtype, device=q.device)
@@ -155,15 +166,22 @@ def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=No
 
 
 def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None,
-        bias=None, max_q=0, max_kv=0, workspace=None, stream=None, grads=None, window=0):
-    """Backward of sum(do * O). Returns (dQ, dK, dV, dbias or None)."""
+        bias=None, max_q=0, max_kv=0, workspace=None, stream=None, grads=None, window=0,
+        q_shared=False):
+    """Backward of sum(do * O). Returns (dQ, dK, dV, dbias or None).
+
+    q_shared: q (and so dQ) is one block [max_q, H, D] read by every sample; dQ is the sum of
+    the samples' gradients. total_q is then do's row count.
+    """
     lib = load()
     total_q, H, D = q.shape
+    if q_shared:
+        max_q, total_q = q.shape[0], do.shape[0]
     B = q_offsets.numel() - 1
     dt = _dtype_of(q)
     nb = 0 if bias is None else bias.shape[1]
     prob = problem(B, H, D, total_q, k.shape[0], dtype=dt, act=act, causal=causal, scale=scale,
-                   bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=window)
+                   bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=window, q_shared=q_shared)
     if grads is None:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)

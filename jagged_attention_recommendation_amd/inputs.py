@@ -141,6 +141,7 @@ class Problem:
     q_scale: Optional[np.ndarray] = None
     k_scale: Optional[np.ndarray] = None
     v_scale: Optional[np.ndarray] = None
+    seeds: Optional[np.ndarray] = None  # shared query block [max_q, H, D] (PMA), or None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -168,7 +169,9 @@ def make_problem(name, *, seed, H, D, lq, lk, dtype="bf16", act="softmax", causa
                  bias_buckets=0, with_grad=True, shared_q=False, scale=None):
     """Draw one problem. lq/lk: per-sample lengths, or a callable rng -> lengths.
 
-    shared_q: every sample's query block is the same Lq rows (PMA seeds, materialised per sample).
+    shared_q: one block of max(Lq) seed rows is every sample's query block (PMA seeds): local
+    query i of each sample is seed row i. p.seeds holds the block; p.Q holds it materialised per
+    sample (the jagged layout), so both the shared and the per-sample call can be made.
     """
     rng = np.random.default_rng(seed)
     lq = np.asarray(lq(rng) if callable(lq) else lq, dtype=np.int64)
@@ -177,10 +180,11 @@ def make_problem(name, *, seed, H, D, lq, lk, dtype="bf16", act="softmax", causa
     B = len(lq)
     q_off, kv_off = offsets_from_lengths(lq), offsets_from_lengths(lk)
     tq, tk = int(q_off[-1]), int(kv_off[-1])
+    seeds = None
     if shared_q:
-        assert np.all(lq == lq[0])
-        seeds = _normal(rng, (int(lq[0]), H, D))
-        Qf = np.tile(seeds, (B, 1, 1)) if B > 0 else np.zeros((0, H, D), np.float32)
+        seeds = _normal(rng, (max(int(lq.max()) if B > 0 else 1, 1), H, D))
+        local = np.concatenate([np.arange(n) for n in lq]) if B > 0 else np.zeros(0, np.int64)
+        Qf = seeds[local]
     else:
         Qf = _normal(rng, (tq, H, D))
     Kf = _normal(rng, (tk, H, D))
@@ -193,6 +197,8 @@ def make_problem(name, *, seed, H, D, lq, lk, dtype="bf16", act="softmax", causa
         scale = 1.0 / float(np.sqrt(D))
     p = Problem(name=name, B=B, H=H, D=D, q_off=q_off, kv_off=kv_off, dtype=dtype, act=act,
                 causal=causal, scale=scale, Q=None, K=None, V=None, bias=bias)
+    if seeds is not None:
+        p.seeds = bf16_bits(seeds) if dtype == "bf16" else seeds
     if dtype == "f32":
         p.Q, p.K, p.V = Qf, Kf, Vf
         p.dO = dOf

@@ -47,12 +47,18 @@ def elem_bytes(p):
     return {"f32": 4, "bf16": 2, "mxfp8": 1}[p.dtype]
 
 
+def q_read_rows(p):
+    """Rows of Q a pass reads: the shared seed block when the problem has one, else every query."""
+    return p.seeds.shape[0] if getattr(p, "seeds", None) is not None else p.total_q
+
+
 def fwd_bytes(p):
     """Each input read once and each output written once (the algorithmic minimum)."""
     e_in = elem_bytes(p)
     e_out = 4 if p.dtype == "f32" else 2
     H, D = p.H, p.D
-    b = (p.total_q * H * D * e_in + 2 * p.total_kv * H * D * e_in + p.total_q * H * D * e_out)
+    b = (q_read_rows(p) * H * D * e_in + 2 * p.total_kv * H * D * e_in
+         + p.total_q * H * D * e_out)
     if p.dtype == "mxfp8":
         b += (p.total_q + 2 * p.total_kv) * H * (D // 32)
     if p.act == "softmax":
@@ -63,12 +69,13 @@ def fwd_bytes(p):
 
 
 def bwd_bytes(p):
-    """Reads Q, K, V, dO (+ O, lse, and D written then read, for softmax); writes dQ, dK, dV."""
+    """Reads Q, K, V, dO (+ O, lse, and D written then read, for softmax); writes dQ, dK, dV.
+    With a shared seed block, Q and dQ are that block."""
     e = elem_bytes(p)
     H, D = p.H, p.D
-    tq, tk = p.total_q, p.total_kv
-    b = (2 * tq * H * D * e + 2 * tk * H * D * e   # Q, dO, K, V
-         + tq * H * D * e + 2 * tk * H * D * e)    # dQ, dK, dV
+    tq, tk, rq = p.total_q, p.total_kv, q_read_rows(p)
+    b = ((rq + tq) * H * D * e + 2 * tk * H * D * e   # Q, dO, K, V
+         + rq * H * D * e + 2 * tk * H * D * e)       # dQ, dK, dV
     if p.act == "softmax":
         b += tq * H * D * e + tq * H * 4 + 2 * tq * H * 4  # O, lse, D write + read
     if p.bias is not None:
@@ -82,16 +89,18 @@ def kernel_bytes(p, kernel):
 
     fwd: Q, K, V read, O (+ lse) written. dq: Q, dO, K, V (+ O and lse for softmax, whose
     prologue forms D) read, dQ (+ D) written. dkdv: Q, dO, K, V (+ lse, D) read, dK, dV written.
+    With a shared seed block Q is that block, and the dq kernel's result is every sample's query
+    gradient in fp32 (summed over samples by a small reduction afterwards).
     """
     if kernel == "fwd":
         return fwd_bytes(p)
     e = elem_bytes(p)
     H, D = p.H, p.D
-    tq, tk = p.total_q, p.total_kv
-    b = (2 * tq + 2 * tk) * H * D * e
+    tq, tk, rq = p.total_q, p.total_kv, q_read_rows(p)
+    b = (rq + tq + 2 * tk) * H * D * e
     sm = p.act == "softmax"
     if kernel == "dq":
-        b += tq * H * D * e
+        b += tq * H * D * (4 if getattr(p, "seeds", None) is not None else e)
         if sm:
             b += tq * H * D * e + tq * H * 4 + tq * H * 4
     elif kernel == "dkdv":

@@ -24,7 +24,7 @@ def test_library_exports_every_symbol():
     lib = gdpa.load()
     for name in declared_symbols():
         assert hasattr(lib, name), name
-    assert lib.gdpa_abi_version() == 2
+    assert lib.gdpa_abi_version() == 3
     assert lib.gdpa_status_string(0) == b"ok"
 
 
@@ -33,6 +33,7 @@ def test_problem_struct_layout():
     assert gdpa.GdpaProblem.total_q.offset == 16
     assert gdpa.GdpaProblem.scale.offset == 48
     assert gdpa.GdpaProblem.window.offset == 56
+    assert gdpa.GdpaProblem.q_shared.offset == 60
 
 
 def test_workspace_size_validation():
@@ -65,6 +66,28 @@ def test_window_validation():
         with pytest.raises(gdpa.GdpaError) as e:
             gdpa.workspace_size(gdpa.problem(4, 2, D, 100, 100, **kw))
         assert e.value.status == status, kw
+
+
+def test_shared_query_validation():
+    """A shared query block needs bf16 and max_q >= 1; the backward workspace then holds the
+    per-sample fp32 query gradients (total_q * H * D floats) on top of the unshared layout."""
+    kw = dict(max_q=32)
+    ok = gdpa.problem(8, 2, 64, 256, 1000, q_shared=True, **kw)
+    base = gdpa.problem(8, 2, 64, 256, 1000, **kw)
+    assert gdpa.workspace_size(ok) == gdpa.workspace_size(base)
+    assert gdpa.workspace_size(ok, True) >= gdpa.workspace_size(base, True) + 256 * 2 * 64 * 4
+    for prob, status in [(gdpa.problem(8, 2, 64, 256, 1000, q_shared=True), 1),  # max_q = 0
+                         (gdpa.problem(8, 2, 64, 256, 1000, q_shared=True, dtype="f32", **kw), 2),
+                         (gdpa.problem(8, 2, 128, 256, 1000, q_shared=True, dtype="mxfp8", **kw),
+                          2)]:
+        with pytest.raises(gdpa.GdpaError) as e:
+            gdpa.workspace_size(prob)
+        assert e.value.status == status
+    bad = gdpa.problem(8, 2, 64, 256, 1000, **kw)
+    bad.q_shared = 2
+    with pytest.raises(gdpa.GdpaError) as e:
+        gdpa.workspace_size(bad)
+    assert e.value.status == 1
 
 
 def test_fwd_rejects_host_checkable_errors_without_launching():
