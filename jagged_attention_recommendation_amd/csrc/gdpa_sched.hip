@@ -442,10 +442,12 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
 // Shared query block: dQ[i, h, :] = the sum of the samples' fp32 gradient rows for query i. A
 // workgroup owns one (i, h); each thread holds 4 columns of a row and takes the samples s,
 // s + S, s + 2S, ... (S = 256 / (D / 4) rows in flight), then one thread per 4 columns adds
-// the S partial sums in order. The order is fixed, so the result is bitwise reproducible.
+// the S partial sums in order. The order is fixed, so the result is bitwise reproducible. Only
+// 256 workgroups run for the PMA shape, so a thread issues the offsets of U samples, then their
+// U row loads, before it adds anything: two memory latencies per U samples.
 template <int D>
 __global__ __launch_bounds__(256) void dq_shared_reduce(DqSharedArgs a) {
-  constexpr int LPR = D / 4, S = 256 / LPR, U = 4;
+  constexpr int LPR = D / 4, S = 256 / LPR, U = 16;
   __shared__ f32x4 red[256];
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   if (hdr->error != 0) return;
@@ -453,16 +455,19 @@ __global__ __launch_bounds__(256) void dq_shared_reduce(DqSharedArgs a) {
   const int tid = threadIdx.x, c = tid % LPR, s = tid / LPR;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int b0 = s; b0 < a.B; b0 += U * S) {
+    int q0[U], q1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = min(b0 + u * S, a.B - 1);
+      q0[u] = a.q_off[b];
+      q1[u] = a.q_off[b + 1];
+    }
     f32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int b = b0 + u * S;
       v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (b < a.B) {
-        const int q0 = a.q_off[b];
-        if (i < a.q_off[b + 1] - q0)
-          v[u] = *(const f32x4*)(a.part + ((int64_t)(q0 + i) * a.H + h) * D + 4 * c);
-      }
+      if (b0 + u * S < a.B && i < q1[u] - q0[u])
+        v[u] = *(const f32x4*)(a.part + ((int64_t)(q0[u] + i) * a.H + h) * D + 4 * c);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc += v[u];
