@@ -200,6 +200,89 @@ def bwd_shared_q(q_off, kv_off, seeds, K, V, dO, **kw):
     return g
 
 
+def rope_angles(pos, D, base=10000.0):
+    """Rotary position embedding angles [rows, D/2]: pair m of a row at position p turns by
+    p * base**(-2m/D). The pages name the rotary embedding but give no formula; this is the
+    rotary form of Su et al. (RoFormer), with consecutive elements (2m, 2m+1) as the pairs."""
+    assert D % 2 == 0
+    m = np.arange(D // 2, dtype=np.float64)
+    inv = base ** (-2.0 * m / D)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+
+
+def rope(x, pos, base=10000.0):
+    """Rotate each (2m, 2m+1) pair of x [rows, H, D] by its row's angle (see rope_angles)."""
+    x = _f64(x)
+    th = rope_angles(pos, x.shape[2], base)[:, None, :]
+    c, s = np.cos(th), np.sin(th)
+    e, o = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = c * e - s * o
+    y[..., 1::2] = s * e + c * o
+    return y
+
+
+def rope_bwd(g, pos, base=10000.0):
+    """Gradient through rope(): each pair's rotation is orthogonal, so the gradient with respect
+    to the input is the gradient rotated back (the transpose, i.e. the angle negated)."""
+    g = _f64(g)
+    th = rope_angles(pos, g.shape[2], base)[:, None, :]
+    c, s = np.cos(th), np.sin(th)
+    e, o = g[..., 0::2], g[..., 1::2]
+    y = np.empty_like(g)
+    y[..., 0::2] = c * e + s * o
+    y[..., 1::2] = -s * e + c * o
+    return y
+
+
+def local_positions(off):
+    """Position of every row inside its sample."""
+    off = np.asarray(off, dtype=np.int64)
+    lens = np.diff(off)
+    return np.concatenate([np.arange(n) for n in lens]) if len(lens) else np.zeros(0, np.int64)
+
+
+def block_offsets(off, block=64):
+    """Offsets of the fixed-size blocks of every sample: sample b's rows are cut into blocks of
+    `block` consecutive tokens (the last one shorter). In block-aligned attention (page "GEM
+    Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", block-
+    attention paragraph) a query block attends only to the key block at the same place, so the
+    blocks are independent attention problems."""
+    off = np.asarray(off, dtype=np.int64)
+    out = [0]
+    for b in range(len(off) - 1):
+        L = int(off[b + 1] - off[b])
+        for s0 in range(0, L, block):
+            out.append(out[-1] + min(block, L - s0))
+    return np.asarray(out, dtype=np.int64)
+
+
+def block_fwd(off, Q, K, V, *, act="softmax", causal=False, scale=None, block=64, rotary=True,
+              base=10000.0, nthreads=None):
+    """Block-aligned self-attention with rotary embeddings: Q and K are rotated at their
+    positions in the sample, then every block of `block` tokens attends within itself (causal:
+    also j <= i). Q, K, V: [total, H, D] over the sample offsets `off`. Returns (O, lse)."""
+    pos = local_positions(off)
+    Qr = rope(Q, pos, base) if rotary else _f64(Q)
+    Kr = rope(K, pos, base) if rotary else _f64(K)
+    bo = block_offsets(off, block)
+    return fwd(bo, bo, Qr, Kr, V, act=act, causal=causal, scale=scale, nthreads=nthreads)
+
+
+def block_bwd(off, Q, K, V, dO, *, act="softmax", causal=False, scale=None, block=64,
+              rotary=True, base=10000.0, nthreads=None):
+    """Backward of sum(dO * O) for block_fwd: the blocks' gradients with respect to the rotated
+    Q and K, rotated back (rope_bwd). Returns dict with dQ, dK, dV."""
+    pos = local_positions(off)
+    Qr = rope(Q, pos, base) if rotary else _f64(Q)
+    Kr = rope(K, pos, base) if rotary else _f64(K)
+    bo = block_offsets(off, block)
+    g = bwd(bo, bo, Qr, Kr, V, dO, act=act, causal=causal, scale=scale, nthreads=nthreads)
+    dQ = rope_bwd(g["dQ"], pos, base) if rotary else g["dQ"]
+    dK = rope_bwd(g["dK"], pos, base) if rotary else g["dK"]
+    return {"dQ": dQ, "dK": dK, "dV": g["dV"]}
+
+
 def act(name, x, derivative=False):
     """The oracle's own activation (or its derivative) on an array."""
     lib = _load()

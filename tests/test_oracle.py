@@ -708,3 +708,132 @@ def test_config_generators_shapes():
     assert np.all(p4.lq == 32) and p4.lk.min() >= 16
     seeds = p4.Q.reshape(16, 32, 8, 64)
     assert np.all(seeds == seeds[:1])
+
+
+# ---- block-aligned attention with rotary embeddings
+
+def test_rope_closed_forms():
+    """D = 2 turns (1, 0) to (cos p, sin p); position 0 is the identity; with D = 4 and base 100
+    the second pair turns by p / 10."""
+    p = np.array([0, 1, 2, 7])
+    y = oracle.rope(np.tile(np.array([1.0, 0.0]), (4, 1, 1)), p)
+    np.testing.assert_allclose(y[:, 0, 0], np.cos(p), atol=1e-15)
+    np.testing.assert_allclose(y[:, 0, 1], np.sin(p), atol=1e-15)
+    x = np.random.default_rng(80).standard_normal((3, 2, 8))
+    np.testing.assert_array_equal(oracle.rope(x, np.zeros(3, np.int64)), x)
+    z = oracle.rope(np.array([[[0.0, 0.0, 0.0, 1.0]]]), np.array([3]), base=100.0)
+    np.testing.assert_allclose(z[0, 0], [0.0, 0.0, -np.sin(0.3), np.cos(0.3)], atol=1e-15)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(81)
+    q, k = rng.standard_normal((1, 1, 16)), rng.standard_normal((1, 1, 16))
+    dot = lambda i, j: float((oracle.rope(q, np.array([i])) * oracle.rope(k, np.array([j]))).sum())
+    for i, j in [(5, 2), (9, 9), (3, 11)]:
+        for shift in (1, 17, 250):
+            assert abs(dot(i, j) - dot(i + shift, j + shift)) < 1e-12
+    assert abs(dot(0, 0) - float((q * k).sum())) < 1e-15
+
+
+def test_rope_backward_is_the_transpose():
+    rng = np.random.default_rng(82)
+    x, g = rng.standard_normal((6, 2, 8)), rng.standard_normal((6, 2, 8))
+    pos = np.array([0, 1, 5, 63, 64, 1000])
+    lhs = float((oracle.rope(x, pos) * g).sum())
+    rhs = float((x * oracle.rope_bwd(g, pos)).sum())
+    assert abs(lhs - rhs) < 1e-12
+    np.testing.assert_allclose(oracle.rope_bwd(oracle.rope(x, pos), pos), x, atol=1e-14)
+
+
+def test_block_offsets():
+    got = oracle.block_offsets(np.array([0, 130, 194, 194, 199]), 64)
+    np.testing.assert_array_equal(np.diff(got), [64, 64, 2, 64, 5])
+
+
+def _block_attention_loops(off, Q, K, V, act, causal, scale, block):
+    """Pure-Python loops: rotate q_i and k_j at their positions in the sample (pairs (2m, 2m+1),
+    angle p * 10000^(-2m/D)), then each query attends to the keys of its own block."""
+    import math
+    total, H, D = Q.shape
+    O = np.zeros((total, H, D))
+
+    def rot(v, p):
+        out = [0.0] * D
+        for m in range(D // 2):
+            a = p * 10000.0 ** (-2.0 * m / D)
+            out[2 * m] = math.cos(a) * v[2 * m] - math.sin(a) * v[2 * m + 1]
+            out[2 * m + 1] = math.sin(a) * v[2 * m] + math.cos(a) * v[2 * m + 1]
+        return out
+    for b in range(len(off) - 1):
+        s0, L = int(off[b]), int(off[b + 1] - off[b])
+        for h in range(H):
+            for i in range(L):
+                qi = rot(Q[s0 + i, h], i)
+                keys = [j for j in range(L) if j // block == i // block and (not causal or j <= i)]
+                sc = []
+                for j in keys:
+                    kj = rot(K[s0 + j, h], j)
+                    sc.append(scale * sum(qi[d] * kj[d] for d in range(D)))
+                if act == "softmax":
+                    mx = max(sc)
+                    w = [math.exp(x - mx) for x in sc]
+                    w = [x / sum(w) for x in w]
+                else:  # silu
+                    w = [x / (1.0 + math.exp(-x)) for x in sc]
+                for wj, j in zip(w, keys):
+                    O[s0 + i, h] += wj * V[s0 + j, h]
+    return O
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_attention_brute_force_tiny(act, causal):
+    rng = np.random.default_rng(83)
+    off = np.array([0, 9, 12, 12, 17])
+    Q, K, V = (rng.standard_normal((17, 2, 6)) for _ in range(3))
+    got, _ = oracle.block_fwd(off, Q, K, V, act=act, causal=causal, scale=0.7, block=4)
+    ref = _block_attention_loops(off, Q, K, V, act, causal, 0.7, 4)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_block_attention_short_samples_and_block_local_positions():
+    """Samples no longer than a block are plain attention; rotary scores depend only on i - j, so
+    rotating at block-local positions gives the same output as at sample positions."""
+    rng = np.random.default_rng(84)
+    off = np.array([0, 40, 104, 300])
+    Q, K, V = (rng.standard_normal((300, 2, 16)) for _ in range(3))
+    short = np.array([0, 40, 104])
+    O1, _ = oracle.block_fwd(short, Q[:104], K[:104], V[:104], rotary=False)
+    O2, _ = oracle.fwd(short, short, Q[:104], K[:104], V[:104])
+    np.testing.assert_array_equal(O1, O2)
+    bo = oracle.block_offsets(off, 64)
+    bpos = oracle.local_positions(bo)
+    O3, _ = oracle.fwd(bo, bo, oracle.rope(Q, bpos), oracle.rope(K, bpos), V, causal=True)
+    O4, _ = oracle.block_fwd(off, Q, K, V, causal=True)
+    np.testing.assert_allclose(O3, O4, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_block_attention_gradient_finite_differences(act):
+    rng = np.random.default_rng(85)
+    off = np.array([0, 7, 10])
+    Q, K, V, dO = (rng.standard_normal((10, 1, 4)) for _ in range(4))
+    kw = dict(act=act, causal=True, scale=0.9, block=4)
+    g = oracle.block_bwd(off, Q, K, V, dO, **kw)
+
+    def loss(q, k, v):
+        O, _ = oracle.block_fwd(off, q, k, v, **kw)
+        return float((O * dO).sum())
+    h = 1e-6
+    for name, key in (("Q", "dQ"), ("K", "dK"), ("V", "dV")):
+        base = {"Q": Q, "K": K, "V": V}
+        fd = np.zeros_like(base[name])
+        for idx in np.ndindex(fd.shape):
+            plus = {n: a.copy() for n, a in base.items()}
+            minus = {n: a.copy() for n, a in base.items()}
+            plus[name][idx] += h
+            minus[name][idx] -= h
+            fd[idx] = (loss(plus["Q"], plus["K"], plus["V"]) -
+                       loss(minus["Q"], minus["K"], minus["V"])) / (2 * h)
+        err = np.abs(fd - g[key]) / np.maximum(1.0, np.abs(g[key]))
+        assert err.max() < 1e-6, (name, err.max())
