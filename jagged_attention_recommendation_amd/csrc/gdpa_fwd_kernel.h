@@ -11,7 +11,8 @@
 //
 // Work decomposition: one workgroup (4 waves) per scheduler item = 128 query rows of one
 // (sample, head). Each wave owns 32 queries. Keys stream through LDS in tiles of 64 rows; the
-// next tile's global loads are issued before the current tile is computed.
+// global loads of the next tile (bf16: of the next two tiles, in two register stages) are
+// issued before the current tile is computed.
 //
 // Operand choice (wave64 MFMA):
 //   S^T = K Q^T  : A = K rows from LDS, B = Q^T from registers. The accumulator puts one query
@@ -197,14 +198,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
                  bwin, bias_h, a.nb, row_blk - (kt_hi * BN - 1), w_hi, true, inv_scale, tid, NT)) != 0;
   }
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < kt_hi) load_tile(kt + 1);
+  // one key tile: scores, probabilities and the P.V products, from the tile in LDS
+  auto compute = [&](int kt) {
     const int k0 = kt * BN;
-    if (!wave_active) continue;
-    if (CAUSAL && k0 > wrow + 31) continue;  // every key of the tile is after every query
+    if (!wave_active) return;
+    if (CAUSAL && k0 > wrow + 31) return;  // every key of the tile is after every query
 
     // ---- S^T = K Q^T for two 32-key blocks. With a bias the accumulators start from
     // bias / scale read straight from the LDS window (register r of block kb is key
@@ -324,6 +322,43 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int n = 0; n < D / 32; ++n)
           o[n] = mfma32(tile_tr_op<D>(Vs, kb * 32 + 16 * s2, n, lane), pb, o[n]);
+      }
+    }
+  };
+  if constexpr (MX) {
+    // one tile in flight in registers while the previous one is computed
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+      __syncthreads();
+      store_tile();
+      __syncthreads();
+      if (kt + 1 < kt_hi) load_tile(kt + 1);
+      compute(kt);
+    }
+  } else {
+    // bf16: two tiles in flight in two register stages (A: even offsets from kt_lo, B: odd),
+    // which doubles the bytes a workgroup has in flight; short query blocks (one busy wave, as
+    // in PMA) are bound by exactly that
+    TileLoader<D, NT> lk2_, lv2_;
+    if (kt_lo + 1 < kt_hi) {
+      lk2_.load((const __bf16*)a.K, (kt_lo + 1) * BN, Lk, kv0, H, h, tid);
+      lv2_.load((const __bf16*)a.V, (kt_lo + 1) * BN, Lk, kv0, H, h, tid);
+    }
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
+      __syncthreads();
+      store_tile();
+      __syncthreads();
+      if (kt + 2 < kt_hi) load_tile(kt + 2);
+      compute(kt);
+      if (kt + 1 < kt_hi) {
+        __syncthreads();
+        lk2_.store(Ks, tid);
+        lv2_.store(Vs, tid);
+        __syncthreads();
+        if (kt + 3 < kt_hi) {
+          lk2_.load((const __bf16*)a.K, (kt + 3) * BN, Lk, kv0, H, h, tid);
+          lv2_.load((const __bf16*)a.V, (kt + 3) * BN, Lk, kv0, H, h, tid);
+        }
+        compute(kt + 1);
       }
     }
   }
