@@ -1,8 +1,11 @@
 """Host logic of the HBM traffic summary: copy calibration and per-kernel scaling."""
 import csv
 import json
+import os
 
 from jagged_attention_recommendation_amd import counters
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
 
@@ -78,3 +81,13 @@ def test_sq_summary_mfma_busy(tmp_path):
     assert s["fwd"]["dispatches"] == 2
     assert s["fwd"]["GRBM_GUI_ACTIVE"] == 1000 and s["fwd"]["SQ_VALU_MFMA_BUSY_CYCLES"] == 1024 * 100
     assert s["fwd"]["mfma_busy_pct"] == 10.0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU; --gpus N > 1 exits with a message before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
