@@ -27,16 +27,16 @@ def seeds_dev(p):
     return torch.from_numpy(np.ascontiguousarray(p.seeds).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run_shared(p, headers=False):
+def run_shared(p, headers=False, window=0):
     from jagged_attention_recommendation_amd import gdpa
     d = to_device(p)
     sd = seeds_dev(p)
-    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"])
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"], window=window)
     max_q, H, D = p.seeds.shape
     nb = 0 if p.bias is None else p.bias.shape[1]
     prob = gdpa.problem(p.B, H, D, p.total_q, int(p.kv_off[-1]), dtype="bf16", act=p.act,
                         causal=p.causal, scale=p.scale, bias_buckets=nb, max_q=max_q,
-                        q_shared=True)
+                        q_shared=True, window=window)
     wf = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
     wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
     O, lse = gdpa.fwd(sd, d["K"], d["V"], d["q_off"], d["kv_off"], q_shared=True,
@@ -56,14 +56,14 @@ def head_slice(p, h):
     return f("seeds"), f("K"), f("V"), f("dO"), bias
 
 
-def oracle_shared(p, heads=None):
+def oracle_shared(p, heads=None, window=0):
     """fp64 oracle outputs of the shared-query problem, for the given heads (all by default),
     concatenated along the head axis."""
     heads = range(p.H) if heads is None else heads
     outs = []
     for h in heads:
         S, K, V, dO, bias = head_slice(p, h)
-        kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias)
+        kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, window=window)
         O, lse = oracle.fwd_shared_q(p.q_off, p.kv_off, S, K, V, **kw)
         g = oracle.bwd_shared_q(p.q_off, p.kv_off, S, K, V, dO, error_scale=True, **kw)
         outs.append((O, lse, g))
@@ -77,10 +77,10 @@ def oracle_shared(p, heads=None):
     return O, lse, g
 
 
-def check(p, got, heads=None):
+def check(p, got, heads=None, window=0):
     O, lse, dq, dk, dv, dbias = got
     hs = list(range(p.H)) if heads is None else list(heads)
-    O_ref, lse_ref, rb = oracle_shared(p, hs)
+    O_ref, lse_ref, rb = oracle_shared(p, hs, window)
     sel = lambda t: t[:, hs]
     assert_close(sel(O), O_ref, p.q_off, "bf16", f"{p.name} O")
     if p.act == "softmax":
@@ -115,6 +115,14 @@ def test_shared_query_ragged(D, act, nb, causal):
     p = ragged(D, act, nb, causal, seed=500 + D + nb)
     print(f"[case] {p.name} B={p.B} lq={p.q_off[-1]} lk={p.kv_off[-1]}", flush=True)
     check(p, run_shared(p))
+
+
+@pytest.mark.parametrize("act,window", [("softmax", 7), ("silu", 24)])
+def test_shared_query_with_sliding_window(act, window):
+    """The shared block and a causal sliding window together (bf16, D = 128, bias)."""
+    p = ragged(128, act, 16, True, seed=650 + window)
+    print(f"[case] {p.name} window={window}", flush=True)
+    check(p, run_shared(p, window=window), window=window)
 
 
 @pytest.mark.parametrize("D,act", [(64, "silu"), (128, "softmax"), (32, "gelu_tanh")])
