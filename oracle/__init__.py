@@ -11,6 +11,7 @@ normalisation. This module only marshals numpy arrays into that library.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -27,22 +28,21 @@ ACTS = {"softmax": ACT_SOFTMAX, "gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with gcc (plain C, -O2, OpenMP). Always recompiles."""
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+def build(src=None, out=None) -> str:
+    """Compile the oracle with gcc (plain C, -O2, OpenMP). Always recompiles. `src` and `out`
+    default to this package's source and library; the planted-mistake tests compile altered
+    copies of the source elsewhere."""
+    src = src or _SRC
+    out = out or _LIB_PATH
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+def _bind(path):
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int32)
     up = ctypes.POINTER(ctypes.c_uint8)
@@ -61,8 +61,30 @@ def _load():
     lib.gdpa_oracle_decode_e8m0.restype = None
     lib.gdpa_oracle_decode_mx.argtypes = [up, up, c_long, c_int, dp]
     lib.gdpa_oracle_decode_mx.restype = c_int
-    _lib = lib
     return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Run the oracle's functions on another build of its source (the planted-mistake tests load
+    a copy with one deliberate error and check that the pins reject it)."""
+    global _lib
+    saved = _lib
+    _lib = _bind(path)
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def default_threads() -> int:

@@ -33,14 +33,18 @@
  *     dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij do_i
  *     dbias[h,r] = sum over b and valid (i,j) with clamp(i-j,0,NB-1) = r of ds_ij
  *   error scale of dbias (optional output, not a result): a low-precision softmax backward forms
- *   D_i from a forward output whose element o_ic carries independent rounding errors: one per
- *   probability in sum_j p_ij v_jc and one when o_ic is stored. With errors of relative size eps
- *   and unit variance per |x|^2, D_i moves with variance eps^2 w_i,
- *     w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2),
- *   and bucket r, which takes m_ir = sum of p_ij over the row's pairs in r, moves with variance
- *   eps^2 sum_i m_ir^2 w_i. dbias_scale[h,r] = sqrt(sum over b, i of m_ir^2 w_i) (0 for GDPA,
- *   which has no D_i). Buckets that sum whole rows cancel (softmax rows of ds sum to 0), so this
- *   term, not |dbias|, sets how close a rounded backward can come there.
+ *   D_i from a forward output that carries rounding. Each rounding multiplies the value it rounds
+ *   by (1 + delta), with independent zero-mean deltas of standard deviation eps: one per
+ *   probability p_ij, rounded once before the product with V (so the same delta reaches every
+ *   column c of o_i), and one per element o_ic when the output is stored. Then
+ *     delta D_i = sum_j delta_ij p_ij dp_ij + sum_c delta'_ic do_ic o_ic,
+ *   of variance eps^2 w_i with
+ *     w_i = sum_j p_ij^2 dp_ij^2 + sum_c do_ic^2 o_ic^2,
+ *   and since ds_ij = p_ij (dp_ij - D_i), bucket r moves by -sum_i m_ir delta D_i, where m_ir is
+ *   the sum of p_ij over the row's pairs in r: variance eps^2 sum_i m_ir^2 w_i.
+ *   dbias_scale[h,r] = sqrt(sum over b, i of m_ir^2 w_i) (0 for GDPA, which has no D_i).
+ *   Buckets that sum whole rows cancel (softmax rows of ds sum to 0), so this term, not |dbias|,
+ *   sets how close a rounded backward can come there.
  *   gelu_tanh(x) = x/2 (1 + tanh(c (x + a x^3))), c = sqrt(2/pi), a = 0.044715
  *   silu(x)      = x sigmoid(x)
  *
@@ -305,20 +309,17 @@ int gdpa_oracle_bwd(int B, int H, int D, const int32_t* q_off, const int32_t* kv
             if (part) part[bias_index(i, j, nb)] += ds[j];
           }
           if (spart) {
-            /* w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2); m_ir per bucket of the row */
-            double* o2 = pv;
-            double* pv2 = pv + D;
-            for (int c = 0; c < D; ++c) o2[c] = pv2[c] = 0.0;
+            /* w_i = sum_j p_ij^2 dp_ij^2 + sum_c do_ic^2 o_ic^2; m_ir per bucket of the row */
+            double* oc = pv;
+            for (int c = 0; c < D; ++c) oc[c] = 0.0;
+            double wi = 0.0;
             for (long j = 0; j < Lk; ++j) {
               if (!valid[j]) continue;
               const double* vj = Vb + (size_t)j * H * D + (size_t)h * D;
-              for (int c = 0; c < D; ++c) {
-                o2[c] += p[j] * vj[c];
-                pv2[c] += p[j] * p[j] * vj[c] * vj[c];
-              }
+              for (int c = 0; c < D; ++c) oc[c] += p[j] * vj[c];
+              wi += p[j] * p[j] * dp[j] * dp[j];
             }
-            double wi = 0.0;
-            for (int c = 0; c < D; ++c) wi += doi[c] * doi[c] * (o2[c] * o2[c] + pv2[c]);
+            for (int c = 0; c < D; ++c) wi += doi[c] * doi[c] * oc[c] * oc[c];
             for (long j = 0; j < Lk; ++j)
               if (valid[j]) mr[bias_index(i, j, nb)] += p[j];
             /* the row's buckets are bias_index(i, Lk - 1) .. bias_index(i, 0) */

@@ -1,13 +1,20 @@
 """Helpers for GPU-vs-oracle parity tests (test infrastructure).
 
-Tolerance, stated before any kernel ran and never tuned to pass: an element g of a GPU output and
-the oracle's r agree when |g - r| <= atol * s + rtol * |r|, where s = max(1, rms of r over the
-output's (sample, head) block, taken over the rows that form a sum: rows whose oracle value is
-identically zero, such as keys that no query reaches under a causal mask when Lq < Lk, carry no
-rounding error and are left out of it). The rms term keeps the check meaningful for GDPA, whose
-outputs are unnormalised sums of up to thousands of terms; for softmax outputs s is 1. bf16 results use
-atol = rtol = 2e-2 (half a bf16 ulp is 2^-9 ~ 2e-3 per rounding, and P is rounded to bf16 before
-the second product), fp32 results 1e-4 / 1e-4, lse 1e-3 / 1e-4.
+Tolerance: an element g of a GPU output and the oracle's r agree when
+|g - r| <= atol * s + rtol * |r|, where s = max(1, rms of r over the output's (sample, head)
+block). The rms term keeps the check meaningful for GDPA, whose outputs are unnormalised sums of
+up to thousands of terms; for softmax outputs s is 1. bf16 results use atol = rtol = 2e-2 (half a
+bf16 ulp is 2^-9 ~ 2e-3 per rounding, and P is rounded to bf16 before the second product), fp32
+results 1e-4 / 1e-4, lse 1e-3 / 1e-4. These numbers were fixed before any kernel ran.
+
+One reading was added later, after a GPU result failed: the rms is taken over the block's rows
+that form a sum. A row whose oracle value is identically zero (a key that no query reaches under a
+causal mask when Lq < Lk) carries no rounding, and counting it diluted s for the rows that do. A
+dV element of a causal SiLU sample with 40 queries and 350 keys exceeded the diluted bound by
+13 %; tests/test_tolerance.py rounds P to bf16 on the CPU for such a sample and shows that this
+rounding alone produces errors of that size, and that the zero rows stay exactly zero. Because
+the wider s would otherwise also admit stray values on those rows, rows whose oracle value is
+identically zero must be exactly zero on the GPU.
 """
 from __future__ import annotations
 
@@ -96,6 +103,10 @@ def assert_close(g, r, off, kind, name):
         s = np.ones_like(r)
     err = np.abs(g - r)
     bound = atol * s + rtol * np.abs(r)
+    if g.ndim == 3:
+        # rows (per head) whose oracle value is identically zero carry no rounding: exact zeros
+        zero_rows = ~(r != 0).any(axis=2)
+        bound = np.where(zero_rows[..., None], 0.0, bound)
     bad = err > bound
     if bad.any():
         idx = np.argwhere(bad)[:5]

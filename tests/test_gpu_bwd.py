@@ -29,19 +29,22 @@ def run_fwd_bwd(p):
 
 
 def assert_dbias_close(g, r, name, err_scale=None):
-    """Bias gradient: the bf16 tolerance on the table's rms and each entry, plus 8 standard
-    deviations of the error a bf16 forward output puts into the bucket. The softmax backward
-    forms D_i from the forward output O, whose elements carry two bf16 roundings (P rounded for
-    P V, then O stored), each of standard deviation 2^-9 |x| / sqrt(3); a bucket that sums whole
-    rows of dS cancels (the rows sum to zero) and keeps that error. err_scale is the oracle's
-    square root of the bucket's error variance in units of those roundings."""
+    """Bias gradient: the bf16 tolerance on the table's rms and each entry, plus 4 standard
+    deviations of the error a rounded forward output puts into the bucket. The softmax backward
+    forms D_i from the forward output O, which carries bf16 roundings (P rounded once per pair
+    for P V, then O stored); a bucket that sums whole rows of dS cancels (the rows sum to zero)
+    and keeps that error. err_scale is the oracle's standard deviation of the bucket per unit
+    relative rounding error (pinned by a Monte-Carlo simulation in test_oracle.py). A bf16
+    round-to-nearest changes a value by a relative amount of at most u = 2^-8, and a uniform
+    error on [-u, u] has standard deviation u / sqrt(3), the largest of any rounding; that is
+    the unit used here."""
     g = g.detach().double().cpu().numpy()
     atol, rtol = TOL["bf16"]
     s = max(1.0, float(np.sqrt((r ** 2).mean())))
     err = np.abs(g - r)
     tol = atol * s + rtol * np.abs(r)
     if err_scale is not None:
-        tol = tol + 8.0 * 2.0 ** -9 / np.sqrt(3.0) * err_scale
+        tol = tol + 4.0 * 2.0 ** -8 / np.sqrt(3.0) * err_scale
     bad = err > tol
     assert not bad.any(), f"{name}: {bad.sum()} bad, max err {err.max():.3e}, rms {s:.3e}"
 

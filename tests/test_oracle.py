@@ -182,8 +182,8 @@ def test_brute_force_pure_python_tiny():
 def test_dbias_error_scale_brute_force_tiny():
     """The bias buckets' error scale (a tolerance input, not a result) by a loop-only evaluation:
     scale[h, r]^2 = sum over rows i of m_ir^2 w_i, m_ir = sum of p_ij over the row's pairs in
-    bucket r, w_i = sum_c do_ic^2 (o_ic^2 + sum_j p_ij^2 v_jc^2), for softmax; zero for GDPA,
-    which has no row term D_i."""
+    bucket r, w_i = sum_j p_ij^2 dp_ij^2 + sum_c do_ic^2 o_ic^2, for softmax; zero for GDPA,
+    which has no row term D_i. The Monte-Carlo test below pins what the formula stands for."""
     pb = rand_problem(8, B=2, H=2, D=3, lq=[4, 2], lk=[3, 5], nb=3)
     scale = 0.8
     for causal in (False, True):
@@ -203,10 +203,12 @@ def test_dbias_error_scale_brute_force_tiny():
                     tot = sum(w.values())
                     pr = {j: w[j] / tot for j in js}
                     wi = 0.0
+                    for j in js:
+                        dpj = sum(pb["dO"][q0 + i, h, c] * pb["V"][k0 + j, h, c] for c in range(3))
+                        wi += pr[j] ** 2 * dpj ** 2
                     for c in range(3):
                         oc = sum(pr[j] * pb["V"][k0 + j, h, c] for j in js)
-                        e2 = sum(pr[j] ** 2 * pb["V"][k0 + j, h, c] ** 2 for j in js)
-                        wi += pb["dO"][q0 + i, h, c] ** 2 * (oc * oc + e2)
+                        wi += pb["dO"][q0 + i, h, c] ** 2 * oc * oc
                     m = [0.0, 0.0, 0.0]
                     for j in js:
                         m[min(max(i - j, 0), 2)] += pr[j]
@@ -215,6 +217,72 @@ def test_dbias_error_scale_brute_force_tiny():
         np.testing.assert_allclose(g["dbias_scale"], np.sqrt(ref), rtol=1e-12, atol=1e-14)
         gd = run_oracle_bwd(pb, "gelu_tanh", causal, scale)
         assert np.array_equal(gd["dbias_scale"], np.zeros((2, 3)))
+
+
+def _perturbed_dbias_spread(pb, causal, scale, trials, seed):
+    """Monte-Carlo simulation of a rounded softmax forward feeding the backward's row term.
+
+    Dense numpy, written here from the definition (no oracle call): exact p_ij, dp_ij, o_i per
+    row; then, per trial, every probability is multiplied by (1 + eps z_ij) once (the product
+    with V sees the same rounded value in every column) and every output element by
+    (1 + eps z'_ic), z ~ N(0, 1) independent. D_i is formed from the perturbed output, ds_ij =
+    p_ij (dp_ij - D_i) and the bias gradient are formed from it by their definition, and the
+    per-bucket standard deviation of the bias gradient over trials is returned in units of eps."""
+    rng = np.random.default_rng(seed)
+    eps = 1e-6
+    qo, ko = pb["qo"], pb["ko"]
+    H, D = pb["Q"].shape[1:]
+    nb = pb["bias"].shape[1]
+    dev = np.zeros((trials, H, nb))
+    for b in range(len(qo) - 1):
+        Lq, Lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
+        for h in range(H):
+            q = pb["Q"][qo[b]:qo[b + 1], h]
+            k = pb["K"][ko[b]:ko[b + 1], h]
+            v = pb["V"][ko[b]:ko[b + 1], h]
+            do = pb["dO"][qo[b]:qo[b + 1], h]
+            ii, jj = np.meshgrid(np.arange(Lq), np.arange(Lk), indexing="ij")
+            valid = (jj <= ii) if causal else np.ones((Lq, Lk), bool)
+            bucket = np.clip(ii - jj, 0, nb - 1)
+            s = scale * q @ k.T + pb["bias"][h][bucket]
+            s = np.where(valid, s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)                       # [Lq, Lk]
+            dp = do @ v.T
+            z = rng.standard_normal((trials, Lq, Lk))
+            zo = rng.standard_normal((trials, Lq, D))
+            o_t = np.einsum("tij,jc->tic", p[None] * (1 + eps * z), v) * (1 + eps * zo)
+            D_t = np.einsum("tic,ic->ti", o_t, do)
+            D_x = (p * dp).sum(axis=1)                                 # exact row term
+            ds_t = p[None] * (dp[None] - D_t[:, :, None])
+            ds_x = p * (dp - D_x[:, None])
+            diff = np.where(valid[None], ds_t - ds_x[None], 0.0)
+            for r in range(nb):
+                dev[:, h, r] += diff[:, bucket == r].sum(axis=1)
+    return dev.std(axis=0, ddof=1) / eps
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dbias_error_scale_monte_carlo(causal):
+    """Pin of the oracle's bias-bucket error scale against a simulation of what it models: the
+    standard deviation of each bucket under independent relative perturbations of the forward's
+    probabilities (once per pair) and output elements (once per element) matches
+    dbias_scale within the sampling error of the estimate. With T trials the sample variance of
+    a Gaussian has relative standard deviation sqrt(2 / T) (0.032 at T = 2000); the check allows
+    five of those. Short rows make the sum_j p^2 dp^2 term comparable to the sum_c do^2 o^2 term,
+    and buckets that take a single diagonal (m_ir < 1) sit beside clamped edge buckets that take
+    whole rows (m_ir = 1), so a dropped term or m_ir in place of m_ir^2 moves some bucket far
+    outside the bound."""
+    pb = rand_problem(31, B=3, H=2, D=5, lq=[7, 3, 9], nb=4)
+    pb["bias"] = pb["bias"] * 2.0
+    T = 2000
+    sim = _perturbed_dbias_spread(pb, causal, 0.7, T, seed=5)
+    g = run_oracle_bwd(pb, "softmax", causal, 0.7)["dbias_scale"]
+    live = g > 1e-9
+    assert live.sum() >= 6
+    assert np.array_equal(live, sim > 1e-9)
+    ratio = sim[live] ** 2 / g[live] ** 2
+    assert np.all(np.abs(ratio - 1.0) <= 5.0 * np.sqrt(2.0 / T)), ratio
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
