@@ -90,7 +90,10 @@ typedef struct {
   float scale;          /* s = scale * q.k (+ bias); must be > 0 for GDPA_BF16 / GDPA_MXFP8_E4M3 */
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
   int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1,
-                           GDPA_BF16 and D = 128 (otherwise GDPA_ENOTSUP) */
+                           GDPA_BF16 and D = 128 (otherwise GDPA_ENOTSUP). A W that no query can
+                           reach (W >= total_q, or W >= max_q when max_q > 0) drops nothing and
+                           is the same as no window; any other W >= 1 needs
+                           total_q + total_kv <= INT32_MAX - 1024 (otherwise GDPA_ENOTSUP) */
   int32_t q_shared;     /* 0 or 1. 1: Q and dQ are [max_q, H, D], shared by all samples; needs
                            GDPA_BF16 (else GDPA_ENOTSUP) and max_q >= 1 (else GDPA_EINVAL); a
                            sample with Lq_b > max_q is a malformed q_offsets (device error 1) */
@@ -126,6 +129,20 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
 /* Waits for `stream`, then reads the device error word of the last call that used `workspace`
  * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err);
+
+/* Diagnostics (host-only, reads nothing from the device): where the scheduler's work-item list
+ * `list` sits in a workspace of problem *p. The forward (for_bwd = 0) has list 0, its query-tile
+ * items; the backward has list 0 (query-tile items, dQ) and list 1 (key-tile items, dK/dV).
+ * *offset receives the list's byte offset from the start of the workspace and *capacity the
+ * number of items it can hold; the workspace header's item counts (int32 words 1 and 2) say
+ * how many items the last call wrote. An item is 8 int32: sample, tile, head, the tile's
+ * canonical index (tiles numbered sample by sample), the first and one-past-last inner tile it
+ * covers, its chunk slot (-1 when its tile is not split) and chunk index | chunk count << 16.
+ * Items are listed by non-increasing inner-tile count (hi - lo, counted up to 1023). The tiles
+ * are those of the page named above, JFA paragraph: short sequences must not idle the GPU, so
+ * the list orders and splits work by cost. */
+int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
+                       int64_t* capacity);
 
 /* Profiling aid for benchmarks (not thread-safe). Between gdpa_profile_start(mask) and
  * gdpa_profile_stop(), every launch of a selected kernel is bracketed by a pair of HIP events

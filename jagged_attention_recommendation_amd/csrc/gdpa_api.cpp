@@ -19,6 +19,18 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// The window the kernels see. A window of W keys drops key j for query i only when j <= i - W,
+// which needs i >= W; when W is at least every sample's query count (Lq <= total_q, and
+// Lq <= max_q when that bound is given) it drops nothing and is treated as no window. The kernels
+// then only form positions plus W with W < total_q, which stays inside int32 because
+// check_problem() bounds total_q + total_kv.
+int32_t effective_window(const gdpa_problem* p) {
+  if (p->window <= 0) return 0;
+  if ((int64_t)p->window >= p->total_q) return 0;
+  if (p->max_q > 0 && p->window >= p->max_q) return 0;
+  return p->window;
+}
+
 int32_t check_problem(const gdpa_problem* p) {
   if (p == nullptr) return GDPA_EINVAL;
   if (p->B < 0 || p->H < 1 || p->total_q < 0 || p->total_kv < 0) return GDPA_EINVAL;
@@ -35,6 +47,8 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->window < 0) return GDPA_EINVAL;
   // sliding windows: causal self-attention on the bf16 D = 128 kernels
   if (p->window > 0 && (p->causal != 1 || p->dtype != GDPA_BF16 || p->D != 128)) return GDPA_ENOTSUP;
+  // window arithmetic adds a key or query position to W in int32
+  if (effective_window(p) > 0 && p->total_q + p->total_kv > INT32_MAX - 1024) return GDPA_ENOTSUP;
   // a shared query block: bf16 kernels, max_q rows
   if (p->q_shared != 0 && p->q_shared != 1) return GDPA_EINVAL;
   if (p->q_shared && p->max_q < 1) return GDPA_EINVAL;
@@ -48,7 +62,7 @@ Prob to_prob(const gdpa_problem* p) {
   Prob r;
   r.B = p->B; r.H = p->H; r.D = p->D; r.dtype = p->dtype; r.act = p->act; r.causal = p->causal;
   r.nb = p->bias_buckets; r.total_q = p->total_q; r.total_kv = p->total_kv;
-  r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale; r.win = p->window;
+  r.max_q = p->max_q; r.max_kv = p->max_kv; r.scale = p->scale; r.win = effective_window(p);
   r.q_rows = p->q_shared ? p->max_q : 0;
   return r;
 }
@@ -261,7 +275,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.mode = SCHED_QTILES;
-  sa.causal = p->causal; sa.win = p->window; sa.q_rows = pr.q_rows;
+  sa.causal = p->causal; sa.win = pr.win; sa.q_rows = pr.q_rows;
   sa.tile_item = fwd_tile_rows(p->dtype);
   sa.tile_loop = fwd_loop_rows(p->dtype); sa.max_items = (int)L.max_items; sa.list = 0;
   sa.split = L.split ? 1 : 0; sa.nslot = split_nslot(pr);
@@ -276,7 +290,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   fa.q_off = q_offsets; fa.kv_off = kv_offsets; fa.bias = bias; fa.O = O;
   fa.lse = p->act == GDPA_ACT_SOFTMAX ? lse : nullptr;
   fa.hdr = ws + L.header; fa.items = ws + L.items; fa.H = p->H; fa.nb = p->bias_buckets;
-  fa.scale = p->scale; fa.win = p->window; fa.q_shared = p->q_shared; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
+  fa.scale = p->scale; fa.win = pr.win; fa.q_shared = p->q_shared; fa.split_cnt = (int32_t*)(ws + L.split_cnt);
   fa.part_o = (float*)(ws + L.part_o); fa.part_ml = (float*)(ws + L.part_ml);
   const int grid = (int)L.max_items;
   if (p->dtype == GDPA_F32) e = launch_fwd_f32(pr, fa, grid, s);
@@ -318,7 +332,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   SchedArgs sa;
   sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
   sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
-  sa.win = p->window; sa.q_rows = pr.q_rows; sa.ws_header = ws + L.header;
+  sa.win = pr.win; sa.q_rows = pr.q_rows; sa.ws_header = ws + L.header;
   // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
   sa.nslot = split_nslot(pr);
   SchedArgs sq = sa, sk = sa;
@@ -349,7 +363,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.split_cnt_q = (int32_t*)(ws + L.split_cnt_q); ba.split_cnt_k = (int32_t*)(ws + L.split_cnt_k);
   ba.part_dq = (float*)(ws + L.part_dq); ba.part_dk = (float*)(ws + L.part_dk);
   ba.part_dv = (float*)(ws + L.part_dv);
-  ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale; ba.win = p->window;
+  ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale; ba.win = pr.win;
   ba.q_shared = p->q_shared;
   ba.dq_f32 = p->q_shared ? (float*)(ws + L.dq_f32) : nullptr;
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
@@ -368,11 +382,30 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
     da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
     da.part = ba.dbias_part; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
     da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
-    da.causal = p->causal; da.win = p->window; da.tile_rows = tq;
+    da.causal = p->causal; da.win = pr.win; da.tile_rows = tq;
     da.loop_rows = bwd_k_loop(p->dtype);
     e = launch_dbias_reduce(da, s);
   }
   return map_hip(e);
+}
+
+int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
+                       int64_t* capacity) {
+  if (!offset || !capacity) return GDPA_EINVAL;
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (for_bwd && p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
+  if (list < 0 || list > (for_bwd ? 1 : 0)) return GDPA_EINVAL;
+  if (!for_bwd) {
+    const FwdLayout L = fwd_layout(p);
+    *offset = L.items;
+    *capacity = L.max_items;
+  } else {
+    const BwdLayout L = bwd_layout(p);
+    *offset = list == 0 ? L.items_q : L.items_k;
+    *capacity = list == 0 ? L.max_q_items : L.max_k_items;
+  }
+  return GDPA_OK;
 }
 
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err) {

@@ -20,7 +20,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE
 
 # Every symbol include/gdpa.h declares.
 EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd", "gdpa_bwd",
-           "gdpa_read_device_error", "gdpa_profile_start", "gdpa_profile_read",
+           "gdpa_read_device_error", "gdpa_item_list", "gdpa_profile_start", "gdpa_profile_read",
            "gdpa_profile_stop"]
 
 # kernels selectable by the profiling hook
@@ -67,6 +67,9 @@ def load():
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_read_device_error.restype = ctypes.c_int32
     lib.gdpa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.gdpa_item_list.restype = ctypes.c_int32
+    lib.gdpa_item_list.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(sz),
+                                   ctypes.POINTER(ctypes.c_int64)]
     lib.gdpa_profile_start.restype = ctypes.c_int32
     lib.gdpa_profile_start.argtypes = [ctypes.c_int32]
     lib.gdpa_profile_read.restype = ctypes.c_int32
@@ -218,6 +221,22 @@ def workspace_header(workspace):
     torch.cuda.synchronize(workspace.device)
     w = workspace[:28].view(torch.int32).cpu().tolist()
     return dict(zip(["error", "items", "items2", "split", "split2", "chunk", "chunk2"], w))
+
+
+def item_list(prob, workspace, for_bwd=False, which=0):
+    """The scheduler's work items of the last call that used `workspace` (diagnostics;
+    synchronises): an int32 array [n, 8] of (sample, tile, head, canonical tile, lo, hi, slot,
+    chunk) in list order."""
+    off = ctypes.c_size_t(0)
+    cap = ctypes.c_int64(0)
+    st = load().gdpa_item_list(ctypes.byref(prob), int(bool(for_bwd)), int(which),
+                               ctypes.byref(off), ctypes.byref(cap))
+    if st != 0:
+        raise GdpaError(st, "gdpa_item_list")
+    n = workspace_header(workspace)["items2" if which else "items"]
+    assert 0 <= n <= cap.value
+    o = int(off.value)
+    return workspace[o:o + 32 * n].view(torch.int32).view(n, 8).cpu().numpy()
 
 
 def profile_start(kernels):

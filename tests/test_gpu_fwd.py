@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from jagged_attention_recommendation_amd import inputs
-from parity_util import assert_close, assert_lse_close, oracle_fwd, subproblem, to_device
+from parity_util import assert_close, assert_lse_close, live_rows, oracle_fwd, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def check_fwd(p, nthreads=None):
     O, lse = run_fwd(p)
     Or, lser = oracle_fwd(p, nthreads=nthreads)
     kind = p.dtype
-    err = assert_close(O, Or, p.q_off, kind, f"{p.name} O")
+    err = assert_close(O, Or, p.q_off, kind, f"{p.name} O", live_rows(p, "q"))
     if p.act == "softmax":
         assert_lse_close(lse, lser, f"{p.name} lse")
     return err
@@ -95,23 +95,17 @@ def test_config4_reduced():
     check_fwd(inputs.config_problem(4, B=24))
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("k", [2, 3, 4])
-def test_full_config_sampled(k):
-    """Full-size workload, one launch as the benchmark runs it; the oracle recomputes a few whole
-    samples (the longest, the shortest and one in between) on their own."""
+def test_full_config(k):
+    """Full-size workload, one launch as the benchmark runs it; every output element of every
+    sample is compared with the fp64 oracle (run on all host cores)."""
     p = inputs.config_problem(k)
     O, lse = run_fwd(p)
-    Og = O.float().cpu().numpy()
-    lseg = lse.cpu().numpy() if lse is not None else None
-    L = p.lq * np.maximum(p.lk, 1)
-    picks = sorted({int(np.argmax(L)), int(np.argmin(L)), len(L) // 2})
-    for b in picks:
-        sp = subproblem(p, b)
-        Or, lser = oracle_fwd(sp)
-        rows = slice(int(p.q_off[b]), int(p.q_off[b + 1]))
-        assert_close(Og[rows].astype(np.float64), Or, sp.q_off, p.dtype, f"config{k} sample {b}")
-        if lseg is not None:
-            assert_lse_close(lseg[rows], lser, f"config{k} sample {b} lse")
+    Or, lser = oracle_fwd(p)
+    assert_close(O, Or, p.q_off, p.dtype, f"config{k} O", live_rows(p, "q"))
+    if lse is not None:
+        assert_lse_close(lse, lser, f"config{k} lse")
 
 
 def test_deterministic_repeat():
@@ -160,22 +154,17 @@ def test_config5_reduced(act):
     check_fwd(inputs.config_problem(5, act=act, B=6, seed=2005))
 
 
+@pytest.mark.timeout(400)
 @pytest.mark.parametrize("act", ["softmax", "silu"])
-def test_config5_full_sampled(act):
-    """Full-size MX workload in one launch; the oracle recomputes a few whole samples of up to
-    4096 tokens (the shortest, one near the median, and the longest such sample)."""
+def test_config5_full(act):
+    """Full-size MX workload in one launch; every sample (up to 7,824 tokens for this draw) is
+    compared element by element with the fp64 oracle on the dequantised inputs."""
     p = inputs.config_problem(5, act=act)
     O, lse = run_fwd(p)
-    Og = O.float().cpu().numpy()
+    Og = O.float().cpu().numpy().astype(np.float64)
     lseg = lse.cpu().numpy() if lse is not None else None
-    L = p.lq
-    ok = np.where(L <= 4096)[0]
-    picks = sorted({int(ok[np.argmin(L[ok])]), int(ok[np.argmax(L[ok])]),
-                    int(ok[np.argsort(L[ok])[len(ok) // 2]])})
-    for b in picks:
-        sp = subproblem(p, b)
-        Or, lser = oracle_fwd(sp)
-        rows = slice(int(p.q_off[b]), int(p.q_off[b + 1]))
-        assert_close(Og[rows].astype(np.float64), Or, sp.q_off, "mxfp8", f"config5 sample {b}")
-        if lseg is not None:
-            assert_lse_close(lseg[rows], lser, f"config5 sample {b} lse")
+    del O, lse
+    Or, lser = oracle_fwd(p)
+    assert_close(Og, Or, p.q_off, "mxfp8", "config5 O", live_rows(p, "q"))
+    if lseg is not None:
+        assert_lse_close(lseg, lser, "config5 lse")

@@ -1,0 +1,198 @@
+"""The jagged work scheduler's item lists, copied back and checked bit for bit.
+
+Short sequences must not leave compute units idle while long ones finish (page "GEM Training: How
+Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA paragraph; the GDPA
+paragraph on redesigned scheduling for large batches and short or asymmetric K/V). The scheduler
+emits one item per (sample, tile, head), listed by decreasing cost (inner tiles visited), and cuts
+a tile that costs more than T = max(8, ceil(H * total cost / nslot)) inner tiles into ceil(cost / T)
+chunks. This file enumerates the expected items on the host from that rule and checks the GPU's
+list against it: the exact multiset of (sample, tile, head, lo, hi), non-increasing cost,
+canonical tile numbering, chunks that tile each range exactly with consecutive slots, and chunk
+words. The relative order of equal-cost items is free (any order gives the same results).
+"""
+from collections import Counter
+
+import numpy as np
+import pytest
+import torch
+
+from jagged_attention_recommendation_amd import inputs
+from parity_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from jagged_attention_recommendation_amd import gdpa
+    gdpa.load()
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def item_cost(mode, causal, win, Lq, Lk, t, ti, tl):
+    """Inner tiles an item visits (query tiles visit key tiles, key tiles visit query tiles)."""
+    if mode == "q":
+        if Lk <= 0:
+            return 0
+        nk = cdiv(Lk, tl)
+        if causal:
+            nk = min(nk, (min(Lq, (t + 1) * ti) - 1) // tl + 1)
+        first = max(0, t * ti - win + 1) // tl if win > 0 else 0
+        return max(0, nk - first)
+    if Lq <= 0:
+        return 0
+    nq = cdiv(Lq, tl)
+    first = 0
+    if causal:
+        if t * ti >= Lq:
+            return 0
+        first = (t * ti) // tl
+    if win > 0:
+        k_hi = min(Lk, (t + 1) * ti) - 1
+        nq = min(nq, (k_hi + win - 1) // tl + 1)
+    return max(0, nq - first)
+
+
+def expected_items(lq, lk, H, mode, causal, win, ti, tl, split, nslot):
+    """(sample, tile, head, canonical tile, lo, hi, n_chunks, chunk) for every expected item, and
+    the chunk length T (0 when nothing is split)."""
+    tiles = []  # (b, t, cost), canonical order
+    for b, (Lq, Lk) in enumerate(zip(lq, lk)):
+        n = cdiv(int(Lq if mode == "q" else Lk), ti)
+        for t in range(n):
+            tiles.append((b, t, item_cost(mode, causal, win, int(Lq), int(Lk), t, ti, tl)))
+    T = None
+    if split and tiles:
+        total = H * sum(c for _, _, c in tiles)
+        t_mean = max(cdiv(total, nslot), 8)
+        if max(c for _, _, c in tiles) > t_mean:
+            T = t_mean
+    out = []
+    for canon, (b, t, c) in enumerate(tiles):
+        n = cdiv(c, T) if T is not None and c > T else 1
+        for h in range(H):
+            for k in range(n):
+                lo, hi = (0, c) if n == 1 else (k * T, min(c, (k + 1) * T))
+                out.append((b, t, h, canon, lo, hi, n, k))
+    return out, (T or 0)
+
+
+def check_list(items, exp, chunk_T, header_T, nslot):
+    assert header_T == chunk_T
+    assert len(items) == len(exp)
+    got = Counter(tuple(int(x) for x in (it[0], it[1], it[2], it[3], it[4], it[5])) for it in items)
+    want = Counter(e[:6] for e in exp)
+    assert got == want, "item multiset differs"
+    cost = np.minimum(items[:, 5] - items[:, 4], 1023)
+    assert np.all(np.diff(cost) <= 0), "costs are not non-increasing"
+    n_of = {(e[0], e[1], e[2]): e[6] for e in exp}
+    slots = {}
+    for it in items:
+        b, t, h, _, lo, hi, slot, chunk = (int(x) for x in it)
+        n = n_of[(b, t, h)]
+        if n == 1:
+            assert slot == -1 and chunk == 0
+        else:
+            k = chunk & 0xFFFF
+            assert chunk >> 16 == n and 0 <= k < n
+            assert lo == k * header_T
+            slots.setdefault((b, t, h), {})[k] = slot
+    used = []
+    for key, ks in slots.items():
+        n = n_of[key]
+        assert sorted(ks) == list(range(n))
+        base = ks[0]
+        assert [ks[k] for k in range(n)] == list(range(base, base + n)), "slots not consecutive"
+        used.extend(range(base, base + n))
+    assert len(used) == len(set(used)) and all(0 <= s < 2 * nslot for s in used)
+
+
+def tile_sizes(dtype):
+    # forward item / loop, dQ item / loop, dK/dV item / loop (rows)
+    return ((64, 64), (64, 64), (64, 64)) if dtype == "f32" else ((128, 64), (128, 64), (128, 64))
+
+
+def run_and_check(p, window=0, backward=True):
+    from jagged_attention_recommendation_amd import gdpa
+    d = to_device(p)
+    nb = 0 if p.bias is None else p.bias.shape[1]
+    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, dtype=p.dtype, act=p.act,
+                        causal=p.causal, scale=p.scale, bias_buckets=nb, window=window)
+    lq, lk = np.diff(p.q_off), np.diff(p.kv_off)
+    win = window if 0 < window < p.total_q else 0
+    nslot = 256 if p.D == 128 else 512
+    bf16 = p.dtype == "bf16"
+    (fi, fl), (qi, ql), (ki, kl) = tile_sizes(p.dtype)
+    wf = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"], window=window)
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf,
+                      q_scale=d["q_scale"], k_scale=d["k_scale"], v_scale=d["v_scale"], **kw)
+    hf = gdpa.workspace_header(wf)
+    assert hf["error"] == 0
+    exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, fi, fl, bf16, nslot)
+    check_list(gdpa.item_list(prob, wf), exp, T, hf["chunk"], nslot)
+    if not backward:
+        return
+    wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    gdpa.bwd(d["Q"], d["K"], d["V"], O, d["dO"], lse, d["q_off"], d["kv_off"], workspace=wb, **kw)
+    hb = gdpa.workspace_header(wb)
+    assert hb["error"] == 0
+    split_q = bf16 and (p.D == 128 or nb == 0)
+    split_k = bf16 and p.D == 128
+    exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, qi, ql, split_q, nslot)
+    check_list(gdpa.item_list(prob, wb, True, 0), exp, T, hb["chunk"], nslot)
+    exp, T = expected_items(lq, lk, p.H, "k", p.causal, win, ki, kl, split_k, nslot)
+    check_list(gdpa.item_list(prob, wb, True, 1), exp, T, hb["chunk2"], nslot)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_full_workload_lists(k):
+    """The lists of the benchmark's full-size workloads (JFA causal; cross; PMA, where the long
+    lognormal tail splits the D = 64 forward and dQ tiles)."""
+    run_and_check(inputs.config_problem(k))
+
+
+def test_mx_workload_forward_list():
+    run_and_check(inputs.config_problem(5, act="softmax"), backward=False)
+
+
+def test_split_lists():
+    lq = np.array([1500, 70, 5])
+    p = inputs.make_problem("sched-split", seed=81, H=1, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=600)
+    run_and_check(p)
+    lq, lk = np.array([200, 2100, 33]), np.array([2500, 90, 700])
+    p = inputs.make_problem("sched-split-cross", seed=82, H=2, D=128, lq=lq, lk=lk, dtype="bf16",
+                            act="gelu_tanh", causal=False)
+    run_and_check(p)
+
+
+@pytest.mark.parametrize("window", [1, 100, 513])
+def test_window_lists(window):
+    lq = np.array([2100, 40, 700, 9, 0, 1])
+    p = inputs.make_problem("sched-window", seed=83, H=2, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=64)
+    run_and_check(p, window=window)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 32), ("bf16", 64)])
+def test_small_d_and_f32_lists(dtype, D):
+    lq = np.array([1, 63, 64, 65, 127, 128, 129, 0, 5, 900])
+    lk = np.array([1, 63, 64, 65, 127, 128, 129, 7, 0, 3])
+    p = inputs.make_problem("sched-edges", seed=84, H=3, D=D, lq=lq, lk=lk, dtype=dtype,
+                            act="silu", causal=False, bias_buckets=16)
+    run_and_check(p)
+    pc = inputs.make_problem("sched-edges-causal", seed=85, H=2, D=D, lq=lq, lk=lq, dtype=dtype,
+                             act="softmax", causal=True)
+    run_and_check(pc)
+
+
+def test_empty_batch():
+    p = inputs.make_problem("sched-empty", seed=86, H=2, D=128, lq=np.array([0, 0]),
+                            lk=np.array([0, 5]), dtype="bf16", act="softmax", causal=False)
+    run_and_check(p)

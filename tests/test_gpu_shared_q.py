@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from jagged_attention_recommendation_amd import inputs
-from parity_util import assert_close, assert_lse_close, to_device
+from parity_util import assert_close, assert_lse_close, live_rows, to_device
 from test_gpu_bwd import assert_dbias_close
 
 pytestmark = pytest.mark.gpu
@@ -82,14 +82,14 @@ def check(p, got, heads=None, window=0):
     hs = list(range(p.H)) if heads is None else list(heads)
     O_ref, lse_ref, rb = oracle_shared(p, hs, window)
     sel = lambda t: t[:, hs]
-    assert_close(sel(O), O_ref, p.q_off, "bf16", f"{p.name} O")
+    assert_close(sel(O), O_ref, p.q_off, "bf16", f"{p.name} O", live_rows(p, "q", window))
     if p.act == "softmax":
         assert_lse_close(sel(lse), lse_ref, f"{p.name} lse")
     max_q = p.seeds.shape[0]
     assert dq.shape == (max_q, p.H, p.D)
     assert_close(sel(dq), rb["dQ"], np.array([0, max_q]), "bf16", f"{p.name} dQ (seeds)")
-    assert_close(sel(dk), rb["dK"], p.kv_off, "bf16", f"{p.name} dK")
-    assert_close(sel(dv), rb["dV"], p.kv_off, "bf16", f"{p.name} dV")
+    assert_close(sel(dk), rb["dK"], p.kv_off, "bf16", f"{p.name} dK", live_rows(p, "k", window))
+    assert_close(sel(dv), rb["dV"], p.kv_off, "bf16", f"{p.name} dV", live_rows(p, "k", window))
     if p.bias is not None:
         assert_dbias_close(dbias[hs], rb["dbias"], f"{p.name} dbias", rb["dbias_scale"])
 
@@ -148,16 +148,18 @@ def test_shared_query_bitwise_repeatable():
             assert torch.equal(x, y)
 
 
+@pytest.mark.timeout(300)
 def test_shared_query_pma_workload_full_size():
     """The PMA workload at its full size (B = 512, H = 8, D = 64, 32 seeds, keys ~ lognormal):
-    every output of two heads against the oracle, and the whole of O, dK and dV bitwise equal to
-    the same kernels' outputs on the seeds materialised per sample (same values, same order)."""
+    every output of every head against the oracle, and the whole of O, dK and dV bitwise equal
+    to the same kernels' outputs on the seeds materialised per sample (same values, same
+    order)."""
     from jagged_attention_recommendation_amd import gdpa
     p = inputs.config_problem(4)
     assert p.seeds.shape == (32, 8, 64)
     print(f"[case] {p.name} B={p.B} total_kv={p.kv_off[-1]}", flush=True)
     got = run_shared(p)
-    check(p, got, heads=[0, 7])
+    check(p, got)
     d = to_device(p)
     O_mat, _ = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], act=p.act,
                         causal=p.causal, scale=p.scale)

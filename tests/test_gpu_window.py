@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from jagged_attention_recommendation_amd import inputs
-from parity_util import assert_close, assert_lse_close, host_f64, to_device
+from parity_util import assert_close, assert_lse_close, host_f64, live_rows, to_device
 from test_gpu_bwd import assert_dbias_close
 
 pytestmark = pytest.mark.gpu
@@ -57,14 +57,14 @@ def check(p, W, nthreads=None):
     Or, lser = oracle.fwd(*oracle_args(p), act=p.act, causal=True, scale=p.scale, bias=bias,
                           nthreads=nthreads, window=W)
     tag = f"{p.name} W={W}"
-    assert_close(O, Or, p.q_off, "bf16", f"{tag} O")
+    assert_close(O, Or, p.q_off, "bf16", f"{tag} O", live_rows(p, "q", W))
     if p.act == "softmax":
         assert_lse_close(lse, lser, f"{tag} lse")
     g = oracle.bwd(*oracle_args(p), host_f64(p, "dO"), act=p.act, causal=True, scale=p.scale,
                    bias=bias, nthreads=nthreads, error_scale=True, window=W)
-    assert_close(dq, g["dQ"], p.q_off, "bf16", f"{tag} dQ")
-    assert_close(dk, g["dK"], p.kv_off, "bf16", f"{tag} dK")
-    assert_close(dv, g["dV"], p.kv_off, "bf16", f"{tag} dV")
+    assert_close(dq, g["dQ"], p.q_off, "bf16", f"{tag} dQ", live_rows(p, "q", W))
+    assert_close(dk, g["dK"], p.kv_off, "bf16", f"{tag} dK", live_rows(p, "k", W))
+    assert_close(dv, g["dV"], p.kv_off, "bf16", f"{tag} dV", live_rows(p, "k", W))
     if p.bias is not None:
         assert_dbias_close(dbias, g["dbias"], f"{tag} dbias", g["dbias_scale"])
     return hf, hb
@@ -121,3 +121,22 @@ def test_window_workload_shape():
     bias table) on 8 samples with a 512-key window, checked on every sample and head."""
     p = inputs.config_problem(2, B=8)
     check(p, 512)
+
+
+def test_window_beyond_every_length_is_plain_causal():
+    """A window no query can reach (W = 2^31 - 1) drops nothing: every output and gradient
+    matches the plain causal oracle, and the window arithmetic does not overflow."""
+    W = 2**31 - 1
+    p = ragged(121, "softmax", 96, B=4, hi=700)
+    O, lse, (dq, dk, dv, dbias), hf, hb = run(p, W)
+    assert hf["error"] == 0 and hb["error"] == 0
+    bias = p.bias.astype(np.float64)
+    Or, lser = oracle.fwd(*oracle_args(p), act=p.act, causal=True, scale=p.scale, bias=bias)
+    assert_close(O, Or, p.q_off, "bf16", "W=max O", live_rows(p, "q"))
+    assert_lse_close(lse, lser, "W=max lse")
+    g = oracle.bwd(*oracle_args(p), host_f64(p, "dO"), act=p.act, causal=True, scale=p.scale,
+                   bias=bias, error_scale=True)
+    assert_close(dq, g["dQ"], p.q_off, "bf16", "W=max dQ", live_rows(p, "q"))
+    assert_close(dk, g["dK"], p.kv_off, "bf16", "W=max dK", live_rows(p, "k"))
+    assert_close(dv, g["dV"], p.kv_off, "bf16", "W=max dV", live_rows(p, "k"))
+    assert_dbias_close(dbias, g["dbias"], "W=max dbias", g["dbias_scale"])

@@ -17,7 +17,7 @@ import numpy as np
 import torch
 
 from jagged_attention_recommendation_amd import inputs
-from parity_util import TOL, assert_close, block_scale, oracle_bwd
+from parity_util import TOL, assert_close, block_scale, live_rows, oracle_bwd
 
 
 def _silu(x):
@@ -43,11 +43,12 @@ def test_zero_rows_and_bf16_probability_rounding():
     assert not ref[Lq:].any() and not sim[Lq:].any()
     assert (ref[:Lq] != 0).any(axis=2).all()
     # the parity rule accepts the simulated rounding
-    assert_close(sim, ref, p.kv_off, "bf16", "simulated bf16 dV")
+    assert_close(sim, ref, p.kv_off, "bf16", "simulated bf16 dV", live_rows(p, "k"))
     # the rms over all rows is the rms over the live rows times sqrt(live / all)
     rms_live = np.sqrt((ref[:Lq] ** 2).mean())
     rms_all = np.sqrt((ref ** 2).mean())
     np.testing.assert_allclose(rms_all, rms_live * np.sqrt(Lq / Lk), rtol=1e-12)
+    assert block_scale(ref, p.kv_off, live_rows(p, "k"))[0, 0] == max(1.0, rms_live)
     assert block_scale(ref, p.kv_off)[0, 0] == max(1.0, rms_live)
     # P's rounding alone moves dV by a few parts in a thousand of the block rms
     err = np.abs(_bf16(P).T @ dO - P.T @ dO)
