@@ -126,6 +126,26 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
                  const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
                  float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Same arguments and results as gdpa_fwd minus
+ * the workspace. The scratch space gdpa_fwd takes from its workspace (work-item list, chunk
+ * counters, partial results of split tiles) is instead one fixed buffer of
+ * GDPA_STATIC_SCRATCH_BYTES inside the library, one per GPU, placed in device memory when the
+ * library's code is loaded on that GPU and held until the process ends; the first call on a GPU
+ * looks up its address there. No call allocates device memory. The GPU is the calling thread's
+ * current device. A problem whose gdpa_workspace_size(p, 0, ...) exceeds
+ * GDPA_STATIC_SCRATCH_BYTES returns GDPA_EWORKSPACE and enqueues nothing; other errors are those
+ * of gdpa_fwd. Every call on one GPU uses that GPU's one buffer, which keeps the last call's
+ * contents (nothing in it has to start at zero): calls that can overlap in time on one GPU
+ * (different streams, different host threads) race on it and must be ordered by the caller, for
+ * example on one stream. Its device error word cannot be read back; gdpa_fwd with a workspace
+ * diagnoses malformed offsets. */
+#define GDPA_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+int32_t gdpa_fwd_static(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                        const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                        void* O, float* lse, void* stream);
+
 /* Waits for `stream`, then reads the device error word of the last call that used `workspace`
  * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err);

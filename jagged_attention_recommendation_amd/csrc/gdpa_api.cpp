@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdpa.h"
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
@@ -155,6 +157,31 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   return L;
 }
 
+// ---- scratch of gdpa_fwd_static: one fixed buffer per GPU in place of a caller workspace.
+// Host code never uses the array's name as an address (on the host it only names the symbol):
+// every launch takes the device address that hipGetSymbolAddress returned for the current GPU.
+static __device__ __align__(256) char scratch[GDPA_STATIC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_DEVICES];  // device address of `scratch` per GPU, null until looked up
+
+// Device address of `scratch` on the current GPU: looked up once per GPU, with that GPU current.
+int32_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GDPA_EHIP;
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return GDPA_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return GDPA_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDPA_OK;
+}
+
 // ---- profiling hook state
 constexpr int PROF_KERNELS = 4;
 constexpr int PROF_MAX = 1024;
@@ -297,6 +324,20 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   else if (p->dtype == GDPA_BF16) e = launch_fwd_bf16(pr, fa, grid, s);
   else e = launch_fwd_mx(pr, fa, grid, s);
   return map_hip(e);
+}
+
+int32_t gdpa_fwd_static(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                        const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                        void* O, float* lse, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (fwd_layout(p).total > GDPA_STATIC_SCRATCH_BYTES) return GDPA_EWORKSPACE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != GDPA_OK) return st;
+  return gdpa_fwd(p, Q, K, V, q_scale, k_scale, v_scale, q_offsets, kv_offsets, bias, O, lse, ws,
+                  GDPA_STATIC_SCRATCH_BYTES, stream);
 }
 
 int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,

@@ -19,7 +19,8 @@ DTYPE = {"f32": 0, "bf16": 1, "mxfp8": 2}
 STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE", 4: "GDPA_EHIP"}
 
 # Every symbol include/gdpa.h declares.
-EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd", "gdpa_bwd",
+EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd",
+           "gdpa_fwd_static", "gdpa_bwd",
            "gdpa_read_device_error", "gdpa_item_list", "gdpa_profile_start", "gdpa_profile_read",
            "gdpa_profile_stop"]
 
@@ -63,6 +64,8 @@ def load():
     lib.gdpa_workspace_size.argtypes = [P, ctypes.c_int32, ctypes.POINTER(sz)]
     lib.gdpa_fwd.restype = ctypes.c_int32
     lib.gdpa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd_static.restype = ctypes.c_int32
+    lib.gdpa_fwd_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdpa_bwd.restype = ctypes.c_int32
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_read_device_error.restype = ctypes.c_int32
@@ -165,6 +168,30 @@ def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=No
                       _stream(stream))
     if st != 0:
         raise GdpaError(st, "gdpa_fwd")
+    return out, lse
+
+
+STATIC_SCRATCH_BYTES = 48 << 20  # GDPA_STATIC_SCRATCH_BYTES
+
+
+def fwd_static(q, k, v, q_offsets, kv_offsets, out, lse=None, *, act="softmax", causal=False,
+               scale=None, bias=None, q_scale=None, k_scale=None, v_scale=None, max_q=0,
+               max_kv=0, stream=None, window=0):
+    """gdpa_fwd_static: the forward with the library's fixed per-GPU scratch instead of a
+    workspace. The caller passes the outputs (out [total_q, H, D]; lse [total_q, H] for softmax,
+    or None); nothing is allocated here or in the library. Calls on one GPU must not overlap in
+    time (they share the scratch)."""
+    lib = load()
+    total_q, H, D = q.shape
+    prob = problem(q_offsets.numel() - 1, H, D, total_q, k.shape[0], dtype=_dtype_of(q), act=act,
+                   causal=causal, scale=scale, bias_buckets=0 if bias is None else bias.shape[1],
+                   max_q=max_q, max_kv=max_kv, window=window)
+    st = lib.gdpa_fwd_static(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                             _ptr(k_scale), _ptr(v_scale), _ptr(q_offsets), _ptr(kv_offsets),
+                             _ptr(bias), _ptr(out), _ptr(lse if act == "softmax" else None),
+                             _stream(stream))
+    if st != 0:
+        raise GdpaError(st, "gdpa_fwd_static")
     return out, lse
 
 
