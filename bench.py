@@ -9,7 +9,16 @@ indexed by clamp(i-j). Inputs are seeded synthetic data, resident in HBM before 
 
 Metric: useful (unpadded) TFLOPS of forward + backward, i.e. matrix-product flops of unmasked
 (query, key) pairs only (4*D per pair and head forward, 10*D backward), divided by the measured
-step time. Prints one JSON line on stdout.
+step time. Prints one JSON line on stdout:
+  - value / ms_per_step: K steps back to back, timed by the host clock between two device
+    synchronisations (inputs resident, caches warm from the previous step);
+  - cold: each gdpa_fwd and gdpa_bwd call timed alone with device events after a 512 MiB write
+    that evicts the 256 MB last-level cache and the L2s; medians (and minima) over the reps;
+  - warm_per_call: the same per-call medians without the eviction;
+  - roofline: the dominant kernel's algorithmic flops (or bytes) per launch over its average
+    launch time, from HIP events the library records on the launch stream over the timed steps;
+  - workloads: the same figures for the cross-attention, PMA and MX-fp8 workloads;
+  - cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,6 +33,7 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLUSH_BYTES = 512 << 20     # twice the last-level (Infinity) cache
 
 WORKLOADS = {
     2: "jfa_softmax_causal_bias_B64_H4_D128_L1-2048_bf16",
@@ -41,7 +51,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
-                    help="workload (default: the causal JFA softmax workload)")
+                    help="workload of the headline line (default: the causal JFA workload)")
+    ap.add_argument("--reps", type=int, default=20, help="per-call reps for the medians")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads' summaries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -96,8 +109,8 @@ def prefix_problem(p, n):
 def cpu_baseline(p, target_s):
     """Time the fp64 oracle (forward + backward) on the first samples of the same workload.
 
-    A one-sample run calibrates the oracle's rate; the sample is then grown to about target_s
-    of work and timed in one call (OpenMP over samples x heads on every host thread).
+    A calibration run sizes the sample to about target_s of work, which is then timed in one
+    call (OpenMP over samples x heads on every host thread).
     """
     import oracle
     from jagged_attention_recommendation_amd import inputs, workload
@@ -114,7 +127,6 @@ def cpu_baseline(p, target_s):
                    scale=sp.scale, bias=bias, nthreads=nthreads)
         return time.perf_counter() - t0
 
-    # calibrate on enough samples to occupy every thread, then size the timed sample
     n0 = max(1, min(p.B, -(-nthreads // p.H)))
     sp0 = prefix_problem(p, n0)
     t_cal = run(sp0)
@@ -133,6 +145,216 @@ def cpu_baseline(p, target_s):
                       f"{secs:.1f} s wall"}
 
 
+class Flusher:
+    """Writes a buffer twice the size of the last-level cache, so the next call starts cold."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
+
+
+def per_call_medians(torch, calls, reps, flush=None):
+    """Median and minimum device time (ms) of each call in `calls` (name -> fn), each timed
+    alone between two events on the current stream; with `flush`, the cache is evicted before
+    every call (outside the events)."""
+    times = {k: [] for k in calls}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(reps):
+        for name, fn in calls.items():
+            if flush is not None:
+                flush()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            ev[1].synchronize()
+            times[name].append(ev[0].elapsed_time(ev[1]))
+    return {k: (float(np.median(v)), float(np.min(v))) for k, v in times.items()}
+
+
+def timed_steps(torch, gdpa, step, steps, kernels):
+    """Host-clock time of `steps` back-to-back steps between two synchronisations, and every
+    selected kernel's average launch time from the library's HIP events over the same region."""
+    torch.cuda.synchronize()
+    gdpa.profile_start(kernels)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdpa.profile_stop()
+    kern_ms = {}
+    for kern in kernels:
+        n, ms = gdpa.profile_read(kern)
+        kern_ms[kern] = ms / max(n, 1)
+    return (t1 - t0) * 1e3 / steps, kern_ms
+
+
+def run_bf16(args, config, torch, gdpa, inputs, workload, dev, flush, window=0, steps=None,
+             reps=None):
+    """Forward + backward of a bf16 workload: warm K-step rate, per-call medians, per-kernel
+    times and the dominant kernel's roofline."""
+    steps = args.steps if steps is None else steps
+    reps = args.reps if reps is None else reps
+    p = inputs.config_problem(config)
+
+    def up_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # the PMA workload reads one shared block of seed queries (dQ is that block's gradient)
+    shared = p.seeds is not None
+    Q = up_bf16(p.seeds if shared else p.Q)
+    K, V, dO = up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
+    q_off = torch.from_numpy(p.q_off).to(dev)
+    kv_off = torch.from_numpy(p.kv_off).to(dev)
+    bias = torch.from_numpy(p.bias).to(dev) if p.bias is not None else None
+    nb = 0 if bias is None else bias.shape[1]
+    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
+    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, act=p.act, causal=p.causal,
+                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv,
+                        window=window, q_shared=shared)
+    ws_f = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
+    O = torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev)
+    lse = (torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev)
+           if p.act == "softmax" else None)
+    grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
+             torch.empty_like(bias) if bias is not None else None)
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv,
+              window=window, q_shared=shared)
+
+    def fwd():
+        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
+
+    def bwd():
+        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("fwd", "dq", "dkdv"))
+    cold = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps, flush)
+    warm = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps)
+    for t in (O, *grads[:3]):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError("non-finite output")
+
+    f_fwd = workload.useful_flops(p, "fwd", window)
+    f_bwd = workload.useful_flops(p, "bwd", window)
+    tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 2)
+
+    def split(m):
+        return {"fwd_ms": round(m["fwd"][0], 4), "bwd_ms": round(m["bwd"][0], 4),
+                "fwd_ms_min": round(m["fwd"][1], 4), "bwd_ms_min": round(m["bwd"][1], 4),
+                "fwd_tflops": tf(f_fwd, m["fwd"][0]), "bwd_tflops": tf(f_bwd, m["bwd"][0]),
+                "fwdbwd_tflops": tf(f_fwd + f_bwd, m["fwd"][0] + m["bwd"][0]),
+                "fwd_gbs": round(workload.fwd_bytes(p) / (m["fwd"][0] * 1e-3) / 1e9, 1),
+                "bwd_gbs": round(workload.bwd_bytes(p) / (m["bwd"][0] * 1e-3) / 1e9, 1),
+                "reps": reps}
+
+    dom = max(kern_ms, key=kern_ms.get)
+    if config in HBM_BOUND:
+        # short keys (cross) or short queries (PMA): the kernels stream the long side once
+        achieved = workload.kernel_bytes(p, dom) / (kern_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = dominant_kernel_flops(p, dom, window) / (kern_ms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roofline.update({"traffic": None if window else measured_traffic(config, dom),
+                     "avg_launch_ms": round(kern_ms[dom], 4),
+                     "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+                     "kernel_tflops": {k: round(dominant_kernel_flops(p, k, window)
+                                                / (v * 1e-3) / 1e12, 1)
+                                       for k, v in kern_ms.items()},
+                     "kernel_gbs": {k: round(workload.kernel_bytes(p, k) / (v * 1e-3) / 1e9, 1)
+                                    for k, v in kern_ms.items()}})
+    res = {"p": p, "ms_step": ms_step, "value": (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12,
+           "cold": split(cold), "warm": split(warm), "roofline": roofline, "nb": nb,
+           "max_q": max_q}
+    del Q, K, V, dO, O, lse, grads, ws_f, ws_b
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=None):
+    """MX-fp8 forward workload: one step = the causal forward with softmax and with SiLU on the
+    same e4m3 + e8m0 inputs (scaled fp8 products for Q.K^T, bf16 for P.V, fp32 accumulation)."""
+    steps = args.steps if steps is None else steps
+    reps = args.reps if reps is None else reps
+    p = inputs.config_problem(5)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    Q, K, V = u8(p.Q), u8(p.K), u8(p.V)
+    qs, ks, vs = u8(p.q_scale), u8(p.k_scale), u8(p.v_scale)
+    q_off = torch.from_numpy(p.q_off).to(dev)
+    kv_off = torch.from_numpy(p.kv_off).to(dev)
+    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
+    acts = ("softmax", "silu")
+    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, dtype="mxfp8", act="softmax",
+                        causal=True, scale=p.scale, bias_buckets=0, max_q=max_q, max_kv=max_kv)
+    ws = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
+    O = {a: torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev) for a in acts}
+    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev)
+
+    def call(a):
+        return lambda: gdpa.fwd(Q, K, V, q_off, kv_off, act=a, causal=True, scale=p.scale,
+                                q_scale=qs, k_scale=ks, v_scale=vs, max_q=max_q, max_kv=max_kv,
+                                out=O[a], lse=lse if a == "softmax" else None, workspace=ws)
+
+    calls = {a: call(a) for a in acts}
+
+    def step():
+        for a in acts:
+            calls[a]()
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("fwd",))
+    cold = per_call_medians(torch, calls, reps, flush)
+    warm = per_call_medians(torch, calls, reps)
+    for a in acts:
+        if not torch.isfinite(O[a].float()).all():
+            raise RuntimeError("non-finite output")
+    f_fwd = workload.useful_flops(p, "fwd")
+    tf = lambda ms: round(f_fwd / (ms * 1e-3) / 1e12, 2)
+    achieved = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
+    res = {"p": p, "ms_step": ms_step, "value": len(acts) * f_fwd / (ms_step * 1e-3) / 1e12,
+           "cold": {f"{a}_ms": round(cold[a][0], 4) for a in acts}
+           | {f"{a}_tflops": tf(cold[a][0]) for a in acts} | {"reps": reps},
+           "warm": {f"{a}_ms": round(warm[a][0], 4) for a in acts}
+           | {f"{a}_tflops": tf(warm[a][0]) for a in acts} | {"reps": reps},
+           "roofline": {"bound": "mfma", "kernel": "fwd", "achieved": round(achieved, 2),
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                        "avg_launch_ms": round(kern_ms["fwd"], 4),
+                        "hbm_gbs": round(workload.fwd_bytes(p) / (kern_ms["fwd"] * 1e-3) / 1e9,
+                                         1)}}
+    del Q, K, V, qs, ks, vs, O, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(config, r):
+    """The figures of a non-headline workload on the headline line."""
+    s = {"workload": WORKLOADS[config], "ms_per_step": round(r["ms_step"], 4),
+         "tflops": round(r["value"], 2), "cold": r["cold"], "warm_per_call": r["warm"],
+         "dominant": {k: r["roofline"][k] for k in ("kernel", "bound", "achieved", "unit",
+                                                    "frac", "avg_launch_ms")}}
+    if "kernel_avg_ms" in r["roofline"]:
+        s["kernel_avg_ms"] = r["roofline"]["kernel_avg_ms"]
+        s["kernel_gbs"] = r["roofline"]["kernel_gbs"]
+    return s
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -148,80 +370,18 @@ def main():
         sys.exit(1)
     gdpa.load()
     dev = torch.device("cuda:0")
-    if args.config == 5:
-        return main_mx(args, torch, gdpa, inputs, workload, dev)
     if args.window and args.config != 2:
         print("--window applies to the causal JFA workload (--config 2)", file=sys.stderr)
         sys.exit(2)
+    flush = Flusher(torch, dev)
     win = args.window
-    p = inputs.config_problem(args.config)
-
-    def up_bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    # the PMA workload reads one shared block of seed queries (dQ is that block's gradient)
-    shared = p.seeds is not None
-    Q = up_bf16(p.seeds if shared else p.Q)
-    K, V, dO = up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
-    q_off = torch.from_numpy(p.q_off).to(dev)
-    kv_off = torch.from_numpy(p.kv_off).to(dev)
-    bias = torch.from_numpy(p.bias).to(dev) if p.bias is not None else None
-    nb = 0 if bias is None else bias.shape[1]
-    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
-    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, act=p.act, causal=p.causal,
-                        scale=p.scale, bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=win,
-                        q_shared=shared)
-    ws_f = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
-    O = torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev) if p.act == "softmax" else None
-    grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V),
-             torch.empty_like(bias) if bias is not None else None)
-    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv,
-              window=win, q_shared=shared)
-
-    def step():
-        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
-        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region; the library brackets each launch of the main kernels with HIP events on
-    # the launch stream, which gives every kernel's average duration over this same region
-    kernels = ("fwd", "dq", "dkdv")
-    torch.cuda.synchronize()
-    gdpa.profile_start(kernels)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gdpa.profile_stop()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = {}
-    for kern in kernels:
-        n, ms = gdpa.profile_read(kern)
-        kern_ms[kern] = ms / max(n, 1)
-
-    # forward-only and backward-only splits (secondary numbers)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    fwd_ms = bwd_ms = 0.0
-    for _ in range(args.steps):
-        ev[0].record()
-        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
-        ev[1].record()
-        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
-        ev[2].record()
-        torch.cuda.synchronize()
-        fwd_ms += ev[0].elapsed_time(ev[1])
-        bwd_ms += ev[1].elapsed_time(ev[2])
-    fwd_ms /= args.steps
-    bwd_ms /= args.steps
-    for t in (O, *grads[:3]):
-        if not torch.isfinite(t.float()).all():
-            raise RuntimeError("non-finite output")
+    print(f"[bench] workload {args.config} ({WORKLOADS[args.config]})", file=sys.stderr,
+          flush=True)
+    if args.config == 5:
+        r = run_mx(args, torch, gdpa, inputs, workload, dev, flush)
+    else:
+        r = run_bf16(args, args.config, torch, gdpa, inputs, workload, dev, flush, window=win)
+    p = r["p"]
 
     if args.copy_calibration:
         # plain copy of known size, for scaling the HBM byte counters of a profiling run
@@ -230,114 +390,60 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    f_fwd = workload.useful_flops(p, "fwd", win)
-    f_bwd = workload.useful_flops(p, "bwd", win)
-    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-
-    dom = max(kern_ms, key=kern_ms.get)
-    if args.config in HBM_BOUND:
-        # short keys (cross) or short queries (PMA): the kernels stream the long side once
-        achieved = workload.kernel_bytes(p, dom) / (kern_ms[dom] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = dominant_kernel_flops(p, dom, win) / (kern_ms[dom] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roofline.update({"traffic": None if win else measured_traffic(args.config, dom),
-                     "avg_launch_ms": round(kern_ms[dom], 4),
-                     "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()},
-                     "kernel_gbs": {k: round(workload.kernel_bytes(p, k) / (v * 1e-3) / 1e9, 1)
-                                    for k, v in kern_ms.items()}})
-
+    mx = args.config == 5
     out = {
-        "metric": "useful (unpadded) TFLOPS fwd+bwd, jagged sparsity 0.5, and % of MFMA peak",
-        "value": round(value, 2),
+        "metric": ("useful (unpadded) TFLOPS fwd, MX-fp8 (softmax + SiLU), and % of fp8 MFMA peak"
+                   if mx else
+                   "useful (unpadded) TFLOPS fwd+bwd, jagged sparsity 0.5, and % of MFMA peak"),
+        "value": round(r["value"], 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8_e4m3" if mx else "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config] + (f"_window{win}" if win else ""),
-                   "B": p.B, "H": p.H, "D": p.D, "window": win,
-                   "total_tokens": p.total_q, "causal": p.causal, "act": p.act,
-                   "bias_buckets": nb,
-                   "token_sparsity": round(1 - p.total_q / (p.B * max(max_q, 1)), 4)},
-        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "roofline": roofline,
     }
-    if not args.no_cpu_baseline and not win:
+    if mx:
+        out["config"] = {"workload": WORKLOADS[5], "B": p.B, "H": p.H, "D": p.D,
+                         "total_tokens": p.total_q, "causal": True, "acts": ["softmax", "silu"]}
+        out["pct_fp8_peak"] = round(100 * r["value"] / PEAK_FP8_TFLOPS, 2)
+    else:
+        out["config"] = {"workload": WORKLOADS[args.config] + (f"_window{win}" if win else ""),
+                         "B": p.B, "H": p.H, "D": p.D, "window": win,
+                         "total_tokens": p.total_q, "causal": p.causal, "act": p.act,
+                         "bias_buckets": r["nb"],
+                         "token_sparsity": round(1 - p.total_q / (p.B * max(r["max_q"], 1)), 4)}
+        out["pct_bf16_peak"] = round(100 * r["value"] / PEAK_BF16_TFLOPS, 2)
+        out["fwd_tflops"] = r["warm"]["fwd_tflops"]
+        out["bwd_tflops"] = r["warm"]["bwd_tflops"]
+        out["fwd_ms"] = r["warm"]["fwd_ms"]
+        out["bwd_ms"] = r["warm"]["bwd_ms"]
+    out["cold"] = r["cold"]
+    out["warm_per_call"] = r["warm"]
+    out["roofline"] = r["roofline"]
+    if not args.no_others:
+        others = {}
+        for c in (2, 3, 4, 5):
+            if c == args.config:
+                continue
+            print(f"[bench] workload {c} ({WORKLOADS[c]})", file=sys.stderr, flush=True)
+            if c == 5:
+                rc = run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=10, reps=10)
+            else:
+                rc = run_bf16(args, c, torch, gdpa, inputs, workload, dev, flush, steps=10,
+                              reps=10)
+            others[str(c)] = summary(c, rc)
+            del rc
+        out["workloads"] = others
+    if not args.no_cpu_baseline and not win and not mx:
+        print("[bench] oracle on the host cores", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
-
-
-def main_mx(args, torch, gdpa, inputs, workload, dev):
-    """MX-fp8 forward workload: one step = the causal forward with softmax and with SiLU on the
-    same e4m3 + e8m0 inputs (scaled fp8 products for Q.K^T, bf16 for P.V, fp32 accumulation)."""
-    p = inputs.config_problem(5)
-    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    Q, K, V = u8(p.Q), u8(p.K), u8(p.V)
-    qs, ks, vs = u8(p.q_scale), u8(p.k_scale), u8(p.v_scale)
-    q_off = torch.from_numpy(p.q_off).to(dev)
-    kv_off = torch.from_numpy(p.kv_off).to(dev)
-    max_q, max_kv = int(p.lq.max()), int(p.lk.max())
-    acts = ("softmax", "silu")
-    prob = gdpa.problem(p.B, p.H, p.D, p.total_q, p.total_kv, dtype="mxfp8", act="softmax",
-                        causal=True, scale=p.scale, bias_buckets=0, max_q=max_q, max_kv=max_kv)
-    ws = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device=dev)
-    O = {a: torch.empty((p.total_q, p.H, p.D), dtype=torch.bfloat16, device=dev) for a in acts}
-    lse = torch.empty((p.total_q, p.H), dtype=torch.float32, device=dev)
-
-    def step():
-        for a in acts:
-            gdpa.fwd(Q, K, V, q_off, kv_off, act=a, causal=True, scale=p.scale, q_scale=qs,
-                     k_scale=ks, v_scale=vs, max_q=max_q, max_kv=max_kv, out=O[a],
-                     lse=lse if a == "softmax" else None, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    gdpa.profile_start(("fwd",))
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gdpa.profile_stop()
-    n, ms = gdpa.profile_read("fwd")
-    kern_ms = ms / max(n, 1)
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    for a in acts:
-        if not torch.isfinite(O[a].float()).all():
-            raise RuntimeError("non-finite output")
-    f_fwd = workload.useful_flops(p, "fwd")
-    value = len(acts) * f_fwd / (ms_step * 1e-3) / 1e12
-    achieved = f_fwd / (kern_ms * 1e-3) / 1e12
-    out = {
-        "metric": "useful (unpadded) TFLOPS fwd, MX-fp8 (softmax + SiLU), and % of fp8 MFMA peak",
-        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8_e4m3", "data": "synthetic",
-        "config": {"workload": WORKLOADS[5], "B": p.B, "H": p.H, "D": p.D,
-                   "total_tokens": p.total_q, "causal": True, "acts": list(acts)},
-        "pct_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "fwd", "achieved": round(achieved, 2),
-                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                     "avg_launch_ms": round(kern_ms, 4),
-                     "hbm_gbs": round(workload.fwd_bytes(p) / (kern_ms * 1e-3) / 1e9, 1)},
-    }
     print(json.dumps(out), flush=True)
 
 

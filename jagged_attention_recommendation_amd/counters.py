@@ -9,8 +9,12 @@ while the sources are unchanged.
     python -m jagged_attention_recommendation_amd.counters FETCH_DIR WRITE_DIR > summary.txt
 
 A second summary reads one run of shader-sequencer counters (`--sq DIR`): per kernel family the
-mean per dispatch of each counter and the MFMA busy fraction
-SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), the same ratio as rocprofv3's MfmaUtil.
+mean per dispatch of each counter and the MFMA busy fraction. SQ_VALU_MFMA_BUSY_CYCLES sums the
+cycles in which a SIMD's matrix unit was busy over all 1024 SIMDs; GRBM_GUI_ACTIVE, as rocprofv3
+reports it on MI355X, sums the GPU-busy clock over the 8 XCDs (a 137 us launch reads about
+2.4e6, eight times its ~3e5 cycles). The busy fraction is therefore
+SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024): the share of the launch's cycles in
+which the average SIMD's matrix unit worked.
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNELS = {"fwd": ("fwd_dl_kernel", "fwd_kernel"), "dq": ("dq_dl_kernel", "dq_kernel"),
            "dkdv": ("dkdv_dl_kernel", "dkdv_kernel")}
 SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8      # accelerator complex dies; GRBM_GUI_ACTIVE is summed over them
 
 
 def family(kernel_name):
@@ -110,7 +115,7 @@ def summarize_sq(run_dir):
         mean["dispatches"] = len(ds)
         if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE", 0) > 0:
             mean["mfma_busy_pct"] = round(100.0 * mean["SQ_VALU_MFMA_BUSY_CYCLES"]
-                                          / (mean["GRBM_GUI_ACTIVE"] * SIMDS), 2)
+                                          / (mean["GRBM_GUI_ACTIVE"] / XCDS * SIMDS), 2)
         out[short] = mean
     return out
 

@@ -20,6 +20,7 @@ e4m3 with ties to even and saturated to +-448.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -97,7 +98,32 @@ def e4m3_encode(y):
 
 
 def mx_quantize(x, block=32):
-    """x: float array [..., D] -> (e4m3 codes [..., D] uint8, e8m0 scales [..., D/block] uint8)."""
+    """x: float array [..., D] -> (e4m3 codes [..., D] uint8, e8m0 scales [..., D/block] uint8).
+
+    Every block is quantised on its own, so large arrays are cut into row chunks that a thread
+    pool quantises side by side (numpy releases the interpreter lock inside these operations);
+    the bits are those of one pass over the whole array."""
+    x = np.asarray(x)
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    if rows >= 1 << 16:
+        import concurrent.futures as cf
+        flat = x.reshape(rows, x.shape[-1])
+        step = 1 << 14
+        codes = np.empty(flat.shape, dtype=np.uint8)
+        scales = np.empty((rows, x.shape[-1] // block), dtype=np.uint8)
+
+        def run(r0):
+            c, s = _mx_quantize(flat[r0:r0 + step], block)
+            codes[r0:r0 + step], scales[r0:r0 + step] = c, s
+
+        workers = min(16, os.cpu_count() or 1)
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, range(0, rows, step)))
+        return codes.reshape(x.shape), scales.reshape(x.shape[:-1] + (x.shape[-1] // block,))
+    return _mx_quantize(x, block)
+
+
+def _mx_quantize(x, block):
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
     assert D % block == 0

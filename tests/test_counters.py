@@ -62,7 +62,8 @@ def test_kernel_bytes_count_each_operand_once():
 
 def test_sq_summary_mfma_busy(tmp_path):
     """Shader-sequencer summary: SQ counters summed over instances, GRBM clock maxed, and the
-    MFMA busy fraction over all 1024 SIMDs."""
+    MFMA busy fraction over all 1024 SIMDs against the clock of one XCD (GRBM_GUI_ACTIVE sums
+    the 8 XCDs' clocks)."""
     d = tmp_path / "sq"
     d.mkdir()
     rows = []
@@ -80,7 +81,7 @@ def test_sq_summary_mfma_busy(tmp_path):
     s = counters.summarize_sq(d)
     assert s["fwd"]["dispatches"] == 2
     assert s["fwd"]["GRBM_GUI_ACTIVE"] == 1000 and s["fwd"]["SQ_VALU_MFMA_BUSY_CYCLES"] == 1024 * 100
-    assert s["fwd"]["mfma_busy_pct"] == 10.0
+    assert s["fwd"]["mfma_busy_pct"] == 80.0  # 1024 * 100 / (1000 / 8 * 1024)
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -905,3 +905,12 @@ def test_block_attention_gradient_finite_differences(act):
                        loss(minus["Q"], minus["K"], minus["V"])) / (2 * h)
         err = np.abs(fd - g[key]) / np.maximum(1.0, np.abs(g[key]))
         assert err.max() < 1e-6, (name, err.max())
+
+
+def test_mx_quantize_threaded_chunks_give_the_same_bits():
+    """Large arrays are quantised in row chunks by a thread pool; the bits equal one pass."""
+    rng = np.random.default_rng(90)
+    x = rng.standard_normal((70000, 2, 64), dtype=np.float32) * 3.0
+    codes, scales = inputs.mx_quantize(x)
+    c1, s1 = inputs._mx_quantize(x, 32)
+    assert np.array_equal(codes, c1) and np.array_equal(scales, s1)
