@@ -17,7 +17,8 @@ step time. Prints one JSON line on stdout:
   - warm_per_call: the same per-call medians without the eviction;
   - roofline: the dominant kernel's algorithmic flops (or bytes) per launch over its average
     launch time, from HIP events the library records on the launch stream over the timed steps;
-  - workloads: the same figures for the cross-attention, PMA and MX-fp8 workloads;
+  - workloads: the same figures for the cross-attention, PMA, MX-fp8 and block-aligned rotary
+    workloads;
   - cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -40,6 +41,7 @@ WORKLOADS = {
     3: "gdpa_cross_gelu_B256_H4_D128_Lq64-4096_Lk8-64_bf16",
     4: "gdpa_pma_silu_B512_H8_D64_Lq32_Lk_lognormal_bf16",
     5: "mxfp8_causal_softmax_and_silu_fwd_B128_H8_D128_L_lognormal",
+    6: "block64_rope_softmax_causal_B64_H4_D128_L1-2048_bf16",
 }
 # Workloads bound by HBM bandwidth (short key or query sequences): their roofline is in GB/s.
 HBM_BOUND = (3, 4)
@@ -343,6 +345,66 @@ def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=Non
     return res
 
 
+def run_block(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=None):
+    """Block-aligned attention with rotary embeddings on the JFA workload's samples (B = 64,
+    H = 4, D = 128, lengths uniform in [1, 2048], causal softmax, no bias): fixed 64-token blocks,
+    each attending within itself. HBM-bound (every block reads Q, K, V once and writes O), so
+    the roofline is in GB/s."""
+    steps = args.steps if steps is None else steps
+    reps = args.reps if reps is None else reps
+    p = inputs.config_problem(2)
+
+    def up_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V, dO = up_bf16(p.Q), up_bf16(p.K), up_bf16(p.V), up_bf16(p.dO)
+    off = torch.from_numpy(p.q_off).to(dev)
+    prob = gdpa.block_problem(p.B, p.H, p.D, p.total_q, act=p.act, causal=True, scale=p.scale)
+    ws = torch.empty(gdpa.block_workspace_size(prob), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(Q)
+    grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    kw = dict(act=p.act, causal=True, scale=p.scale, rotary=True)
+
+    def fwd():
+        gdpa.block_fwd(Q, K, V, off, out=O, workspace=ws, **kw)
+
+    def bwd():
+        gdpa.block_bwd(Q, K, V, dO, off, grads=grads, workspace=ws, **kw)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("block_fwd", "block_bwd"))
+    cold = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps, flush)
+    warm = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps)
+    for t in (O, *grads):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError("non-finite output")
+    fb, bb = workload.block_bytes(p, "fwd"), workload.block_bytes(p, "bwd")
+    ff, bf = workload.block_flops(p, "fwd"), workload.block_flops(p, "bwd")
+    gbs = lambda by, ms: round(by / (ms * 1e-3) / 1e9, 1)
+
+    def split(m):
+        return {"fwd_ms": round(m["fwd"][0], 4), "bwd_ms": round(m["bwd"][0], 4),
+                "fwd_gbs": gbs(fb, m["fwd"][0]), "bwd_gbs": gbs(bb, m["bwd"][0]), "reps": reps}
+
+    kgbs = {"block_fwd": gbs(fb, kern_ms["block_fwd"]), "block_bwd": gbs(bb, kern_ms["block_bwd"])}
+    dom = max(kern_ms, key=kern_ms.get)
+    res = {"p": p, "ms_step": ms_step, "value": (ff + bf) / (ms_step * 1e-3) / 1e12,
+           "cold": split(cold), "warm": split(warm),
+           "roofline": {"bound": "hbm", "kernel": dom, "achieved": kgbs[dom], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(kgbs[dom] / PEAK_HBM_GBS, 4),
+                        "traffic": None, "avg_launch_ms": round(kern_ms[dom], 4),
+                        "kernel_avg_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+                        "kernel_gbs": kgbs}}
+    del Q, K, V, dO, O, grads, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def summary(config, r):
     """The figures of a non-headline workload on the headline line."""
     s = {"workload": WORKLOADS[config], "ms_per_step": round(r["ms_step"], 4),
@@ -379,6 +441,8 @@ def main():
           flush=True)
     if args.config == 5:
         r = run_mx(args, torch, gdpa, inputs, workload, dev, flush)
+    elif args.config == 6:
+        r = run_block(args, torch, gdpa, inputs, workload, dev, flush)
     else:
         r = run_bf16(args, args.config, torch, gdpa, inputs, workload, dev, flush, window=win)
     p = r["p"]
@@ -393,6 +457,7 @@ def main():
         del src, dst
 
     mx = args.config == 5
+    blk = args.config == 6
     out = {
         "metric": ("useful (unpadded) TFLOPS fwd, MX-fp8 (softmax + SiLU), and % of fp8 MFMA peak"
                    if mx else
@@ -413,6 +478,10 @@ def main():
         out["config"] = {"workload": WORKLOADS[5], "B": p.B, "H": p.H, "D": p.D,
                          "total_tokens": p.total_q, "causal": True, "acts": ["softmax", "silu"]}
         out["pct_fp8_peak"] = round(100 * r["value"] / PEAK_FP8_TFLOPS, 2)
+    elif blk:
+        out["config"] = {"workload": WORKLOADS[6], "B": p.B, "H": p.H, "D": p.D, "block": 64,
+                         "rotary": True, "total_tokens": p.total_q, "causal": True,
+                         "act": p.act}
     else:
         out["config"] = {"workload": WORKLOADS[args.config] + (f"_window{win}" if win else ""),
                          "B": p.B, "H": p.H, "D": p.D, "window": win,
@@ -429,19 +498,21 @@ def main():
     out["roofline"] = r["roofline"]
     if not args.no_others:
         others = {}
-        for c in (2, 3, 4, 5):
+        for c in (2, 3, 4, 5, 6):
             if c == args.config:
                 continue
             print(f"[bench] workload {c} ({WORKLOADS[c]})", file=sys.stderr, flush=True)
             if c == 5:
                 rc = run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=10, reps=10)
+            elif c == 6:
+                rc = run_block(args, torch, gdpa, inputs, workload, dev, flush, steps=10, reps=10)
             else:
                 rc = run_bf16(args, c, torch, gdpa, inputs, workload, dev, flush, steps=10,
                               reps=10)
             others[str(c)] = summary(c, rc)
             del rc
         out["workloads"] = others
-    if not args.no_cpu_baseline and not win and not mx:
+    if not args.no_cpu_baseline and not win and not mx and not blk:
         print("[bench] oracle on the host cores", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -146,6 +146,43 @@ int32_t gdpa_fwd_static(const gdpa_problem* p, const void* Q, const void* K, con
                         const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
                         void* O, float* lse, void* stream);
 
+/* Block-aligned attention with rotary embeddings (same page, block-attention paragraph): every
+ * sample is cut into fixed blocks of `block` consecutive tokens (the last one shorter), and each
+ * block attends only within itself, with the softmax or GDPA activation of the other entry points
+ * and no bias table. With rotary = 1, Q and K are first rotated at their positions in the sample
+ * (counted from its first token): the pair (2m, 2m+1) of a row at position p turns by
+ * p * rope_base^(-2m/D) radians (the rotary form of Su et al.); the backward turns the gradients
+ * of Q and K back (the transpose) in fp32. causal = 1 keeps key j <= query i inside a block.
+ * A block fits one tile, so the kernels take the softmax's row maximum and sum in one pass and
+ * form the backward's row term from P and dP in the tile: no logsumexp is written, and the
+ * backward needs neither O nor lse.
+ * Supported: GDPA_BF16, D = 128, block = 64, scale > 0 (else GDPA_ENOTSUP). Q, K, V, O, dO, dQ,
+ * dK, dV are [total, H, 128] bf16 over one offsets array [B + 1]. Memory, workspace, stream and
+ * error conventions are those of gdpa_fwd / gdpa_bwd; malformed offsets set device error 3
+ * (the one offsets array is checked as both the query and the key offsets). */
+typedef struct {
+  int32_t B;         /* samples (>= 0) */
+  int32_t H;         /* heads (>= 1) */
+  int32_t D;         /* head dimension: 128 */
+  int32_t dtype;     /* gdpa_dtype: GDPA_BF16 */
+  int64_t total;     /* rows of every tensor (= offsets[B]) */
+  int32_t act;       /* gdpa_act */
+  int32_t causal;    /* 0 or 1: keep j <= i inside a block */
+  float scale;       /* s = scale * q.k */
+  int32_t block;     /* tokens per block: 64 */
+  int32_t rotary;    /* 0 or 1 */
+  float rope_base;   /* rotary base (> 1), e.g. 10000 */
+} gdpa_block_problem;
+
+int32_t gdpa_block_workspace_size(const gdpa_block_problem* p, size_t* bytes);
+int32_t gdpa_block_fwd(const gdpa_block_problem* p, const void* Q, const void* K, const void* V,
+                       const int32_t* offsets, void* O, void* workspace, size_t workspace_bytes,
+                       void* stream);
+/* Gradients of sum(dO * O) with respect to Q, K and V (bf16, overwritten). */
+int32_t gdpa_block_bwd(const gdpa_block_problem* p, const void* Q, const void* K, const void* V,
+                       const void* dO, const int32_t* offsets, void* dQ, void* dK, void* dV,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Waits for `stream`, then reads the device error word of the last call that used `workspace`
  * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err);
@@ -167,7 +204,8 @@ int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, siz
 /* Profiling aid for benchmarks (not thread-safe). Between gdpa_profile_start(mask) and
  * gdpa_profile_stop(), every launch of a selected kernel is bracketed by a pair of HIP events
  * recorded on its launch stream. Bit k of mask selects kernel k: 0 = forward main kernel,
- * 1 = backward dQ kernel, 2 = backward dK/dV kernel, 3 = scheduler. At most 1024 launches per
+ * 1 = backward dQ kernel, 2 = backward dK/dV kernel, 3 = scheduler, 4 / 5 = block-aligned
+ * forward / backward. At most 1024 launches per
  * kernel are timed. gdpa_profile_read() waits for the recorded events of one kernel and returns
  * how many of its launches were timed and their summed duration in milliseconds. Events are
  * created on the first start and kept for the life of the process. */

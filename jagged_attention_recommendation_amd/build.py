@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libgdpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["gdpa_api.cpp", "gdpa_sched.hip", "gdpa_fwd_bf16.hip", "gdpa_fwd_mx.hip",
-           "gdpa_f32.hip", "gdpa_bwd_bf16.hip"]
+           "gdpa_f32.hip", "gdpa_bwd_bf16.hip", "gdpa_block.hip"]
 
 # No packed fp32 instructions; no NaN canonicalisation in min/max (the kernels never form NaNs
 # from finite inputs, and masking uses -inf, which stays honoured).

@@ -183,11 +183,11 @@ int32_t static_scratch(void** out) {
 }
 
 // ---- profiling hook state
-constexpr int PROF_KERNELS = 4;
+constexpr int PROF_KERNELS = 6;
 constexpr int PROF_MAX = 1024;
 struct ProfState {
   int mask = 0;
-  int n[PROF_KERNELS] = {0, 0, 0, 0};
+  int n[PROF_KERNELS] = {};
   bool created = false;
   hipEvent_t ev[PROF_KERNELS][2 * PROF_MAX];
 };
@@ -204,11 +204,11 @@ int32_t map_hip(hipError_t e) {
 namespace gdpa {
 void prof_before(int kernel, hipStream_t s) {
   if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
-  hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel]], s);
+  (void)hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel]], s);
 }
 void prof_after(int kernel, hipStream_t s) {
   if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
-  hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel] + 1], s);
+  (void)hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel] + 1], s);
   ++g_prof.n[kernel];
 }
 }  // namespace gdpa
@@ -447,6 +447,100 @@ int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, siz
     *capacity = list == 0 ? L.max_q_items : L.max_k_items;
   }
   return GDPA_OK;
+}
+
+namespace {
+
+int32_t check_block_problem(const gdpa_block_problem* p) {
+  if (p == nullptr) return GDPA_EINVAL;
+  if (p->B < 0 || p->H < 1 || p->total < 0 || p->total >= (int64_t)1 << 31) return GDPA_EINVAL;
+  if (p->dtype < GDPA_F32 || p->dtype > GDPA_MXFP8_E4M3) return GDPA_EINVAL;
+  if (p->act < GDPA_ACT_SOFTMAX || p->act > GDPA_ACT_SILU) return GDPA_EINVAL;
+  if (p->causal != 0 && p->causal != 1) return GDPA_EINVAL;
+  if (p->rotary != 0 && p->rotary != 1) return GDPA_EINVAL;
+  if (!isfinite(p->scale) || !isfinite(p->rope_base)) return GDPA_EINVAL;
+  if (p->rotary && !(p->rope_base > 1.0f)) return GDPA_EINVAL;
+  if (p->dtype != GDPA_BF16 || p->D != 128 || p->block != BLOCK_TOKENS) return GDPA_ENOTSUP;
+  if (!(p->scale > 0.0f)) return GDPA_ENOTSUP;
+  if ((int64_t)p->H * p->D > (1 << 20)) return GDPA_ENOTSUP;
+  return GDPA_OK;
+}
+
+struct BlockLayout {
+  size_t items, total;
+  int64_t max_items;
+};
+
+BlockLayout block_layout(const gdpa_block_problem* p) {
+  BlockLayout L;
+  L.max_items = items_bound(p->total, p->B, p->H, BLOCK_TOKENS, 0);
+  L.items = ALIGN;
+  L.total = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  return L;
+}
+
+// Builds the item list (one per block and head), then runs the forward or backward kernel.
+int32_t block_call(const gdpa_block_problem* p, const int32_t* offsets, BlockArgs& ba,
+                   void* workspace, size_t workspace_bytes, void* stream, bool bwd) {
+  const BlockLayout L = block_layout(p);
+  if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
+  if (L.max_items > INT32_MAX) return GDPA_ENOTSUP;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  SchedArgs sa;
+  sa.q_off = offsets; sa.kv_off = offsets; sa.B = p->B; sa.H = p->H;
+  sa.total_q = p->total; sa.total_kv = p->total; sa.mode = SCHED_QTILES;
+  sa.causal = 0; sa.win = 0; sa.q_rows = 0;
+  sa.tile_item = BLOCK_TOKENS; sa.tile_loop = BLOCK_TOKENS;
+  sa.max_items = (int)L.max_items; sa.list = 0; sa.split = 0; sa.nslot = SPLIT_NSLOT;
+  sa.tile_base = nullptr; sa.split_slot = nullptr; sa.split_cnt = nullptr;
+  sa.ws_header = ws; sa.items = ws + L.items;
+  hipError_t e = launch_sched(sa, s);
+  if (e != hipSuccess) return map_hip(e);
+  ba.off = offsets; ba.hdr = ws; ba.items = ws + L.items; ba.H = p->H; ba.scale = p->scale;
+  ba.rope_log2_base = p->rotary ? log2((double)p->rope_base) : 0.0;
+  e = launch_block(p->act, p->causal != 0, p->rotary != 0, ba, (int)L.max_items, bwd, s);
+  return map_hip(e);
+}
+
+}  // namespace
+
+int32_t gdpa_block_workspace_size(const gdpa_block_problem* p, size_t* bytes) {
+  if (bytes == nullptr) return GDPA_EINVAL;
+  const int32_t st = check_block_problem(p);
+  if (st != GDPA_OK) return st;
+  *bytes = block_layout(p).total;
+  return GDPA_OK;
+}
+
+int32_t gdpa_block_fwd(const gdpa_block_problem* p, const void* Q, const void* K, const void* V,
+                       const int32_t* offsets, void* O, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  const int32_t st = check_block_problem(p);
+  if (st != GDPA_OK) return st;
+  if (!offsets || !workspace) return GDPA_EINVAL;
+  if (p->total > 0 && (!Q || !K || !V || !O)) return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace) ||
+      ((uintptr_t)offsets & 3u))
+    return GDPA_EINVAL;
+  BlockArgs ba = {};
+  ba.Q = Q; ba.K = K; ba.V = V; ba.O = O;
+  return block_call(p, offsets, ba, workspace, workspace_bytes, stream, false);
+}
+
+int32_t gdpa_block_bwd(const gdpa_block_problem* p, const void* Q, const void* K, const void* V,
+                       const void* dO, const int32_t* offsets, void* dQ, void* dK, void* dV,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const int32_t st = check_block_problem(p);
+  if (st != GDPA_OK) return st;
+  if (!offsets || !workspace) return GDPA_EINVAL;
+  if (p->total > 0 && (!Q || !K || !V || !dO || !dQ || !dK || !dV)) return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || !aligned16(workspace) || ((uintptr_t)offsets & 3u))
+    return GDPA_EINVAL;
+  BlockArgs ba = {};
+  ba.Q = Q; ba.K = K; ba.V = V; ba.dO = dO; ba.dQ = dQ; ba.dK = dK; ba.dV = dV;
+  return block_call(p, offsets, ba, workspace, workspace_bytes, stream, true);
 }
 
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err) {

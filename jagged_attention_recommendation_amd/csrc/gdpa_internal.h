@@ -182,8 +182,32 @@ inline int split_nslot(const Prob& p) { return p.D == 128 ? SPLIT_NSLOT : 2 * SP
 inline int split_slots(const Prob& p) { return 2 * split_nslot(p); }
 hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
+// Block-aligned attention: fixed blocks of BLOCK_TOKENS consecutive tokens per sample, each
+// attending only within itself, with rotary embeddings of Q and K (gdpa_block.hip). Items are the
+// scheduler's query tiles of BLOCK_TOKENS rows.
+constexpr int BLOCK_TOKENS = 64;
+struct BlockArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const int32_t* off;  // [B + 1] sample offsets (Q, K, V, O share them)
+  void* O;
+  void* dQ;
+  void* dK;
+  void* dV;
+  const void* hdr;
+  const void* items;
+  int H;
+  float scale;
+  double rope_log2_base;  // log2 of the rotary base (pair m turns by p * base^(-2m/D))
+};
+hipError_t launch_block(int act, bool causal, bool rope, const BlockArgs& a, int grid, bool bwd,
+                        hipStream_t s);
+
 // Profiling hook: brackets launches of one kernel with HIP events (see gdpa_profile_start).
-enum { PROF_FWD = 0, PROF_DQ = 1, PROF_DKDV = 2, PROF_SCHED = 3 };
+enum { PROF_FWD = 0, PROF_DQ = 1, PROF_DKDV = 2, PROF_SCHED = 3, PROF_BLOCK_FWD = 4,
+       PROF_BLOCK_BWD = 5 };
 void prof_before(int kernel, hipStream_t s);
 void prof_after(int kernel, hipStream_t s);
 

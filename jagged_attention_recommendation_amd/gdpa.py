@@ -20,12 +20,13 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE
 
 # Every symbol include/gdpa.h declares.
 EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd",
-           "gdpa_fwd_static", "gdpa_bwd",
+           "gdpa_fwd_static", "gdpa_bwd", "gdpa_block_workspace_size", "gdpa_block_fwd",
+           "gdpa_block_bwd",
            "gdpa_read_device_error", "gdpa_item_list", "gdpa_profile_start", "gdpa_profile_read",
            "gdpa_profile_stop"]
 
 # kernels selectable by the profiling hook
-PROFILE_KERNELS = {"fwd": 0, "dq": 1, "dkdv": 2, "sched": 3}
+PROFILE_KERNELS = {"fwd": 0, "dq": 1, "dkdv": 2, "sched": 3, "block_fwd": 4, "block_bwd": 5}
 
 
 class GdpaProblem(ctypes.Structure):
@@ -35,6 +36,13 @@ class GdpaProblem(ctypes.Structure):
                 ("max_kv", ctypes.c_int32), ("act", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("bias_buckets", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("q_shared", ctypes.c_int32)]
+
+
+class GdpaBlockProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("total", ctypes.c_int64), ("act", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("block", ctypes.c_int32),
+                ("rotary", ctypes.c_int32), ("rope_base", ctypes.c_float)]
 
 
 class GdpaError(RuntimeError):
@@ -66,6 +74,13 @@ def load():
     lib.gdpa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_fwd_static.restype = ctypes.c_int32
     lib.gdpa_fwd_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    BP = ctypes.POINTER(GdpaBlockProblem)
+    lib.gdpa_block_workspace_size.restype = ctypes.c_int32
+    lib.gdpa_block_workspace_size.argtypes = [BP, ctypes.POINTER(sz)]
+    lib.gdpa_block_fwd.restype = ctypes.c_int32
+    lib.gdpa_block_fwd.argtypes = [BP, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_block_bwd.restype = ctypes.c_int32
+    lib.gdpa_block_bwd.argtypes = [BP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd.restype = ctypes.c_int32
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_read_device_error.restype = ctypes.c_int32
@@ -228,6 +243,62 @@ def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=Fal
     if st != 0:
         raise GdpaError(st, "gdpa_bwd")
     return dq, dk, dv, dbias
+
+
+def block_problem(B, H, D, total, *, act="softmax", causal=False, scale=None, block=64,
+                  rotary=True, rope_base=10000.0, dtype="bf16"):
+    if scale is None:
+        scale = D ** -0.5
+    return GdpaBlockProblem(B=B, H=H, D=D, dtype=DTYPE[dtype], total=total, act=ACT[act],
+                            causal=int(bool(causal)), scale=float(scale), block=block,
+                            rotary=int(bool(rotary)), rope_base=float(rope_base))
+
+
+def block_workspace_size(prob):
+    n = ctypes.c_size_t(0)
+    st = load().gdpa_block_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    if st != 0:
+        raise GdpaError(st, "gdpa_block_workspace_size")
+    return int(n.value)
+
+
+def _block_prob(q, offsets, act, causal, scale, block, rotary, rope_base):
+    total, H, D = q.shape
+    return block_problem(offsets.numel() - 1, H, D, total, act=act, causal=causal, scale=scale,
+                         block=block, rotary=rotary, rope_base=rope_base, dtype=_dtype_of(q))
+
+
+def block_fwd(q, k, v, offsets, *, act="softmax", causal=False, scale=None, block=64,
+              rotary=True, rope_base=10000.0, out=None, workspace=None, stream=None):
+    """Block-aligned attention with rotary embeddings over jagged q/k/v [total, H, D] (one
+    offsets array). Returns O."""
+    prob = _block_prob(q, offsets, act, causal, scale, block, rotary, rope_base)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = _workspace(block_workspace_size(prob), q.device)
+    st = load().gdpa_block_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets),
+                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    if st != 0:
+        raise GdpaError(st, "gdpa_block_fwd")
+    return out
+
+
+def block_bwd(q, k, v, do, offsets, *, act="softmax", causal=False, scale=None, block=64,
+              rotary=True, rope_base=10000.0, grads=None, workspace=None, stream=None):
+    """Backward of sum(do * O) for block_fwd. Returns (dQ, dK, dV)."""
+    prob = _block_prob(q, offsets, act, causal, scale, block, rotary, rope_base)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    if workspace is None:
+        workspace = _workspace(block_workspace_size(prob), q.device)
+    st = load().gdpa_block_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                               _ptr(offsets), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                               workspace.numel(), _stream(stream))
+    if st != 0:
+        raise GdpaError(st, "gdpa_block_bwd")
+    return dq, dk, dv
 
 
 def read_device_error(workspace, stream=None):

@@ -110,3 +110,28 @@ def kernel_bytes(p, kernel):
     else:
         raise ValueError(kernel)
     return float(b)
+
+
+def block_lengths(lengths, block=64):
+    """Lengths of the fixed blocks every sample is cut into (the last one of a sample shorter)."""
+    out = []
+    for L in np.asarray(lengths, dtype=np.int64):
+        out.extend([block] * int(L // block))
+        if L % block:
+            out.append(int(L % block))
+    return np.asarray(out, dtype=np.int64)
+
+
+def block_flops(p, direction="fwd", block=64):
+    """Useful flops of block-aligned attention over p's samples: pairs inside each block (causal
+    when p is), 4*D per pair and head forward, 10*D backward."""
+    bl = block_lengths(p.lq, block)
+    pairs = int(pairs_per_sample(bl, bl, p.causal).sum())
+    return float({"fwd": 4, "bwd": 10}[direction]) * p.D * p.H * pairs
+
+
+def block_bytes(p, direction="fwd"):
+    """Algorithmic HBM bytes of block-aligned attention (bf16): forward reads Q, K, V and writes
+    O; backward reads Q, K, V, dO and writes dQ, dK, dV. No lse or row term touches HBM."""
+    per = p.total_q * p.H * p.D * 2
+    return float(per * (4 if direction == "fwd" else 7))

@@ -115,3 +115,29 @@ def test_fwd_rejects_host_checkable_errors_without_launching():
     st = lib.gdpa_fwd(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, fake, None,
                       fake, fake, fake, big, None)
     assert st == 1
+
+
+def test_block_problem_validation():
+    """Block-aligned attention: the struct matches the header's layout (48 bytes), and argument
+    errors are reported without any launch."""
+    import ctypes
+    assert ctypes.sizeof(gdpa.GdpaBlockProblem) == 48
+    ok = gdpa.block_problem(3, 2, 128, 500)
+    assert gdpa.block_workspace_size(ok) >= 256
+    bad = [(dict(D=64), 2), (dict(dtype="f32"), 2), (dict(block=32), 2), (dict(scale=-1.0), 2),
+           (dict(rope_base=1.0), 1), (dict(act="nope"), None)]
+    for kw, status in bad:
+        if status is None:
+            continue
+        args = dict(B=3, H=2, D=128, total=500)
+        args.update({k: v for k, v in kw.items() if k in ("B", "H", "D", "total")})
+        p = gdpa.block_problem(args["B"], args["H"], args["D"], args["total"],
+                               **{k: v for k, v in kw.items() if k not in args})
+        with pytest.raises(gdpa.GdpaError) as e:
+            gdpa.block_workspace_size(p)
+        assert e.value.status == status, kw
+    p = gdpa.block_problem(3, 2, 128, 500)
+    p.act = 7
+    with pytest.raises(gdpa.GdpaError) as e:
+        gdpa.block_workspace_size(p)
+    assert e.value.status == 1
