@@ -293,7 +293,7 @@ def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=Non
     same e4m3 + e8m0 inputs (scaled fp8 products for Q.K^T, bf16 for P.V, fp32 accumulation)."""
     steps = args.steps if steps is None else steps
     reps = args.reps if reps is None else reps
-    p = inputs.config_problem(5)
+    p = inputs.config_problem(5, with_grad=True)  # dO for the MX backward's timing
     u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     Q, K, V = u8(p.Q), u8(p.K), u8(p.V)
     qs, ks, vs = u8(p.q_scale), u8(p.k_scale), u8(p.v_scale)
@@ -326,6 +326,20 @@ def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=Non
     for a in acts:
         if not torch.isfinite(O[a].float()).all():
             raise RuntimeError("non-finite output")
+    # the MX backward (softmax): exact dequantisation to bf16, then the bf16 backward kernels
+    dO = torch.from_numpy(np.ascontiguousarray(p.dO).view(np.int16)).view(torch.bfloat16).to(dev)
+    wsb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty((r, p.H, p.D), dtype=torch.bfloat16, device=dev)
+                  for r in (p.total_q, p.total_kv, p.total_kv)) + (None,)
+
+    def bwd():
+        gdpa.bwd(Q, K, V, O["softmax"], dO, lse, q_off, kv_off, act="softmax", causal=True,
+                 scale=p.scale, q_scale=qs, k_scale=ks, v_scale=vs, max_q=max_q, max_kv=max_kv,
+                 workspace=wsb, grads=grads)
+
+    bwd()
+    bcold = per_call_medians(torch, {"bwd": bwd}, max(3, reps // 2), flush)["bwd"]
+    f_bwd = workload.useful_flops(p, "bwd")
     f_fwd = workload.useful_flops(p, "fwd")
     tf = lambda ms: round(f_fwd / (ms * 1e-3) / 1e12, 2)
     achieved = f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12
@@ -334,13 +348,16 @@ def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=Non
            | {f"{a}_tflops": tf(cold[a][0]) for a in acts} | {"reps": reps},
            "warm": {f"{a}_ms": round(warm[a][0], 4) for a in acts}
            | {f"{a}_tflops": tf(warm[a][0]) for a in acts} | {"reps": reps},
+           "bwd_softmax_cold": {"ms": round(bcold[0], 4),
+                                "tflops": round(f_bwd / (bcold[0] * 1e-3) / 1e12, 2),
+                                "reps": max(3, reps // 2)},
            "roofline": {"bound": "mfma", "kernel": "fwd", "achieved": round(achieved, 2),
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
                         "avg_launch_ms": round(kern_ms["fwd"], 4),
                         "hbm_gbs": round(workload.fwd_bytes(p) / (kern_ms["fwd"] * 1e-3) / 1e9,
                                          1)}}
-    del Q, K, V, qs, ks, vs, O, lse, ws
+    del Q, K, V, qs, ks, vs, O, lse, ws, dO, wsb, grads
     torch.cuda.empty_cache()
     return res
 
@@ -409,6 +426,7 @@ def summary(config, r):
     """The figures of a non-headline workload on the headline line."""
     s = {"workload": WORKLOADS[config], "ms_per_step": round(r["ms_step"], 4),
          "tflops": round(r["value"], 2), "cold": r["cold"], "warm_per_call": r["warm"],
+         **({"bwd_softmax_cold": r["bwd_softmax_cold"]} if "bwd_softmax_cold" in r else {}),
          "dominant": {k: r["roofline"][k] for k in ("kernel", "bound", "achieved", "unit",
                                                     "frac", "avg_launch_ms")}}
     if "kernel_avg_ms" in r["roofline"]:
@@ -495,6 +513,8 @@ def main():
         out["bwd_ms"] = r["warm"]["bwd_ms"]
     out["cold"] = r["cold"]
     out["warm_per_call"] = r["warm"]
+    if "bwd_softmax_cold" in r:
+        out["bwd_softmax_cold"] = r["bwd_softmax_cold"]
     out["roofline"] = r["roofline"]
     if not args.no_others:
         others = {}

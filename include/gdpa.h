@@ -69,7 +69,7 @@ typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1, GDPA_MXFP8_E4M3 = 2 } gdpa_dtype;
 typedef enum {
   GDPA_OK = 0,
   GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
-  GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX backward,
+  GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX in gdpa_bwd,
                           scale <= 0 outside fp32, a window outside causal bf16 D = 128, ... */
   GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
   GDPA_EHIP = 4        /* the HIP runtime refused a launch */
@@ -182,6 +182,22 @@ int32_t gdpa_block_fwd(const gdpa_block_problem* p, const void* Q, const void* K
 int32_t gdpa_block_bwd(const gdpa_block_problem* p, const void* Q, const void* K, const void* V,
                        const void* dO, const int32_t* offsets, void* dQ, void* dK, void* dV,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward for MX-fp8 inputs (GDPA_MXFP8_E4M3; same page, low-precision part: MXFP8 for the
+ * forward and the backward). Arguments as gdpa_bwd plus the e8m0 scale arrays of Q, K and V
+ * ([rows, H, D/32] u8, as for gdpa_fwd). Returns the gradients of sum(dO * O) with respect to the
+ * dequantised values (the e4m3 code times its block's power of two), in bf16; O and lse come
+ * from gdpa_fwd on the same inputs. Q, K and V are first dequantised exactly to bf16 in the
+ * workspace (an e4m3 value times a power of two has at most 4 significant bits), so every
+ * matrix product, the recomputed scores included, sees exactly the values the MX forward's
+ * scaled products see; the gradient products then run as in the bf16 backward (their operands'
+ * scales run along D, not along the contraction). gdpa_workspace_size(p, 1, ...) gives the
+ * workspace. gdpa_bwd itself returns GDPA_ENOTSUP for MX problems. */
+int32_t gdpa_bwd_mx(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                    const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                    const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                    const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                    float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Waits for `stream`, then reads the device error word of the last call that used `workspace`
  * (0 = none, 1 = malformed q_offsets, 2 = malformed kv_offsets). Diagnostics only. */

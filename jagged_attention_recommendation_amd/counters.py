@@ -29,7 +29,7 @@ import sys
 COPY_BYTES = 256 << 20
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # kernel families: the D = 128 direct-load kernels and the D = 32 / 64 / MX kernels
-KERNELS = {"fwd": ("fwd_dl_kernel", "fwd_kernel"), "dq": ("dq_dl_kernel", "dq_kernel"),
+KERNELS = {"fwd": ("fwd_dl_kernel", "fwd_pp_kernel", "fwd_kernel"), "dq": ("dq_dl_kernel", "dq_kernel"),
            "dkdv": ("dkdv_dl_kernel", "dkdv_kernel")}
 SIMDS = 1024  # MI355X: 256 compute units x 4 SIMDs
 XCDS = 8      # accelerator complex dies; GRBM_GUI_ACTIVE is summed over them

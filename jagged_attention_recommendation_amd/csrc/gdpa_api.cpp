@@ -157,6 +157,53 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   return L;
 }
 
+// Host-checkable arguments of a backward call (Q, K, V are the bf16 / fp32 tensors the kernels
+// read; for the MX backward they are the dequantised copies, checked with placeholders).
+int32_t check_bwd_args(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                       const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                       const int32_t* kv_offsets, const float* bias, const void* dQ,
+                       const void* dK, const void* dV, const float* dbias, const void* workspace) {
+  if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
+  if (p->total_q > 0 && (!Q || !dO || !dQ)) return GDPA_EINVAL;
+  if (p->q_shared && (!Q || !dQ)) return GDPA_EINVAL;  // dQ is written even with no queries
+  if (p->total_kv > 0 && (!K || !V || !dK || !dV)) return GDPA_EINVAL;
+  const bool softmax = p->act == GDPA_ACT_SOFTMAX;
+  if (softmax && p->total_q > 0 && (!O || !lse)) return GDPA_EINVAL;
+  if ((p->bias_buckets > 0) != (bias != nullptr)) return GDPA_EINVAL;
+  if ((p->bias_buckets > 0) != (dbias != nullptr)) return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+    return GDPA_EINVAL;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)bias & 3u) || ((uintptr_t)dbias & 3u) ||
+      ((uintptr_t)q_offsets & 3u) || ((uintptr_t)kv_offsets & 3u))
+    return GDPA_EINVAL;
+  return GDPA_OK;
+}
+
+// MX backward: Q, K, V dequantised exactly to bf16 at the start of the workspace, then the bf16
+// backward's own workspace.
+struct MxBwdLayout {
+  size_t q, k, v, bwd, total;
+};
+
+gdpa_problem bf16_view(const gdpa_problem* p) {
+  gdpa_problem r = *p;
+  r.dtype = GDPA_BF16;
+  return r;
+}
+
+MxBwdLayout mx_bwd_layout(const gdpa_problem* p) {
+  MxBwdLayout L;
+  const size_t row = (size_t)p->H * p->D * 2;
+  L.q = 0;
+  L.k = L.q + align_up((size_t)p->total_q * row);
+  L.v = L.k + align_up((size_t)p->total_kv * row);
+  L.bwd = L.v + align_up((size_t)p->total_kv * row);
+  const gdpa_problem pb = bf16_view(p);
+  L.total = L.bwd + bwd_layout(&pb).total;
+  return L;
+}
+
 // ---- scratch of gdpa_fwd_static: one fixed buffer per GPU in place of a caller workspace.
 // Host code never uses the array's name as an address (on the host it only names the symbol):
 // every launch takes the device address that hipGetSymbolAddress returned for the current GPU.
@@ -267,8 +314,8 @@ int32_t gdpa_workspace_size(const gdpa_problem* p, int32_t for_bwd, size_t* byte
   if (bytes == nullptr) return GDPA_EINVAL;
   int32_t st = check_problem(p);
   if (st != GDPA_OK) return st;
-  if (for_bwd && p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
-  *bytes = for_bwd ? bwd_layout(p).total : fwd_layout(p).total;
+  if (for_bwd && p->dtype == GDPA_MXFP8_E4M3) *bytes = mx_bwd_layout(p).total;
+  else *bytes = for_bwd ? bwd_layout(p).total : fwd_layout(p).total;
   return GDPA_OK;
 }
 
@@ -347,20 +394,9 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   int32_t st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
-  if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
-  if (p->total_q > 0 && (!Q || !dO || !dQ)) return GDPA_EINVAL;
-  if (p->q_shared && (!Q || !dQ)) return GDPA_EINVAL;  // dQ is written even with no queries
-  if (p->total_kv > 0 && (!K || !V || !dK || !dV)) return GDPA_EINVAL;
-  const bool softmax = p->act == GDPA_ACT_SOFTMAX;
-  if (softmax && p->total_q > 0 && (!O || !lse)) return GDPA_EINVAL;
-  if ((p->bias_buckets > 0) != (bias != nullptr)) return GDPA_EINVAL;
-  if ((p->bias_buckets > 0) != (dbias != nullptr)) return GDPA_EINVAL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
-      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
-    return GDPA_EINVAL;
-  if (((uintptr_t)lse & 3u) || ((uintptr_t)bias & 3u) || ((uintptr_t)dbias & 3u) ||
-      ((uintptr_t)q_offsets & 3u) || ((uintptr_t)kv_offsets & 3u))
-    return GDPA_EINVAL;
+  st = check_bwd_args(p, Q, K, V, O, dO, lse, q_offsets, kv_offsets, bias, dQ, dK, dV, dbias,
+                      workspace);
+  if (st != GDPA_OK) return st;
   const BwdLayout L = bwd_layout(p);
   if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
   if (L.max_q_items > INT32_MAX || L.max_k_items > INT32_MAX) return GDPA_ENOTSUP;
@@ -541,6 +577,42 @@ int32_t gdpa_block_bwd(const gdpa_block_problem* p, const void* Q, const void* K
   BlockArgs ba = {};
   ba.Q = Q; ba.K = K; ba.V = V; ba.dO = dO; ba.dQ = dQ; ba.dK = dK; ba.dV = dV;
   return block_call(p, offsets, ba, workspace, workspace_bytes, stream, true);
+}
+
+int32_t gdpa_bwd_mx(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                    const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                    const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                    const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                    float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (p->dtype != GDPA_MXFP8_E4M3) return GDPA_EINVAL;
+  if (!workspace || !aligned16(workspace)) return GDPA_EINVAL;
+  if ((p->total_q > 0 && (!Q || !q_scale)) || (p->total_kv > 0 && (!K || !V || !k_scale || !v_scale)))
+    return GDPA_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V)) return GDPA_EINVAL;  // 16-byte code reads
+  const MxBwdLayout L = mx_bwd_layout(p);
+  if (workspace_bytes < L.total) return GDPA_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const gdpa_problem pb = bf16_view(p);
+  // every argument is checked before anything is enqueued (the dequantised copies stand for Q,
+  // K, V, and are 256-byte aligned workspace regions)
+  st = check_problem(&pb);
+  if (st != GDPA_OK) return st;
+  st = check_bwd_args(&pb, ws + L.q, ws + L.k, ws + L.v, O, dO, lse, q_offsets, kv_offsets, bias,
+                      dQ, dK, dV, dbias, ws + L.bwd);
+  if (st != GDPA_OK) return st;
+  {
+    const BwdLayout LB = bwd_layout(&pb);
+    if (LB.max_q_items > INT32_MAX || LB.max_k_items > INT32_MAX) return GDPA_ENOTSUP;
+  }
+  hipError_t e = launch_mx_dequant((const uint8_t*)Q, q_scale, ws + L.q, p->total_q, p->H, p->D, s);
+  if (e == hipSuccess) e = launch_mx_dequant((const uint8_t*)K, k_scale, ws + L.k, p->total_kv, p->H, p->D, s);
+  if (e == hipSuccess) e = launch_mx_dequant((const uint8_t*)V, v_scale, ws + L.v, p->total_kv, p->H, p->D, s);
+  if (e != hipSuccess) return map_hip(e);
+  return gdpa_bwd(&pb, ws + L.q, ws + L.k, ws + L.v, O, dO, lse, q_offsets, kv_offsets, bias, dQ,
+                  dK, dV, dbias, ws + L.bwd, workspace_bytes - L.bwd, stream);
 }
 
 int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err) {

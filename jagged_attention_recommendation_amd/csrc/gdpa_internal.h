@@ -118,6 +118,9 @@ constexpr int BIAS_WMAX = 4096;
 
 hipError_t launch_fwd_bf16(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_fwd_mx(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
+// Exact MX-fp8 -> bf16 dequantisation of a [rows, H, D] tensor (D = 128).
+hipError_t launch_mx_dequant(const uint8_t* codes, const uint8_t* scales, void* out, int64_t rows,
+                             int H, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const Prob& p, const FwdArgs& a, int grid, hipStream_t s);
 
 struct BwdArgs {

@@ -20,7 +20,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE
 
 # Every symbol include/gdpa.h declares.
 EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd",
-           "gdpa_fwd_static", "gdpa_bwd", "gdpa_block_workspace_size", "gdpa_block_fwd",
+           "gdpa_fwd_static", "gdpa_bwd", "gdpa_bwd_mx", "gdpa_block_workspace_size", "gdpa_block_fwd",
            "gdpa_block_bwd",
            "gdpa_read_device_error", "gdpa_item_list", "gdpa_profile_start", "gdpa_profile_read",
            "gdpa_profile_stop"]
@@ -74,6 +74,9 @@ def load():
     lib.gdpa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_fwd_static.restype = ctypes.c_int32
     lib.gdpa_fwd_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdpa_bwd_mx.restype = ctypes.c_int32
+    lib.gdpa_bwd_mx.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, sz, vp]
     BP = ctypes.POINTER(GdpaBlockProblem)
     lib.gdpa_block_workspace_size.restype = ctypes.c_int32
     lib.gdpa_block_workspace_size.argtypes = [BP, ctypes.POINTER(sz)]
@@ -212,11 +215,13 @@ def fwd_static(q, k, v, q_offsets, kv_offsets, out, lse=None, *, act="softmax", 
 
 def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None,
         bias=None, max_q=0, max_kv=0, workspace=None, stream=None, grads=None, window=0,
-        q_shared=False):
+        q_shared=False, q_scale=None, k_scale=None, v_scale=None):
     """Backward of sum(do * O). Returns (dQ, dK, dV, dbias or None).
 
     q_shared: q (and so dQ) is one block [max_q, H, D] read by every sample; dQ is the sum of
     the samples' gradients. total_q is then do's row count.
+    MX-fp8 inputs (uint8 codes with q_scale/k_scale/v_scale) go to gdpa_bwd_mx; the gradients
+    are bf16.
     """
     lib = load()
     total_q, H, D = q.shape
@@ -228,14 +233,24 @@ def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=Fal
     prob = problem(B, H, D, total_q, k.shape[0], dtype=dt, act=act, causal=causal, scale=scale,
                    bias_buckets=nb, max_q=max_q, max_kv=max_kv, window=window, q_shared=q_shared)
     if grads is None:
-        dq = torch.empty_like(q)
-        dk = torch.empty_like(k)
-        dv = torch.empty_like(v)
+        gdt = torch.bfloat16 if dt == "mxfp8" else q.dtype
+        dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+        dk = torch.empty(k.shape, dtype=gdt, device=k.device)
+        dv = torch.empty(v.shape, dtype=gdt, device=v.device)
         dbias = torch.empty_like(bias) if bias is not None else None
     else:
         dq, dk, dv, dbias = grads
     if workspace is None:
         workspace = _workspace(workspace_size(prob, True), q.device)
+    if dt == "mxfp8":
+        st = lib.gdpa_bwd_mx(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
+                             _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(do), _ptr(lse),
+                             _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+        if st != 0:
+            raise GdpaError(st, "gdpa_bwd_mx")
+        return dq, dk, dv, dbias
     st = lib.gdpa_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                       _ptr(lse), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq),
                       _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel(),

@@ -251,14 +251,16 @@ CONFIG_NAMES = {
 }
 
 
-def config_problem(k, act=None, B=None, seed=None):
-    """Problem for workload k (1..5). B overrides the sample count (same per-sample recipe)."""
+def config_problem(k, act=None, B=None, seed=None, with_grad=None):
+    """Problem for workload k (1..5). B overrides the sample count (same per-sample recipe).
+    with_grad=True also draws dO for the forward-only workloads (1 and 5); it is drawn after V and
+    before any bias, so Q, K and V keep their bits."""
     seed = 1000 + k if seed is None else seed
     if k == 1:
         b = 4 if B is None else B
         u = lambda rng: lengths_uniform(rng, b, 1, 64)
         return _same_len_problem("config1", seed, b, 2, 32, u, dtype="f32", act=act or "silu",
-                                 causal=False, bias_buckets=0, with_grad=False)
+                                 causal=False, bias_buckets=0, with_grad=bool(with_grad))
     if k == 2:
         b = 64 if B is None else B
         u = lambda rng: lengths_uniform(rng, b, 1, 2048)
@@ -280,7 +282,8 @@ def config_problem(k, act=None, B=None, seed=None):
         b = 128 if B is None else B
         u = lambda rng: lengths_lognormal(rng, b, 7.0, 1.0, 16, 16384)
         return _same_len_problem("config5", seed, b, 8, 128, u, dtype="mxfp8",
-                                 act=act or "softmax", causal=True, bias_buckets=0, with_grad=False)
+                                 act=act or "softmax", causal=True, bias_buckets=0,
+                                 with_grad=bool(with_grad))
     raise ValueError(k)
 
 

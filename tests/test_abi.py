@@ -48,9 +48,10 @@ def test_workspace_size_validation():
     with pytest.raises(gdpa.GdpaError) as e:
         gdpa.workspace_size(gdpa.problem(-1, 2, 64, 100, 100))
     assert e.value.status == 1
-    with pytest.raises(gdpa.GdpaError) as e:
-        gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100, dtype="mxfp8"), True)
-    assert e.value.status == 2  # MX backward not provided
+    # the MX backward's workspace holds the dequantised Q, K, V and the bf16 backward's own
+    mx = gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100, dtype="mxfp8"), True)
+    bf = gdpa.workspace_size(gdpa.problem(4, 2, 128, 100, 100, dtype="bf16"), True)
+    assert mx >= bf + 3 * 100 * 2 * 128 * 2
 
 
 def test_window_validation():
@@ -141,3 +142,30 @@ def test_block_problem_validation():
     with pytest.raises(gdpa.GdpaError) as e:
         gdpa.block_workspace_size(p)
     assert e.value.status == 1
+
+
+def test_bwd_mx_rejects_host_checkable_errors_without_launching():
+    """gdpa_bwd_mx checks every argument (its own and those of the bf16 backward it runs after
+    the dequantisation) before anything is enqueued; gdpa_bwd refuses MX problems."""
+    lib = gdpa.load()
+    p = gdpa.problem(2, 1, 128, 10, 10, dtype="mxfp8")
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    big = 1 << 30
+    args = [fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, fake, fake,
+            fake, None, fake, big, None]
+    bad = list(args)
+    bad[7] = None  # dO
+    assert lib.gdpa_bwd_mx(ctypes.byref(p), *bad) == 1
+    bad = list(args)
+    bad[3] = None  # q_scale
+    assert lib.gdpa_bwd_mx(ctypes.byref(p), *bad) == 1
+    bad = list(args)
+    bad[17] = 64  # workspace too small
+    assert lib.gdpa_bwd_mx(ctypes.byref(p), *bad) == 3
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x1004)  # misaligned codes
+    assert lib.gdpa_bwd_mx(ctypes.byref(p), *bad) == 1
+    pb = gdpa.problem(2, 1, 128, 10, 10, dtype="bf16")
+    assert lib.gdpa_bwd_mx(ctypes.byref(pb), *args) == 1  # not an MX problem
+    assert lib.gdpa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                        fake, fake, fake, None, fake, big, None) == 2

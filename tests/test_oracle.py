@@ -914,3 +914,12 @@ def test_mx_quantize_threaded_chunks_give_the_same_bits():
     codes, scales = inputs.mx_quantize(x)
     c1, s1 = inputs._mx_quantize(x, 32)
     assert np.array_equal(codes, c1) and np.array_equal(scales, s1)
+
+
+def test_config_generator_with_grad_keeps_input_bits():
+    """Drawing dO for a forward-only workload leaves its Q, K, V (and MX scales) unchanged."""
+    a = inputs.config_problem(5, B=3, seed=77)
+    b = inputs.config_problem(5, B=3, seed=77, with_grad=True)
+    for n in ("Q", "K", "V", "q_scale", "k_scale", "v_scale", "q_off", "kv_off"):
+        assert np.array_equal(getattr(a, n), getattr(b, n)), n
+    assert a.dO is None and b.dO.shape == (b.total_q, b.H, b.D)
