@@ -30,8 +30,8 @@
  * This MX encoding follows the OCP Microscaling Formats v1.0 (same page, low-precision part:
  * MXFP8 block-scaled matrix products).
  * Sliding-window attention (same page, the paragraph on sliding-window attention): with
- * causal = 1 and window = W >= 1, query i attends to keys i - W + 1 .. i only; tiles wholly
- * outside the window are neither scheduled nor loaded.
+ * causal = 1 and window = W >= 1, query i attends to keys i - W + 1 .. i only; on the bf16 path
+ * tiles wholly outside the window are neither scheduled nor loaded.
  * Shared queries (PMA, same page, GDPA paragraph: a fixed set of learned seed queries attends to
  * every sample's keys): with q_shared = 1, Q and dQ are one block [max_q, H, D] used by every
  * sample, whose local query i reads row i; O, dO and lse stay jagged over q_offsets. The
@@ -70,7 +70,8 @@ typedef enum {
   GDPA_OK = 0,
   GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
   GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX in gdpa_bwd,
-                          scale <= 0 outside fp32, a window outside causal bf16 D = 128, ... */
+                          scale <= 0 outside fp32, a window on a bf16 D = 32 / 64 or MX
+                          problem, ... */
   GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
   GDPA_EHIP = 4        /* the HIP runtime refused a launch */
 } gdpa_status;
@@ -89,13 +90,15 @@ typedef struct {
   int32_t causal;       /* 0 or 1: keep j <= i on local positions (top-left aligned) */
   float scale;          /* s = scale * q.k (+ bias); must be > 0 for GDPA_BF16 / GDPA_MXFP8_E4M3 */
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
-  int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1,
-                           GDPA_BF16 and D = 128 (otherwise GDPA_ENOTSUP). A W that no query can
+  int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1
+                           and GDPA_F32, or GDPA_BF16 with D = 128 (otherwise GDPA_ENOTSUP). A W
+                           that no query can
                            reach (W >= total_q, or W >= max_q when max_q > 0) drops nothing and
                            is the same as no window; any other W >= 1 needs
                            total_q + total_kv <= INT32_MAX - 1024 (otherwise GDPA_ENOTSUP) */
   int32_t q_shared;     /* 0 or 1. 1: Q and dQ are [max_q, H, D], shared by all samples; needs
-                           GDPA_BF16 (else GDPA_ENOTSUP) and max_q >= 1 (else GDPA_EINVAL); a
+                           GDPA_BF16 or GDPA_F32 (else GDPA_ENOTSUP) and max_q >= 1 (else
+                           GDPA_EINVAL); a
                            sample with Lq_b > max_q is a malformed q_offsets (device error 1) */
 } gdpa_problem;
 

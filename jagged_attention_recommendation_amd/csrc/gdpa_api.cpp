@@ -47,14 +47,16 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->D != 32 && p->D != 64 && p->D != 128) return GDPA_ENOTSUP;
   if (p->dtype == GDPA_MXFP8_E4M3 && p->D != 128) return GDPA_ENOTSUP;
   if (p->window < 0) return GDPA_EINVAL;
-  // sliding windows: causal self-attention on the bf16 D = 128 kernels
-  if (p->window > 0 && (p->causal != 1 || p->dtype != GDPA_BF16 || p->D != 128)) return GDPA_ENOTSUP;
+  // sliding windows: causal attention on the fp32 kernels and the bf16 D = 128 kernels
+  if (p->window > 0 && (p->causal != 1 || p->dtype == GDPA_MXFP8_E4M3 ||
+                        (p->dtype == GDPA_BF16 && p->D != 128)))
+    return GDPA_ENOTSUP;
   // window arithmetic adds a key or query position to W in int32
   if (effective_window(p) > 0 && p->total_q + p->total_kv > INT32_MAX - 1024) return GDPA_ENOTSUP;
   // a shared query block: bf16 kernels, max_q rows
   if (p->q_shared != 0 && p->q_shared != 1) return GDPA_EINVAL;
   if (p->q_shared && p->max_q < 1) return GDPA_EINVAL;
-  if (p->q_shared && p->dtype != GDPA_BF16) return GDPA_ENOTSUP;
+  if (p->q_shared && p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
   // element counts must fit the kernels' 64-bit addressing and the scheduler's int32 counters
   if ((int64_t)p->H * p->D > (1 << 20)) return GDPA_ENOTSUP;
   return GDPA_OK;
@@ -450,6 +452,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
     DqSharedArgs qa;
     qa.q_off = q_offsets; qa.part = ba.dq_f32; qa.dQ = dQ; qa.hdr = ws + L.header;
     qa.B = p->B; qa.H = p->H; qa.D = p->D; qa.q_rows = pr.q_rows;
+    qa.f32_out = p->dtype == GDPA_F32 ? 1 : 0;
     e = launch_dq_shared_reduce(qa, s);
     if (e != hipSuccess) return map_hip(e);
   }

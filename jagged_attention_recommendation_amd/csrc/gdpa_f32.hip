@@ -5,6 +5,10 @@
 // for small problems and exact-ish fp32 results: one thread per query (forward, dQ) or per key
 // (dK/dV), keys / queries streamed through LDS in tiles of 64 rows. gfx950 has no fp32 matrix
 // instruction faster than its vector units on these shapes, so no MFMA is used here.
+// A causal sliding window (a.win = W > 0: key j is valid for query i when j > i - W) is one more
+// mask term (the forward also starts at the first key tile the item's window reaches); a shared
+// query block (a.q_shared) is read at row i for every sample, and the dQ kernel then writes each
+// sample's fp32 gradient for the reduction over samples.
 #include <math.h>
 
 #include "gdpa_common.h"
@@ -43,24 +47,26 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const int i = it.tile * TM + tid;
   const bool qv = i < Lq;
   const float* Q = (const float*)a.Q;
+  const int64_t qin = a.q_shared ? (int64_t)i * H + h : (int64_t)(q0 + i) * H + h;
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = qv ? Q[((int64_t)(q0 + i) * H + h) * D + c] : 0.0f;
+    q[c] = qv ? Q[qin * D + c] : 0.0f;
     o[c] = 0.0f;
   }
   int nkt = (Lk + TN - 1) / TN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, (it.tile + 1) * TM) - 1) / TN + 1);
+  const int win = a.win;
   float m = -INFINITY, l = 0.0f;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = win_first_ktile(it.tile * TM, win, TN); kt < nkt; ++kt) {
     __syncthreads();
     load_tile_f32<D>(Ks, (const float*)a.K, kt * TN, Lk, kv0, H, h, tid);
     load_tile_f32<D>(Vs, (const float*)a.V, kt * TN, Lk, kv0, H, h, tid);
     __syncthreads();
     for (int jj = 0; jj < TN; ++jj) {
       const int j = kt * TN + jj;
-      if (j >= Lk || (CAUSAL && j > i)) continue;
+      if (j >= Lk || (CAUSAL && j > i) || (win > 0 && j <= i - win)) continue;
       float s = 0.0f;
 #pragma unroll
       for (int c = 0; c < D; ++c) s += q[c] * Ks[jj][c];
@@ -125,11 +131,13 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
   const int i = i0 + tid;
   const bool qv = i < Lq;
   const int64_t row = (int64_t)(q0 + (qv ? i : 0)) * H + h;
+  const int64_t qin = a.q_shared ? (int64_t)(qv ? i : 0) * H + h : row;
+  const int win = a.win;
   float q[D], dO[D], dq[D];
   float Di = 0.0f, lse_i = 0.0f;
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = qv ? ((const float*)a.Q)[row * D + c] : 0.0f;
+    q[c] = qv ? ((const float*)a.Q)[qin * D + c] : 0.0f;
     dO[c] = qv ? ((const float*)a.dO)[row * D + c] : 0.0f;
     dq[c] = 0.0f;
   }
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
     for (int jj = 0; jj < TN; ++jj) {
       const int j = kt * TN + jj;
       float ds = 0.0f;
-      if (qv && j < Lk && !(CAUSAL && j > i)) {
+      if (qv && j < Lk && !(CAUSAL && j > i) && !(win > 0 && j <= i - win)) {
         float s = 0.0f, dp = 0.0f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
@@ -214,7 +222,8 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
     }
   }
   if (!qv) return;
-  float* dqrow = (float*)a.dQ + row * D;
+  // a shared query block: this sample's gradient at O's row, summed over samples afterwards
+  float* dqrow = (a.dq_f32 ? a.dq_f32 : (float*)a.dQ) + row * D;
 #pragma unroll
   for (int c = 0; c < D; ++c) dqrow[c] = dq[c] * a.scale;
 }
@@ -242,11 +251,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdArgs a) {
     dk[c] = 0.0f;
     dv[c] = 0.0f;
   }
-  const int nqt = (Lq + TM - 1) / TM;
+  const int win = a.win;
+  const int nqt = win_end_qtile(min(Lk, (it.tile + 1) * TN) - 1, win, TM, (Lq + TM - 1) / TM);
   const int qt0 = CAUSAL ? (it.tile * TN) / TM : 0;
   for (int qt = qt0; qt < nqt; ++qt) {
     __syncthreads();
-    load_tile_f32<D>(Qs, (const float*)a.Q, qt * TM, Lq, q0, H, h, tid);
+    load_tile_f32<D>(Qs, (const float*)a.Q, qt * TM, Lq, a.q_shared ? 0 : q0, H, h, tid);
     load_tile_f32<D>(dOs, (const float*)a.dO, qt * TM, Lq, q0, H, h, tid);
     {
       const int ii = qt * TM + tid;
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdArgs a) {
     if (!kvalid) continue;
     for (int ii = 0; ii < TM; ++ii) {
       const int i = qt * TM + ii;
-      if (i >= Lq || (CAUSAL && j > i)) continue;
+      if (i >= Lq || (CAUSAL && j > i) || (win > 0 && j <= i - win)) continue;
       float s = 0.0f, dp = 0.0f;
 #pragma unroll
       for (int c = 0; c < D; ++c) {

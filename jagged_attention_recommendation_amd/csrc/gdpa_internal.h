@@ -9,7 +9,7 @@ namespace gdpa {
 
 struct Prob {
   int B, H, D, dtype, act, causal, nb;
-  int win;  // sliding window W (0: none); only with causal bf16 D = 128
+  int win;  // sliding window W (0: none); only with causal, fp32 or bf16 D = 128
   int q_rows;  // shared query block: rows of Q / dQ (0: Q is jagged like O)
   int64_t total_q, total_kv;
   int max_q, max_kv;
@@ -158,13 +158,14 @@ struct BwdArgs {
 };
 
 // Shared query block: dQ[i, h] = sum over samples b with Lq_b > i of dq_f32[q_off[b] + i, h],
-// summed in a fixed order, rounded once to bf16.
+// summed in a fixed order, rounded once to bf16 (or kept in fp32 for fp32 problems).
 struct DqSharedArgs {
   const int32_t* q_off;
   const float* part;
   void* dQ;
   const void* hdr;
   int B, H, D, q_rows;
+  int f32_out;  // 1: dQ is fp32, else bf16
 };
 hipError_t launch_dq_shared_reduce(const DqSharedArgs& a, hipStream_t s);
 

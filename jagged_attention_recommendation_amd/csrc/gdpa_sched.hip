@@ -442,10 +442,11 @@ hipError_t launch_dbias_reduce(const DbiasArgs& a, hipStream_t s) {
 // Shared query block: dQ[i, h, :] = the sum of the samples' fp32 gradient rows for query i. A
 // workgroup owns one (i, h); each thread holds 4 columns of a row and takes the samples s,
 // s + S, s + 2S, ... (S = 256 / (D / 4) rows in flight), then one thread per 4 columns adds
-// the S partial sums in order. The order is fixed, so the result is bitwise reproducible. Only
+// the S partial sums in order. The order is fixed, so the result is bitwise reproducible; it is
+// rounded once to bf16, or written in fp32 for fp32 problems. Only
 // 256 workgroups run for the PMA shape, so a thread issues the offsets of U samples, then their
 // U row loads, before it adds anything: two memory latencies per U samples.
-template <int D>
+template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void dq_shared_reduce(DqSharedArgs a) {
   constexpr int LPR = D / 4, S = 256 / LPR, U = 16;
   __shared__ f32x4 red[256];
@@ -477,8 +478,12 @@ __global__ __launch_bounds__(256) void dq_shared_reduce(DqSharedArgs a) {
   if (tid < LPR) {
     f32x4 t = red[c];
     for (int k = 1; k < S; ++k) t += red[k * LPR + c];
-    const bf16x2 lo = pack_bf16(t[0], t[1]), hi = pack_bf16(t[2], t[3]);
-    *(bf16x4*)((__bf16*)a.dQ + ((int64_t)i * a.H + h) * D + 4 * c) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+    if (F32OUT) {
+      *(f32x4*)((float*)a.dQ + ((int64_t)i * a.H + h) * D + 4 * c) = t;
+    } else {
+      const bf16x2 lo = pack_bf16(t[0], t[1]), hi = pack_bf16(t[2], t[3]);
+      *(bf16x4*)((__bf16*)a.dQ + ((int64_t)i * a.H + h) * D + 4 * c) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
+    }
   }
 }
 
@@ -487,10 +492,17 @@ hipError_t launch_dq_shared_reduce(const DqSharedArgs& a, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (n > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n);
-  if (a.D == 32) hipLaunchKernelGGL(dq_shared_reduce<32>, grid, dim3(256), 0, s, a);
-  else if (a.D == 64) hipLaunchKernelGGL(dq_shared_reduce<64>, grid, dim3(256), 0, s, a);
-  else if (a.D == 128) hipLaunchKernelGGL(dq_shared_reduce<128>, grid, dim3(256), 0, s, a);
-  else return hipErrorInvalidValue;
+  if (a.f32_out) {
+    if (a.D == 32) hipLaunchKernelGGL((dq_shared_reduce<32, true>), grid, dim3(256), 0, s, a);
+    else if (a.D == 64) hipLaunchKernelGGL((dq_shared_reduce<64, true>), grid, dim3(256), 0, s, a);
+    else if (a.D == 128) hipLaunchKernelGGL((dq_shared_reduce<128, true>), grid, dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (a.D == 32) hipLaunchKernelGGL((dq_shared_reduce<32, false>), grid, dim3(256), 0, s, a);
+    else if (a.D == 64) hipLaunchKernelGGL((dq_shared_reduce<64, false>), grid, dim3(256), 0, s, a);
+    else if (a.D == 128) hipLaunchKernelGGL((dq_shared_reduce<128, false>), grid, dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

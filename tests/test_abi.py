@@ -55,13 +55,17 @@ def test_workspace_size_validation():
 
 
 def test_window_validation():
-    """A sliding window needs causal bf16 D = 128; a negative window is an argument error."""
+    """A sliding window needs causal attention on the fp32 kernels or the bf16 D = 128 ones; a
+    negative window is an argument error."""
     ok = gdpa.problem(4, 2, 128, 100, 100, causal=True, window=33)
     assert gdpa.workspace_size(ok) >= 256 and gdpa.workspace_size(ok, True) >= 256
+    for D in (32, 64, 128):
+        f32 = gdpa.problem(4, 2, D, 100, 100, causal=True, window=8, dtype="f32")
+        assert gdpa.workspace_size(f32, True) >= 256
     for kw, status in [(dict(D=128, causal=True, window=-1), 1),
                        (dict(D=128, causal=False, window=8), 2),
                        (dict(D=64, causal=True, window=8), 2),
-                       (dict(D=128, causal=True, window=8, dtype="f32"), 2),
+                       (dict(D=64, causal=False, window=8, dtype="f32"), 2),
                        (dict(D=128, causal=True, window=8, dtype="mxfp8"), 2)]:
         D = kw.pop("D")
         with pytest.raises(gdpa.GdpaError) as e:
@@ -70,15 +74,16 @@ def test_window_validation():
 
 
 def test_shared_query_validation():
-    """A shared query block needs bf16 and max_q >= 1; the backward workspace then holds the
-    per-sample fp32 query gradients (total_q * H * D floats) on top of the unshared layout."""
+    """A shared query block needs bf16 or fp32 and max_q >= 1; the backward workspace then holds
+    the per-sample fp32 query gradients (total_q * H * D floats) on top of the unshared layout."""
     kw = dict(max_q=32)
     ok = gdpa.problem(8, 2, 64, 256, 1000, q_shared=True, **kw)
     base = gdpa.problem(8, 2, 64, 256, 1000, **kw)
     assert gdpa.workspace_size(ok) == gdpa.workspace_size(base)
     assert gdpa.workspace_size(ok, True) >= gdpa.workspace_size(base, True) + 256 * 2 * 64 * 4
+    f32 = gdpa.problem(8, 2, 64, 256, 1000, q_shared=True, dtype="f32", **kw)
+    assert gdpa.workspace_size(f32, True) >= 256 * 2 * 64 * 4
     for prob, status in [(gdpa.problem(8, 2, 64, 256, 1000, q_shared=True), 1),  # max_q = 0
-                         (gdpa.problem(8, 2, 64, 256, 1000, q_shared=True, dtype="f32", **kw), 2),
                          (gdpa.problem(8, 2, 128, 256, 1000, q_shared=True, dtype="mxfp8", **kw),
                           2)]:
         with pytest.raises(gdpa.GdpaError) as e:

@@ -187,3 +187,33 @@ def test_shared_query_sample_longer_than_block_is_a_device_error():
             gdpa.bwd(sd, d["K"], d["V"], O, d["dO"], None, d["q_off"], d["kv_off"], act="silu",
                      q_shared=True, workspace=ws)
         assert gdpa.read_device_error(ws) == 1
+
+
+@pytest.mark.parametrize("D,act,nb,causal", [(32, "silu", 0, False), (64, "softmax", 8, True),
+                                             (128, "gelu_tanh", 0, False)])
+def test_shared_query_f32(D, act, nb, causal):
+    """fp32 kernels with the shared seed block: Q read at row i for every sample, per-sample
+    fp32 query gradients summed over samples in a fixed order (kept in fp32)."""
+    from jagged_attention_recommendation_amd import gdpa
+    rng = np.random.default_rng(900 + D)
+    lq = rng.integers(0, 21, 10)
+    lq[0] = 20
+    lk = rng.integers(1, 150, 10)
+    p = inputs.make_problem(f"shared_f32_D{D}_{act}", seed=900 + D, H=2, D=D, lq=lq, lk=lk,
+                            dtype="f32", act=act, causal=causal, bias_buckets=nb, shared_q=True)
+    d = to_device(p)
+    sd = torch.from_numpy(np.ascontiguousarray(p.seeds)).cuda()
+    kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=d["bias"])
+    O, lse = gdpa.fwd(sd, d["K"], d["V"], d["q_off"], d["kv_off"], q_shared=True,
+                      total_q=p.total_q, **kw)
+    dq, dk, dv, dbias = gdpa.bwd(sd, d["K"], d["V"], O, d["dO"], lse, d["q_off"], d["kv_off"],
+                                 q_shared=True, **kw)
+    torch.cuda.synchronize()
+    assert O.dtype == torch.float32 and dq.dtype == torch.float32
+    O_ref, lse_ref, rb = oracle_shared(p)
+    assert_close(O, O_ref, p.q_off, "f32", f"{p.name} O", live_rows(p, "q"))
+    if p.act == "softmax":
+        assert_lse_close(lse, lse_ref, f"{p.name} lse")
+    assert_close(dq, rb["dQ"], np.array([0, p.seeds.shape[0]]), "f32", f"{p.name} dQ (seeds)")
+    assert_close(dk, rb["dK"], p.kv_off, "f32", f"{p.name} dK", live_rows(p, "k"))
+    assert_close(dv, rb["dV"], p.kv_off, "f32", f"{p.name} dV", live_rows(p, "k"))

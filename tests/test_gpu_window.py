@@ -140,3 +140,41 @@ def test_window_beyond_every_length_is_plain_causal():
     assert_close(dk, g["dK"], p.kv_off, "bf16", "W=max dK", live_rows(p, "k"))
     assert_close(dv, g["dV"], p.kv_off, "bf16", "W=max dV", live_rows(p, "k"))
     assert_dbias_close(dbias, g["dbias"], "W=max dbias", g["dbias_scale"])
+
+
+def check_f32(p, W):
+    from jagged_attention_recommendation_amd import gdpa
+    d = to_device(p)
+    kw = dict(act=p.act, causal=True, scale=p.scale, bias=d["bias"], window=W)
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], **kw)
+    dq, dk, dv, dbias = gdpa.bwd(d["Q"], d["K"], d["V"], O, d["dO"], lse, d["q_off"], d["kv_off"],
+                                 **kw)
+    torch.cuda.synchronize()
+    bias = None if p.bias is None else p.bias.astype(np.float64)
+    Or, lser = oracle.fwd(*oracle_args(p), act=p.act, causal=True, scale=p.scale, bias=bias,
+                          window=W)
+    tag = f"{p.name} W={W}"
+    assert_close(O, Or, p.q_off, "f32", f"{tag} O", live_rows(p, "q", W))
+    if p.act == "softmax":
+        assert_lse_close(lse, lser, f"{tag} lse")
+    g = oracle.bwd(*oracle_args(p), host_f64(p, "dO"), act=p.act, causal=True, scale=p.scale,
+                   bias=bias, window=W)
+    assert_close(dq, g["dQ"], p.q_off, "f32", f"{tag} dQ", live_rows(p, "q", W))
+    assert_close(dk, g["dK"], p.kv_off, "f32", f"{tag} dK", live_rows(p, "k", W))
+    assert_close(dv, g["dV"], p.kv_off, "f32", f"{tag} dV", live_rows(p, "k", W))
+    if bias is not None:
+        err = np.abs(dbias.double().cpu().numpy() - g["dbias"])
+        assert np.all(err <= 1e-4 * max(1.0, np.sqrt((g["dbias"] ** 2).mean())) + 1e-4 * np.abs(g["dbias"]))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("act", ["softmax", "silu", "gelu_tanh"])
+def test_f32_window(D, act):
+    """fp32 kernels: the window is one more mask term (the forward also starts at the first key
+    tile an item's window reaches), every output and gradient against the oracle."""
+    rng = np.random.default_rng(130 + D)
+    lq = np.concatenate([rng.integers(1, 200, size=4), [0, 129]])
+    p = inputs.make_problem(f"win-f32-{D}-{act}", seed=130 + D, H=2, D=D, lq=lq, lk=lq,
+                            dtype="f32", act=act, causal=True, bias_buckets=24)
+    for W in (1, 17, 64, 150):
+        check_f32(p, W)
