@@ -214,9 +214,15 @@ int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err
  * how many items the last call wrote. An item is 8 int32: sample, tile, head, the tile's
  * canonical index (tiles numbered sample by sample), the first and one-past-last inner tile it
  * covers, its chunk slot (-1 when its tile is not split) and chunk index | chunk count << 16.
- * Items are listed by non-increasing inner-tile count (hi - lo, counted up to 1023). The tiles
- * are those of the page named above, JFA paragraph: short sequences must not idle the GPU, so
- * the list orders and splits work by cost. */
+ * Placement: item i runs on die i % 8 of the GPU. The (sample, head) groups are ranked by cost
+ * (inner tiles, all of the group's items), largest first, and dealt to the dies in a snake
+ * (0..7, 7..0, ...); each die lists its groups in rank order, a group's items consecutive with
+ * its costliest tile first, and its q-th item takes index 8q + die. Header words 7..14 (list 0)
+ * and 15..22 (list 1) hold each die's item count c_x. Die x takes indices 8q + x for
+ * q < t_x = floor(n / 8) + (x < n mod 8 ? 1 : 0); a die with c_x > t_x passes its last items,
+ * in order, to the dies with c_x < t_x (dies in increasing order, each from q = c_x on), so
+ * the list of n items is dense. The tiles are those of the page named above, JFA paragraph: short sequences
+ * must not idle the GPU, so the list balances and splits work by cost. */
 int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
                        int64_t* capacity);
 

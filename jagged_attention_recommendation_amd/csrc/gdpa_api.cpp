@@ -79,7 +79,7 @@ int bwd_k_item(int dtype) { return dtype == GDPA_F32 ? F32_BN : BWD_K_ITEM; }
 int bwd_q_loop(int dtype) { return dtype == GDPA_F32 ? F32_BM : BWD_Q_LOOP; }
 
 struct FwdLayout {
-  size_t header, items, split_cnt, part_o, part_ml, total;
+  size_t header, items, sched, split_cnt, part_o, part_ml, total;
   int64_t max_items;
   bool split;
   int slots;  // chunk slots (0 without splitting)
@@ -93,7 +93,8 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
   L.max_items = items_bound(p->total_q, p->B, p->H, fwd_tile_rows(p->dtype), L.slots);
   L.header = 0;
   L.items = ALIGN;
-  L.split_cnt = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.sched = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.split_cnt = L.sched + align_up(sched_scratch_bytes(p->B, p->H));
   L.part_o = L.part_ml = L.total = L.split_cnt;
   if (L.split) {
     const size_t rows = (size_t)L.slots * fwd_tile_rows(p->dtype);
@@ -105,7 +106,7 @@ FwdLayout fwd_layout(const gdpa_problem* p) {
 }
 
 struct BwdLayout {
-  size_t header, items_q, items_k, dvec, tile_base, part, part_bh, split_cnt_q, split_cnt_k,
+  size_t header, items_q, items_k, sched_q, sched_k, dvec, tile_base, part, part_bh, split_cnt_q, split_cnt_k,
       split_slot, part_dq, part_dk, part_dv, part_x, dq_f32, total;
   int64_t max_q_items, max_k_items, max_qtiles;
   bool split, split_q, split_k;  // split storage present / per list
@@ -126,7 +127,9 @@ BwdLayout bwd_layout(const gdpa_problem* p) {
   L.header = 0;
   L.items_q = ALIGN;
   L.items_k = L.items_q + align_up((size_t)L.max_q_items * sizeof(Item));
-  L.dvec = L.items_k + align_up((size_t)L.max_k_items * sizeof(Item));
+  L.sched_q = L.items_k + align_up((size_t)L.max_k_items * sizeof(Item));
+  L.sched_k = L.sched_q + align_up(sched_scratch_bytes(p->B, p->H));
+  L.dvec = L.sched_k + align_up(sched_scratch_bytes(p->B, p->H));
   L.tile_base = L.dvec + align_up((size_t)p->total_q * p->H * sizeof(float));
   L.part = L.tile_base + align_up((size_t)(p->B + 1) * sizeof(int32_t));
   L.part_bh = L.part;
@@ -358,6 +361,7 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.tile_base = nullptr; sa.split_slot = nullptr;
   sa.ws_header = ws + L.header; sa.items = ws + L.items;
   sa.split_cnt = (int32_t*)(ws + L.split_cnt);
+  set_sched_scratch(sa, ws + L.sched, p->B);
   hipError_t e = launch_sched(sa, s);
   if (e != hipSuccess) return map_hip(e);
 
@@ -427,6 +431,8 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sk.tile_base = nullptr; sk.items = ws + L.items_k;
   sk.split_cnt = (int32_t*)(ws + L.split_cnt_k);
   sk.split_slot = nullptr;
+  set_sched_scratch(sq, ws + L.sched_q, p->B);
+  set_sched_scratch(sk, ws + L.sched_k, p->B);
   hipError_t e = launch_sched2(sq, sk, s);
   if (e != hipSuccess) return map_hip(e);
 
@@ -506,7 +512,7 @@ int32_t check_block_problem(const gdpa_block_problem* p) {
 }
 
 struct BlockLayout {
-  size_t items, total;
+  size_t items, sched, total;
   int64_t max_items;
 };
 
@@ -514,7 +520,8 @@ BlockLayout block_layout(const gdpa_block_problem* p) {
   BlockLayout L;
   L.max_items = items_bound(p->total, p->B, p->H, BLOCK_TOKENS, 0);
   L.items = ALIGN;
-  L.total = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.sched = L.items + align_up((size_t)L.max_items * sizeof(Item));
+  L.total = L.sched + align_up(sched_scratch_bytes(p->B, p->H));
   return L;
 }
 
@@ -534,6 +541,7 @@ int32_t block_call(const gdpa_block_problem* p, const int32_t* offsets, BlockArg
   sa.max_items = (int)L.max_items; sa.list = 0; sa.split = 0; sa.nslot = SPLIT_NSLOT;
   sa.tile_base = nullptr; sa.split_slot = nullptr; sa.split_cnt = nullptr;
   sa.ws_header = ws; sa.items = ws + L.items;
+  set_sched_scratch(sa, ws + L.sched, p->B);
   hipError_t e = launch_sched(sa, s);
   if (e != hipSuccess) return map_hip(e);
   ba.off = offsets; ba.hdr = ws; ba.items = ws + L.items; ba.H = p->H; ba.scale = p->scale;

@@ -511,7 +511,10 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)(srt + w * QL), 4, r * H * 4, 0, 0, 0);
     }
   };
-  if (t_lo < t_hi) issue(sq0, so0, rt, qt0 + t_lo);
+  // Query tiles are visited last to first: every key tile of a sample then starts at the same
+  // query tile, so the key tiles of one (sample, head), which the scheduler starts together on
+  // one die, stream the shared query tiles through its L2 in step.
+  if (t_lo < t_hi) issue(sq0, so0, rt, qt0 + t_hi - 1);
 
   bf16x8 kop[D / 16], vop[D / 16];
 #pragma unroll
@@ -668,20 +671,20 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   // Two stages, as in the dQ kernel.
   GDPA_LDS float* rt0 = rt;
   GDPA_LDS float* rt1 = rt + (SM ? 2 * QL : 0);
-  for (int t = t_lo; t < t_hi; t += 2) {
+  for (int t = t_hi - 1; t >= t_lo; t -= 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < t_hi) issue(sq1, so1, rt1, qt0 + t + 1);
+    if (t - 1 >= t_lo) issue(sq1, so1, rt1, qt0 + t - 1);
     {
       const int i0 = (qt0 + t) * QL;
       if (wave_needs(i0)) tile(sq0, so0, rt0, i0);
     }
-    if (t + 1 >= t_hi) break;
+    if (t - 1 < t_lo) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 2 < t_hi) issue(sq0, so0, rt0, qt0 + t + 2);
+    if (t - 2 >= t_lo) issue(sq0, so0, rt0, qt0 + t - 2);
     {
-      const int i0 = (qt0 + t + 1) * QL;
+      const int i0 = (qt0 + t - 1) * QL;
       if (wave_needs(i0)) tile(sq1, so1, rt1, i0);
     }
   }

@@ -52,7 +52,9 @@ struct WsHeader {
   int n_split2;   // split tiles of the second list
   int chunk;      // inner tiles per chunk, first list (0: no splitting)
   int chunk2;     // inner tiles per chunk, second list
-  int pad[57];
+  int die_items[8];   // items placed on each die as their group's own (first list)
+  int die_items2[8];  // same, second list
+  int pad[41];
 };
 
 constexpr float LOG2E = 1.4426950408889634f;

@@ -50,7 +50,26 @@ struct SchedArgs {
   int32_t* split_cnt;        // [2 * nslot] chunk counters, indexed by a split tile's first slot
   void* ws_header;
   void* items;
+  // per-sample and per-group values of batches larger than one scheduler workgroup holds in LDS
+  // (sched_scratch_bytes; unused otherwise)
+  unsigned long long* scratch_cost;  // [B]
+  int32_t* scratch_nch;              // [B]
+  int32_t* scratch_rank;             // [B]
+  int32_t* scratch_at;               // [B]
+  int32_t* scratch_gpre;             // [B * H]
 };
+
+// Workspace bytes of one list's scheduler scratch, and where its arrays sit in it.
+inline size_t sched_scratch_bytes(int B, int H) {
+  return (size_t)B * (8 + 3 * 4) + (size_t)B * H * 4;
+}
+inline void set_sched_scratch(SchedArgs& a, char* p, int B) {
+  a.scratch_cost = (unsigned long long*)p;
+  a.scratch_nch = (int32_t*)(p + (size_t)B * 8);
+  a.scratch_rank = a.scratch_nch + B;
+  a.scratch_at = a.scratch_rank + B;
+  a.scratch_gpre = a.scratch_at + B;
+}
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);

@@ -4,16 +4,28 @@
 // How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA paragraph; the GDPA
 // paragraph adds that short or asymmetric K/V and large batches break occupancy assumptions and
 // that scheduling was redesigned). The scheduler turns the offsets into a list of equal-shaped
-// work items, one per (sample, head, tile), sorted by decreasing cost: the cost of an item is the
-// number of inner-loop tiles it visits (all tiles, or only those allowed by causal masking).
-// Workgroups are handed out by the hardware in index order, so the longest items start first
-// and short ones fill the gaps at the end (longest-processing-time-first list scheduling).
+// work items, one per (sample, head, tile) or per chunk of a long tile. The cost of an item is
+// the number of inner-loop tiles it visits (all tiles, or only those allowed by causal masking
+// and the sliding window).
+//
+// Placement. The GPU has eight accelerator dies, each with its own L2 cache; the dispatcher
+// hands workgroup i to die i % 8, and each die consumes its own workgroups in index order. The
+// items of one (sample, head) group all read the same K and V (query tiles) or Q and dO (key
+// tiles), so a group is kept on one die: groups are ranked by cost, largest first, and dealt to
+// the dies in a snake (0..7, 7..0, ...), which balances the dies' total cost. On each die the
+// groups run in rank order with a group's items consecutive (costliest tile first), so a group's
+// items start together and stream the shared operand through that die's L2 in step, and the
+// cheapest groups fill the end. Die x's q-th item goes to list index 8q + x; when the dies hold
+// different item counts, the surplus at the end of a longer die's sequence fills the missing
+// indices of the shorter ones, so the list stays dense. Equal-cost groups are ranked in no fixed
+// order, which cannot change results: every item computes its outputs on its own, and split
+// tiles combine their chunks in chunk order.
 //
 // One workgroup of 1024 threads per list (the backward builds its query-tile and key-tile lists
-// in one launch). Samples are walked in chunks of 1024: a scan of their tile counts gives each
-// tile a canonical index, threads then take tiles (not samples) so long samples do not serialise.
-// The relative order of equal-cost items is not fixed, which cannot change results: every item
-// computes its outputs on its own.
+// in one launch). Samples are walked in chunks of 1024, a scan of their tile counts gives each
+// tile a canonical index, and threads then take tiles (not samples) so long samples do not
+// serialise. Per-sample values live in LDS when the batch fits one chunk, else in workspace
+// scratch.
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
 
@@ -21,6 +33,8 @@ namespace gdpa {
 
 constexpr int NBUCKET = 1024;
 constexpr int SNT = 1024;
+constexpr int XCDS = 8;      // accelerator dies
+constexpr int GCAP = 8192;   // (sample, head) groups whose placement table fits in LDS
 
 // Inner tiles an item visits. Query-tile items (forward, dQ) visit key tiles
 // [first, last): all of them, or up to the causal limit, and with a sliding window of W keys
@@ -50,12 +64,35 @@ __device__ __forceinline__ int item_cost(int mode, int causal, int win, int Lq, 
   return max(0, nq - first);
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+// Rank bucket of a group cost, larger costs first: exact below 512, then eight buckets per
+// octave.
+__device__ __forceinline__ int cost_bucket(unsigned long long c) {
+  int key;
+  if (c < 512) {
+    key = (int)c;
+  } else {
+    const int o = 63 - __clzll(c);  // 9 .. 63
+    key = min(NBUCKET - 1, 512 + (o - 9) * 8 + (int)((c >> (o - 3)) & 7));
   }
+  return NBUCKET - 1 - key;
+}
+
+// Die of group rank r (snake over the dies) and its rank among that die's groups.
+__device__ __forceinline__ int group_xcd(int r) {
+  const int s = r & 15;
+  return s < XCDS ? s : 2 * XCDS - 1 - s;
+}
+
+// Inclusive scan over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4 and 8 within
+// each row of 16 lanes, then row 0's total into row 1, row 2's into row 3, and lane 31's running
+// total into rows 2 and 3. A lane whose source falls outside its row adds zero.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
@@ -64,11 +101,11 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 __device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
   const int lane = tid & 63, w = tid >> 6;
   __syncthreads();
-  int x = wave_incl_scan(buf[tid], lane);
+  int x = wave_incl_scan(buf[tid]);
   if (lane == 63) wsum[w] = x;
   __syncthreads();
   if (w == 0) {
-    const int v = wave_incl_scan(lane < SNT / 64 ? wsum[lane] : 0, lane);
+    const int v = wave_incl_scan(lane < SNT / 64 ? wsum[lane] : 0);
     if (lane < SNT / 64) wsum[lane] = v;
   }
   __syncthreads();
@@ -78,31 +115,104 @@ __device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
 
 __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) {
   const SchedArgs& a = blockIdx.x == 0 ? a0 : a1;
-  __shared__ int bucket[NBUCKET];
-  __shared__ int cnt[SNT];  // inclusive scan of the chunk's per-sample tile counts
+  __shared__ int cnt[SNT];   // inclusive scan of the chunk's per-sample tile counts
+  __shared__ int sbuf[SNT];  // scan of chunk counts per tile
   __shared__ int wsum[SNT / 64];
+  __shared__ int lq_c[SNT], lk_c[SNT];  // lengths of the chunk's samples
+  __shared__ unsigned long long ccost[SNT];  // per-sample cost (one head) of the chunk
+  __shared__ int cnch[SNT];                  // per-sample item count (one head) of the chunk
+  __shared__ int first_e[SNT];               // chunk index of each sample's first tile
+  __shared__ int s_rank[SNT], s_at[SNT];     // rank of a sample / sample of a rank
+  __shared__ int s_gpre[GCAP];               // first position of each group on its die
+  __shared__ int bucket[NBUCKET];
+  __shared__ int xtot[XCDS], tgt[XCDS], spre[XCDS], dpre[XCDS + 1];
   __shared__ int err, carry, split_count, slot_count;
   __shared__ unsigned long long wtot[SNT / 64];
   __shared__ int wmax[SNT / 64];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   WsHeader* hdr = (WsHeader*)a.ws_header;
   Item* items = (Item*)a.items;
-  for (int i = tid; i < NBUCKET; i += SNT) bucket[i] = 0;
-  if (tid == 0) err = 0;
-  __syncthreads();
-  for (int b = tid; b < a.B; b += SNT) {
-    if (a.q_off[b + 1] < a.q_off[b]) atomicOr(&err, 1);
-    if (a.q_rows > 0 && a.q_off[b + 1] - a.q_off[b] > a.q_rows) atomicOr(&err, 1);
-    if (a.kv_off[b + 1] < a.kv_off[b]) atomicOr(&err, 2);
-  }
+  const int B = a.B, H = a.H, G = B * H;
   if (tid == 0) {
-    if (a.q_off[0] != 0 || (int64_t)a.q_off[a.B] != a.total_q) atomicOr(&err, 1);
-    if (a.kv_off[0] != 0 || (int64_t)a.kv_off[a.B] != a.total_kv) atomicOr(&err, 2);
+    // the offsets' ends; each sample's own lengths are checked as its chunk is loaded
+    int e = 0;
+    if (a.q_off[0] != 0 || (int64_t)a.q_off[B] != a.total_q) e |= 1;
+    if (a.kv_off[0] != 0 || (int64_t)a.kv_off[B] != a.total_kv) e |= 2;
+    err = e;
+  }
+  // per-sample values: LDS when the batch is one chunk, else the workspace scratch
+  const bool small = B <= SNT;
+  unsigned long long* cost = small ? ccost : a.scratch_cost;
+  int* nch = small ? cnch : a.scratch_nch;
+  int* rank = small ? s_rank : a.scratch_rank;
+  int* at = small ? s_at : a.scratch_at;
+  int* gpre = G <= GCAP ? s_gpre : a.scratch_gpre;
+
+  const int ti = a.tile_item, tl = a.tile_loop;
+  const bool qmode = a.mode == SCHED_QTILES;
+  // Load chunk [base, base + SNT) of samples (lengths, tile-count scan); returns its tile count.
+  // A sample with a negative length (or more queries than a shared query block holds) sets the
+  // error word and counts as empty.
+  auto load_chunk = [&](int base) {
+    const int b = base + tid;
+    int n = 0;
+    __syncthreads();
+    if (b < B) {
+      int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
+      const int e = (Lq < 0 || (a.q_rows > 0 && Lq > a.q_rows) ? 1 : 0) | (Lk < 0 ? 2 : 0);
+      if (e != 0) {
+        atomicOr(&err, e);
+        Lq = Lk = 0;
+      }
+      lq_c[tid] = Lq;
+      lk_c[tid] = Lk;
+      n = qmode ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
+    }
+    cnt[tid] = n;
+    block_scan(cnt, wsum, tid);
+    return cnt[SNT - 1];
+  };
+  // local sample and tile of the chunk's tile u
+  auto locate = [&](int u, int& bl, int& t) {
+    int lo = 0, hi = SNT - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cnt[mid] > u) hi = mid; else lo = mid + 1;
+    }
+    bl = lo;
+    t = u - (lo > 0 ? cnt[lo - 1] : 0);
+  };
+  auto cost_of = [&](int bl, int t) { return item_cost(a.mode, a.causal, a.win, lq_c[bl], lk_c[bl], t, ti, tl); };
+
+  // 1. per-sample cost (one head), total cost and the largest tile cost
+  unsigned long long tot = 0;
+  int mx = 0;
+  for (int base = 0; base < B; base += SNT) {
+    const int total = load_chunk(base);
+    if (err != 0) break;  // read after the scan's barrier: uniform
+    ccost[tid] = 0;
+    cnch[tid] = base + tid < B ? cnt[tid] - (tid > 0 ? cnt[tid - 1] : 0) : 0;  // tiles
+    __syncthreads();
+    for (int u = tid; u < total; u += SNT) {
+      int bl, t;
+      locate(u, bl, t);
+      const int c = cost_of(bl, t);
+      atomicAdd(&ccost[bl], (unsigned long long)c);
+      tot += (unsigned long long)c;
+      mx = max(mx, c);
+    }
+    __syncthreads();
+    if (!small && base + tid < B) {
+      cost[base + tid] = ccost[tid];
+      nch[base + tid] = cnch[tid];
+    }
   }
   __syncthreads();
   if (err != 0) {
     if (tid == 0) {
       hdr->error = err;
+      int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
+      for (int x = 0; x < XCDS; ++x) die[x] = 0;
       if (a.list == 0) {
         hdr->n_items = 0; hdr->n_split = 0;
       } else {
@@ -111,51 +221,6 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     }
     return;
   }
-  const int ti = a.tile_item, tl = a.tile_loop;
-  auto ntiles = [&](int b) {
-    const int Lq = a.q_off[b + 1] - a.q_off[b];
-    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    return a.mode == SCHED_QTILES ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
-  };
-  // Walk the samples chunk by chunk; for every tile of the chunk call f(b, t, canonical index).
-  auto for_each_tile = [&](auto&& f) {
-    if (tid == 0) carry = 0;
-    for (int base = 0; base < a.B; base += SNT) {
-      const int b = base + tid;
-      const int n = b < a.B ? ntiles(b) : 0;
-      __syncthreads();
-      cnt[tid] = n;
-      block_scan(cnt, wsum, tid);
-      const int total = cnt[SNT - 1];
-      const int first = carry;
-      for (int u = tid; u < total; u += SNT) {
-        // sample of tile u: first index k with cnt[k] > u
-        int lo = 0, hi = SNT - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (cnt[mid] > u) hi = mid; else lo = mid + 1;
-        }
-        const int t = u - (lo > 0 ? cnt[lo - 1] : 0);
-        f(base + lo, t, first + u);
-      }
-      if (a.tile_base != nullptr && b < a.B) a.tile_base[b] = first + cnt[tid] - n;
-      __syncthreads();
-      if (tid == 0) carry = first + total;
-      __syncthreads();
-    }
-  };
-  // 1. histogram of tile costs (bucket NBUCKET-1-cost puts expensive items first), and with
-  //    splitting the total cost (all heads) and the largest tile cost, reduced over the block
-  unsigned long long tot = 0;
-  int mx = 0;
-  for_each_tile([&](int b, int t, int) {
-    const int Lq = a.q_off[b + 1] - a.q_off[b];
-    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
-    atomicAdd(&bucket[NBUCKET - 1 - min(c, NBUCKET - 1)], a.H);
-    tot += (unsigned long long)c;
-    mx = max(mx, c);
-  });
   int T = 0x7fffffff;  // chunk length; no splitting unless a tile costs more
   if (a.split) {
 #pragma unroll
@@ -163,9 +228,9 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       tot += __shfl_xor(tot, off, 64);
       mx = max(mx, __shfl_xor(mx, off, 64));
     }
-    if ((tid & 63) == 0) {
-      wtot[tid >> 6] = tot;
-      wmax[tid >> 6] = mx;
+    if (lane == 0) {
+      wtot[wv] = tot;
+      wmax[wv] = mx;
     }
     __syncthreads();
     unsigned long long total = 0;
@@ -174,85 +239,166 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       total += wtot[w];
       biggest = max(biggest, wmax[w]);
     }
-    total *= (unsigned long long)a.H;
+    total *= (unsigned long long)H;
     const unsigned long long tpc = (total + a.nslot - 1) / a.nslot;
     const int t_mean = (int)min(max(tpc, (unsigned long long)SPLIT_MIN_TILES), (unsigned long long)0x7fffffff);
-    if (biggest > t_mean) {
-      T = t_mean;
-      // some tiles are split: the histogram counts chunks instead
-      __syncthreads();
-      bucket[tid] = 0;
-      __syncthreads();
-      for_each_tile([&](int b, int t, int) {
-        const int Lq = a.q_off[b + 1] - a.q_off[b];
-        const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-        const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
-        const int n = c > T ? (c + T - 1) / T : 1;
-        for (int k = 0; k < n; ++k) {
-          const int cc = n == 1 ? c : min(T, c - k * T);
-          atomicAdd(&bucket[NBUCKET - 1 - min(cc, NBUCKET - 1)], a.H);
-        }
-      });
-    }
-  }
-  if (tid == 0) {
-    split_count = 0;
-    slot_count = 0;
+    if (biggest > t_mean) T = t_mean;
   }
   // chunks of a tile of cost c: ceil(c / T) when c > T (the last one may be shorter), else one
   auto chunks = [&](int c) { return c > T ? (c + T - 1) / T : 1; };
+  if (T != 0x7fffffff) {
+    // 1b. with split tiles a sample's item count is its chunk count
+    for (int base = 0; base < B; base += SNT) {
+      const int total = small ? cnt[SNT - 1] : load_chunk(base);
+      cnch[tid] = 0;
+      __syncthreads();
+      for (int u = tid; u < total; u += SNT) {
+        int bl, t;
+        locate(u, bl, t);
+        atomicAdd(&cnch[bl], chunks(cost_of(bl, t)));
+      }
+      __syncthreads();
+      if (!small && base + tid < B) nch[base + tid] = cnch[tid];
+    }
+  }
+  // 2. rank the samples by cost, largest first (counting sort over cost buckets)
+  for (int i = tid; i < NBUCKET; i += SNT) bucket[i] = 0;
   __syncthreads();
-  // 2. exclusive scan over the buckets (NBUCKET == SNT)
+  for (int b = tid; b < B; b += SNT) atomicAdd(&bucket[cost_bucket(cost[b])], 1);
+  __syncthreads();
   const int own = bucket[tid];
-  block_scan(bucket, wsum, tid);
-  const int total_items = bucket[NBUCKET - 1];
-  __syncthreads();
+  block_scan(bucket, wsum, tid);  // NBUCKET == SNT
   bucket[tid] -= own;
   __syncthreads();
-  // 3. scatter the chunks (b, tile, h, canonical tile index, inner range, slot, chunk); a split
-  //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared
-  for_each_tile([&](int b, int t, int canon) {
-    const int Lq = a.q_off[b + 1] - a.q_off[b];
-    const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const int c = item_cost(a.mode, a.causal, a.win, Lq, Lk, t, ti, tl);
-    const int n = chunks(c);
-    int sbase = -1;
-    if (n > 1) {
-      sbase = atomicAdd(&slot_count, n * a.H);
-      atomicAdd(&split_count, a.H);
-      if (sbase + n * a.H > 2 * a.nslot) {
-        atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
-        sbase = -1;
-      } else {
-        for (int h = 0; h < a.H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
-      }
+  for (int b = tid; b < B; b += SNT) {
+    const int r = atomicAdd(&bucket[cost_bucket(cost[b])], 1);
+    rank[b] = r;
+    if (r < B) at[r] = b;
+  }
+  __syncthreads();
+  // 3. group r = rank * H + head goes to die group_xcd(r); wave x lays out die x's groups in rank
+  //    order: gpre[r] is the group's first position on its die, xtot[x] the die's item count.
+  //    Round k of sixteen ranks holds die x's groups 16k + x and 16k + 15 - x, in that order.
+  if (wv < XCDS) {
+    const int x = wv;
+    int run = 0;
+    for (int k0 = 0; 16 * k0 < G; k0 += 64) {
+      const int k = k0 + lane;
+      const int r0 = 16 * k + x, r1 = 16 * k + 2 * XCDS - 1 - x;
+      const int n0 = r0 < G ? nch[at[r0 / H]] : 0;
+      const int n1 = r1 < G ? nch[at[r1 / H]] : 0;
+      const int incl = wave_incl_scan(n0 + n1);
+      const int excl = run + incl - (n0 + n1);
+      if (r0 < G) gpre[r0] = excl;
+      if (r1 < G) gpre[r1] = excl + n0;
+      run += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (a.split_slot != nullptr)
-      for (int h = 0; h < a.H; ++h) a.split_slot[(int64_t)canon * a.H + h] = sbase < 0 ? -1 : sbase + h * n;
-    for (int k = 0; k < n; ++k) {
-      const int cc = n == 1 ? c : min(T, c - k * T);
-      const int pos = atomicAdd(&bucket[NBUCKET - 1 - min(cc, NBUCKET - 1)], a.H);
-      for (int h = 0; h < a.H; ++h) {
-        if (pos + h < a.max_items) {
-          Item it;
-          it.b = b; it.tile = t; it.h = h; it.aux = canon;
-          it.lo = n == 1 ? 0 : k * T;
-          it.hi = n == 1 ? c : min(c, (k + 1) * T);
-          it.slot = sbase < 0 ? -1 : sbase + h * n + k;
-          it.chunk = sbase < 0 ? 0 : k | (n << 16);
-          items[pos + h] = it;
+    if (lane == 0) xtot[x] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int x = 0; x < XCDS; ++x) n += xtot[x];
+    int sp = 0, dp = 0;
+    for (int x = 0; x < XCDS; ++x) {
+      tgt[x] = n / XCDS + (x < n % XCDS ? 1 : 0);  // indices x, x + 8, ... below n
+      spre[x] = sp;
+      dpre[x] = dp;
+      sp += max(0, xtot[x] - tgt[x]);
+      dp += max(0, tgt[x] - xtot[x]);
+    }
+    dpre[XCDS] = dp;
+    split_count = 0;
+    slot_count = 0;
+    carry = 0;
+  }
+  __syncthreads();
+  // list index of die x's q-th item
+  auto position = [&](int x, int q) {
+    if (q < tgt[x]) return XCDS * q + x;
+    const int k = spre[x] + (q - tgt[x]);  // surplus item k fills the k-th missing index
+    int y = 0;
+    while (y < XCDS - 1 && k >= dpre[y + 1]) ++y;
+    return XCDS * (xtot[y] + k - dpre[y]) + y;
+  };
+  // 4. scatter the items (b, tile, h, canonical tile index, inner range, slot, chunk); a split
+  //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared.
+  //    Within a sample, chunks are numbered in tile order (sbuf scan); a group lists its
+  //    costliest tiles first: the last query tiles (causal), or the first key tiles.
+  for (int base = 0; base < B; base += SNT) {
+    const int total = small ? cnt[SNT - 1] : load_chunk(base);  // one chunk: still loaded
+    const int first = carry;
+    if (a.tile_base != nullptr && base + tid < B) a.tile_base[base + tid] = first + (tid > 0 ? cnt[tid - 1] : 0);
+    int run = 0;  // chunks of the chunk's earlier tiles
+    for (int u0 = 0; u0 < total; u0 += SNT) {
+      const int u = u0 + tid;
+      int bl = 0, t = 0, c = 0, n = 0;
+      if (u < total) {
+        locate(u, bl, t);
+        c = cost_of(bl, t);
+        n = chunks(c);
+      }
+      int ci = t;  // chunk number of the tile's first chunk within its sample
+      if (T != 0x7fffffff) {
+        __syncthreads();
+        sbuf[tid] = n;
+        block_scan(sbuf, wsum, tid);
+        const int e = run + sbuf[tid] - n;  // first chunk of this tile
+        if (u < total && t == 0) first_e[bl] = e;
+        __syncthreads();
+        run += sbuf[SNT - 1];
+        ci = e - first_e[bl];
+      }
+      if (u >= total) continue;
+      const int b = base + bl, canon = first + u;
+      int sbase = -1;
+      if (n > 1) {
+        sbase = atomicAdd(&slot_count, n * H);
+        atomicAdd(&split_count, H);
+        if (sbase + n * H > 2 * a.nslot) {
+          atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
+          sbase = -1;
+        } else {
+          for (int h = 0; h < H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
+        }
+      }
+      if (a.split_slot != nullptr)
+        for (int h = 0; h < H; ++h) a.split_slot[(int64_t)canon * H + h] = sbase < 0 ? -1 : sbase + h * n;
+      const int nb = small ? cnch[bl] : nch[b];
+      const int rb = rank[b];
+      for (int k = 0; k < n; ++k) {
+        Item it;
+        it.b = b; it.tile = t; it.aux = canon;
+        it.lo = n == 1 ? 0 : k * T;
+        it.hi = n == 1 ? c : min(c, (k + 1) * T);
+        it.chunk = sbase < 0 ? 0 : k | (n << 16);
+        const int w = qmode ? nb - 1 - (ci + k) : ci + k;
+        for (int h = 0; h < H; ++h) {
+          const int r = rb * H + h;
+          const int pos = position(group_xcd(r), gpre[r] + w);
+          if (pos >= 0 && pos < a.max_items) {
+            it.h = h;
+            it.slot = sbase < 0 ? -1 : sbase + h * n + k;
+            items[pos] = it;
+          }
         }
       }
     }
-  });
-  __syncthreads();
+    __syncthreads();
+    if (tid == 0) carry = first + total;
+    __syncthreads();
+  }
   if (tid == 0) {
     // Only the first list writes the error word (both lists see the same offsets); a list that
     // failed on its own is left empty.
-    if (a.tile_base != nullptr) a.tile_base[a.B] = carry;
-    const int n = err != 0 ? 0 : min(total_items, a.max_items);
+    if (a.tile_base != nullptr) a.tile_base[B] = carry;
+    int n = 0;
+    for (int x = 0; x < XCDS; ++x) n += xtot[x];
+    n = err != 0 ? 0 : min(n, a.max_items);
     const int ns = err != 0 ? 0 : split_count;
     const int chunk = a.split && T != 0x7fffffff ? T : 0;
+    int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
+    for (int x = 0; x < XCDS; ++x) die[x] = err != 0 ? 0 : xtot[x];
     if (a.list == 0) {
       hdr->error = err;
       hdr->n_items = n; hdr->n_split = ns; hdr->chunk = chunk;

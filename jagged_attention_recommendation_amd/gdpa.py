@@ -329,11 +329,15 @@ def workspace_header(workspace):
     """Scheduler counters of the last call that used this workspace (diagnostics; synchronises).
 
     Keys: error, items, items2 (forward / dQ list, dK/dV list), split, split2 (tiles split into
-    chunks), chunk, chunk2 (inner tiles per chunk; 0 when splitting is off).
+    chunks), chunk, chunk2 (inner tiles per chunk; 0 when splitting is off), die_items,
+    die_items2 (per die, the items placed there as their own group's, before the surplus of
+    longer dies fills shorter ones).
     """
     torch.cuda.synchronize(workspace.device)
-    w = workspace[:28].view(torch.int32).cpu().tolist()
-    return dict(zip(["error", "items", "items2", "split", "split2", "chunk", "chunk2"], w))
+    w = workspace[:92].view(torch.int32).cpu().tolist()
+    d = dict(zip(["error", "items", "items2", "split", "split2", "chunk", "chunk2"], w[:7]))
+    d["die_items"], d["die_items2"] = w[7:15], w[15:23]
+    return d
 
 
 def item_list(prob, workspace, for_bwd=False, which=0):

@@ -126,3 +126,12 @@ def test_bitwise_repeatable():
     b = run_fwd_bwd(p)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_batch_larger_than_one_scheduler_chunk():
+    """1,300 samples, 7 heads: the scheduler keeps its per-sample and placement tables in the
+    workspace; every output and gradient element against the oracle."""
+    rng = np.random.default_rng(1310)
+    lq = rng.integers(0, 160, size=1300)
+    check_bwd(inputs.make_problem("bwd-large-batch", seed=1311, H=7, D=128, lq=lq, lk=lq,
+                                  dtype="bf16", act="softmax", causal=True, bias_buckets=32))

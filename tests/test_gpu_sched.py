@@ -3,12 +3,15 @@
 Short sequences must not leave compute units idle while long ones finish (page "GEM Training: How
 Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation Model", JFA paragraph; the GDPA
 paragraph on redesigned scheduling for large batches and short or asymmetric K/V). The scheduler
-emits one item per (sample, tile, head), listed by decreasing cost (inner tiles visited), and cuts
-a tile that costs more than T = max(8, ceil(H * total cost / nslot)) inner tiles into ceil(cost / T)
-chunks. This file enumerates the expected items on the host from that rule and checks the GPU's
-list against it: the exact multiset of (sample, tile, head, lo, hi), non-increasing cost,
-canonical tile numbering, chunks that tile each range exactly with consecutive slots, and chunk
-words. The relative order of equal-cost items is free (any order gives the same results).
+emits one item per (sample, tile, head) and cuts a tile that costs more than
+T = max(8, ceil(H * total cost / nslot)) inner tiles into ceil(cost / T) chunks. Items are placed
+for the eight dies of the GPU: list index i runs on die i % 8, a (sample, head) group's items sit
+on one die as one run, costliest tile first, and the dies' total costs are balanced. This file
+enumerates the expected items on the host from that rule and checks the GPU's list against it:
+the exact multiset of (sample, tile, head, lo, hi), canonical tile numbering, chunks that tile
+each range exactly with consecutive slots, chunk words, one run per group and die in tile order,
+and the die balance. Which of two equal-cost groups ranks first is free (any order gives the same
+results), so the exact positions are not fixed.
 """
 from collections import Counter
 
@@ -82,14 +85,92 @@ def expected_items(lq, lk, H, mode, causal, win, ti, tl, split, nslot):
     return out, (T or 0)
 
 
-def check_list(items, exp, chunk_T, header_T, nslot):
+DIES = 8
+
+
+def cost_bucket(c):
+    """Rank bucket of a group cost (larger first): exact below 512, then eight per octave."""
+    if c < 512:
+        key = c
+    else:
+        o = int(c).bit_length() - 1
+        key = min(1023, 512 + (o - 9) * 8 + ((int(c) >> (o - 3)) & 7))
+    return 1023 - key
+
+
+def snake_rank(x, j):
+    """Group rank of the j-th group dealt to die x: ranks go 0..7 then 7..0 over the dies."""
+    return 16 * (j // 2) + (x if j % 2 == 0 else 2 * DIES - 1 - x)
+
+
+def check_placement(items, mode, H, die_items):
+    """Die placement. List index i runs on die i % 8. On every die each (sample, head) group is
+    one run whose chunks follow canonical tile order (backwards for query tiles, whose later
+    tiles cost more under causal masking). Die x holds its own groups' items at q < c_x (the
+    header's per-die counts; past that come items passed on by longer dies); reading those
+    runs in order and undoing the snake deal gives every group a rank: the head must match,
+    all heads of a sample must get the ranks s * H + h of one sample rank s, no two samples may
+    share s, and the cost buckets must not increase with s (checked up to the first cost-0
+    group, after which empty groups hold ranks unseen in the list); a sample with no rank must
+    have been passed on whole. Finally no die's total cost exceeds the mean by more than twice
+    the costliest group."""
+    n = len(items)
+    assert sum(die_items) == n
+    if n == 0:
+        return
+    cost = (items[:, 5] - items[:, 4]).astype(np.int64)
+    group_cost = Counter()
+    for it, c in zip(items, cost):
+        group_cost[(int(it[0]), int(it[2]))] += int(c)
+    sample_rank = {}
+    for x in range(DIES):
+        runs = []
+        for i in range(x, n, DIES):
+            g = (int(items[i, 0]), int(items[i, 2]))
+            if runs and runs[-1][0] == g:
+                runs[-1][1].append(i)
+            else:
+                runs.append((g, [i]))
+        groups = [g for g, _ in runs]
+        assert len(groups) == len(set(groups)), f"a group forms two runs on die {x}"
+        for g, idx in runs:
+            seq = [(int(items[i, 3]), int(items[i, 7]) & 0xFFFF) for i in idx]
+            assert seq == sorted(seq, reverse=(mode == "q")), f"group {g} out of tile order"
+        t_x = n // DIES + (1 if x < n % DIES else 0)
+        own = []
+        for i in range(x, DIES * min(t_x, die_items[x]), DIES):
+            g = (int(items[i, 0]), int(items[i, 2]))
+            if not own or own[-1] != g:
+                own.append(g)
+        for j, (b, h) in enumerate(own):
+            if group_cost[(b, h)] == 0:
+                break
+            r = snake_rank(x, j)
+            assert r % H == h, f"die {x} run {j}: head {h} where rank {r} deals head {r % H}"
+            assert sample_rank.setdefault(b, r // H) == r // H, f"sample {b} ranked twice"
+    ranked = sorted(sample_rank.items(), key=lambda kv: kv[1])
+    assert len({r for _, r in ranked}) == len(ranked), "two samples share a rank"
+    # a sample seen on no die as its own must have every item past its die's own count: a
+    # short group at the end of a longer die, passed on whole
+    own_end = [min(n // DIES + (1 if x < n % DIES else 0), die_items[x]) for x in range(DIES)]
+    for i, it in enumerate(items):
+        if int(it[0]) not in sample_rank and group_cost[(int(it[0]), int(it[2]))] > 0:
+            assert i // DIES >= own_end[i % DIES], f"sample {int(it[0])} has no rank"
+    for b, _ in ranked:
+        assert all((b, h) in group_cost for h in range(H)), f"sample {b} misses a head"
+    buckets = [cost_bucket(group_cost[(b, 0)]) for b, _ in ranked]
+    assert buckets == sorted(buckets), "samples not ranked by cost"
+    die_cost = [int(cost[x::DIES].sum()) for x in range(DIES)]
+    assert max(die_cost) <= sum(die_cost) / DIES + 2 * max(group_cost.values()), die_cost
+
+
+def check_list(items, exp, chunk_T, header_T, nslot, mode, H, die_items):
     assert header_T == chunk_T
     assert len(items) == len(exp)
     got = Counter(tuple(int(x) for x in (it[0], it[1], it[2], it[3], it[4], it[5])) for it in items)
     want = Counter(e[:6] for e in exp)
     assert got == want, "item multiset differs"
-    cost = np.minimum(items[:, 5] - items[:, 4], 1023)
-    assert np.all(np.diff(cost) <= 0), "costs are not non-increasing"
+    check_placement(items, mode, H, die_items)
     n_of = {(e[0], e[1], e[2]): e[6] for e in exp}
     slots = {}
     for it in items:
@@ -135,7 +216,7 @@ def run_and_check(p, window=0, backward=True):
     hf = gdpa.workspace_header(wf)
     assert hf["error"] == 0
     exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, fi, fl, bf16, nslot)
-    check_list(gdpa.item_list(prob, wf), exp, T, hf["chunk"], nslot)
+    check_list(gdpa.item_list(prob, wf), exp, T, hf["chunk"], nslot, "q", p.H, hf["die_items"])
     if not backward:
         return
     wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
@@ -145,9 +226,9 @@ def run_and_check(p, window=0, backward=True):
     split_q = bf16 and (p.D == 128 or nb == 0)
     split_k = bf16 and p.D == 128
     exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, qi, ql, split_q, nslot)
-    check_list(gdpa.item_list(prob, wb, True, 0), exp, T, hb["chunk"], nslot)
+    check_list(gdpa.item_list(prob, wb, True, 0), exp, T, hb["chunk"], nslot, "q", p.H, hb["die_items"])
     exp, T = expected_items(lq, lk, p.H, "k", p.causal, win, ki, kl, split_k, nslot)
-    check_list(gdpa.item_list(prob, wb, True, 1), exp, T, hb["chunk2"], nslot)
+    check_list(gdpa.item_list(prob, wb, True, 1), exp, T, hb["chunk2"], nslot, "k", p.H, hb["die_items2"])
 
 
 @pytest.mark.parametrize("k", [2, 3, 4])
@@ -195,4 +276,14 @@ def test_small_d_and_f32_lists(dtype, D):
 def test_empty_batch():
     p = inputs.make_problem("sched-empty", seed=86, H=2, D=128, lq=np.array([0, 0]),
                             lk=np.array([0, 5]), dtype="bf16", act="softmax", causal=False)
+    run_and_check(p)
+
+
+def test_batch_larger_than_one_scheduler_chunk():
+    """1,300 samples and 7 heads: per-sample values and the group placement table no longer fit
+    the scheduler's LDS and go through the workspace scratch."""
+    rng = np.random.default_rng(87)
+    lq = rng.integers(0, 200, size=1300)
+    p = inputs.make_problem("sched-large-batch", seed=87, H=7, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=32)
     run_and_check(p)
