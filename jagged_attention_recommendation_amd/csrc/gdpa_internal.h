@@ -193,6 +193,12 @@ constexpr int BWD_K_LOOP = 64;   // keys per tile in the dQ loop (bf16)
 constexpr int BWD_K_ITEM = 128;  // keys per dK/dV work item (bf16)
 constexpr int BWD_Q_LOOP = 64;   // queries per tile in the dK/dV loop (bf16)
 
+// The scheduler divides by tile sizes with shifts: every tile size is a power of two.
+constexpr bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+static_assert(pow2(FWD_BM_BF16) && pow2(FWD_BN_BF16) && pow2(F32_BM) && pow2(F32_BN) &&
+                  pow2(BWD_Q_ITEM) && pow2(BWD_K_LOOP) && pow2(BWD_K_ITEM) && pow2(BWD_Q_LOOP),
+              "tile sizes must be powers of two");
+
 hipError_t launch_bwd_bf16(const Prob& p, const BwdArgs& a, int grid_q, int grid_k, hipStream_t s);
 
 // Which lists of this problem take split items (the last chunk of a split tile combines the
@@ -209,6 +215,7 @@ hipError_t launch_bwd_f32(const Prob& p, const BwdArgs& a, int grid_q, int grid_
 // attending only within itself, with rotary embeddings of Q and K (gdpa_block.hip). Items are the
 // scheduler's query tiles of BLOCK_TOKENS rows.
 constexpr int BLOCK_TOKENS = 64;
+static_assert(pow2(BLOCK_TOKENS), "tile sizes must be powers of two");
 struct BlockArgs {
   const void* Q;
   const void* K;

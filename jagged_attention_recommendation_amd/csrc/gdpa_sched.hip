@@ -34,33 +34,35 @@ namespace gdpa {
 constexpr int NBUCKET = 1024;
 constexpr int SNT = 1024;
 constexpr int XCDS = 8;      // accelerator dies
-constexpr int GCAP = 8192;   // (sample, head) groups whose placement table fits in LDS
+constexpr int GCAP = 4096;   // (sample, head) groups whose placement table fits in LDS
+constexpr int OCAP = 16384;  // tiles of a chunk of samples whose owning sample is looked up in LDS
 
 // Inner tiles an item visits. Query-tile items (forward, dQ) visit key tiles
 // [first, last): all of them, or up to the causal limit, and with a sliding window of W keys
-// from the tile holding key t*ti - W + 1 (win_first_ktile); key-tile items (dK/dV) visit query
-// tiles from the causal start to the last query whose window reaches the item's last key. Item
-// ranges [lo, hi) count from the first visited tile.
+// from the tile holding key t*ti - W + 1; key-tile items (dK/dV) visit query tiles from the
+// causal start to the last query whose window reaches the item's last key. Item ranges [lo, hi)
+// count from the first visited tile. Tile sizes are powers of two, passed as shifts (tis, tls);
+// every quotient below has a non-negative dividend.
 __device__ __forceinline__ int item_cost(int mode, int causal, int win, int Lq, int Lk, int t,
-                                         int ti, int tl) {
+                                         int tis, int tls) {
+  const int tl = 1 << tls;
   if (mode == SCHED_QTILES) {
     if (Lk <= 0) return 0;
-    int nk = (Lk + tl - 1) / tl;
-    if (causal) {
-      int i_max = min(Lq, (t + 1) * ti) - 1;
-      nk = min(nk, i_max / tl + 1);
-    }
-    return max(0, nk - win_first_ktile(t * ti, win, tl));
+    int nk = (Lk + tl - 1) >> tls;
+    const int q_lo = t << tis;
+    if (causal) nk = min(nk, ((min(Lq, q_lo + (1 << tis)) - 1) >> tls) + 1);
+    const int first = win > 0 ? max(0, q_lo - win + 1) >> tls : 0;
+    return max(0, nk - first);
   }
   if (Lq <= 0) return 0;
-  int nq = (Lq + tl - 1) / tl;
-  const int j0 = t * ti;
+  int nq = (Lq + tl - 1) >> tls;
+  const int j0 = t << tis;
   int first = 0;
   if (causal) {
     if (j0 >= Lq) return 0;
-    first = j0 / tl;
+    first = j0 >> tls;
   }
-  nq = win_end_qtile(min(Lk, (t + 1) * ti) - 1, win, tl, nq);
+  if (win > 0) nq = min(nq, ((min(Lk, j0 + (1 << tis)) - 1 + win - 1) >> tls) + 1);
   return max(0, nq - first);
 }
 
@@ -96,6 +98,24 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Sum and maximum over the 64 lanes of a wave, returned to lane 63, with the moves of
+// wave_incl_scan (64-bit sum carried as two 32-bit halves).
+template <int CTRL, int RMASK>
+__device__ __forceinline__ void sum_max_step(unsigned long long& s, int& m) {
+  const unsigned lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)s, CTRL, RMASK, 0xf, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(s >> 32), CTRL, RMASK, 0xf, false);
+  s += ((unsigned long long)hi << 32) | lo;
+  m = max(m, __builtin_amdgcn_update_dpp(0, m, CTRL, RMASK, 0xf, false));
+}
+__device__ __forceinline__ void wave_sum_max(unsigned long long& s, int& m) {
+  sum_max_step<0x111, 0xf>(s, m);
+  sum_max_step<0x112, 0xf>(s, m);
+  sum_max_step<0x114, 0xf>(s, m);
+  sum_max_step<0x118, 0xf>(s, m);
+  sum_max_step<0x142, 0xa>(s, m);
+  sum_max_step<0x143, 0xc>(s, m);
+}
+
 // In-place inclusive scan of SNT ints in LDS (all threads participate): a scan inside each wave,
 // then a scan of the 16 wave totals by wave 0.
 __device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
@@ -113,50 +133,64 @@ __device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
   __syncthreads();
 }
 
+// SMALL: the batch fits one chunk of samples and its groups fit the LDS placement table, so every
+// per-sample and per-group value lives in LDS; otherwise they go through the workspace scratch.
+template <bool SMALL>
 __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) {
   const SchedArgs& a = blockIdx.x == 0 ? a0 : a1;
   __shared__ int cnt[SNT];   // inclusive scan of the chunk's per-sample tile counts
   __shared__ int sbuf[SNT];  // scan of chunk counts per tile
   __shared__ int wsum[SNT / 64];
-  __shared__ int lq_c[SNT], lk_c[SNT];  // lengths of the chunk's samples
+  __shared__ int lq_c[SNT], lk_c[SNT];       // lengths of the chunk's samples
   __shared__ unsigned long long ccost[SNT];  // per-sample cost (one head) of the chunk
   __shared__ int cnch[SNT];                  // per-sample item count (one head) of the chunk
   __shared__ int first_e[SNT];               // chunk index of each sample's first tile
-  __shared__ int s_rank[SNT], s_at[SNT];     // rank of a sample / sample of a rank
-  __shared__ int s_gpre[GCAP];               // first position of each group on its die
+  __shared__ int s_rank[SMALL ? SNT : 1], s_at[SMALL ? SNT : 1];  // rank of a sample / its inverse
+  __shared__ int s_gpre[SMALL ? GCAP : 1];   // first position of each group on its die
   __shared__ int bucket[NBUCKET];
+  __shared__ unsigned short owner[OCAP];  // local sample of each of the chunk's first OCAP tiles
+  // one batch of tiles between their numbering and their items: local sample, tile, cost,
+  // chunks, first chunk number within the sample, first chunk slot
+  __shared__ int bt_bl[SNT], bt_t[SNT], bt_c[SNT], bt_n[SNT], bt_ci[SNT], bt_sb[SNT];
   __shared__ int xtot[XCDS], tgt[XCDS], spre[XCDS], dpre[XCDS + 1];
-  __shared__ int err, carry, split_count, slot_count;
-  __shared__ unsigned long long wtot[SNT / 64];
-  __shared__ int wmax[SNT / 64];
+  __shared__ int err, carry, split_count, slot_count, big_sh, t_sh;
+  __shared__ unsigned long long tot_sh;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   WsHeader* hdr = (WsHeader*)a.ws_header;
   Item* items = (Item*)a.items;
   const int B = a.B, H = a.H, G = B * H;
-  if (tid == 0) {
-    // the offsets' ends; each sample's own lengths are checked as its chunk is loaded
-    int e = 0;
-    if (a.q_off[0] != 0 || (int64_t)a.q_off[B] != a.total_q) e |= 1;
-    if (a.kv_off[0] != 0 || (int64_t)a.kv_off[B] != a.total_kv) e |= 2;
-    err = e;
-  }
-  // per-sample values: LDS when the batch is one chunk, else the workspace scratch
-  const bool small = B <= SNT;
-  unsigned long long* cost = small ? ccost : a.scratch_cost;
-  int* nch = small ? cnch : a.scratch_nch;
-  int* rank = small ? s_rank : a.scratch_rank;
-  int* at = small ? s_at : a.scratch_at;
-  int* gpre = G <= GCAP ? s_gpre : a.scratch_gpre;
+  // per-sample and per-group tables
+  auto cost_of_sample = [&](int b) -> unsigned long long {
+    if constexpr (SMALL) return ccost[b]; else return a.scratch_cost[b];
+  };
+  auto nch_of = [&](int b) -> int {
+    if constexpr (SMALL) return cnch[b]; else return a.scratch_nch[b];
+  };
+  auto rank_of = [&](int b) -> int {
+    if constexpr (SMALL) return s_rank[b]; else return a.scratch_rank[b];
+  };
+  auto sample_at = [&](int r) -> int {
+    if constexpr (SMALL) return s_at[r]; else return a.scratch_at[r];
+  };
+  auto gpre_of = [&](int r) -> int {
+    if constexpr (SMALL) return s_gpre[r]; else return a.scratch_gpre[r];
+  };
 
-  const int ti = a.tile_item, tl = a.tile_loop;
+  const int tis = __builtin_ctz(a.tile_item), tls = __builtin_ctz(a.tile_loop);
   const bool qmode = a.mode == SCHED_QTILES;
   // Load chunk [base, base + SNT) of samples (lengths, tile-count scan); returns its tile count.
   // A sample with a negative length (or more queries than a shared query block holds) sets the
-  // error word and counts as empty.
+  // error word and counts as empty; the first chunk's load also checks the offsets' ends.
   auto load_chunk = [&](int base) {
     const int b = base + tid;
     int n = 0;
     __syncthreads();
+    if (base == 0 && tid == 0) {
+      int e = 0;
+      if (a.q_off[0] != 0 || (int64_t)a.q_off[B] != a.total_q) e |= 1;
+      if (a.kv_off[0] != 0 || (int64_t)a.kv_off[B] != a.total_kv) e |= 2;
+      if (e != 0) atomicOr(&err, e);
+    }
     if (b < B) {
       int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
       const int e = (Lq < 0 || (a.q_rows > 0 && Lq > a.q_rows) ? 1 : 0) | (Lk < 0 ? 2 : 0);
@@ -166,45 +200,58 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       }
       lq_c[tid] = Lq;
       lk_c[tid] = Lk;
-      n = qmode ? (Lq + ti - 1) / ti : (Lk + ti - 1) / ti;
+      n = ((qmode ? Lq : Lk) + (1 << tis) - 1) >> tis;
     }
     cnt[tid] = n;
     block_scan(cnt, wsum, tid);
+    for (int u = cnt[tid] - n; u < min(cnt[tid], OCAP); ++u) owner[u] = (unsigned short)tid;
+    __syncthreads();
     return cnt[SNT - 1];
   };
-  // local sample and tile of the chunk's tile u
-  auto locate = [&](int u, int& bl, int& t) {
-    int lo = 0, hi = SNT - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (cnt[mid] > u) hi = mid; else lo = mid + 1;
+  // local sample and tile of the chunk's tile u (samples [0, ns) of the chunk)
+  auto locate = [&](int u, int ns, int& bl, int& t) {
+    int lo = 0;
+    if (u < OCAP) {
+      lo = owner[u];
+    } else {
+      int hi = ns - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cnt[mid] > u) hi = mid; else lo = mid + 1;
+      }
     }
     bl = lo;
     t = u - (lo > 0 ? cnt[lo - 1] : 0);
   };
-  auto cost_of = [&](int bl, int t) { return item_cost(a.mode, a.causal, a.win, lq_c[bl], lk_c[bl], t, ti, tl); };
+  auto cost_of = [&](int bl, int t) { return item_cost(a.mode, a.causal, a.win, lq_c[bl], lk_c[bl], t, tis, tls); };
 
   // 1. per-sample cost (one head), total cost and the largest tile cost
+  if (tid == 0) {
+    err = 0;
+    tot_sh = 0;
+    big_sh = 0;
+  }
   unsigned long long tot = 0;
   int mx = 0;
   for (int base = 0; base < B; base += SNT) {
     const int total = load_chunk(base);
     if (err != 0) break;  // read after the scan's barrier: uniform
+    const int ns = min(SNT, B - base);
     ccost[tid] = 0;
-    cnch[tid] = base + tid < B ? cnt[tid] - (tid > 0 ? cnt[tid - 1] : 0) : 0;  // tiles
+    cnch[tid] = tid < ns ? cnt[tid] - (tid > 0 ? cnt[tid - 1] : 0) : 0;  // tiles
     __syncthreads();
     for (int u = tid; u < total; u += SNT) {
       int bl, t;
-      locate(u, bl, t);
+      locate(u, ns, bl, t);
       const int c = cost_of(bl, t);
       atomicAdd(&ccost[bl], (unsigned long long)c);
       tot += (unsigned long long)c;
       mx = max(mx, c);
     }
     __syncthreads();
-    if (!small && base + tid < B) {
-      cost[base + tid] = ccost[tid];
-      nch[base + tid] = cnch[tid];
+    if (!SMALL && tid < ns) {
+      a.scratch_cost[base + tid] = ccost[tid];
+      a.scratch_nch[base + tid] = cnch[tid];
     }
   }
   __syncthreads();
@@ -223,57 +270,59 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   }
   int T = 0x7fffffff;  // chunk length; no splitting unless a tile costs more
   if (a.split) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      tot += __shfl_xor(tot, off, 64);
-      mx = max(mx, __shfl_xor(mx, off, 64));
-    }
-    if (lane == 0) {
-      wtot[wv] = tot;
-      wmax[wv] = mx;
+    wave_sum_max(tot, mx);  // costs are non-negative: the zero fills add and max nothing
+    if (lane == 63) {
+      atomicAdd(&tot_sh, tot);
+      atomicMax(&big_sh, mx);
     }
     __syncthreads();
-    unsigned long long total = 0;
-    int biggest = 0;
-    for (int w = 0; w < SNT / 64; ++w) {
-      total += wtot[w];
-      biggest = max(biggest, wmax[w]);
+    if (tid == 0) {
+      const unsigned long long total = tot_sh * (unsigned long long)H;
+      const unsigned long long tpc =
+          total < 0xffffffffull - a.nslot ? (unsigned)(total + a.nslot - 1) / (unsigned)a.nslot
+                                          : (total + a.nslot - 1) / a.nslot;
+      const int t_mean = (int)min(max(tpc, (unsigned long long)SPLIT_MIN_TILES), (unsigned long long)0x7fffffff);
+      t_sh = big_sh > t_mean ? t_mean : 0x7fffffff;
     }
-    total *= (unsigned long long)H;
-    const unsigned long long tpc = (total + a.nslot - 1) / a.nslot;
-    const int t_mean = (int)min(max(tpc, (unsigned long long)SPLIT_MIN_TILES), (unsigned long long)0x7fffffff);
-    if (biggest > t_mean) T = t_mean;
+    __syncthreads();
+    T = t_sh;
   }
   // chunks of a tile of cost c: ceil(c / T) when c > T (the last one may be shorter), else one
   auto chunks = [&](int c) { return c > T ? (c + T - 1) / T : 1; };
   if (T != 0x7fffffff) {
     // 1b. with split tiles a sample's item count is its chunk count
     for (int base = 0; base < B; base += SNT) {
-      const int total = small ? cnt[SNT - 1] : load_chunk(base);
+      const int total = SMALL ? cnt[SNT - 1] : load_chunk(base);
+      const int ns = min(SNT, B - base);
       cnch[tid] = 0;
       __syncthreads();
       for (int u = tid; u < total; u += SNT) {
         int bl, t;
-        locate(u, bl, t);
+        locate(u, ns, bl, t);
         atomicAdd(&cnch[bl], chunks(cost_of(bl, t)));
       }
       __syncthreads();
-      if (!small && base + tid < B) nch[base + tid] = cnch[tid];
+      if (!SMALL && tid < ns) a.scratch_nch[base + tid] = cnch[tid];
     }
   }
   // 2. rank the samples by cost, largest first (counting sort over cost buckets)
   for (int i = tid; i < NBUCKET; i += SNT) bucket[i] = 0;
   __syncthreads();
-  for (int b = tid; b < B; b += SNT) atomicAdd(&bucket[cost_bucket(cost[b])], 1);
+  for (int b = tid; b < B; b += SNT) atomicAdd(&bucket[cost_bucket(cost_of_sample(b))], 1);
   __syncthreads();
   const int own = bucket[tid];
   block_scan(bucket, wsum, tid);  // NBUCKET == SNT
   bucket[tid] -= own;
   __syncthreads();
   for (int b = tid; b < B; b += SNT) {
-    const int r = atomicAdd(&bucket[cost_bucket(cost[b])], 1);
-    rank[b] = r;
-    if (r < B) at[r] = b;
+    const int r = atomicAdd(&bucket[cost_bucket(cost_of_sample(b))], 1);
+    if constexpr (SMALL) {
+      s_rank[b] = r;
+      if (r < B) s_at[r] = b;
+    } else {
+      a.scratch_rank[b] = r;
+      if (r < B) a.scratch_at[r] = b;
+    }
   }
   __syncthreads();
   // 3. group r = rank * H + head goes to die group_xcd(r); wave x lays out die x's groups in rank
@@ -285,12 +334,17 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     for (int k0 = 0; 16 * k0 < G; k0 += 64) {
       const int k = k0 + lane;
       const int r0 = 16 * k + x, r1 = 16 * k + 2 * XCDS - 1 - x;
-      const int n0 = r0 < G ? nch[at[r0 / H]] : 0;
-      const int n1 = r1 < G ? nch[at[r1 / H]] : 0;
+      const int n0 = r0 < G ? nch_of(sample_at(r0 / H)) : 0;
+      const int n1 = r1 < G ? nch_of(sample_at(r1 / H)) : 0;
       const int incl = wave_incl_scan(n0 + n1);
       const int excl = run + incl - (n0 + n1);
-      if (r0 < G) gpre[r0] = excl;
-      if (r1 < G) gpre[r1] = excl + n0;
+      if constexpr (SMALL) {
+        if (r0 < G) s_gpre[r0] = excl;
+        if (r1 < G) s_gpre[r1] = excl + n0;
+      } else {
+        if (r0 < G) a.scratch_gpre[r0] = excl;
+        if (r1 < G) a.scratch_gpre[r1] = excl + n0;
+      }
       run += __builtin_amdgcn_readlane(incl, 63);
     }
     if (lane == 0) xtot[x] = run;
@@ -324,17 +378,20 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   // 4. scatter the items (b, tile, h, canonical tile index, inner range, slot, chunk); a split
   //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared.
   //    Within a sample, chunks are numbered in tile order (sbuf scan); a group lists its
-  //    costliest tiles first: the last query tiles (causal), or the first key tiles.
+  //    costliest tiles first: the last query tiles (causal), or the first key tiles. Tiles are
+  //    numbered in batches of SNT; the batch's items are then written one (tile, head) pair per
+  //    thread.
   for (int base = 0; base < B; base += SNT) {
-    const int total = small ? cnt[SNT - 1] : load_chunk(base);  // one chunk: still loaded
+    const int total = SMALL ? cnt[SNT - 1] : load_chunk(base);  // one chunk: still loaded
+    const int ns = min(SNT, B - base);
     const int first = carry;
-    if (a.tile_base != nullptr && base + tid < B) a.tile_base[base + tid] = first + (tid > 0 ? cnt[tid - 1] : 0);
+    if (a.tile_base != nullptr && tid < ns) a.tile_base[base + tid] = first + (tid > 0 ? cnt[tid - 1] : 0);
     int run = 0;  // chunks of the chunk's earlier tiles
     for (int u0 = 0; u0 < total; u0 += SNT) {
       const int u = u0 + tid;
       int bl = 0, t = 0, c = 0, n = 0;
       if (u < total) {
-        locate(u, bl, t);
+        locate(u, ns, bl, t);
         c = cost_of(bl, t);
         n = chunks(c);
       }
@@ -349,10 +406,8 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
         run += sbuf[SNT - 1];
         ci = e - first_e[bl];
       }
-      if (u >= total) continue;
-      const int b = base + bl, canon = first + u;
       int sbase = -1;
-      if (n > 1) {
+      if (u < total && n > 1) {
         sbase = atomicAdd(&slot_count, n * H);
         atomicAdd(&split_count, H);
         if (sbase + n * H > 2 * a.nslot) {
@@ -362,25 +417,30 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
           for (int h = 0; h < H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
         }
       }
-      if (a.split_slot != nullptr)
-        for (int h = 0; h < H; ++h) a.split_slot[(int64_t)canon * H + h] = sbase < 0 ? -1 : sbase + h * n;
-      const int nb = small ? cnch[bl] : nch[b];
-      const int rb = rank[b];
-      for (int k = 0; k < n; ++k) {
+      if (u < total && a.split_slot != nullptr)
+        for (int h = 0; h < H; ++h) a.split_slot[(int64_t)(first + u) * H + h] = sbase < 0 ? -1 : sbase + h * n;
+      __syncthreads();  // the previous batch's items are out
+      bt_bl[tid] = bl; bt_t[tid] = t; bt_c[tid] = c; bt_n[tid] = n; bt_ci[tid] = ci; bt_sb[tid] = sbase;
+      __syncthreads();
+      // items of the batch, one (tile, head) pair per thread at a time
+      const int nt_b = min(SNT, total - u0);
+      for (int pr = tid; pr < nt_b * H; pr += SNT) {
+        const int j = pr / H, h = pr - j * H;
+        const int bj = bt_bl[j], tj = bt_t[j], cj = bt_c[j], nj = bt_n[j], cij = bt_ci[j], sbj = bt_sb[j];
+        const int b = base + bj;
+        const int nb = SMALL ? cnch[bj] : nch_of(b);
+        const int r = rank_of(b) * H + h;
+        const int x = group_xcd(r), g0 = gpre_of(r);
         Item it;
-        it.b = b; it.tile = t; it.aux = canon;
-        it.lo = n == 1 ? 0 : k * T;
-        it.hi = n == 1 ? c : min(c, (k + 1) * T);
-        it.chunk = sbase < 0 ? 0 : k | (n << 16);
-        const int w = qmode ? nb - 1 - (ci + k) : ci + k;
-        for (int h = 0; h < H; ++h) {
-          const int r = rb * H + h;
-          const int pos = position(group_xcd(r), gpre[r] + w);
-          if (pos >= 0 && pos < a.max_items) {
-            it.h = h;
-            it.slot = sbase < 0 ? -1 : sbase + h * n + k;
-            items[pos] = it;
-          }
+        it.b = b; it.tile = tj; it.h = h; it.aux = first + u0 + j;
+        for (int k = 0; k < nj; ++k) {
+          it.lo = nj == 1 ? 0 : k * T;
+          it.hi = nj == 1 ? cj : min(cj, (k + 1) * T);
+          it.slot = sbj < 0 ? -1 : sbj + h * nj + k;
+          it.chunk = sbj < 0 ? 0 : k | (nj << 16);
+          const int w = qmode ? nb - 1 - (cij + k) : cij + k;
+          const int pos = position(x, g0 + w);
+          if (pos >= 0 && pos < a.max_items) items[pos] = it;
         }
       }
     }
@@ -408,16 +468,24 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   }
 }
 
+bool sched_small(const SchedArgs& a) { return a.B <= SNT && (int64_t)a.B * a.H <= GCAP; }
+
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
   prof_before(PROF_SCHED, s);
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(SNT), 0, s, a, a);
+  if (sched_small(a))
+    hipLaunchKernelGGL(sched_kernel<true>, dim3(1), dim3(SNT), 0, s, a, a);
+  else
+    hipLaunchKernelGGL(sched_kernel<false>, dim3(1), dim3(SNT), 0, s, a, a);
   prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }
 
 hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) {
   prof_before(PROF_SCHED, s);
-  hipLaunchKernelGGL(sched_kernel, dim3(2), dim3(SNT), 0, s, a, b);
+  if (sched_small(a) && sched_small(b))
+    hipLaunchKernelGGL(sched_kernel<true>, dim3(2), dim3(SNT), 0, s, a, b);
+  else
+    hipLaunchKernelGGL(sched_kernel<false>, dim3(2), dim3(SNT), 0, s, a, b);
   prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }
