@@ -70,8 +70,7 @@ typedef enum {
   GDPA_OK = 0,
   GDPA_EINVAL = 1,     /* a null or misaligned pointer, a negative size, a bad enum value */
   GDPA_ENOTSUP = 2,    /* valid but unsupported: D not in {32, 64, 128}, MX in gdpa_bwd,
-                          scale <= 0 outside fp32, a window on a bf16 D = 32 / 64 or MX
-                          problem, ... */
+                          scale <= 0 outside fp32, a window on an MX problem, ... */
   GDPA_EWORKSPACE = 3, /* workspace_bytes smaller than gdpa_workspace_size() */
   GDPA_EHIP = 4        /* the HIP runtime refused a launch */
 } gdpa_status;
@@ -91,9 +90,8 @@ typedef struct {
   float scale;          /* s = scale * q.k (+ bias); must be > 0 for GDPA_BF16 / GDPA_MXFP8_E4M3 */
   int32_t bias_buckets; /* NB >= 0; 0 = no bias table */
   int32_t window;       /* W >= 0; 0 = no window. W >= 1 keeps keys j > i - W and needs causal = 1
-                           and GDPA_F32, or GDPA_BF16 with D = 128 (otherwise GDPA_ENOTSUP). A W
-                           that no query can
-                           reach (W >= total_q, or W >= max_q when max_q > 0) drops nothing and
+                           and GDPA_F32 or GDPA_BF16 (otherwise GDPA_ENOTSUP). A W that no query
+                           can reach (W >= total_q, or W >= max_q when max_q > 0) drops nothing and
                            is the same as no window; any other W >= 1 needs
                            total_q + total_kv <= INT32_MAX - 1024 (otherwise GDPA_ENOTSUP) */
   int32_t q_shared;     /* 0 or 1. 1: Q and dQ are [max_q, H, D], shared by all samples; needs

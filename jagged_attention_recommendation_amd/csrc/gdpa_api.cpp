@@ -47,10 +47,8 @@ int32_t check_problem(const gdpa_problem* p) {
   if (p->D != 32 && p->D != 64 && p->D != 128) return GDPA_ENOTSUP;
   if (p->dtype == GDPA_MXFP8_E4M3 && p->D != 128) return GDPA_ENOTSUP;
   if (p->window < 0) return GDPA_EINVAL;
-  // sliding windows: causal attention on the fp32 kernels and the bf16 D = 128 kernels
-  if (p->window > 0 && (p->causal != 1 || p->dtype == GDPA_MXFP8_E4M3 ||
-                        (p->dtype == GDPA_BF16 && p->D != 128)))
-    return GDPA_ENOTSUP;
+  // sliding windows: causal attention on the fp32 and bf16 kernels
+  if (p->window > 0 && (p->causal != 1 || p->dtype == GDPA_MXFP8_E4M3)) return GDPA_ENOTSUP;
   // window arithmetic adds a key or query position to W in int32
   if (effective_window(p) > 0 && p->total_q + p->total_kv > INT32_MAX - 1024) return GDPA_ENOTSUP;
   // a shared query block: bf16 kernels, max_q rows

@@ -66,7 +66,8 @@ __device__ __forceinline__ float dscore(float s2, float s, float lse2, float Di,
 // reduction.
 constexpr int DSP = 68;  // floats per row of a wave's dS buffer (16-byte aligned rows)
 
-template <int D, int ACT, bool CAUSAL, bool BIAS>
+// WIN: causal sliding window of a.win keys (query i sees keys i - win + 1 .. i).
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   using T = Tile<D>;
   constexpr int BIAS_BYTES = BIAS ? BIAS_WMAX * 4 + 4 * 32 * DSP * 4 : 0;
@@ -127,8 +128,10 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
   if (i0 >= Lq) nkt = 0;
   // key tiles of this item: all of them, or one chunk of a split tile (splitting is used only
-  // without a bias table, whose partial rows assume whole tiles)
-  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
+  // without a bias table, whose partial rows assume whole tiles), counted from the first tile
+  // the item's sliding window reaches
+  const int kt_first = WIN ? win_first_ktile(i0, a.win, KL) : 0;
+  const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
 
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
@@ -168,10 +171,11 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
     lk_.load((const __bf16*)a.K, kt_lo * KL, Lk, kv0, H, h, tid);
     lv_.load((const __bf16*)a.V, kt_lo * KL, Lk, kv0, H, h, tid);
   }
-  if (BIAS && nkt > 0) {  // staged while the first tile's loads are in flight
-    w_hi = i0 + QI - 1;  // raw diagonals iq - j: iq in [i0, i0 + QI), j in [0, nkt * KL)
+  if (BIAS && kt_lo < kt_hi) {  // staged while the first tile's loads are in flight
+    // raw diagonals iq - j: iq in [i0, i0 + QI), j in the item's key tiles
+    w_hi = i0 + QI - 1 - kt_lo * KL;
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
-                 bwin, bias_h, nb, i0 - (nkt * KL - 1), w_hi, true, bmul, tid, NT)) != 0;
+                 bwin, bias_h, nb, i0 - (kt_hi * KL - 1), w_hi, true, bmul, tid, NT)) != 0;
   }
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
     __syncthreads();
@@ -183,7 +187,9 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
       lv_.load((const __bf16*)a.V, (kt + 1) * KL, Lk, kv0, H, h, tid);
     }
     const int k0 = kt * KL;
-    if (!wave_active || (CAUSAL && k0 > wrow + 31)) continue;
+    // the wave's tiles: not wholly after its last query (causal) nor wholly before its first
+    // query's window (the bias-gradient reduction assumes the same range)
+    if (!wave_active || (CAUSAL && k0 > wrow + 31) || (WIN && k0 + KL <= wrow - a.win + 1)) continue;
     k0_last = k0;
     f32x16 ds_acc[2], dp_acc[2];
 #pragma unroll
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
         dp_acc[kb] = mfma32(tile_row_op<D>(Vs, kb * 32, s, lane), doop[s], dp_acc[kb]);
       }
     }
-    const bool need_mask = (k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow);
+    const bool need_mask = (k0 + KL > Lk) || (CAUSAL && k0 + KL - 1 > wrow) || (WIN && k0 < wrow + 32 - a.win);
     // scores in place: x = s * scale (* log2 e for softmax) + bias of diagonal iq - j
     const float sc = ACT == ACT_SOFTMAX ? sl2 : a.scale;
     if (BIAS) {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
         const float x = ds_acc[kb][r];
         float p;
         float ds = dscore<ACT>(x, x, lse2, Di, dp_acc[kb][r], p);
-        if (!qv || (need_mask && (j >= Lk || (CAUSAL && j > iq)))) ds = 0.0f;
+        if (!qv || (need_mask && (j >= Lk || (CAUSAL && j > iq) || (WIN && j <= iq - a.win)))) ds = 0.0f;
         ds_acc[kb][r] = ds;
       }
     }
@@ -340,7 +346,8 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
 // dK, dV
 // Three workgroups per compute unit at D = 32 (their item count is large and each item short);
 // at D = 64 the third does not fit without spills.
-template <int D, int ACT, bool CAUSAL, bool BIAS>
+// WIN: causal sliding window of a.win keys (key j is seen by queries j .. j + win - 1).
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + 2 * QL * 4 + (BIAS ? BIAS_WMAX * 4 : 0)];
@@ -377,7 +384,10 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
     dk[n] = f32x16{};
     dv[n] = f32x16{};
   }
-  const int nqt = (Lq + QL - 1) / QL;
+  // query tiles [qt0, nqt): from the causal start to the last tile whose window reaches the
+  // item's last key
+  const int nqt_all = (Lq + QL - 1) / QL;
+  const int nqt = WIN ? win_end_qtile(min(Lk, j0 + KI) - 1, a.win, QL, nqt_all) : nqt_all;
   const int qt0 = CAUSAL ? j0 / QL : 0;
   const float sl2 = a.scale * LOG2E;
   const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
@@ -422,7 +432,9 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
     const int i0 = qt * QL;
     if (!wave_active) continue;
     if (CAUSAL && i0 + QL - 1 < wkey) continue;  // every query of the tile precedes every key
-    const bool need_mask = (i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31);
+    if (WIN && i0 > min(wkey + 31, Lk - 1) + a.win - 1) continue;  // ... or is past every window
+    const bool need_mask = (i0 + QL > Lq) || (wkey + 32 > Lk) || (CAUSAL && i0 < wkey + 31) ||
+                           (WIN && i0 + QL - 1 > wkey + a.win - 1);
 #pragma unroll 1  // rolled: unrolling makes the register allocator spill
     for (int qb = 0; qb < 2; ++qb) {
       if (i0 + qb * 32 >= Lq) break;  // a half past the last query adds nothing (short queries)
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
             const int i = i0 + ql + e;
             float p;
             float ds = dscore<ACT>(sacc[r], sacc[r], l4[e], d4[e], dpacc[r], p);
-            if (need_mask && (i >= Lq || !kvalid || (CAUSAL && jk > i))) {
+            if (need_mask && (i >= Lq || !kvalid || (CAUSAL && jk > i) || (WIN && i > jk + a.win - 1))) {
               p = 0.0f;
               ds = 0.0f;
             }
@@ -495,18 +507,18 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int D, int ACT, bool C, bool BI>
+template <int D, int ACT, bool C, bool BI, bool WIN = false>
 hipError_t launch_t(const BwdArgs& a, int gq, int gk, hipStream_t s) {
   if (gq > 0) {
     prof_before(PROF_DQ, s);
-    hipLaunchKernelGGL((dq_kernel<D, ACT, C, BI>), dim3(gq), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dq_kernel<D, ACT, C, BI, WIN>), dim3(gq), dim3(NT), 0, s, a);
     prof_after(PROF_DQ, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (gk > 0) {
     prof_before(PROF_DKDV, s);
-    hipLaunchKernelGGL((dkdv_kernel<D, ACT, C, BI>), dim3(gk), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, ACT, C, BI, WIN>), dim3(gk), dim3(NT), 0, s, a);
     prof_after(PROF_DKDV, s);
   }
   return hipGetLastError();
@@ -515,6 +527,8 @@ hipError_t launch_t(const BwdArgs& a, int gq, int gk, hipStream_t s) {
 template <int D, int ACT>
 hipError_t launch_cb(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t s) {
   const bool bias = p.nb > 0;
+  if (p.win > 0)
+    return bias ? launch_t<D, ACT, true, true, true>(a, gq, gk, s) : launch_t<D, ACT, true, false, true>(a, gq, gk, s);
   if (p.causal) return bias ? launch_t<D, ACT, true, true>(a, gq, gk, s) : launch_t<D, ACT, true, false>(a, gq, gk, s);
   return bias ? launch_t<D, ACT, false, true>(a, gq, gk, s) : launch_t<D, ACT, false, false>(a, gq, gk, s);
 }

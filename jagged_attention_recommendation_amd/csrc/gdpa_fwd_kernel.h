@@ -59,9 +59,11 @@ struct Smem {
   static constexpr int BIAS_BYTES = BIAS_WMAX * 4;
 };
 
-template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX>
+// WIN: causal sliding window of a.win keys (query i sees keys i - win + 1 .. i); bf16 only.
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX, bool WIN = false>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   static_assert(!MX || D == 128, "MX path is for D = 128");
+  static_assert(!WIN || (CAUSAL && !MX), "windows are causal, bf16");
   using S = Smem<D, MX>;
   __shared__ __attribute__((aligned(16))) char smem[S::K_BYTES + S::V_BYTES + (BIAS ? S::BIAS_BYTES : 0)];
   GDPA_LDS char* Ks = (GDPA_LDS char*)smem;
@@ -91,8 +93,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int i_max = min(Lq, row_blk + BM) - 1;
     nkt = min(nkt, i_max / BN + 1);
   }
-  // key tiles of this item: all of them, or one chunk of a split tile (bf16 only)
-  const int kt_lo = it.lo, kt_hi = min(it.hi, nkt);
+  // key tiles of this item: all of them, or one chunk of a split tile (bf16 only), counted from
+  // the first tile the item's sliding window reaches
+  const int kt_first = WIN ? win_first_ktile(row_blk, a.win, BN) : 0;
+  const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
 
   // ---- Q^T operand: lane holds query iq
   bf16x8 qop[MX ? 1 : D / 16];
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int k0 = kt * BN;
     if (!wave_active) return;
     if (CAUSAL && k0 > wrow + 31) return;  // every key of the tile is after every query
+    if (WIN && k0 + BN <= wrow - a.win + 1) return;  // ... or before every query's window
 
     // ---- S^T = K Q^T for two 32-key blocks. With a bias the accumulators start from
     // bias / scale read straight from the LDS window (register r of block kb is key
@@ -248,18 +253,23 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    // ---- scores -> probabilities. Masking is needed only on tiles that reach past the keys or
-    // past the wave's first query (causal); valid keys of block kb satisfy
-    // (r/4)*8 + 4g + r%4 < lim_kb.
+    // ---- scores -> probabilities. Masking is needed only on tiles that reach past the keys,
+    // past the wave's first query (causal) or before its last query's window; valid keys of
+    // block kb satisfy lo_kb <= (r/4)*8 + 4g + r%4 < lim_kb.
     const bool need_mask = __builtin_amdgcn_readfirstlane(
-        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow))) != 0;
-    int lim[2];
+        (int)((k0 + BN > Lk) || (CAUSAL && k0 + BN - 1 > wrow) || (WIN && k0 < wrow + 32 - a.win))) != 0;
+    int lim[2], lo[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       int l = Lk - (k0 + kb * 32);
       if (CAUSAL) l = min(l, iq - (k0 + kb * 32) + 1);
       lim[kb] = l - 4 * g;
+      lo[kb] = WIN ? iq - a.win + 1 - (k0 + kb * 32) - 4 * g : -64;
     }
+    auto masked = [&](int kb, int r) {
+      const int off = (r >> 2) * 8 + (r & 3);
+      return off >= lim[kb] || (WIN && off < lo[kb]);
+    };
     float p[2][16];
     if (ACT == ACT_SOFTMAX) {
       if (need_mask) {
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) sacc[kb][r] = -INFINITY;
+            if (masked(kb, r)) sacc[kb][r] = -INFINITY;
       }
       // row max on the raw accumulators (scale > 0 preserves order), then one fma + exp2
       float mt = -INFINITY;
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if ((r >> 2) * 8 + (r & 3) >= lim[kb]) p[kb][r] = 0.0f;
+            if (masked(kb, r)) p[kb][r] = 0.0f;
       }
     }
 
@@ -403,10 +413,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(orow, o[n], n, g, inv);
 }
 
-template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX>
+template <int D, int ACT, bool CAUSAL, bool BIAS, bool MX, bool WIN = false>
 hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
   prof_before(PROF_FWD, s);
-  hipLaunchKernelGGL((fwd_kernel<D, ACT, CAUSAL, BIAS, MX>), dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel<D, ACT, CAUSAL, BIAS, MX, WIN>), dim3(grid), dim3(NT), 0, s, a);
   prof_after(PROF_FWD, s);
   return hipGetLastError();
 }
@@ -414,6 +424,11 @@ hipError_t launch_t(const FwdArgs& a, int grid, hipStream_t s) {
 template <int D, int ACT, bool MX>
 hipError_t launch_cb(const Prob& p, const FwdArgs& a, int grid, hipStream_t s) {
   const bool bias = p.nb > 0;
+  if constexpr (!MX) {
+    if (p.win > 0)
+      return bias ? launch_t<D, ACT, true, true, false, true>(a, grid, s)
+                  : launch_t<D, ACT, true, false, false, true>(a, grid, s);
+  }
   if (p.causal)
     return bias ? launch_t<D, ACT, true, true, MX>(a, grid, s) : launch_t<D, ACT, true, false, MX>(a, grid, s);
   return bias ? launch_t<D, ACT, false, true, MX>(a, grid, s) : launch_t<D, ACT, false, false, MX>(a, grid, s);

@@ -1,4 +1,4 @@
-"""Sliding-window attention (causal; query i sees keys i - W + 1 .. i) on the bf16 D = 128 path.
+"""Sliding-window attention (causal; query i sees keys i - W + 1 .. i) on the bf16 and fp32 paths.
 
 The window is the attention variant of page "GEM Training: How Meta Doubled the Efficiency of Its
 LLM-Scale Ads Foundation Model" (sliding-window attention paragraph). The fp64 oracle applies it
@@ -70,10 +70,10 @@ def check(p, W, nthreads=None):
     return hf, hb
 
 
-def ragged(seed, act, nb, B=5, H=2, hi=300):
+def ragged(seed, act, nb, B=5, H=2, hi=300, D=128):
     rng = np.random.default_rng(seed)
     lq = rng.integers(1, hi + 1, size=B)
-    return inputs.make_problem(f"win-{seed}", seed=seed, H=H, D=128, lq=lq, lk=lq, dtype="bf16",
+    return inputs.make_problem(f"win-{seed}-{D}", seed=seed, H=H, D=D, lq=lq, lk=lq, dtype="bf16",
                                act=act, causal=True, bias_buckets=nb)
 
 
@@ -82,6 +82,27 @@ def ragged(seed, act, nb, B=5, H=2, hi=300):
 @pytest.mark.parametrize("W", [1, 31, 32, 33, 64, 100, 129, 400])
 def test_window_ragged(act, nb, W):
     check(ragged(300 + W, act, nb), W)
+
+
+@pytest.mark.parametrize("D", [32, 64])
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh", "silu"])
+@pytest.mark.parametrize("nb", [0, 48])
+@pytest.mark.parametrize("W", [1, 33, 64, 129, 400])
+def test_window_small_head_dim(D, act, nb, W):
+    """The D = 32 / 64 kernels: per-wave key and query tile ranges, masks and the bias-gradient
+    diagonals under the window."""
+    check(ragged(500 + W, act, nb, D=D), W)
+
+
+@pytest.mark.parametrize("D", [32, 64])
+def test_window_small_head_dim_split(D):
+    """A long sample without a bias table: the D = 32 / 64 forward and dQ tiles are cut into
+    chunks that start inside the window."""
+    lq = np.array([2100, 40, 70, 9])
+    p = inputs.make_problem(f"win-split-{D}", seed=12, H=1, D=D, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True)
+    hf, hb = check(p, 900)
+    assert hf["split"] > 0 and hb["split"] > 0, (hf, hb)
 
 
 def test_window_edge_lengths():
