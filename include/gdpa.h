@@ -224,9 +224,11 @@ int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err
 int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
                        int64_t* capacity);
 
-/* Profiling aid for benchmarks (not thread-safe). Between gdpa_profile_start(mask) and
- * gdpa_profile_stop(), every launch of a selected kernel is bracketed by a pair of HIP events
- * recorded on its launch stream. Bit k of mask selects kernel k: 0 = forward main kernel,
+/* Profiling aid for benchmarks. Between gdpa_profile_start(mask) and gdpa_profile_stop(), every
+ * launch of a selected kernel is bracketed by a pair of HIP events recorded on its launch stream.
+ * Launches stay reentrant while profiling is on (several host threads may launch; each launch
+ * claims its own event pair), but gdpa_profile_start, _read and _stop must not run concurrently
+ * with one another or with launches of the kernels they select. Bit k of mask selects kernel k: 0 = forward main kernel,
  * 1 = backward dQ kernel, 2 = backward dK/dV kernel, 3 = scheduler, 4 / 5 = block-aligned
  * forward / backward. At most 1024 launches per
  * kernel are timed. gdpa_profile_read() waits for the recorded events of one kernel and returns

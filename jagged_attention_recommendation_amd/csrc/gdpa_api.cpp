@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "gdpa.h"
@@ -235,13 +237,18 @@ int32_t static_scratch(void** out) {
 // ---- profiling hook state
 constexpr int PROF_KERNELS = 6;
 constexpr int PROF_MAX = 1024;
+// Launches may come from several host threads: the mask and the per-kernel slot counters are
+// atomic, and the slot a launch claimed in prof_before is handed to prof_after (same thread,
+// same launch) through a thread-local.
 struct ProfState {
-  int mask = 0;
-  int n[PROF_KERNELS] = {};
+  std::atomic<int> mask{0};
+  std::atomic<int> n[PROF_KERNELS];
   bool created = false;
   hipEvent_t ev[PROF_KERNELS][2 * PROF_MAX];
 };
 ProfState g_prof;
+thread_local int t_prof_slot[PROF_KERNELS] = {-1, -1, -1, -1, -1, -1};
+static_assert(PROF_KERNELS == 6, "t_prof_slot initialiser");
 
 int32_t map_hip(hipError_t e) {
   if (e == hipSuccess) return GDPA_OK;
@@ -253,13 +260,18 @@ int32_t map_hip(hipError_t e) {
 
 namespace gdpa {
 void prof_before(int kernel, hipStream_t s) {
-  if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
-  (void)hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel]], s);
+  t_prof_slot[kernel] = -1;
+  if (!(g_prof.mask.load(std::memory_order_acquire) >> kernel & 1)) return;
+  const int i = g_prof.n[kernel].fetch_add(1, std::memory_order_relaxed);
+  if (i >= PROF_MAX) return;
+  t_prof_slot[kernel] = i;
+  (void)hipEventRecord(g_prof.ev[kernel][2 * i], s);
 }
 void prof_after(int kernel, hipStream_t s) {
-  if (!(g_prof.mask >> kernel & 1) || g_prof.n[kernel] >= PROF_MAX) return;
-  (void)hipEventRecord(g_prof.ev[kernel][2 * g_prof.n[kernel] + 1], s);
-  ++g_prof.n[kernel];
+  const int i = t_prof_slot[kernel];
+  if (i < 0) return;
+  (void)hipEventRecord(g_prof.ev[kernel][2 * i + 1], s);
+  t_prof_slot[kernel] = -1;
 }
 }  // namespace gdpa
 
@@ -273,15 +285,15 @@ int32_t gdpa_profile_start(int32_t mask) {
         if (hipEventCreate(&g_prof.ev[k][i]) != hipSuccess) return GDPA_EHIP;
     g_prof.created = true;
   }
-  g_prof.mask = mask;
-  for (int k = 0; k < PROF_KERNELS; ++k) g_prof.n[k] = 0;
+  for (int k = 0; k < PROF_KERNELS; ++k) g_prof.n[k].store(0, std::memory_order_relaxed);
+  g_prof.mask.store(mask, std::memory_order_release);
   return GDPA_OK;
 }
 
 int32_t gdpa_profile_read(int32_t kernel, int32_t* launches, double* total_ms) {
   if (!launches || !total_ms || kernel < 0 || kernel >= PROF_KERNELS) return GDPA_EINVAL;
   double tot = 0.0;
-  const int n = g_prof.n[kernel];
+  const int n = std::min(g_prof.n[kernel].load(std::memory_order_acquire), PROF_MAX);
   for (int i = 0; i < n; ++i) {
     float ms = 0.0f;
     if (hipEventSynchronize(g_prof.ev[kernel][2 * i + 1]) != hipSuccess) return GDPA_EHIP;
@@ -296,7 +308,7 @@ int32_t gdpa_profile_read(int32_t kernel, int32_t* launches, double* total_ms) {
 }
 
 int32_t gdpa_profile_stop(void) {
-  g_prof.mask = 0;
+  g_prof.mask.store(0, std::memory_order_release);
   return GDPA_OK;
 }
 
