@@ -105,6 +105,66 @@ __device__ __forceinline__ void rope_tiles(GDPA_LDS char* sq, GDPA_LDS char* sk,
   }
 }
 
+// The forward's version of rope_tiles for K alone (its Q is rotated in registers, rope_q_regs).
+template <int NTH>
+__device__ __forceinline__ void rope_k_tile(GDPA_LDS char* sk, GDPA_LDS char* skl, int n, int p0,
+                                            const GDPA_LDS double* c, int tid) {
+  constexpr int TPR = NTH / BL;
+  constexpr int CH = (D / 8) / TPR;
+  const int r = tid / TPR, k0 = (tid % TPR) * CH;
+  if (r >= n) {
+#pragma unroll
+    for (int k = k0; k < k0 + CH; ++k) *(GDPA_LDS bf16x8*)(skl + xoff(r, k)) = zero_bf16x8();
+    return;
+  }
+#pragma unroll
+  for (int k = k0; k < k0 + CH; ++k) {
+    GDPA_LDS bf16x8* pk = (GDPA_LDS bf16x8*)(sk + xoff(r, k));
+    const bf16x8 kk = *pk;
+    float kf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sn, cs;
+      rope_sc(c[4 * k + e], p0 + r, sn, cs);
+      const float ke = (float)kk[2 * e], ko = (float)kk[2 * e + 1];
+      kf[2 * e] = cs * ke - sn * ko;
+      kf[2 * e + 1] = sn * ke + cs * ko;
+    }
+    const bf16x8 kh = pack8(kf);
+    float kl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kl[e] = kf[e] - (float)kh[e];
+    *pk = kh;
+    *(GDPA_LDS bf16x8*)(skl + xoff(r, k)) = pack8(kl);
+  }
+}
+
+// A lane's Q operands (query row at position pos; register s holds D indices 16s + 8g .. + 7,
+// the pairs m = 8s + 4g + 0..3) rotated in registers as hi and lo parts, the same arithmetic as
+// rope_tiles.
+__device__ __forceinline__ void rope_q_regs(bf16x8* qop, bf16x8* qlo, int pos, int g,
+                                            const GDPA_LDS double* c) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const bf16x8 q = qop[s];
+    float qf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sn, cs;
+      rope_sc(c[8 * s + 4 * g + e], pos, sn, cs);
+      const float qe = (float)q[2 * e], qo = (float)q[2 * e + 1];
+      qf[2 * e] = cs * qe - sn * qo;
+      qf[2 * e + 1] = sn * qe + cs * qo;
+    }
+    const bf16x8 qh = pack8(qf);
+    float ql[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ql[e] = qf[e] - (float)qh[e];
+    qop[s] = qh;
+    qlo[s] = pack8(ql);
+  }
+}
+
 // Turn a lane's fp32 gradient row back (the transpose of the rotation): register r of block n
 // holds D index 32n + 8(r/4) + 4g + r%4, so registers (r, r+1), r%4 in {0, 2}, are the pair
 // m = 16n + 4(r/4) + 2g + (r%4)/2 of the row at position pos.
@@ -133,19 +193,17 @@ __device__ __forceinline__ bool item_of(const BlockArgs& a, int& b, int& t, int&
 }
 
 // ------------------------------------------------------------------------------------------
-// forward: 2 waves of 32 queries each
+// forward: 2 waves of 32 queries each. Q goes straight to registers (rotated there), so the
+// workgroup holds only the K (hi, lo) and V tiles in LDS: 48 KiB, three workgroups per compute
+// unit.
 template <int ACT, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(128) void block_fwd_kernel(BlockArgs a) {
-  __shared__ __attribute__((aligned(16))) char sq_[TILE];
   __shared__ __attribute__((aligned(16))) char sk_[TILE];
   __shared__ __attribute__((aligned(16))) char sv_[TILE];
-  __shared__ __attribute__((aligned(16))) char sql_[ROPE ? TILE : 16];
   __shared__ __attribute__((aligned(16))) char skl_[ROPE ? TILE : 16];
   __shared__ double c_[ROPE ? D / 2 : 1];
-  GDPA_LDS char* sq = (GDPA_LDS char*)sq_;
   GDPA_LDS char* sk = (GDPA_LDS char*)sk_;
   GDPA_LDS char* sv = (GDPA_LDS char*)sv_;
-  GDPA_LDS char* sql = (GDPA_LDS char*)sql_;
   GDPA_LDS char* skl = (GDPA_LDS char*)skl_;
   GDPA_LDS double* c = (GDPA_LDS double*)c_;
   int b, t, h;
@@ -157,25 +215,26 @@ __global__ __launch_bounds__(128) void block_fwd_kernel(BlockArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // each wave issues the loads of two of the four row groups of a tile
   for (int u = w; u < 4; u += 2) {
-    issue_tile(sq, (const __bf16*)a.Q, r0, L, base, H, h, u, lane);
     issue_tile(sk, (const __bf16*)a.K, r0, L, base, H, h, u, lane);
     issue_tile(sv, (const __bf16*)a.V, r0, L, base, H, h, u, lane);
+  }
+  const int iq = w * 32 + l32;  // the lane's query inside the block
+  const bool qv = iq < n;
+  bf16x8 qop[D / 16], qlo[D / 16];
+  {
+    const __bf16* Q = (const __bf16*)a.Q + ((int64_t)(base + r0 + (qv ? iq : 0)) * H + h) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qop[s] = qv ? *(const bf16x8*)(Q + 16 * s + 8 * g) : zero_bf16x8();
   }
   if (ROPE) rope_table(c, a.rope_log2_base, tid);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (ROPE) {
-    rope_tiles<128>(sq, sk, sql, skl, n, r0, c, tid);
+    rope_k_tile<128>(sk, skl, n, r0, c, tid);
+    rope_q_regs(qop, qlo, r0 + iq, g, c);
     __syncthreads();
   }
-  const int iq = w * 32 + l32;  // the lane's query inside the block
   if (w * 32 >= n) return;
-  bf16x8 qop[D / 16], qlo[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    qop[s] = row_op(sq, w * 32, s, lane);
-    if (ROPE) qlo[s] = row_op(sql, w * 32, s, lane);
-  }
   f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
