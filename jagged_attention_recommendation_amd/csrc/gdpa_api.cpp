@@ -453,6 +453,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.Dvec = (float*)(ws + L.dvec); ba.hdr = ws + L.header;
   ba.items_q = ws + L.items_q; ba.items_k = ws + L.items_k;
   ba.dbias_part = p->bias_buckets > 0 ? (float*)(ws + L.part) : nullptr;
+  ba.part_rows = (int)(L.max_qtiles * (tq / 32));
   ba.tile_base = (const int32_t*)(ws + L.tile_base);
   ba.dbias_part_x = (float*)(ws + L.part_x);
   ba.split_cnt_q = (int32_t*)(ws + L.split_cnt_q); ba.split_cnt_k = (int32_t*)(ws + L.split_cnt_k);
@@ -476,7 +477,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
     DbiasArgs da;
     da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
     da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
-    da.part = ba.dbias_part; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
+    da.part = ba.dbias_part; da.part_rows = ba.part_rows; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
     da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
     da.causal = p->causal; da.win = pr.win; da.tile_rows = tq;
     da.loop_rows = bwd_k_loop(p->dtype);

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   float e_lo = 0.0f, e_hi = 0.0f;
   bool has_lo = false, has_hi = false;
   if (BIAS) {
-    part = a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb;
+    part = a.dbias_part + ((int64_t)h * a.part_rows + it.aux * (QI / 32) + w) * nb;
   }
   // Writes the complete diagonal d of this wave (value v) to its partial row; the ends of the
   // table collect every diagonal that clamps to them, summed over the wave in a fixed order.

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
   // partial row of this row block: canonical, or the chunk's slot row for a split tile
   float* part = !BIAS ? nullptr
-                : it.slot < 0 ? a.dbias_part + ((int64_t)(it.aux * (QI / 32) + w) * H + h) * nb
+                : it.slot < 0 ? a.dbias_part + ((int64_t)h * a.part_rows + it.aux * (QI / 32) + w) * nb
                               : a.dbias_part_x + ((int64_t)it.slot * (QI / 32) + w) * nb;
   float e_lo = 0.0f, e_hi = 0.0f;
   bool has_lo = false, has_hi = false;

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
   if (BIAS) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      part[q] = a.dbias_part + ((int64_t)(it.aux * 2 + q) * H + h) * nb;
+      part[q] = a.dbias_part + ((int64_t)h * a.part_rows + it.aux * 2 + q) * nb;
       const int wr = i0 + 32 * q;
       if (Lk > 0 && wr < Lq) {
         int last = nkt - 1;

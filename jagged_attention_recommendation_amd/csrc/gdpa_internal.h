@@ -81,6 +81,7 @@ hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);
 // Rows of split dQ tiles go to the slot rows part_x[(slot * R + rb % R) * NB], one per chunk,
 // and are summed in chunk order.
 struct DbiasArgs {
+  int part_rows;  // row blocks per head of part (head-major: [H, part_rows, NB])
   const int32_t* q_off;
   const int32_t* kv_off;
   const int32_t* tile_base;
@@ -160,7 +161,8 @@ struct BwdArgs {
   const void* hdr;
   const void* items_q;   // query-tile items (dQ)
   const void* items_k;   // key-tile items (dK/dV)
-  float* dbias_part;     // [n_rowblocks, H, NB] per 32-query row block diagonal sums of dS
+  float* dbias_part;     // [H, part_rows, NB] per 32-query row block diagonal sums of dS
+  int part_rows;         // row blocks the partial-row buffer holds per head
   float* dbias_part_x;   // split chunks: [2 * nslot * QI / 32, NB]
   int32_t* split_cnt_q;  // chunk counters of split query tiles
   int32_t* split_cnt_k;  // chunk counters of split key tiles

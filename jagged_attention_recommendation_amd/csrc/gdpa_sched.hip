@@ -533,10 +533,12 @@ __device__ __forceinline__ bool chunk_range(int rb, int Lq, int causal, int win,
 // constants.
 template <int QI, int KL, bool WIN>
 __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
+  constexpr int RBC = 1024;  // row blocks whose entry ranges one pass stages in LDS
+  __shared__ int rlo[RBC], rhi[RBC];
   const int win = WIN ? a.win : 0;  // a compile-time zero without a window
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= a.nb) return;
+  const bool live = c < a.nb;  // threads past the table still join the barriers
   const WsHeader* hdr = (const WsHeader*)a.hdr;
   float acc = 0.0f;
   if (hdr->error == 0) {
@@ -547,12 +549,10 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     const int nb = a.nb;
     constexpr int PER = QI / 32;
     constexpr int BATCH = 16;
+    static_assert(BATCH == 16, "the load pins below name 16 registers");
     // Row block rb reaches diagonals up to 32 rb + 31 (clamped), so entry c sees only row blocks
     // rb >= (c - 31) / 32: the loop starts at the wave's first such block (its lowest c) and is
-    // empty past the last row block. Blocks it skips would each have added +0.0. The range
-    // arithmetic is uniform across the wave; every lane loads its entry of the row (in bounds,
-    // and the wave's 64 entries overlap the row's range anyway) and keeps it only inside the
-    // range, so the loads carry no branches.
+    // empty past the last row block. Blocks it skips would each have added +0.0.
     const int c_first = __builtin_amdgcn_readfirstlane(c);
     // With a sliding window a row block's first visited key tile starts at most KL - 1 keys
     // before its first query's window, so it wrote no diagonal above win + KL + 29: a wave whose
@@ -560,29 +560,49 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
     const bool above_window = WIN && c_first > win + KL + 29;
     const int rb_begin = c_first > 32 * nrb - 1 || above_window ? nrb : max(0, (c_first - 31) / 32);
     if (a.split_slot == nullptr || hdr->n_split == 0) {
-      // no split tiles: one row per row block. All loads of a batch first (in bounds, no
-      // branches), then the range tests; an entry outside its row block's range is cleared by a
-      // bit mask (stale bits there may be anything, even NaN), which also keeps every load used.
-      for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
-        int xi[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int rb = min(rb0 + u, nrb - 1);
-          const int64_t row = (int64_t)(tb + rb / PER) * PER + rb % PER;
-          xi[u] = __float_as_int(a.part[(row * a.H + h) * nb + c]);
-        }
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-          const int rb = min(rb0 + u, nrb - 1);
+      // No split tiles: one row per row block. The clamped entry range each row block wrote is
+      // staged in LDS by the workgroup (vector work, RBC row blocks per pass) rather than
+      // recomputed per load by every wave in scalar code, which serialised on the scalar unit.
+      // Each wave then issues a batch's loads (in bounds: the entry is clamped into the row,
+      // no branches), and an entry outside its row block's range is cleared by a bit mask
+      // (stale bits there may be anything, even NaN). The summation order is rb ascending.
+      const int cl = min(c, nb - 1);
+      const int wg_first = max(0, ((int)blockIdx.y * 256 - 31) / 32);
+      for (int r0 = wg_first; r0 < nrb; r0 += RBC) {
+        const int rn = min(RBC, nrb - r0);
+        __syncthreads();  // the previous pass's range reads are done
+        for (int i = threadIdx.x; i < rn; i += 256) {
+          const int rb = r0 + i;
           int kf;
           const int nkt = qtile_cost<QI, KL>(rb / PER, Lq, Lk, a.causal, win, kf);
           int d_lo = 1, d_hi = 0;
-          const bool any = rb0 + u < nrb && chunk_range<KL>(rb, Lq, a.causal, win, kf, kf + nkt, d_lo, d_hi);
-          const bool keep = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1);
-          acc += __int_as_float(xi[u] & (keep ? -1 : 0));
+          const bool any = chunk_range<KL>(rb, Lq, a.causal, win, kf, kf + nkt, d_lo, d_hi);
+          rlo[i] = any ? clampi(d_lo, 0, nb - 1) : nb;
+          rhi[i] = any ? clampi(d_hi, 0, nb - 1) : -1;
+        }
+        __syncthreads();
+        for (int rb0 = max(r0, rb_begin); rb0 < r0 + rn; rb0 += BATCH) {
+          int xi[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int rb = min(rb0 + u, r0 + rn - 1);
+            const int64_t row = (int64_t)(tb + rb / PER) * PER + rb % PER;
+            xi[u] = __float_as_int(a.part[((int64_t)h * a.part_rows + row) * nb + cl]);
+          }
+          // every load of the batch is issued before the first is used
+          asm volatile("" ::"v"(xi[0]), "v"(xi[1]), "v"(xi[2]), "v"(xi[3]), "v"(xi[4]), "v"(xi[5]),
+                       "v"(xi[6]), "v"(xi[7]));
+          asm volatile("" ::"v"(xi[8]), "v"(xi[9]), "v"(xi[10]), "v"(xi[11]), "v"(xi[12]),
+                       "v"(xi[13]), "v"(xi[14]), "v"(xi[15]));
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int i = min(rb0 + u, r0 + rn - 1) - r0;
+            const bool keep = rb0 + u < r0 + rn && c >= rlo[i] && c <= rhi[i];
+            acc += __int_as_float(xi[u] & (keep ? -1 : 0));
+          }
         }
       }
-    } else for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
+    } else if (live) for (int rb0 = rb_begin; rb0 < nrb; rb0 += BATCH) {
       float v[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
@@ -594,7 +614,7 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
         int d_lo = 1, d_hi = 0;
         const bool any = rb0 + u < nrb && sb < 0 && chunk_range<KL>(rb, Lq, a.causal, win, kf, kf + nkt, d_lo, d_hi);
         const int64_t row = (int64_t)(tb + t) * PER + rb % PER;
-        const float x = a.part[(row * a.H + h) * nb + c];
+        const float x = a.part[((int64_t)h * a.part_rows + row) * nb + c];
         v[u] = any && c >= clampi(d_lo, 0, nb - 1) && c <= clampi(d_hi, 0, nb - 1) ? x : 0.0f;
         if (sb >= 0 && rb0 + u < nrb) {
           // split tile: its chunks' rows, in chunk order
@@ -613,7 +633,7 @@ __global__ __launch_bounds__(256) void dbias_stage_a(DbiasArgs a) {
       for (int u = 0; u < BATCH; ++u) acc += v[u];
     }
   }
-  a.part_bh[((int64_t)b * a.H + h) * a.nb + c] = acc;
+  if (live) a.part_bh[((int64_t)b * a.H + h) * a.nb + c] = acc;
 }
 
 // Stage B: dbias[h, c] = sum over samples in order (loads batched as in stage A).
