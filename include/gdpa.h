@@ -209,9 +209,10 @@ int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err
  * items; the backward has list 0 (query-tile items, dQ) and list 1 (key-tile items, dK/dV).
  * *offset receives the list's byte offset from the start of the workspace and *capacity the
  * number of items it can hold; the workspace header's item counts (int32 words 1 and 2) say
- * how many items the last call wrote. An item is 8 int32: sample, tile, head, the tile's
+ * how many items the last call wrote. An item is 12 int32: sample, tile, head, the tile's
  * canonical index (tiles numbered sample by sample), the first and one-past-last inner tile it
- * covers, its chunk slot (-1 when its tile is not split) and chunk index | chunk count << 16.
+ * covers, its chunk slot (-1 when its tile is not split), chunk index | chunk count << 16, and
+ * the sample's first query row, query length, first key row and key length.
  * Placement: item i runs on die i % 8 of the GPU. The (sample, head) groups are ranked by cost
  * (inner tiles, all of the group's items), largest first, and dealt to the dies in a snake
  * (0..7, 7..0, ...); each die lists its groups in rank order, a group's items consecutive with

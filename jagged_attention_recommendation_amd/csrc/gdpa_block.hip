@@ -182,13 +182,16 @@ __device__ __forceinline__ void rope_back(f32x16* acc, int pos, int g, const GDP
     }
 }
 
-__device__ __forceinline__ bool item_of(const BlockArgs& a, int& b, int& t, int& h) {
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return false;
-  const Item it = ((const Item*)a.items)[blockIdx.x];
+// The workgroup's item (sample b, block t, head h, the sample's first row and length); the item
+// and the header come in one round trip (the item slot is in bounds whatever the count).
+__device__ __forceinline__ bool item_of(const BlockArgs& a, int& b, int& t, int& h, int& base, int& L) {
+  Item it;
+  if (!fetch_item(a.hdr, a.items, 0, it)) return false;
   b = it.b;
   t = it.tile;
   h = it.h;
+  base = it.q0;
+  L = it.lq;
   return true;
 }
 
@@ -207,9 +210,9 @@ __global__ __launch_bounds__(128) void block_fwd_kernel(BlockArgs a) {
   GDPA_LDS char* skl = (GDPA_LDS char*)skl_;
   GDPA_LDS double* c = (GDPA_LDS double*)c_;
   int b, t, h;
-  if (!item_of(a, b, t, h)) return;
+  int base, L;
+  if (!item_of(a, b, t, h, base, L)) return;
   const int H = a.H;
-  const int base = a.off[b], L = a.off[b + 1] - base;
   const int r0 = t * BL, n = min(BL, L - r0);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -322,9 +325,9 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(BlockArgs a) {
   GDPA_LDS float* rt = (GDPA_LDS float*)rt_;
   GDPA_LDS double* c = (GDPA_LDS double*)c_;
   int b, t, h;
-  if (!item_of(a, b, t, h)) return;
+  int base, L;
+  if (!item_of(a, b, t, h, base, L)) return;
   const int H = a.H;
-  const int base = a.off[b], L = a.off[b + 1] - base;
   const int r0 = t * BL, n = min(BL, L - r0);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -78,12 +78,11 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
   GDPA_LDS float* dsbuf_all = bwin + BIAS_WMAX;  // [wave][32][DSP]
   __shared__ int flag_;
 
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
-  const Item it = ((const Item*)a.items_q)[blockIdx.x];
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items_q, 0, it)) return;
   const int b = it.b, h = it.h, H = a.H, nb = a.nb;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int i0 = it.tile * QI;
@@ -357,12 +356,11 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   GDPA_LDS float* D_s = lse_s + QL;
   GDPA_LDS float* bwin = D_s + QL;
 
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items2) return;
-  const Item it = ((const Item*)a.items_k)[blockIdx.x];
-  const int b = it.b, h = it.h, H = a.H, nb = a.nb;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items_k, 1, it)) return;
+  const int h = it.h, H = a.H, nb = a.nb;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int j0 = it.tile * KI;

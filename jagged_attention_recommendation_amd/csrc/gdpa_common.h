@@ -37,10 +37,13 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // inner-loop tiles the item covers (counted from the first tile the tile visits). A long tile
 // split into n chunks has one item per chunk: slot is the chunk's partial-result slot (the
 // tile's chunks use consecutive slots) and chunk packs the chunk index (low 16 bits) with n; an
-// unsplit item has slot -1 and chunk 0.
+// unsplit item has slot -1 and chunk 0. The sample's first query and key rows and its lengths
+// ride along, so a workgroup learns everything about its item from one round trip instead of
+// reading the offsets after the item.
 struct Item {
   int b, tile, h, aux;
   int lo, hi, slot, chunk;
+  int q0, lq, kv0, lk;
 };
 
 // Workspace header (first 256 bytes of every workspace).
@@ -56,6 +59,20 @@ struct WsHeader {
   int die_items2[8];  // same, second list
   int pad[41];
 };
+
+// The workgroup's item of list `which` (0: the header's n_items, 1: n_items2) and whether it
+// exists. The header words and the item are loaded together and pinned before the test, so
+// they cost one round trip (the compiler would otherwise load the error word, then the count,
+// then the item, each after the previous test). The item slot is in bounds whatever the count;
+// its contents are not used when the item does not exist.
+__device__ __forceinline__ bool fetch_item(const void* hdr, const void* items, int which, Item& it) {
+  const WsHeader* h = (const WsHeader*)hdr;
+  it = ((const Item*)items)[blockIdx.x];
+  const int err = h->error;
+  const int n = which == 0 ? h->n_items : h->n_items2;
+  asm volatile("" ::"s"(err), "s"(n), "s"(it.b), "s"(it.lk));
+  return err == 0 && (int)blockIdx.x < n;
+}
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;

@@ -38,12 +38,11 @@ template <int D, int ACT, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ks[TN][D];
   __shared__ __attribute__((aligned(16))) float Vs[TN][D];
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
-  const Item it = ((const Item*)a.items)[blockIdx.x];
-  const int b = it.b, h = it.h, H = a.H, tid = threadIdx.x;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items, 0, it)) return;
+  const int h = it.h, H = a.H, tid = threadIdx.x;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int i = it.tile * TM + tid;
   const bool qv = i < Lq;
   const float* Q = (const float*)a.Q;
@@ -121,12 +120,11 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ks[TN][D];
   __shared__ __attribute__((aligned(16))) float Vs[TN][D];
   __shared__ float dS[TM][TN + 1];
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
-  const Item it = ((const Item*)a.items_q)[blockIdx.x];
-  const int b = it.b, h = it.h, H = a.H, tid = threadIdx.x;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items_q, 0, it)) return;
+  const int h = it.h, H = a.H, tid = threadIdx.x;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int i0 = it.tile * TM;
   const int i = i0 + tid;
   const bool qv = i < Lq;
@@ -234,12 +232,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Qs[TM][D];
   __shared__ __attribute__((aligned(16))) float dOs[TM][D];
   __shared__ float lse_s[TM], D_s[TM];
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items2) return;
-  const Item it = ((const Item*)a.items_k)[blockIdx.x];
-  const int b = it.b, h = it.h, H = a.H, tid = threadIdx.x;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items_k, 1, it)) return;
+  const int h = it.h, H = a.H, tid = threadIdx.x;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int j = it.tile * TN + tid;
   const bool kvalid = j < Lk;
   const int64_t krow = (int64_t)(kv0 + (kvalid ? j : 0)) * H + h;

@@ -71,12 +71,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   GDPA_LDS float* bwin = (GDPA_LDS float*)(Vs + S::V_BYTES);
   __shared__ int flag_;
 
-  const WsHeader* hdr = (const WsHeader*)a.hdr;
-  if (hdr->error != 0 || (int)blockIdx.x >= hdr->n_items) return;
-  const Item it = ((const Item*)a.items)[blockIdx.x];
+  Item it;  // carries the sample's offsets and lengths
+  if (!fetch_item(a.hdr, a.items, 0, it)) return;
   const int b = it.b, h = it.h, H = a.H;
-  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
-  const int kv0 = a.kv_off[b], Lk = a.kv_off[b + 1] - kv0;
+  const int q0 = it.q0, Lq = it.lq;
+  const int kv0 = it.kv0, Lk = it.lk;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int row_blk = it.tile * BM;   // first query of the item (local index)

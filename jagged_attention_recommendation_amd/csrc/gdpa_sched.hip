@@ -142,6 +142,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
   __shared__ int sbuf[SNT];  // scan of chunk counts per tile
   __shared__ int wsum[SNT / 64];
   __shared__ int lq_c[SNT], lk_c[SNT];       // lengths of the chunk's samples
+  __shared__ int q0_c[SNT], kv0_c[SNT];      // their first query and key rows
   __shared__ unsigned long long ccost[SNT];  // per-sample cost (one head) of the chunk
   __shared__ int cnch[SNT];                  // per-sample item count (one head) of the chunk
   __shared__ int first_e[SNT];               // chunk index of each sample's first tile
@@ -200,6 +201,8 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       }
       lq_c[tid] = Lq;
       lk_c[tid] = Lk;
+      q0_c[tid] = a.q_off[b];
+      kv0_c[tid] = a.kv_off[b];
       n = ((qmode ? Lq : Lk) + (1 << tis) - 1) >> tis;
     }
     cnt[tid] = n;
@@ -433,6 +436,7 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
         const int x = group_xcd(r), g0 = gpre_of(r);
         Item it;
         it.b = b; it.tile = tj; it.h = h; it.aux = first + u0 + j;
+        it.q0 = q0_c[bj]; it.lq = lq_c[bj]; it.kv0 = kv0_c[bj]; it.lk = lk_c[bj];
         for (int k = 0; k < nj; ++k) {
           it.lo = nj == 1 ? 0 : k * T;
           it.hi = nj == 1 ? cj : min(cj, (k + 1) * T);

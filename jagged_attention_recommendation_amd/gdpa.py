@@ -342,8 +342,8 @@ def workspace_header(workspace):
 
 def item_list(prob, workspace, for_bwd=False, which=0):
     """The scheduler's work items of the last call that used `workspace` (diagnostics;
-    synchronises): an int32 array [n, 8] of (sample, tile, head, canonical tile, lo, hi, slot,
-    chunk) in list order."""
+    synchronises): an int32 array [n, 12] of (sample, tile, head, canonical tile, lo, hi, slot,
+    chunk, first query row, query length, first key row, key length) in list order."""
     off = ctypes.c_size_t(0)
     cap = ctypes.c_int64(0)
     st = load().gdpa_item_list(ctypes.byref(prob), int(bool(for_bwd)), int(which),
@@ -353,7 +353,7 @@ def item_list(prob, workspace, for_bwd=False, which=0):
     n = workspace_header(workspace)["items2" if which else "items"]
     assert 0 <= n <= cap.value
     o = int(off.value)
-    return workspace[o:o + 32 * n].view(torch.int32).view(n, 8).cpu().numpy()
+    return workspace[o:o + 48 * n].view(torch.int32).view(n, 12).cpu().numpy()
 
 
 def profile_start(kernels):

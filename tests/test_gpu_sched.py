@@ -164,9 +164,14 @@ def check_placement(items, mode, H, die_items):
     assert max(die_cost) <= sum(die_cost) / DIES + 2 * max(group_cost.values()), die_cost
 
 
-def check_list(items, exp, chunk_T, header_T, nslot, mode, H, die_items):
+def check_list(items, exp, chunk_T, header_T, nslot, mode, H, die_items, q_off, kv_off):
     assert header_T == chunk_T
     assert len(items) == len(exp)
+    assert items.shape[1] == 12
+    # every item carries its sample's first rows and lengths
+    bs = items[:, 0].astype(np.int64)
+    assert np.array_equal(items[:, 8], q_off[bs]) and np.array_equal(items[:, 9], q_off[bs + 1] - q_off[bs])
+    assert np.array_equal(items[:, 10], kv_off[bs]) and np.array_equal(items[:, 11], kv_off[bs + 1] - kv_off[bs])
     got = Counter(tuple(int(x) for x in (it[0], it[1], it[2], it[3], it[4], it[5])) for it in items)
     want = Counter(e[:6] for e in exp)
     assert got == want, "item multiset differs"
@@ -174,7 +179,7 @@ def check_list(items, exp, chunk_T, header_T, nslot, mode, H, die_items):
     n_of = {(e[0], e[1], e[2]): e[6] for e in exp}
     slots = {}
     for it in items:
-        b, t, h, _, lo, hi, slot, chunk = (int(x) for x in it)
+        b, t, h, _, lo, hi, slot, chunk = (int(x) for x in it[:8])
         n = n_of[(b, t, h)]
         if n == 1:
             assert slot == -1 and chunk == 0
@@ -216,7 +221,8 @@ def run_and_check(p, window=0, backward=True):
     hf = gdpa.workspace_header(wf)
     assert hf["error"] == 0
     exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, fi, fl, bf16, nslot)
-    check_list(gdpa.item_list(prob, wf), exp, T, hf["chunk"], nslot, "q", p.H, hf["die_items"])
+    qo, ko = np.asarray(p.q_off, np.int64), np.asarray(p.kv_off, np.int64)
+    check_list(gdpa.item_list(prob, wf), exp, T, hf["chunk"], nslot, "q", p.H, hf["die_items"], qo, ko)
     if not backward:
         return
     wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
@@ -226,9 +232,9 @@ def run_and_check(p, window=0, backward=True):
     split_q = bf16 and (p.D == 128 or nb == 0)
     split_k = bf16 and p.D == 128
     exp, T = expected_items(lq, lk, p.H, "q", p.causal, win, qi, ql, split_q, nslot)
-    check_list(gdpa.item_list(prob, wb, True, 0), exp, T, hb["chunk"], nslot, "q", p.H, hb["die_items"])
+    check_list(gdpa.item_list(prob, wb, True, 0), exp, T, hb["chunk"], nslot, "q", p.H, hb["die_items"], qo, ko)
     exp, T = expected_items(lq, lk, p.H, "k", p.causal, win, ki, kl, split_k, nslot)
-    check_list(gdpa.item_list(prob, wb, True, 1), exp, T, hb["chunk2"], nslot, "k", p.H, hb["die_items2"])
+    check_list(gdpa.item_list(prob, wb, True, 1), exp, T, hb["chunk2"], nslot, "k", p.H, hb["die_items2"], qo, ko)
 
 
 @pytest.mark.parametrize("k", [2, 3, 4])
