@@ -543,7 +543,7 @@ hipError_t launch_d(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t
 // D = 128: the direct-load kernels of gdpa_bwd_dl.h.
 hipError_t launch_d128(const Prob& p, const BwdArgs& a, int gq, int gk, hipStream_t s) {
   if (gq > 0) {
-    const hipError_t e = bwddl::launch_dq(p, a, gq, s);
+    const hipError_t e = bwddl::launch_dq(p, a, persistent_grid(gq, 1), s);
     if (e != hipSuccess) return e;
   }
   return gk > 0 ? bwddl::launch_dkdv(p, a, gk, s) : hipSuccess;

@@ -68,16 +68,43 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sk1_[TILE];
   __shared__ __attribute__((aligned(16))) char sv1_[TILE];
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
-  __shared__ __attribute__((aligned(16))) float dsbuf_[BIAS ? 4 * 32 * DSP : 1];
-  __shared__ int flag_;
+  // bias-gradient buffer; at the start of an item, also where its dO and O rows land
+  __shared__ __attribute__((aligned(16))) float dsbuf_[4 * 32 * DSP];
+  __shared__ __attribute__((aligned(16))) char sink_[4 * 1024];  // prefetch loads land here
+  __shared__ int flag_, next_[2];
   GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
   GDPA_LDS char* sv0 = (GDPA_LDS char*)sv0_;
   GDPA_LDS char* sk1 = (GDPA_LDS char*)sk1_;
   GDPA_LDS char* sv1 = (GDPA_LDS char*)sv1_;
   GDPA_LDS float* bwin = (GDPA_LDS float*)bwin_;
+  GDPA_LDS int* nxt = (GDPA_LDS int*)next_;
 
-  Item it;  // carries the sample's offsets and lengths
-  if (!fetch_item(a.hdr, a.items_q, 0, it)) return;
+  // Persistent: the workgroup works through its die's items (see ItemQueue). Each item claims
+  // the next one as it starts, so the next record is at hand before the item ends and the next
+  // item's query rows can be prefetched during its last tile. A short item (one or two key tiles)
+  // also claims the item after the next: its last tile is then too early for the next record,
+  // which the previous item already fetched instead. (Claiming that far ahead on long items would
+  // hold back items that another workgroup of the die could start sooner.)
+  ItemQueue qu;
+  if (!queue_open(a.hdr, a.items_q, 0, qu)) return;
+  {
+    const int c0 = queue_claim(qu);
+    if (threadIdx.x == 0) nxt[0] = c0;
+    __syncthreads();
+  }
+  int idx = __builtin_amdgcn_readfirstlane(nxt[0]), nidx = qu.n;
+  int rec = queue_fetch(qu, idx), rec1 = 0;
+  bool have1 = false;  // nidx / rec1 hold the claimed next item
+  for (;;) {
+  if (idx >= qu.n) {  // this die's items are all claimed: take another die's
+    idx = queue_steal(qu, nxt);
+    if (idx >= qu.n) break;
+    rec = queue_fetch(qu, idx);
+    have1 = false;
+  }
+  const Item it = queue_record(rec);  // carries the sample's offsets and lengths
+  int n2idx = qu.n, rec2 = 0;
+  bool fetched = false;
   const int b = it.b, h = it.h, H = a.H, nb = a.nb;
   const int q0 = it.q0, Lq = it.lq;
   const int kv0 = it.kv0, Lk = it.lk;
@@ -89,8 +116,6 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   const bool qv = iq < Lq;
   const bool wave_active = wrow < Lq;
   const int64_t row = (int64_t)(q0 + (qv ? iq : 0)) * H + h;  // O, dO, lse, D row
-  // Q row: in the sample's rows, or in the one block every sample shares
-  const int64_t qin = a.q_shared ? (int64_t)(qv ? iq : 0) * H + h : row;
 
   int nkt = (Lk + KL - 1) / KL;
   if (CAUSAL) nkt = min(nkt, (min(Lq, i0 + QI) - 1) / KL + 1);
@@ -99,33 +124,61 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   // tile the item's sliding window reaches
   const int kt_first = WIN ? win_first_ktile(i0, a.win, KL) : 0;
   const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
+  const bool short_item = kt_hi - kt_lo <= 2;
 
+  // The item's query rows come in as direct-load tiles (whole cache lines per instruction) into
+  // buffers idle until its first key tile: Q into stage 1, dO and O into the bias-gradient
+  // buffer. Rows i0 .. i0 + 63 form the first tile of each, rows i0 + 64 .. i0 + 127 the second.
+  const __bf16* Q = (const __bf16*)a.Q;
+  const __bf16* dO = (const __bf16*)a.dO;
+  GDPA_LDS char* rows_do = (GDPA_LDS char*)dsbuf_;
+  GDPA_LDS char* rows_o = rows_do + 2 * TILE;
+  const bool two = Lq > i0 + ROWS;  // the item has rows in its second 64
+  {
+    const int qbase = a.q_shared ? 0 : q0;
+    issue_tile(sk1, Q, i0, Lq, qbase, H, h, w, lane);
+    issue_tile(rows_do, dO, i0, Lq, q0, H, h, w, lane);
+    if (ACT == ACT_SOFTMAX) issue_tile(rows_o, (const __bf16*)a.O, i0, Lq, q0, H, h, w, lane);
+    if (two) {
+      issue_tile(sv1, Q, i0 + ROWS, Lq, qbase, H, h, w, lane);
+      issue_tile(rows_do + TILE, dO, i0 + ROWS, Lq, q0, H, h, w, lane);
+      if (ACT == ACT_SOFTMAX) issue_tile(rows_o + TILE, (const __bf16*)a.O, i0 + ROWS, Lq, q0, H, h, w, lane);
+    }
+  }
+  const float lse_row = ACT == ACT_SOFTMAX && qv ? a.lse[row] : 0.0f;
+
+  const int claim_a = have1 ? -1 : queue_claim(qu);       // the next item
+  const int claim_b = short_item ? queue_claim(qu) : -1;  // the one after it
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
   if (kt_lo < kt_hi) {
     issue_tile(sk0, K, kt_lo * KL, Lk, kv0, H, h, w, lane);
     issue_tile(sv0, V, kt_lo * KL, Lk, kv0, H, h, w, lane);
   }
-
-  const __bf16* Q = (const __bf16*)a.Q;
-  const __bf16* dO = (const __bf16*)a.dO;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __syncthreads();                // ... and everyone else's
+  // wave w's 32 rows: tile w / 2, rows 32 (w % 2) ..; a wave past the item's rows uses zeros
   bf16x8 qop[D / 16], doop[D / 16];
   float part_d = 0.0f;
+  {
+    const int t = (w >> 1) * TILE, rb = (w & 1) * 32;
+    const GDPA_LDS char* tq = (w >> 1) ? sv1 : sk1;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    qop[s] = qv ? *(const bf16x8*)(Q + qin * D + 16 * s + 8 * g) : zero_bf16x8();
-    doop[s] = qv ? *(const bf16x8*)(dO + row * D + 16 * s + 8 * g) : zero_bf16x8();
-    if (ACT == ACT_SOFTMAX && qv) {
-      const bf16x8 ov = *(const bf16x8*)((const __bf16*)a.O + row * D + 16 * s + 8 * g);
+    for (int s = 0; s < D / 16; ++s) {
+      qop[s] = wave_active ? row_op(tq, rb, s, lane) : zero_bf16x8();
+      doop[s] = wave_active ? row_op(rows_do + t, rb, s, lane) : zero_bf16x8();
+      if (ACT == ACT_SOFTMAX && wave_active) {
+        const bf16x8 ov = row_op(rows_o + t, rb, s, lane);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part_d += (float)doop[s][e] * (float)ov[e];
+        for (int e = 0; e < 8; ++e) part_d += (float)doop[s][e] * (float)ov[e];
+      }
     }
   }
   float Di = 0.0f, lse2 = 0.0f;
   if (ACT == ACT_SOFTMAX) {
     Di = half_sum(part_d);
     if (qv) {
-      lse2 = a.lse[row] * LOG2E;
+      lse2 = lse_row * LOG2E;
       // every chunk computes it; the first writes it
       if (g == 0 && split::chunk_index(it.chunk) == 0) a.Dvec[row] = Di;
     }
@@ -160,10 +213,11 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   // partial-row store is not waited for at once.
   const GDPA_LDS float* dsrd = dsbuf + (63 - lane);
   GDPA_LDS float* dswr = dsbuf + l32 * (DSP - 1) + 64 + 4 * g;  // row l32, key 4g at column 4g - l32 + 64
-  if (BIAS) {  // each store covers 1 KiB of the buffer: 64 lanes on distinct banks
+  // (cleared at the first key tile, once every wave has read its rows from the buffer)
+  auto clear_dsbuf = [&]() {  // each store covers 1 KiB of the buffer: 64 lanes on distinct banks
 #pragma unroll
     for (int u = 0; u < 16; ++u) *(GDPA_LDS f32x4*)(dsbuf + 256 * u + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  };
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
   // partial row of this row block: canonical, or the chunk's slot row for a split tile
   float* part = !BIAS ? nullptr
@@ -383,13 +437,47 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   };
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage stay in flight while the other stage is read.
+  // At the start of tile kt (after its barrier): on the first tile, the records of the items
+  // claimed by this one are fetched; on the last, the next item's query rows are prefetched if its
+  // record is there (no later tile wait of this item then covers those loads).
+  GDPA_LDS char* sink = (GDPA_LDS char*)sink_ + w * 1024;
+  const int kt_pf = kt_hi - 1;
+  auto fetch_claimed = [&]() {
+    if (!have1) {
+      nidx = __builtin_amdgcn_readfirstlane(nxt[0]);
+      rec1 = queue_fetch(qu, nidx);
+    }
+    if (short_item) {
+      n2idx = __builtin_amdgcn_readfirstlane(nxt[1]);
+      rec2 = queue_fetch(qu, n2idx);
+    }
+    fetched = true;
+  };
+  auto at_tile = [&](int kt) {
+    if (kt == kt_lo) {
+      fetch_claimed();
+      if (BIAS) clear_dsbuf();
+    }
+    if (kt == kt_pf && (have1 || kt > kt_lo) && nidx < qu.n) {
+      const Item nx = queue_record(rec1);
+      const int r0 = nx.tile * QI + w * 32;
+      prefetch_rows32(sink, Q, r0, nx.lq, a.q_shared ? 0 : nx.q0, H, nx.h, lane);
+      prefetch_rows32(sink, dO, r0, nx.lq, nx.q0, H, nx.h, lane);
+      if (ACT == ACT_SOFTMAX) prefetch_rows32(sink, (const __bf16*)a.O, r0, nx.lq, nx.q0, H, nx.h, lane);
+    }
+  };
   for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads for tile kt have landed
+    if (kt == kt_lo && tid == 0) {
+      nxt[0] = claim_a;
+      nxt[1] = claim_b;
+    }
     __syncthreads();                // ... and everyone else's; tile kt - 1 is done with stage 1
     if (kt + 1 < kt_hi) {
       issue_tile(sk1, K, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv1, V, (kt + 1) * KL, Lk, kv0, H, h, w, lane);
     }
+    at_tile(kt);
     if (wave_needs(kt)) run_tile(sk0, sv0, kt * KL);
     if (kt + 1 >= kt_hi) break;
     __builtin_amdgcn_s_waitcnt(0);
@@ -398,6 +486,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       issue_tile(sk0, K, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
       issue_tile(sv0, V, (kt + 2) * KL, Lk, kv0, H, h, w, lane);
     }
+    at_tile(kt + 1);
     if (wave_needs(kt + 1)) run_tile(sk1, sv1, (kt + 1) * KL);
   }
 
@@ -434,17 +523,31 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
     if (split::chunk_done(a.split_cnt_q + first, n, (GDPA_LDS int*)&flag_))
       split::combine_dq_tile(a, b, it.tile, h, n, first);
-    return;
-  }
-  if (!qv) return;
-  if (a.dq_f32) {  // shared Q: this sample's gradient, summed over samples afterwards
+  } else if (qv) {
+    if (a.dq_f32) {  // shared Q: this sample's gradient, summed over samples afterwards
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) store_acc_row_f32(a.dq_f32 + row * D, dq[n], n, g, a.scale);
-    return;
-  }
-  __bf16* dqrow = (__bf16*)a.dQ + row * D;
+      for (int n = 0; n < D / 32; ++n) store_acc_row_f32(a.dq_f32 + row * D, dq[n], n, g, a.scale);
+    } else {
+      __bf16* dqrow = (__bf16*)a.dQ + row * D;
 #pragma unroll
-  for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(dqrow, dq[n], n, g, a.scale);
+      for (int n = 0; n < D / 32; ++n) store_acc_row_bf16(dqrow, dq[n], n, g, a.scale);
+    }
+  }
+  if (!fetched) {  // an item without key tiles: publish the claims now
+    if (tid == 0) {
+      nxt[0] = claim_a;
+      nxt[1] = claim_b;
+    }
+    __syncthreads();
+    fetch_claimed();
+  }
+  __syncthreads();  // this item's LDS (stages, bias window, flags) is free again
+  idx = nidx;
+  rec = rec1;
+  have1 = short_item;
+  nidx = n2idx;
+  rec1 = rec2;
+  }
 }
 
 // ------------------------------------------------------------------------------------------

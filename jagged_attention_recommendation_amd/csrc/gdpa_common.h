@@ -57,8 +57,12 @@ struct WsHeader {
   int chunk2;     // inner tiles per chunk, second list
   int die_items[8];   // items placed on each die as their group's own (first list)
   int die_items2[8];  // same, second list
-  int pad[41];
+  int qctr[8];        // per-die claim counters of the persistent kernels (first list)
+  int qctr2[8];       // same, second list
+  int pad[25];
 };
+static_assert(sizeof(WsHeader) == 256, "header size");
+static_assert(sizeof(Item) == 48, "item record size");
 
 // The workgroup's item of list `which` (0: the header's n_items, 1: n_items2) and whether it
 // exists. The header words and the item are loaded together and pinned before the test, so
@@ -72,6 +76,104 @@ __device__ __forceinline__ bool fetch_item(const void* hdr, const void* items, i
   const int n = which == 0 ? h->n_items : h->n_items2;
   asm volatile("" ::"s"(err), "s"(n), "s"(it.b), "s"(it.lk));
   return err == 0 && (int)blockIdx.x < n;
+}
+
+// Persistent consumption of an item list by a grid of a few workgroups per compute unit. The
+// workgroups of die x (x = blockIdx.x % 8: the dispatcher places workgroup i on die i % 8) take
+// that die's items, indices 8q + x for q < t_x, in increasing q, by counting on the die's claim
+// counter in the header (cleared by the scheduler); as the list holds each die's items costliest
+// first, this is the longest-first order of a dispatcher, without a workgroup launch per item.
+// A workgroup claims its next item when it starts the current one and fetches that item's record
+// during the current item, so moving on costs no memory round trip. When its die has no
+// unclaimed item left, it takes items of the die with the most unclaimed ones (queue_steal).
+struct ItemQueue {
+  int* ctr0;         // the eight claim counters
+  const int* items;  // the list, 12 words per item
+  int n, die;        // list length; die whose items the workgroup claims
+};
+
+// Opens list `which` (0: first, 1: second) of the workspace; false if the scheduler failed.
+__device__ __forceinline__ bool queue_open(const void* hdr, const void* items, int which, ItemQueue& q) {
+  WsHeader* h = (WsHeader*)hdr;  // the claim counters are the only header words written here
+  q.die = blockIdx.x & 7;
+  q.ctr0 = which == 0 ? h->qctr : h->qctr2;
+  q.items = (const int*)items;
+  q.n = which == 0 ? h->n_items : h->n_items2;
+  return h->error == 0;
+}
+
+// Claims the die's next item: its index for thread 0, -1 for the other threads.
+__device__ __forceinline__ int queue_claim(const ItemQueue& q) {
+  return threadIdx.x == 0 ? 8 * atomicAdd(q.ctr0 + q.die, 1) + q.die : -1;
+}
+
+// Items of die x in a list of n: t_x.
+__device__ __forceinline__ int queue_die_items(int n, int x) { return (n >> 3) + (x < (n & 7) ? 1 : 0); }
+
+// Called by the whole workgroup when its die has no unclaimed item: claims an item of the die
+// with the most unclaimed items and moves the queue there. Returns the item's index, or n when
+// no die has one left. The counters are read from the device-coherent level; a claim that loses
+// a race (the die's last items went to others) looks again.
+__device__ __forceinline__ int queue_steal(ItemQueue& q, GDPA_LDS int* slot) {
+  for (;;) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      int rem = 0;
+      if (lane < 8) {
+        const int c = __hip_atomic_load(q.ctr0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        rem = queue_die_items(q.n, lane) - c;
+      }
+      int best = -1, best_rem = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int r = __builtin_amdgcn_readlane(rem, x);
+        if (r > best_rem) {
+          best_rem = r;
+          best = x;
+        }
+      }
+      int res = q.n;  // nothing left anywhere
+      if (best >= 0) {
+        res = -1 - best;  // lost the race on die best: look again
+        if (lane == 0) {
+          const int c = atomicAdd(q.ctr0 + best, 1);
+          if (c < queue_die_items(q.n, best)) res = 8 * c + best;
+        }
+      }
+      if (lane == 0) *slot = res;
+    }
+    __syncthreads();
+    const int res = __builtin_amdgcn_readfirstlane(*slot);
+    __syncthreads();  // the slot may be written again
+    if (res >= 0) {
+      if (res < q.n) q.die = res & 7;
+      return res;
+    }
+  }
+}
+
+// Lane l < 12 of the calling wave loads word l of item idx (nothing past the list's end).
+__device__ __forceinline__ int queue_fetch(const ItemQueue& q, int idx) {
+  const int lane = threadIdx.x & 63;
+  return idx < q.n && lane < 12 ? q.items[(int64_t)idx * 12 + lane] : 0;
+}
+
+// The record loaded by queue_fetch, as scalars.
+__device__ __forceinline__ Item queue_record(int v) {
+  Item it;
+  it.b = __builtin_amdgcn_readlane(v, 0);
+  it.tile = __builtin_amdgcn_readlane(v, 1);
+  it.h = __builtin_amdgcn_readlane(v, 2);
+  it.aux = __builtin_amdgcn_readlane(v, 3);
+  it.lo = __builtin_amdgcn_readlane(v, 4);
+  it.hi = __builtin_amdgcn_readlane(v, 5);
+  it.slot = __builtin_amdgcn_readlane(v, 6);
+  it.chunk = __builtin_amdgcn_readlane(v, 7);
+  it.q0 = __builtin_amdgcn_readlane(v, 8);
+  it.lq = __builtin_amdgcn_readlane(v, 9);
+  it.kv0 = __builtin_amdgcn_readlane(v, 10);
+  it.lk = __builtin_amdgcn_readlane(v, 11);
+  return it;
 }
 
 constexpr float LOG2E = 1.4426950408889634f;

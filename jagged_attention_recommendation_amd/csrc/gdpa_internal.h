@@ -72,6 +72,9 @@ inline void set_sched_scratch(SchedArgs& a, char* p, int B) {
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+// Grid of a persistent kernel (ItemQueue) that holds per_cu workgroups per compute unit of the
+// current device: at most cap workgroups (the list's capacity), a multiple of the 8 dies.
+int persistent_grid(int cap, int per_cu);
 hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);
 
 // Bias gradient reduction. The dQ kernels write, per (32-query row block, head), the diagonal

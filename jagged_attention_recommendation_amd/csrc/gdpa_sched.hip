@@ -26,6 +26,8 @@
 // tile a canonical index, and threads then take tiles (not samples) so long samples do not
 // serialise. Per-sample values live in LDS when the batch fits one chunk, else in workspace
 // scratch.
+#include <atomic>
+
 #include "gdpa_common.h"
 #include "gdpa_internal.h"
 
@@ -262,7 +264,8 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     if (tid == 0) {
       hdr->error = err;
       int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
-      for (int x = 0; x < XCDS; ++x) die[x] = 0;
+      int* qc = a.list == 0 ? hdr->qctr : hdr->qctr2;
+      for (int x = 0; x < XCDS; ++x) die[x] = qc[x] = 0;
       if (a.list == 0) {
         hdr->n_items = 0; hdr->n_split = 0;
       } else {
@@ -462,7 +465,11 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     const int ns = err != 0 ? 0 : split_count;
     const int chunk = a.split && T != 0x7fffffff ? T : 0;
     int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
-    for (int x = 0; x < XCDS; ++x) die[x] = err != 0 ? 0 : xtot[x];
+    int* qc = a.list == 0 ? hdr->qctr : hdr->qctr2;  // claim counters of the persistent kernels
+    for (int x = 0; x < XCDS; ++x) {
+      die[x] = err != 0 ? 0 : xtot[x];
+      qc[x] = 0;
+    }
     if (a.list == 0) {
       hdr->error = err;
       hdr->n_items = n; hdr->n_split = ns; hdr->chunk = chunk;
@@ -470,6 +477,18 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
       hdr->n_items2 = n; hdr->n_split2 = ns; hdr->chunk2 = chunk;
     }
   }
+}
+
+int persistent_grid(int cap, int per_cu) {
+  static std::atomic<int> cus[64];  // compute units per device, looked up once
+  int dev = 0, c = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) c = cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    if (dev >= 0 && dev < 64) cus[dev].store(c, std::memory_order_relaxed);
+  }
+  const int g = max(XCDS, (c * per_cu) / XCDS * XCDS);
+  return cap < g ? cap : g;
 }
 
 bool sched_small(const SchedArgs& a) { return a.B <= SNT && (int64_t)a.B * a.H <= GCAP; }
