@@ -546,7 +546,7 @@ hipError_t launch_d128(const Prob& p, const BwdArgs& a, int gq, int gk, hipStrea
     const hipError_t e = bwddl::launch_dq(p, a, persistent_grid(gq, 1), s);
     if (e != hipSuccess) return e;
   }
-  return gk > 0 ? bwddl::launch_dkdv(p, a, gk, s) : hipSuccess;
+  return gk > 0 ? bwddl::launch_dkdv(p, a, persistent_grid(gk, 1), s) : hipSuccess;
 }
 
 }  // namespace

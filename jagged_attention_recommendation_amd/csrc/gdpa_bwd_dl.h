@@ -565,16 +565,38 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char so1_[TILE];
   __shared__ __attribute__((aligned(16))) float rt_[SM ? 2 * 2 * QL : 1];  // [stage][lse, D][QL]
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
-  __shared__ int flag_;
+  __shared__ __attribute__((aligned(16))) char vrows_[2 * TILE];  // the item's V rows
+  __shared__ __attribute__((aligned(16))) char sink_[4 * 1024];   // prefetch loads land here
+  __shared__ int flag_, next_[2];
   GDPA_LDS char* sq0 = (GDPA_LDS char*)sq0_;
   GDPA_LDS char* so0 = (GDPA_LDS char*)so0_;
   GDPA_LDS char* sq1 = (GDPA_LDS char*)sq1_;
   GDPA_LDS char* so1 = (GDPA_LDS char*)so1_;
   GDPA_LDS float* rt = (GDPA_LDS float*)rt_;
   GDPA_LDS float* bwin = (GDPA_LDS float*)bwin_;
+  GDPA_LDS int* nxt = (GDPA_LDS int*)next_;
 
-  Item it;  // carries the sample's offsets and lengths
-  if (!fetch_item(a.hdr, a.items_k, 1, it)) return;
+  // Persistent, with the claims, record fetches and next-item prefetch of the dQ kernel.
+  ItemQueue qu;
+  if (!queue_open(a.hdr, a.items_k, 1, qu)) return;
+  {
+    const int c0 = queue_claim(qu);
+    if (threadIdx.x == 0) nxt[0] = c0;
+    __syncthreads();
+  }
+  int idx = __builtin_amdgcn_readfirstlane(nxt[0]), nidx = qu.n;
+  int rec = queue_fetch(qu, idx), rec1 = 0;
+  bool have1 = false;  // nidx / rec1 hold the claimed next item
+  for (;;) {
+  if (idx >= qu.n) {  // this die's items are all claimed: take another die's
+    idx = queue_steal(qu, nxt);
+    if (idx >= qu.n) break;
+    rec = queue_fetch(qu, idx);
+    have1 = false;
+  }
+  const Item it = queue_record(rec);  // carries the sample's offsets and lengths
+  int n2idx = qu.n, rec2 = 0;
+  bool fetched = false;
   const int b = it.b, h = it.h, H = a.H, nb = a.nb;
   const int q0 = it.q0, Lq = it.lq;
   const int kv0 = it.kv0, Lk = it.lk;
@@ -594,6 +616,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   const int nt = j0 < Lk && qt0 < qend ? qend - qt0 : 0;  // query tiles this key tile visits
   // the item's query tiles qt0 + [t_lo, t_hi): all of them, or one chunk of a split tile
   const int t_lo = it.lo, t_hi = min(it.hi, nt);
+  const bool short_item = t_hi - t_lo <= 2;
 
   const __bf16* Q = (const __bf16*)a.Q;
   const __bf16* dO = (const __bf16*)a.dO;
@@ -615,13 +638,34 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   // Query tiles are visited last to first: every key tile of a sample then starts at the same
   // query tile, so the key tiles of one (sample, head), which the scheduler starts together on
   // one die, stream the shared query tiles through its L2 in step.
+  // The item's key rows come in as direct-load tiles (whole cache lines per instruction): K into
+  // stage 1, idle until the first query tile, and V into their own buffer. Keys j0 .. j0 + 63
+  // form the first tile of each, keys j0 + 64 .. j0 + 127 the second.
+  const __bf16* K = (const __bf16*)a.K;
+  const __bf16* V = (const __bf16*)a.V;
+  GDPA_LDS char* vrows = (GDPA_LDS char*)vrows_;
+  issue_tile(sq1, K, j0, Lk, kv0, H, h, w, lane);
+  issue_tile(vrows, V, j0, Lk, kv0, H, h, w, lane);
+  if (Lk > j0 + ROWS) {
+    issue_tile(so1, K, j0 + ROWS, Lk, kv0, H, h, w, lane);
+    issue_tile(vrows + TILE, V, j0 + ROWS, Lk, kv0, H, h, w, lane);
+  }
+  const int claim_a = have1 ? -1 : queue_claim(qu);       // the next item
+  const int claim_b = short_item ? queue_claim(qu) : -1;  // the one after it
   if (t_lo < t_hi) issue(sq0, so0, rt, qt0 + t_hi - 1);
-
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __syncthreads();                // ... and everyone else's
+  // wave w's 32 keys: tile w / 2, rows 32 (w % 2) ..; a wave past the item's keys uses zeros
   bf16x8 kop[D / 16], vop[D / 16];
+  {
+    const GDPA_LDS char* tk = (w >> 1) ? so1 : sq1;
+    const GDPA_LDS char* tv = vrows + (w >> 1) * TILE;
+    const int rb = (w & 1) * 32;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.K + krow * D + 16 * s + 8 * g) : zero_bf16x8();
-    vop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.V + krow * D + 16 * s + 8 * g) : zero_bf16x8();
+    for (int s = 0; s < D / 16; ++s) {
+      kop[s] = wave_active ? row_op(tk, rb, s, lane) : zero_bf16x8();
+      vop[s] = wave_active ? row_op(tv, rb, s, lane) : zero_bf16x8();
+    }
   }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -769,13 +813,42 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   auto wave_needs = [&](int i0) {
     return wave_active && !(CAUSAL && i0 + QL - 1 < wkey) && !(WIN && i0 > min(wkey + 31, Lk - 1) + a.win - 1);
   };
+  // At the start of query tile t (after its barrier): on the first, the records of the items
+  // claimed by this one are fetched; on the last, the next item's key rows are prefetched if its
+  // record is there.
+  GDPA_LDS char* sink = (GDPA_LDS char*)sink_ + w * 1024;
+  auto fetch_claimed = [&]() {
+    if (!have1) {
+      nidx = __builtin_amdgcn_readfirstlane(nxt[0]);
+      rec1 = queue_fetch(qu, nidx);
+    }
+    if (short_item) {
+      n2idx = __builtin_amdgcn_readfirstlane(nxt[1]);
+      rec2 = queue_fetch(qu, n2idx);
+    }
+    fetched = true;
+  };
+  auto at_tile = [&](int t) {
+    if (t == t_hi - 1) fetch_claimed();
+    if (t == t_lo && (have1 || t < t_hi - 1) && nidx < qu.n) {
+      const Item nx = queue_record(rec1);
+      const int r0 = nx.tile * KI + w * 32;
+      prefetch_rows32(sink, K, r0, nx.lk, nx.kv0, H, nx.h, lane);
+      prefetch_rows32(sink, V, r0, nx.lk, nx.kv0, H, nx.h, lane);
+    }
+  };
   // Two stages, as in the dQ kernel.
   GDPA_LDS float* rt0 = rt;
   GDPA_LDS float* rt1 = rt + (SM ? 2 * QL : 0);
   for (int t = t_hi - 1; t >= t_lo; t -= 2) {
     __builtin_amdgcn_s_waitcnt(0);
+    if (t == t_hi - 1 && tid == 0) {
+      nxt[0] = claim_a;
+      nxt[1] = claim_b;
+    }
     __syncthreads();
     if (t - 1 >= t_lo) issue(sq1, so1, rt1, qt0 + t - 1);
+    at_tile(t);
     {
       const int i0 = (qt0 + t) * QL;
       if (wave_needs(i0)) tile(sq0, so0, rt0, i0);
@@ -784,6 +857,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t - 2 >= t_lo) issue(sq0, so0, rt0, qt0 + t - 2);
+    at_tile(t - 1);
     {
       const int i0 = (qt0 + t - 1) * QL;
       if (wave_needs(i0)) tile(sq1, so1, rt1, i0);
@@ -807,15 +881,29 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     const int first = it.slot - split::chunk_index(it.chunk), n = split::chunk_count(it.chunk);
     if (split::chunk_done(a.split_cnt_k + first, n, (GDPA_LDS int*)&flag_))
       split::combine_dkdv_tile(a, b, it.tile, h, n, first);
-    return;
-  }
-  if (!kvalid) return;
-  __bf16* dkrow = (__bf16*)a.dK + krow * D;
-  __bf16* dvrow = (__bf16*)a.dV + krow * D;
+  } else if (kvalid) {
+    __bf16* dkrow = (__bf16*)a.dK + krow * D;
+    __bf16* dvrow = (__bf16*)a.dV + krow * D;
 #pragma unroll
-  for (int n = 0; n < D / 32; ++n) {
-    store_acc_row_bf16(dkrow, dk[n], n, g, a.scale);
-    store_acc_row_bf16(dvrow, dv[n], n, g, 1.0f);
+    for (int n = 0; n < D / 32; ++n) {
+      store_acc_row_bf16(dkrow, dk[n], n, g, a.scale);
+      store_acc_row_bf16(dvrow, dv[n], n, g, 1.0f);
+    }
+  }
+  if (!fetched) {  // an item without query tiles: publish the claims now
+    if (tid == 0) {
+      nxt[0] = claim_a;
+      nxt[1] = claim_b;
+    }
+    __syncthreads();
+    fetch_claimed();
+  }
+  __syncthreads();  // this item's LDS (stages, rows, bias window, flags) is free again
+  idx = nidx;
+  rec = rec1;
+  have1 = short_item;
+  nidx = n2idx;
+  rec1 = rec2;
   }
 }
 

@@ -54,8 +54,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   const bool wave_active = wrow < Lq;
   const bool qv = iq < Lq;
   const int64_t qrow = (int64_t)(q0 + (qv ? iq : 0)) * H + h;  // O / lse row
-  // Q row: in the sample's rows, or in the one block every sample shares
-  const int64_t qin = a.q_shared ? (int64_t)(qv ? iq : 0) * H + h : qrow;
 
   int nkt = (Lk + BN - 1) / BN;
   if (CAUSAL) nkt = min(nkt, (min(Lq, row_blk + BM) - 1) / BN + 1);
@@ -64,19 +62,29 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   const int kt_first = WIN ? win_first_ktile(row_blk, a.win, BN) : 0;
   const int kt_lo = kt_first + it.lo, kt_hi = min(kt_first + it.hi, nkt);
 
+  // The item's query rows come in as direct-load tiles (whole cache lines per instruction) into
+  // stage 1, idle until the second key tile: rows row_blk .. + 63, then row_blk + 64 .. + 127,
+  // of the sample or of the one block every sample shares.
+  {
+    const __bf16* Q = (const __bf16*)a.Q;
+    const int qbase = a.q_shared ? 0 : q0;
+    issue_tile(sk1, Q, row_blk, Lq, qbase, H, h, w, lane);
+    if (Lq > row_blk + ROWS) issue_tile(sv1, Q, row_blk + ROWS, Lq, qbase, H, h, w, lane);
+  }
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
   if (kt_lo < kt_hi) {
     issue_tile(sk0, K, kt_lo * BN, Lk, kv0, H, h, w, lane);
     issue_tile(sv0, V, kt_lo * BN, Lk, kv0, H, h, w, lane);
   }
-
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __syncthreads();                // ... and everyone else's
+  // wave w's 32 rows: tile w / 2, rows 32 (w % 2) ..; a wave past the item's rows uses zeros
   bf16x8 qop[D / 16];
   {
-    const __bf16* Q = (const __bf16*)a.Q;
+    const GDPA_LDS char* tq = (w >> 1) ? sv1 : sk1;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qop[s] = qv ? *(const bf16x8*)(Q + qin * D + 16 * s + 8 * g) : zero_bf16x8();
+    for (int s = 0; s < D / 16; ++s) qop[s] = wave_active ? row_op(tq, (w & 1) * 32, s, lane) : zero_bf16x8();
   }
   f32x16 o[D / 32];
 #pragma unroll
