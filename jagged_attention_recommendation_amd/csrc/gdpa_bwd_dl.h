@@ -461,9 +461,9 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     if (kt == kt_pf && (have1 || kt > kt_lo) && nidx < qu.n) {
       const Item nx = queue_record(rec1);
       const int r0 = nx.tile * QI + w * 32;
-      prefetch_rows32(sink, Q, r0, nx.lq, a.q_shared ? 0 : nx.q0, H, nx.h, lane);
-      prefetch_rows32(sink, dO, r0, nx.lq, nx.q0, H, nx.h, lane);
-      if (ACT == ACT_SOFTMAX) prefetch_rows32(sink, (const __bf16*)a.O, r0, nx.lq, nx.q0, H, nx.h, lane);
+      prefetch_rows32<D>(sink, Q, r0, nx.lq, a.q_shared ? 0 : nx.q0, H, nx.h, lane);
+      prefetch_rows32<D>(sink, dO, r0, nx.lq, nx.q0, H, nx.h, lane);
+      if (ACT == ACT_SOFTMAX) prefetch_rows32<D>(sink, (const __bf16*)a.O, r0, nx.lq, nx.q0, H, nx.h, lane);
     }
   };
   for (int kt = kt_lo; kt < kt_hi; kt += 2) {
@@ -833,8 +833,8 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     if (t == t_lo && (have1 || t < t_hi - 1) && nidx < qu.n) {
       const Item nx = queue_record(rec1);
       const int r0 = nx.tile * KI + w * 32;
-      prefetch_rows32(sink, K, r0, nx.lk, nx.kv0, H, nx.h, lane);
-      prefetch_rows32(sink, V, r0, nx.lk, nx.kv0, H, nx.h, lane);
+      prefetch_rows32<D>(sink, K, r0, nx.lk, nx.kv0, H, nx.h, lane);
+      prefetch_rows32<D>(sink, V, r0, nx.lk, nx.kv0, H, nx.h, lane);
     }
   };
   // Two stages, as in the dQ kernel.

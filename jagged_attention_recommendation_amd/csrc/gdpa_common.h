@@ -158,6 +158,27 @@ __device__ __forceinline__ int queue_fetch(const ItemQueue& q, int idx) {
   return idx < q.n && lane < 12 ? q.items[(int64_t)idx * 12 + lane] : 0;
 }
 
+// Starts bringing rows r0 .. r0 + 31 of head h of a jagged [rows, H, D] bf16 tensor (sample at
+// row base, L rows) into the caches ahead of the item that will load them: direct loads of 16
+// bytes per lane (whole rows, 64 / (D / 8) rows per instruction) into a 1 KiB LDS area that
+// nothing reads. Rows at or past L lie outside the buffer resource and are not fetched.
+template <int D>
+__device__ __forceinline__ void prefetch_rows32(GDPA_LDS char* sink, const __bf16* src, int r0, int L,
+                                                int base, int H, int h, int lane) {
+  constexpr int RB = 2 * D;     // bytes per row
+  constexpr int LPR = RB / 16;  // lanes per row
+  constexpr int RPI = 64 / LPR; // rows per instruction
+  const int n = min(32, L - r0);
+  if (n <= 0) return;
+  const __bf16* p = src + ((int64_t)(base + r0) * H + h) * D;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, ((n - 1) * H + 1) * RB, 0x00020000);
+#pragma unroll
+  for (int u = 0; u < 32 / RPI; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)sink, 16,
+                                             (RPI * u + lane / LPR) * H * RB + (lane % LPR) * 16, 0, 0, 0);
+}
+
 // The record loaded by queue_fetch, as scalars.
 __device__ __forceinline__ Item queue_record(int v) {
   Item it;

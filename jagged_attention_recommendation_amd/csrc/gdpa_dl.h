@@ -64,22 +64,5 @@ __device__ __forceinline__ void issue_tile(GDPA_LDS char* __restrict__ stage, co
   }
 }
 
-// Starts bringing rows r0 .. r0 + 31 of head h of a jagged [rows, H, 128] tensor (sample at row
-// base, L rows) into the caches ahead of the item that will load them: eight direct loads per
-// wave into a 1 KiB LDS area of the wave that nothing reads. Rows at or past L lie outside the
-// buffer resource and are not fetched.
-__device__ __forceinline__ void prefetch_rows32(GDPA_LDS char* sink, const __bf16* src, int r0, int L,
-                                                int base, int H, int h, int lane) {
-  const int n = min(32, L - r0);
-  if (n <= 0) return;
-  const __bf16* p = src + ((int64_t)(base + r0) * H + h) * D;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, ((n - 1) * H + 1) * ROWB, 0x00020000);
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)sink, 16,
-                                             (4 * u + (lane >> 4)) * H * ROWB + (lane & 15) * 16, 0, 0, 0);
-}
-
 }  // namespace dl
 }  // namespace gdpa
