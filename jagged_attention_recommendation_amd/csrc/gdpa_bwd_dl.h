@@ -146,6 +146,17 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     }
   }
   const float lse_row = ACT == ACT_SOFTMAX && qv ? a.lse[row] : 0.0f;
+  // The bias window (raw diagonals iq - j: iq in [i0, i0 + QI), j in the item's tiles) comes in
+  // the same way, bwin[t] = bias[clamp(w_hi - t)], and is scaled by 1 / scale after the wait.
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  int w_hi = 0, wcnt = 0;
+  if (BIAS && kt_lo < kt_hi) {
+    w_hi = i0 + QI - 1 - kt_lo * KL;
+    wcnt = w_hi - (i0 - (kt_hi * KL - 1)) + 1;
+    if (wcnt > BIAS_WMAX) wcnt = 0;  // too wide to stage: looked up in the table instead
+    issue_window(bwin, bias_h, nb, w_hi, -1, wcnt, w, lane);
+  }
+  const bool win_ok = wcnt > 0;
 
   const int claim_a = have1 ? -1 : queue_claim(qu);       // the next item
   const int claim_b = short_item ? queue_claim(qu) : -1;  // the one after it
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     issue_tile(sk0, K, kt_lo * KL, Lk, kv0, H, h, w, lane);
     issue_tile(sv0, V, kt_lo * KL, Lk, kv0, H, h, w, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row and window loads have landed
   __syncthreads();                // ... and everyone else's
   // wave w's 32 rows: tile w / 2, rows 32 (w % 2) ..; a wave past the item's rows uses zeros
   bf16x8 qop[D / 16], doop[D / 16];
@@ -190,17 +201,8 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
 
   const float sc = ACT == ACT_SOFTMAX ? a.scale * LOG2E : a.scale;
   const float inv_scale = 1.0f / a.scale;
-  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
-  int w_hi = 0;
-  bool win_ok = false;
-  if (BIAS && kt_lo < kt_hi) {  // raw diagonals iq - j: iq in [i0, i0 + QI), j in the item's tiles
-    w_hi = i0 + QI - 1 - kt_lo * KL;
-    const int lo = i0 - (kt_hi * KL - 1);
-    const bool ok = w_hi - lo + 1 <= BIAS_WMAX;
-    if (ok)
-      for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, nb - 1)] * inv_scale;
-    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-  }
+  if (win_ok)  // read at the first key tile, after its barrier
+    for (int t = tid; t < wcnt; t += NT) bwin[t] *= inv_scale;
   GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * 32 * DSP;
   // Bias gradient: diagonal sums of each tile's 32 x 64 dS block. The block is stored skewed:
   // entry (row s, key j) at column j - s + 64 of row s, so a diagonal (fixed j - s) is one column,
@@ -650,10 +652,22 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     issue_tile(so1, K, j0 + ROWS, Lk, kv0, H, h, w, lane);
     issue_tile(vrows + TILE, V, j0 + ROWS, Lk, kv0, H, h, w, lane);
   }
+  // The bias window in natural order (raw diagonals i - jk: i in the item's query tiles, jk in
+  // [j0, j0 + KI)) comes in the same way, bwin[t] = bias[clamp(w_lo + t)], and is scaled by
+  // 1 / scale after the wait: a lane's 16 lookups are then one base address plus constant offsets.
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
+  int w_lo = 0, wcnt = 0;
+  if (BIAS && t_lo < t_hi) {
+    w_lo = (qt0 + t_lo) * QL - (j0 + KI - 1);
+    wcnt = (qt0 + t_hi) * QL - 1 - j0 - w_lo + 1;
+    if (wcnt > BIAS_WMAX) wcnt = 0;  // too wide to stage: looked up in the table instead
+    issue_window(bwin, bias_h, nb, w_lo, 1, wcnt, w, lane);
+  }
+  const bool win_ok = wcnt > 0;
   const int claim_a = have1 ? -1 : queue_claim(qu);       // the next item
   const int claim_b = short_item ? queue_claim(qu) : -1;  // the one after it
   if (t_lo < t_hi) issue(sq0, so0, rt, qt0 + t_hi - 1);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row and window loads have landed
   __syncthreads();                // ... and everyone else's
   // wave w's 32 keys: tile w / 2, rows 32 (w % 2) ..; a wave past the item's keys uses zeros
   bf16x8 kop[D / 16], vop[D / 16];
@@ -675,19 +689,8 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   }
   const float sc = SM ? a.scale * LOG2E : a.scale;
   const float inv_scale = 1.0f / a.scale;
-  const float* bias_h = BIAS ? a.bias + (int64_t)h * nb : nullptr;
-  // bias window in natural order (bwin[t] = bias[clamp(w_lo + t)] / scale): a lane's 16 lookups
-  // are one base address plus constant offsets
-  int w_lo = 0;
-  bool win_ok = false;
-  if (BIAS && t_lo < t_hi) {  // raw diagonals i - jk: i in the item's query tiles, jk in [j0, j0 + KI)
-    w_lo = (qt0 + t_lo) * QL - (j0 + KI - 1);
-    const int w_hi = (qt0 + t_hi) * QL - 1 - j0;
-    const bool ok = w_hi - w_lo + 1 <= BIAS_WMAX;
-    if (ok)
-      for (int t = tid; t <= w_hi - w_lo; t += NT) bwin[t] = bias_h[clampi(w_lo + t, 0, nb - 1)] * inv_scale;
-    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-  }
+  if (win_ok)  // read at the first query tile, after its barrier
+    for (int t = tid; t < wcnt; t += NT) bwin[t] *= inv_scale;
 
   auto tile = [&](const GDPA_LDS char* __restrict__ Qs, const GDPA_LDS char* __restrict__ dOs,
                   const GDPA_LDS float* srt, int i0) {

@@ -64,5 +64,18 @@ __device__ __forceinline__ void issue_tile(GDPA_LDS char* __restrict__ stage, co
   }
 }
 
+// Issues the direct loads that fill win[t] = table[clamp(d0 + dir * t, 0, n - 1)] for t in
+// [0, cnt), raw (the caller scales them after its wait), rounded up to whole waves of 64
+// entries: wave w, lane l fills entry 256 k + 64 w + l with its k-th load. The window buffer
+// must hold cnt rounded up to a multiple of 64.
+__device__ __forceinline__ void issue_window(GDPA_LDS float* win, const float* table, int n, int d0, int dir,
+                                             int cnt, int w, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)table, (short)0, n * 4, 0x00020000);
+  for (int k = 0; 256 * k + 64 * w < cnt; ++k) {
+    const int d = clampi(d0 + dir * (256 * k + 64 * w + lane), 0, n - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)(win + 256 * k + 64 * w), 4, d * 4, 0, 0, 0);
+  }
+}
+
 }  // namespace dl
 }  // namespace gdpa

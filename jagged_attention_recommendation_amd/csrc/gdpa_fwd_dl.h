@@ -71,13 +71,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
     issue_tile(sk1, Q, row_blk, Lq, qbase, H, h, w, lane);
     if (Lq > row_blk + ROWS) issue_tile(sv1, Q, row_blk + ROWS, Lq, qbase, H, h, w, lane);
   }
+  // The bias window (raw diagonals iq - j: iq in the item, j in its key tiles) comes in the same
+  // way, bwin[t] = bias[clamp(w_hi - t)], and is scaled by 1 / scale after the wait.
+  const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
+  int w_hi = 0, wcnt = 0;
+  if (BIAS && kt_lo < kt_hi) {
+    w_hi = row_blk + BM - 1 - kt_lo * BN;
+    wcnt = w_hi - (row_blk - (kt_hi * BN - 1)) + 1;
+    if (wcnt > WMAX) wcnt = 0;  // too wide to stage: looked up in the table instead
+    issue_window(bwin, bias_h, a.nb, w_hi, -1, wcnt, w, lane);
+  }
+  const bool win_ok = wcnt > 0;
   const __bf16* K = (const __bf16*)a.K;
   const __bf16* V = (const __bf16*)a.V;
   if (kt_lo < kt_hi) {
     issue_tile(sk0, K, kt_lo * BN, Lk, kv0, H, h, w, lane);
     issue_tile(sv0, V, kt_lo * BN, Lk, kv0, H, h, w, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's row loads have landed
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's row and window loads have landed
   __syncthreads();                // ... and everyone else's
   // wave w's 32 rows: tile w / 2, rows 32 (w % 2) ..; a wave past the item's rows uses zeros
   bf16x8 qop[D / 16];
@@ -92,17 +103,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_dl_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
   const float sl2 = a.scale * LOG2E;
   const float inv_scale = 1.0f / a.scale;
-  const float* bias_h = BIAS ? a.bias + (int64_t)h * a.nb : nullptr;
-  int w_hi = 0;
-  bool win_ok = false;
-  if (BIAS && kt_lo < kt_hi) {  // raw diagonals iq - j: iq in the item, j in its key tiles
-    w_hi = row_blk + BM - 1 - kt_lo * BN;
-    const int lo = row_blk - (kt_hi * BN - 1);
-    bool ok = w_hi - lo + 1 <= WMAX;
-    if (ok)
-      for (int t = tid; t <= w_hi - lo; t += NT) bwin[t] = bias_h[clampi(w_hi - t, 0, a.nb - 1)] * inv_scale;
-    win_ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-  }
+  if (win_ok)  // read at the first key tile, after its barrier
+    for (int t = tid; t < wcnt; t += NT) bwin[t] *= inv_scale;
 
   // one key tile: scores, probabilities, output update (stage buffers passed in)
   auto tile = [&](const GDPA_LDS char* __restrict__ Ks, const GDPA_LDS char* __restrict__ Vs, int k0) {
