@@ -349,7 +349,10 @@ __global__ __launch_bounds__(NT, 1) void dq_kernel(BwdArgs a) {
 template <int D, int ACT, bool CAUSAL, bool BIAS, bool WIN = false>
 __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   using T = Tile<D>;
+  using WR = WaveRows<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::BYTES + 2 * QL * 4 + (BIAS ? BIAS_WMAX * 4 : 0)];
+  __shared__ __attribute__((aligned(16))) char krows_[4 * WR::BYTES];  // each wave's K rows
+  __shared__ __attribute__((aligned(16))) char vrows_[4 * WR::BYTES];  // ... and V rows
   GDPA_LDS char* Qs = (GDPA_LDS char*)smem;
   GDPA_LDS char* dOs = Qs + T::BYTES;
   GDPA_LDS float* lse_s = (GDPA_LDS float*)(dOs + T::BYTES);
@@ -370,11 +373,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
   const bool wave_active = wkey < Lk;
   const int64_t krow = (int64_t)(kv0 + (kvalid ? jk : 0)) * H + h;
 
-  bf16x8 kop[D / 16], vop[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.K + krow * D + 16 * s + 8 * g) : zero_bf16x8();
-    vop[s] = kvalid ? *(const bf16x8*)((const __bf16*)a.V + krow * D + 16 * s + 8 * g) : zero_bf16x8();
+  // The wave's 32 K and V rows come in by direct loads (whole rows per instruction); they are
+  // read as operands once the wave's loads have landed, below.
+  GDPA_LDS char* kw_rows = (GDPA_LDS char*)krows_ + w * WR::BYTES;
+  GDPA_LDS char* vw_rows = (GDPA_LDS char*)vrows_ + w * WR::BYTES;
+  if (wave_active) {
+    WR::issue(kw_rows, (const __bf16*)a.K, wkey, Lk, kv0, H, h, lane);
+    WR::issue(vw_rows, (const __bf16*)a.V, wkey, Lk, kv0, H, h, lane);
   }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -416,6 +421,13 @@ __global__ __launch_bounds__(NT, D == 64 ? 2 : 3) void dkdv_kernel(BwdArgs a) {
     w_lo = qt0 * QL - (j0 + KI - 1);
     win_ok = __builtin_amdgcn_readfirstlane((int)stage_bias_window(
                  bwin, bias_h, nb, w_lo, nqt * QL - 1 - j0, false, bmul, tid, NT)) != 0;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's K and V rows have landed
+  bf16x8 kop[D / 16], vop[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kop[s] = wave_active ? WR::op(kw_rows, s, lane) : zero_bf16x8();
+    vop[s] = wave_active ? WR::op(vw_rows, s, lane) : zero_bf16x8();
   }
   for (int qt = qt0; qt < nqt && j0 < Lk; ++qt) {
     __syncthreads();

@@ -27,6 +27,41 @@ struct Tile {
   __device__ static __forceinline__ int off(int r, int col) { return prow(r) * P + col * 2; }
 };
 
+// A wave's 32 rows of one head of a jagged [rows, H, D] tensor (D = 32 or 64) in 32 x 2D bytes
+// of LDS, filled by direct loads of 16 bytes per lane (whole rows, 64 / (D / 8) per instruction,
+// no staging registers). Chunk c of row r sits at chunk c ^ sw(r), sw(r) = (r / (128 / 2D)) %
+// (D / 8), so that an operand read (32 rows, one chunk each) spreads over all banks. Rows at or
+// past the sample's end are fetched from the wave's first row: finite values the kernels mask.
+template <int D>
+struct WaveRows {
+  static constexpr int RB = 2 * D;      // bytes per row
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per load instruction
+  static constexpr int BYTES = 32 * RB;
+  __device__ static __forceinline__ int sw(int r) { return (r / (128 / RB)) % CPR; }
+  // rows r0 .. r0 + 31 (r0 < L) of the sample starting at row base
+  __device__ static __forceinline__ void issue(GDPA_LDS char* dst, const __bf16* src, int r0, int L, int base,
+                                               int H, int h, int lane) {
+    const __bf16* p = src + ((int64_t)(base + r0) * H + h) * D;
+    const int n = min(32, L - r0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, ((n - 1) * H + 1) * RB, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+      const int r = RPI * u + lane / CPR;       // the row whose slot this lane fills
+      const int c = (lane % CPR) ^ sw(r);       // the chunk that belongs in it
+      const int rf = r < n ? r : 0;             // the row it is fetched from
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GDPA_LDS void*)(dst + RPI * u * RB), 16, rf * H * RB + c * 16,
+                                               0, 0, 0);
+    }
+  }
+  // MFMA operand whose k runs along D, k-step s: lane reads row l % 32, chunk 2s + l / 32
+  __device__ static __forceinline__ bf16x8 op(const GDPA_LDS char* t, int s, int lane) {
+    const int r = lane & 31, c = 2 * s + (lane >> 5);
+    return *(const GDPA_LDS bf16x8*)(t + r * RB + ((c ^ sw(r)) << 4));
+  }
+};
+
 // Global -> register staging of a 64-row tile of one head of a jagged tensor; rows at or beyond
 // nrows (local) are zero. NT threads cooperate.
 template <int D, int NT>
