@@ -80,11 +80,12 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   GDPA_LDS int* nxt = (GDPA_LDS int*)next_;
 
   // Persistent: the workgroup works through its die's items (see ItemQueue). Each item claims
-  // the next one as it starts, so the next record is at hand before the item ends and the next
-  // item's query rows can be prefetched during its last tile. A short item (one or two key tiles)
-  // also claims the item after the next: its last tile is then too early for the next record,
-  // which the previous item already fetched instead. (Claiming that far ahead on long items would
-  // hold back items that another workgroup of the die could start sooner.)
+  // the next one as it starts, so the next record is at hand before the item ends. A short item
+  // (one or two key tiles) also claims the item after the next, so that the next record is there
+  // a whole item ahead and the next item's query rows can be prefetched during the short item's
+  // last tile. (Claiming that far ahead on long items would hold back items that another
+  // workgroup of the die could start sooner; prefetching at the end of a long item measured
+  // slower, with more traffic, than leaving the next item's rows to its own loads.)
   ItemQueue qu;
   if (!queue_open(a.hdr, a.items_q, 0, qu)) return;
   {
@@ -440,8 +441,8 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   // Two stages, loop unrolled by two so each stage is a distinct LDS object: the direct loads
   // into one stage stay in flight while the other stage is read.
   // At the start of tile kt (after its barrier): on the first tile, the records of the items
-  // claimed by this one are fetched; on the last, the next item's query rows are prefetched if its
-  // record is there (no later tile wait of this item then covers those loads).
+  // claimed by this one are fetched; on the last tile of a short item, the next item's query rows
+  // are prefetched if its record is there (no later tile wait of this item covers those loads).
   GDPA_LDS char* sink = (GDPA_LDS char*)sink_ + w * 1024;
   const int kt_pf = kt_hi - 1;
   auto fetch_claimed = [&]() {
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       fetch_claimed();
       if (BIAS) clear_dsbuf();
     }
-    if (kt == kt_pf && (have1 || kt > kt_lo) && nidx < qu.n) {
+    if (short_item && kt == kt_pf && (have1 || kt > kt_lo) && nidx < qu.n) {
       const Item nx = queue_record(rec1);
       const int r0 = nx.tile * QI + w * 32;
       prefetch_rows32<D>(sink, Q, r0, nx.lq, a.q_shared ? 0 : nx.q0, H, nx.h, lane);
@@ -817,8 +818,8 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
     return wave_active && !(CAUSAL && i0 + QL - 1 < wkey) && !(WIN && i0 > min(wkey + 31, Lk - 1) + a.win - 1);
   };
   // At the start of query tile t (after its barrier): on the first, the records of the items
-  // claimed by this one are fetched; on the last, the next item's key rows are prefetched if its
-  // record is there.
+  // claimed by this one are fetched; on the last tile of a short item, the next item's key rows
+  // are prefetched if its record is there.
   GDPA_LDS char* sink = (GDPA_LDS char*)sink_ + w * 1024;
   auto fetch_claimed = [&]() {
     if (!have1) {
@@ -833,7 +834,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_dl_kernel(BwdArgs a) {
   };
   auto at_tile = [&](int t) {
     if (t == t_hi - 1) fetch_claimed();
-    if (t == t_lo && (have1 || t < t_hi - 1) && nidx < qu.n) {
+    if (short_item && t == t_lo && (have1 || t < t_hi - 1) && nidx < qu.n) {
       const Item nx = queue_record(rec1);
       const int r0 = nx.tile * KI + w * 32;
       prefetch_rows32<D>(sink, K, r0, nx.lk, nx.kv0, H, nx.h, lane);
