@@ -449,37 +449,49 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(BlockArgs a) {
   }
 
   // ---- lane = key jk; registers of query half qb are queries qb*32 + 8(r/4) + 4g + r%4
-  __syncthreads();  // waves 0-1 have written the row terms
+  // The score and dP products need no row terms: they run while waves 0-1 form them, and only
+  // the gradient arithmetic waits for the barrier.
   const int kw = w - 2;
   const int jk = kw * 32 + l32;
-  if (kw * 32 >= n) return;
-  bf16x8 kop[D / 16], klo[D / 16], vop[D / 16];
+  const bool kact = kw * 32 < n;
+  auto half_on = [&](int qb) { return qb * 32 < n && !(CAUSAL && qb * 32 + 31 < kw * 32); };
+  f32x16 sacc2[2], dpacc2[2];
+  if (kact) {
+    bf16x8 kop[D / 16], klo[D / 16], vop[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kop[s] = row_op(sk, kw * 32, s, lane);
-    if (ROPE) klo[s] = row_op(skl, kw * 32, s, lane);
-    vop[s] = row_op(sv, kw * 32, s, lane);
+    for (int s = 0; s < D / 16; ++s) {
+      kop[s] = row_op(sk, kw * 32, s, lane);
+      if (ROPE) klo[s] = row_op(skl, kw * 32, s, lane);
+      vop[s] = row_op(sv, kw * 32, s, lane);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sacc2[qb] = f32x16{};
+      dpacc2[qb] = f32x16{};
+      if (!half_on(qb)) continue;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sacc2[qb] = mfma32(row_op(sq, qb * 32, s, lane), kop[s], sacc2[qb]);
+        if (ROPE) {
+          sacc2[qb] = mfma32(row_op(sql, qb * 32, s, lane), kop[s], sacc2[qb]);
+          sacc2[qb] = mfma32(row_op(sq, qb * 32, s, lane), klo[s], sacc2[qb]);
+        }
+        dpacc2[qb] = mfma32(row_op(so, qb * 32, s, lane), vop[s], dpacc2[qb]);
+      }
+    }
   }
+  __syncthreads();  // waves 0-1 have written the row terms
+  if (!kact) return;
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int nn = 0; nn < D / 32; ++nn) {
     dk[nn] = f32x16{};
     dv[nn] = f32x16{};
   }
-#pragma unroll 1
-  for (int qb = 0; qb < 2; ++qb) {
-    if (qb * 32 >= n) break;
-    if (CAUSAL && qb * 32 + 31 < kw * 32) continue;  // every query of the half precedes the keys
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sacc = mfma32(row_op(sq, qb * 32, s, lane), kop[s], sacc);
-      if (ROPE) {
-        sacc = mfma32(row_op(sql, qb * 32, s, lane), kop[s], sacc);
-        sacc = mfma32(row_op(sq, qb * 32, s, lane), klo[s], sacc);
-      }
-      dpacc = mfma32(row_op(so, qb * 32, s, lane), vop[s], dpacc);
-    }
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!half_on(qb)) continue;
+    const f32x16 sacc = sacc2[qb], dpacc = dpacc2[qb];
     const int ib = qb * 32 + 4 * g;  // query of register r: ib + 8(r/4) + r%4
     float pv[16], dsv[16];
 #pragma unroll
