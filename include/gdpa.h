@@ -121,7 +121,11 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
 
 /* Backward of sum(dO * O). Writes dQ, dK, dV (same layouts and element type as Q, K, V) and,
  * when p->bias_buckets > 0, dbias ([H, NB] fp32). Softmax needs O and the forward's lse; GDPA
- * ignores them (they may be NULL). Results are bitwise reproducible run to run. */
+ * ignores them (they may be NULL). Results are bitwise reproducible run to run. For bf16 with a
+ * bias table or a shared query block, the reductions that follow dQ run on a second stream of the
+ * library's (one per device and calling thread, default priority, created on first use and kept)
+ * that waits on `stream` after dQ and that `stream` waits on before the call's last kernel
+ * completes: to the caller all work stays ordered on `stream`, including under graph capture. */
 int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
                  const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
                  const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,

@@ -250,6 +250,32 @@ ProfState g_prof;
 thread_local int t_prof_slot[PROF_KERNELS] = {-1, -1, -1, -1, -1, -1};
 static_assert(PROF_KERNELS == 6, "t_prof_slot initialiser");
 
+// A second stream (default priority, non-blocking) and two events per device and host thread,
+// created on first use and kept until the thread ends: the backward runs the bias-gradient
+// reduction on it beside the dK/dV kernel (fork after dQ, join before returning). Per thread, so
+// that concurrent callers never share an event between its record and its wait. Null if any of
+// them cannot be created; the caller then stays on its own stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+thread_local SideStream t_side[64];
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = t_side[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      ss.s = nullptr;
+  }
+  return ss.s != nullptr ? &ss : nullptr;
+}
+
 int32_t map_hip(hipError_t e) {
   if (e == hipSuccess) return GDPA_OK;
   if (e == hipErrorNotSupported) return GDPA_ENOTSUP;
@@ -403,6 +429,20 @@ int32_t gdpa_fwd_static(const gdpa_problem* p, const void* Q, const void* K, con
                   GDPA_STATIC_SCRATCH_BYTES, stream);
 }
 
+// The bias-gradient reduction of a backward call (both stages) on stream s.
+static hipError_t launch_dbias(const gdpa_problem* p, const Prob& pr, const BwdArgs& ba, const SchedArgs& sq,
+                               const int32_t* q_offsets, const int32_t* kv_offsets, float* dbias, char* ws,
+                               const BwdLayout& L, int tq, hipStream_t s) {
+  DbiasArgs da;
+  da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
+  da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
+  da.part = ba.dbias_part; da.part_rows = ba.part_rows; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
+  da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
+  da.causal = p->causal; da.win = pr.win; da.tile_rows = tq;
+  da.loop_rows = bwd_k_loop(p->dtype);
+  return launch_dbias_reduce(da, s);
+}
+
 int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
                  const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
                  const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
@@ -462,28 +502,40 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   ba.H = p->H; ba.nb = p->bias_buckets; ba.scale = p->scale; ba.win = pr.win;
   ba.q_shared = p->q_shared;
   ba.dq_f32 = p->q_shared ? (float*)(ws + L.dq_f32) : nullptr;
+  // The reductions that follow dQ (the shared seed block's dQ over samples, the bias gradient)
+  // read only what dQ wrote, so for bf16 they run on a side stream beside dK/dV: their small
+  // workgroups fit next to dK/dV's one per compute unit.
+  auto reductions = [&](hipStream_t rs) -> hipError_t {
+    hipError_t r = hipSuccess;
+    if (p->q_shared) {
+      DqSharedArgs qa;
+      qa.q_off = q_offsets; qa.part = ba.dq_f32; qa.dQ = dQ; qa.hdr = ws + L.header;
+      qa.B = p->B; qa.H = p->H; qa.D = p->D; qa.q_rows = pr.q_rows;
+      qa.f32_out = p->dtype == GDPA_F32 ? 1 : 0;
+      r = launch_dq_shared_reduce(qa, rs);
+      if (r != hipSuccess) return r;
+    }
+    if (p->bias_buckets > 0) r = launch_dbias(p, pr, ba, sq, q_offsets, kv_offsets, dbias, ws, L, tq, rs);
+    return r;
+  };
+  if (p->dtype != GDPA_F32 && (p->bias_buckets > 0 || p->q_shared)) {
+    e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, 0, s);
+    if (e != hipSuccess) return map_hip(e);
+    SideStream* side = side_stream();
+    if (side != nullptr && (hipEventRecord(side->fork, s) != hipSuccess ||
+                            hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess))
+      return GDPA_EHIP;
+    e = reductions(side != nullptr ? side->s : s);
+    if (e != hipSuccess) return map_hip(e);
+    if (side != nullptr && hipEventRecord(side->join, side->s) != hipSuccess) return GDPA_EHIP;
+    e = launch_bwd_bf16(pr, ba, 0, (int)L.max_k_items, s);
+    if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return GDPA_EHIP;
+    return map_hip(e);
+  }
   if (p->dtype == GDPA_F32) e = launch_bwd_f32(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   if (e != hipSuccess) return map_hip(e);
-  if (p->q_shared) {
-    DqSharedArgs qa;
-    qa.q_off = q_offsets; qa.part = ba.dq_f32; qa.dQ = dQ; qa.hdr = ws + L.header;
-    qa.B = p->B; qa.H = p->H; qa.D = p->D; qa.q_rows = pr.q_rows;
-    qa.f32_out = p->dtype == GDPA_F32 ? 1 : 0;
-    e = launch_dq_shared_reduce(qa, s);
-    if (e != hipSuccess) return map_hip(e);
-  }
-  if (p->bias_buckets > 0) {
-    DbiasArgs da;
-    da.q_off = q_offsets; da.kv_off = kv_offsets; da.tile_base = ba.tile_base;
-    da.split_slot = sq.split_slot; da.part_x = ba.dbias_part_x;
-    da.part = ba.dbias_part; da.part_rows = ba.part_rows; da.part_bh = (float*)(ws + L.part_bh); da.dbias = dbias;
-    da.hdr = ws + L.header; da.B = p->B; da.H = p->H; da.nb = p->bias_buckets;
-    da.causal = p->causal; da.win = pr.win; da.tile_rows = tq;
-    da.loop_rows = bwd_k_loop(p->dtype);
-    e = launch_dbias_reduce(da, s);
-  }
-  return map_hip(e);
+  return map_hip(reductions(s));
 }
 
 int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
