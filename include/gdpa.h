@@ -224,8 +224,12 @@ int32_t gdpa_read_device_error(const void* workspace, void* stream, int32_t* err
  * and 15..22 (list 1) hold each die's item count c_x. Die x takes indices 8q + x for
  * q < t_x = floor(n / 8) + (x < n mod 8 ? 1 : 0); a die with c_x > t_x passes its last items,
  * in order, to the dies with c_x < t_x (dies in increasing order, each from q = c_x on), so
- * the list of n items is dense. The tiles are those of the page named above, JFA paragraph: short sequences
- * must not idle the GPU, so the list balances and splits work by cost. */
+ * the list of n items is dense. The D = 128 bf16 dQ and dK/dV kernels consume their list with one
+ * workgroup per compute unit: workgroup i takes die (i mod 8)'s items in order of q by counting
+ * on that die's claim counter, header words 23..30 (list 0) and 31..38 (list 1), which the
+ * scheduler clears (after a call they hold counts past t_x; they are not item counts). The tiles
+ * are those of the page named above, JFA paragraph: short sequences must not idle the GPU, so the
+ * list balances and splits work by cost. */
 int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,
                        int64_t* capacity);
 
