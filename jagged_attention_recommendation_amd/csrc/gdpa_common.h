@@ -152,10 +152,15 @@ __device__ __forceinline__ int queue_steal(ItemQueue& q, GDPA_LDS int* slot) {
   }
 }
 
-// Lane l < 12 of the calling wave loads word l of item idx (nothing past the list's end).
+// Lane l < 12 of the calling wave loads word l of item idx. It is always a load: an index past
+// the list reads item 0 (a kernel runs only on a list with room for at least one), a record that
+// is never used. A register that is only ever loaded into needs no wait before its next load;
+// writing a constant into it instead made the compiler wait for every memory operation in
+// flight, the next tile's loads included, at the first tile of every item.
 __device__ __forceinline__ int queue_fetch(const ItemQueue& q, int idx) {
   const int lane = threadIdx.x & 63;
-  return idx < q.n && lane < 12 ? q.items[(int64_t)idx * 12 + lane] : 0;
+  const int i = idx < q.n ? idx : 0;
+  return q.items[(int64_t)i * 12 + (lane < 12 ? lane : 11)];
 }
 
 // Starts bringing rows r0 .. r0 + 31 of head h of a jagged [rows, H, D] bf16 tensor (sample at
