@@ -189,9 +189,11 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) 
     int n = 0;
     __syncthreads();
     if (base == 0 && tid == 0) {
+      // four independent loads (one round trip, not four in a row while every thread waits)
+      const int q_first = a.q_off[0], q_last = a.q_off[B], k_first = a.kv_off[0], k_last = a.kv_off[B];
       int e = 0;
-      if (a.q_off[0] != 0 || (int64_t)a.q_off[B] != a.total_q) e |= 1;
-      if (a.kv_off[0] != 0 || (int64_t)a.kv_off[B] != a.total_kv) e |= 2;
+      if (q_first != 0 || (int64_t)q_last != a.total_q) e |= 1;
+      if (k_first != 0 || (int64_t)k_last != a.total_kv) e |= 2;
       if (e != 0) atomicOr(&err, e);
     }
     if (b < B) {
