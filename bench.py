@@ -2,7 +2,9 @@
 """Benchmark of the jagged-attention hot path on one MI355X.
 
 One step = one forward + backward pass (work scheduler, forward kernel, backward dQ and dK/dV
-kernels, bias-gradient reduction) over the causal JFA softmax workload: B=64 samples, lengths
+kernels, bias-gradient reduction) as a training step makes it: gdpa_fwd_plan_bwd, whose scheduler
+launch builds the forward's and the backward's work lists, then gdpa_bwd_planned. It runs over
+the causal JFA softmax workload: B=64 samples, lengths
 uniform in [1, 2048] (token sparsity ~0.5 against the longest length), H=4 heads, D=128, bf16
 inputs with fp32 accumulation, a learned per-head relative-position bias table of 4096 entries
 indexed by clamp(i-j). Inputs are seeded synthetic data, resident in HBM before timing starts.
@@ -12,7 +14,7 @@ Metric: useful (unpadded) TFLOPS of forward + backward, i.e. matrix-product flop
 step time. Prints one JSON line on stdout:
   - value / ms_per_step: K steps back to back, timed by the host clock between two device
     synchronisations (inputs resident, caches warm from the previous step);
-  - cold: each gdpa_fwd and gdpa_bwd call timed alone with device events after a 512 MiB write
+  - cold: each (unplanned) gdpa_fwd and gdpa_bwd call timed alone with device events after a 512 MiB write
     that evicts the 256 MB last-level cache and the L2s; medians (and minima) over the reps;
   - warm_per_call: the same per-call medians without the eviction;
   - roofline: the dominant kernel's algorithmic flops (or bytes) per launch over its average
@@ -228,15 +230,18 @@ def run_bf16(args, config, torch, gdpa, inputs, workload, dev, flush, window=0, 
     kw = dict(act=p.act, causal=p.causal, scale=p.scale, bias=bias, max_q=max_q, max_kv=max_kv,
               window=window, q_shared=shared)
 
-    def fwd():
-        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, **kw)
+    def fwd(plan=None):
+        gdpa.fwd(Q, K, V, q_off, kv_off, out=O, lse=lse, workspace=ws_f, plan_bwd=plan, **kw)
 
-    def bwd():
-        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads, **kw)
+    def bwd(planned=False):
+        gdpa.bwd(Q, K, V, O, dO, lse, q_off, kv_off, workspace=ws_b, grads=grads,
+                 planned=planned, **kw)
 
     def step():
-        fwd()
-        bwd()
+        # a training step: the forward's scheduler launch also builds the backward's work lists
+        # (gdpa_fwd_plan_bwd), which the backward then consumes (gdpa_bwd_planned)
+        fwd(ws_b)
+        bwd(True)
 
     for _ in range(args.warmup):
         step()

@@ -131,6 +131,30 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
                  const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
                  float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward of a training step that also schedules its backward (a step runs the forward and then
+ * the backward on the same offsets; the scheduler, page "GEM Training: How Meta Doubled the
+ * Efficiency of Its LLM-Scale Ads Foundation Model", JFA and GDPA paragraphs, is the same one).
+ * Arguments and results as gdpa_fwd (bf16 and fp32 only: GDPA_ENOTSUP for GDPA_MXFP8_E4M3),
+ * plus the backward's workspace (16-byte aligned, at least gdpa_workspace_size(p, 1, ...) bytes,
+ * else GDPA_EINVAL / GDPA_EWORKSPACE): the forward's scheduler launch also builds the backward's
+ * two work-item lists there, in workgroups of their own beside the forward's list, so that
+ * gdpa_bwd_planned on that workspace needs no scheduler launch. Malformed offsets set the device
+ * error word of both workspaces. */
+int32_t gdpa_fwd_plan_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                          void* O, float* lse, void* workspace, size_t workspace_bytes,
+                          void* bwd_workspace, size_t bwd_workspace_bytes, void* stream);
+
+/* Backward on a workspace whose work-item lists gdpa_fwd_plan_bwd wrote. Arguments and results
+ * as gdpa_bwd; the call must use the same problem *p and the same offsets (contents unchanged),
+ * and be ordered after that gdpa_fwd_plan_bwd with no other call on the workspace in between:
+ * one planned backward per plan (its kernels use up the lists' claim counters). None of this is
+ * checked: lists planned for other offsets give unspecified results. */
+int32_t gdpa_bwd_planned(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                         const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                         float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Forward for callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation. Same arguments and results as gdpa_fwd minus
  * the workspace. The scratch space gdpa_fwd takes from its workspace (work-item list, chunk

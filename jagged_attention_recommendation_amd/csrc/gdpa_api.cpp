@@ -268,9 +268,11 @@ SideStream* side_stream() {
   SideStream& ss = t_side[dev];
   if (!ss.tried) {
     ss.tried = true;
+    // fork / join order work between two streams of one device: a device-scope release is enough
+    const unsigned ef = hipEventDisableTiming | hipEventDisableSystemFence;
     if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&ss.fork, ef) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, ef) != hipSuccess)
       ss.s = nullptr;
   }
   return ss.s != nullptr ? &ss : nullptr;
@@ -308,7 +310,10 @@ int32_t gdpa_profile_start(int32_t mask) {
   if (!g_prof.created) {
     for (int k = 0; k < PROF_KERNELS; ++k)
       for (int i = 0; i < 2 * PROF_MAX; ++i)
-        if (hipEventCreate(&g_prof.ev[k][i]) != hipSuccess) return GDPA_EHIP;
+        // timing only: no system-scope fence (no cache writeback and invalidation around the
+        // timed kernels, which would slow them and the work after them)
+        if (hipEventCreateWithFlags(&g_prof.ev[k][i], hipEventDisableSystemFence) != hipSuccess)
+          return GDPA_EHIP;
     g_prof.created = true;
   }
   for (int k = 0; k < PROF_KERNELS; ++k) g_prof.n[k].store(0, std::memory_order_relaxed);
@@ -360,10 +365,41 @@ int32_t gdpa_workspace_size(const gdpa_problem* p, int32_t for_bwd, size_t* byte
   return GDPA_OK;
 }
 
-int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
-                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
-                 const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias, void* O,
-                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+// The backward's two scheduler lists in workspace ws (layout L): query-tile items (dQ, D, bias
+// partials) and key-tile items (dK, dV).
+static void bwd_sched_args(const gdpa_problem* p, const Prob& pr, const BwdLayout& L, char* ws,
+                           const int32_t* q_offsets, const int32_t* kv_offsets, SchedArgs& sq,
+                           SchedArgs& sk) {
+  const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
+  SchedArgs sa;
+  sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
+  sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
+  sa.win = pr.win; sa.q_rows = pr.q_rows; sa.ws_header = ws + L.header;
+  sa.nslot = split_nslot(pr);
+  sq = sa;
+  sk = sa;
+  sq.split = L.split_q ? 1 : 0;
+  sk.split = L.split_k ? 1 : 0;
+  sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
+  sq.max_items = (int)L.max_q_items; sq.list = 0;
+  sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
+  sq.split_cnt = (int32_t*)(ws + L.split_cnt_q);
+  sq.split_slot = L.split_q && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
+  sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
+  sk.max_items = (int)L.max_k_items; sk.list = 1;
+  sk.tile_base = nullptr; sk.items = ws + L.items_k;
+  sk.split_cnt = (int32_t*)(ws + L.split_cnt_k);
+  sk.split_slot = nullptr;
+  set_sched_scratch(sq, ws + L.sched_q, p->B);
+  set_sched_scratch(sk, ws + L.sched_k, p->B);
+}
+
+// gdpa_fwd, and with bwd_ws also the backward's item lists (gdpa_fwd_plan_bwd).
+static int32_t fwd_impl(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                        const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias, void* O,
+                        float* lse, void* workspace, size_t workspace_bytes, void* bwd_ws,
+                        size_t bwd_ws_bytes, void* stream) {
   int32_t st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (!q_offsets || !kv_offsets || !workspace) return GDPA_EINVAL;
@@ -398,7 +434,19 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   sa.ws_header = ws + L.header; sa.items = ws + L.items;
   sa.split_cnt = (int32_t*)(ws + L.split_cnt);
   set_sched_scratch(sa, ws + L.sched, p->B);
-  hipError_t e = launch_sched(sa, s);
+  hipError_t e;
+  if (bwd_ws != nullptr) {
+    // the backward's lists in workgroups of their own, beside the forward's
+    if (!aligned16(bwd_ws)) return GDPA_EINVAL;
+    const BwdLayout LB = bwd_layout(p);
+    if (bwd_ws_bytes < LB.total) return GDPA_EWORKSPACE;
+    if (LB.max_q_items > INT32_MAX || LB.max_k_items > INT32_MAX) return GDPA_ENOTSUP;
+    SchedArgs sq, sk;
+    bwd_sched_args(p, pr, LB, (char*)bwd_ws, q_offsets, kv_offsets, sq, sk);
+    e = launch_sched3(sa, sq, sk, s);
+  } else {
+    e = launch_sched(sa, s);
+  }
   if (e != hipSuccess) return map_hip(e);
 
   FwdArgs fa;
@@ -413,6 +461,26 @@ int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void
   else if (p->dtype == GDPA_BF16) e = launch_fwd_bf16(pr, fa, grid, s);
   else e = launch_fwd_mx(pr, fa, grid, s);
   return map_hip(e);
+}
+
+int32_t gdpa_fwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const uint8_t* q_scale, const uint8_t* k_scale, const uint8_t* v_scale,
+                 const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias, void* O,
+                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(p, Q, K, V, q_scale, k_scale, v_scale, q_offsets, kv_offsets, bias, O, lse,
+                  workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+int32_t gdpa_fwd_plan_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                          void* O, float* lse, void* workspace, size_t workspace_bytes,
+                          void* bwd_workspace, size_t bwd_workspace_bytes, void* stream) {
+  const int32_t st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
+  if (!bwd_workspace) return GDPA_EINVAL;
+  return fwd_impl(p, Q, K, V, nullptr, nullptr, nullptr, q_offsets, kv_offsets, bias, O, lse,
+                  workspace, workspace_bytes, bwd_workspace, bwd_workspace_bytes, stream);
 }
 
 int32_t gdpa_fwd_static(const gdpa_problem* p, const void* Q, const void* K, const void* V,
@@ -443,10 +511,12 @@ static hipError_t launch_dbias(const gdpa_problem* p, const Prob& pr, const BwdA
   return launch_dbias_reduce(da, s);
 }
 
-int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
-                 const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
-                 const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
-                 float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+// gdpa_bwd, or with planned the same on lists a gdpa_fwd_plan_bwd wrote (gdpa_bwd_planned).
+static int32_t bwd_impl(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                        const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                        const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                        float* dbias, void* workspace, size_t workspace_bytes, bool planned,
+                        void* stream) {
   int32_t st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (p->dtype == GDPA_MXFP8_E4M3) return GDPA_ENOTSUP;
@@ -460,31 +530,16 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const Prob pr = to_prob(p);
-  const int tq = bwd_q_item(p->dtype), tk = bwd_k_item(p->dtype);
+  const int tq = bwd_q_item(p->dtype);
 
-  SchedArgs sa;
-  sa.q_off = q_offsets; sa.kv_off = kv_offsets; sa.B = p->B; sa.H = p->H;
-  sa.total_q = p->total_q; sa.total_kv = p->total_kv; sa.causal = p->causal;
-  sa.win = pr.win; sa.q_rows = pr.q_rows; sa.ws_header = ws + L.header;
-  // query-tile items (dQ, D, bias partials) and key-tile items (dK, dV), built in one launch
-  sa.nslot = split_nslot(pr);
-  SchedArgs sq = sa, sk = sa;
-  sq.split = L.split_q ? 1 : 0;
-  sk.split = L.split_k ? 1 : 0;
-  sq.mode = SCHED_QTILES; sq.tile_item = tq; sq.tile_loop = bwd_k_loop(p->dtype);
-  sq.max_items = (int)L.max_q_items; sq.list = 0;
-  sq.tile_base = (int32_t*)(ws + L.tile_base); sq.items = ws + L.items_q;
-  sq.split_cnt = (int32_t*)(ws + L.split_cnt_q);
-  sq.split_slot = L.split_q && p->bias_buckets > 0 ? (int32_t*)(ws + L.split_slot) : nullptr;
-  sk.mode = SCHED_KTILES; sk.tile_item = tk; sk.tile_loop = bwd_q_loop(p->dtype);
-  sk.max_items = (int)L.max_k_items; sk.list = 1;
-  sk.tile_base = nullptr; sk.items = ws + L.items_k;
-  sk.split_cnt = (int32_t*)(ws + L.split_cnt_k);
-  sk.split_slot = nullptr;
-  set_sched_scratch(sq, ws + L.sched_q, p->B);
-  set_sched_scratch(sk, ws + L.sched_k, p->B);
-  hipError_t e = launch_sched2(sq, sk, s);
-  if (e != hipSuccess) return map_hip(e);
+  // query-tile and key-tile items, built in one launch (or already by gdpa_fwd_plan_bwd)
+  SchedArgs sq, sk;
+  bwd_sched_args(p, pr, L, ws, q_offsets, kv_offsets, sq, sk);
+  hipError_t e = hipSuccess;
+  if (!planned) {
+    e = launch_sched2(sq, sk, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
 
   BwdArgs ba;
   ba.Q = Q; ba.K = K; ba.V = V; ba.O = O; ba.dO = dO; ba.lse = lse;
@@ -536,6 +591,22 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
   else e = launch_bwd_bf16(pr, ba, (int)L.max_q_items, (int)L.max_k_items, s);
   if (e != hipSuccess) return map_hip(e);
   return map_hip(reductions(s));
+}
+
+int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                 const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                 float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, Q, K, V, O, dO, lse, q_offsets, kv_offsets, bias, dQ, dK, dV, dbias,
+                  workspace, workspace_bytes, false, stream);
+}
+
+int32_t gdpa_bwd_planned(const gdpa_problem* p, const void* Q, const void* K, const void* V,
+                         const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,
+                         float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, Q, K, V, O, dO, lse, q_offsets, kv_offsets, bias, dQ, dK, dV, dbias,
+                  workspace, workspace_bytes, true, stream);
 }
 
 int32_t gdpa_item_list(const gdpa_problem* p, int32_t for_bwd, int32_t list, size_t* offset,

@@ -76,6 +76,8 @@ hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 // current device: at most cap workgroups (the list's capacity), a multiple of the 8 dies.
 int persistent_grid(int cap, int per_cu);
 hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s);
+// Three lists in one launch (a training forward's list and its backward's two).
+hipError_t launch_sched3(const SchedArgs& a, const SchedArgs& b, const SchedArgs& c, hipStream_t s);
 
 // Bias gradient reduction. The dQ kernels write, per (32-query row block, head), the diagonal
 // sums of dS its queries produced (one row of NB floats, canonical row order); the reduction sums

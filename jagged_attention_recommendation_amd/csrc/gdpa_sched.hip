@@ -135,11 +135,17 @@ __device__ __forceinline__ void block_scan(int* buf, int* wsum, int tid) {
   __syncthreads();
 }
 
+// One list per workgroup: workgroup i builds lists.l[i] (indexed in the kernel-argument segment;
+// choosing among separate arguments made the compiler copy them to scratch memory).
+struct SchedLists {
+  SchedArgs l[3];
+};
+
 // SMALL: the batch fits one chunk of samples and its groups fit the LDS placement table, so every
 // per-sample and per-group value lives in LDS; otherwise they go through the workspace scratch.
 template <bool SMALL>
-__global__ __launch_bounds__(SNT) void sched_kernel(SchedArgs a0, SchedArgs a1) {
-  const SchedArgs& a = blockIdx.x == 0 ? a0 : a1;
+__global__ __launch_bounds__(SNT) void sched_kernel(SchedLists lists) {
+  const SchedArgs& a = lists.l[blockIdx.x];
   __shared__ int cnt[SNT];   // inclusive scan of the chunk's per-sample tile counts
   __shared__ int sbuf[SNT];  // scan of chunk counts per tile
   __shared__ int wsum[SNT / 64];
@@ -495,24 +501,29 @@ int persistent_grid(int cap, int per_cu) {
 
 bool sched_small(const SchedArgs& a) { return a.B <= SNT && (int64_t)a.B * a.H <= GCAP; }
 
-hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
+// One workgroup per list (lists share the batch, so they all fit the LDS tables or none does).
+static hipError_t launch_lists(int n, const SchedArgs& a, const SchedArgs& b, const SchedArgs& c, hipStream_t s) {
   prof_before(PROF_SCHED, s);
+  SchedLists lists;
+  lists.l[0] = a;
+  lists.l[1] = b;
+  lists.l[2] = c;
   if (sched_small(a))
-    hipLaunchKernelGGL(sched_kernel<true>, dim3(1), dim3(SNT), 0, s, a, a);
+    hipLaunchKernelGGL(sched_kernel<true>, dim3(n), dim3(SNT), 0, s, lists);
   else
-    hipLaunchKernelGGL(sched_kernel<false>, dim3(1), dim3(SNT), 0, s, a, a);
+    hipLaunchKernelGGL(sched_kernel<false>, dim3(n), dim3(SNT), 0, s, lists);
   prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }
 
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s) { return launch_lists(1, a, a, a, s); }
+
 hipError_t launch_sched2(const SchedArgs& a, const SchedArgs& b, hipStream_t s) {
-  prof_before(PROF_SCHED, s);
-  if (sched_small(a) && sched_small(b))
-    hipLaunchKernelGGL(sched_kernel<true>, dim3(2), dim3(SNT), 0, s, a, b);
-  else
-    hipLaunchKernelGGL(sched_kernel<false>, dim3(2), dim3(SNT), 0, s, a, b);
-  prof_after(PROF_SCHED, s);
-  return hipGetLastError();
+  return launch_lists(2, a, b, b, s);
+}
+
+hipError_t launch_sched3(const SchedArgs& a, const SchedArgs& b, const SchedArgs& c, hipStream_t s) {
+  return launch_lists(3, a, b, c, s);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -20,7 +20,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_EINVAL", 2: "GDPA_ENOTSUP", 3: "GDPA_EWORKSPACE
 
 # Every symbol include/gdpa.h declares.
 EXPORTS = ["gdpa_abi_version", "gdpa_status_string", "gdpa_workspace_size", "gdpa_fwd",
-           "gdpa_fwd_static", "gdpa_bwd", "gdpa_bwd_mx", "gdpa_block_workspace_size", "gdpa_block_fwd",
+           "gdpa_fwd_static", "gdpa_fwd_plan_bwd", "gdpa_bwd", "gdpa_bwd_planned", "gdpa_bwd_mx", "gdpa_block_workspace_size", "gdpa_block_fwd",
            "gdpa_block_bwd",
            "gdpa_read_device_error", "gdpa_item_list", "gdpa_profile_start", "gdpa_profile_read",
            "gdpa_profile_stop"]
@@ -86,6 +86,10 @@ def load():
     lib.gdpa_block_bwd.argtypes = [BP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd.restype = ctypes.c_int32
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_bwd_planned.restype = ctypes.c_int32
+    lib.gdpa_bwd_planned.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd_plan_bwd.restype = ctypes.c_int32
+    lib.gdpa_fwd_plan_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.gdpa_read_device_error.restype = ctypes.c_int32
     lib.gdpa_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.gdpa_item_list.restype = ctypes.c_int32
@@ -148,12 +152,15 @@ def _workspace(nbytes, device):
 
 def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None, bias=None,
         q_scale=None, k_scale=None, v_scale=None, max_q=0, max_kv=0, out=None, lse=None,
-        workspace=None, stream=None, return_lse=True, window=0, q_shared=False, total_q=None):
+        workspace=None, stream=None, return_lse=True, window=0, q_shared=False, total_q=None,
+        plan_bwd=None):
     """Forward over jagged tensors q [total_q, H, D], k/v [total_kv, H, D].
 
     bf16 / fp32 tensors, or uint8 e4m3 codes with uint8 e8m0 scales [rows, H, D/32] (MX).
     q_shared: q is one block [max_q, H, D] that every sample reads (local query i = row i); the
     output row count total_q (= q_offsets[-1]) then comes from `total_q` or `out`.
+    plan_bwd: the backward's workspace (bf16 / fp32): the forward also builds the backward's work
+    lists there (gdpa_fwd_plan_bwd), for one bwd(..., workspace=plan_bwd, planned=True).
     Returns (O, lse); lse is None for GDPA activations.
     """
     lib = load()
@@ -180,6 +187,14 @@ def fwd(q, k, v, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=No
         lse = None
     if workspace is None:
         workspace = _workspace(workspace_size(prob, False), q.device)
+    if plan_bwd is not None:
+        st = lib.gdpa_fwd_plan_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets),
+                                   _ptr(kv_offsets), _ptr(bias), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), workspace.numel(), _ptr(plan_bwd),
+                                   plan_bwd.numel(), _stream(stream))
+        if st != 0:
+            raise GdpaError(st, "gdpa_fwd_plan_bwd")
+        return out, lse
     st = lib.gdpa_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale),
                       _ptr(k_scale), _ptr(v_scale), _ptr(q_offsets), _ptr(kv_offsets),
                       _ptr(bias), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -215,14 +230,19 @@ def fwd_static(q, k, v, q_offsets, kv_offsets, out, lse=None, *, act="softmax", 
 
 def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=False, scale=None,
         bias=None, max_q=0, max_kv=0, workspace=None, stream=None, grads=None, window=0,
-        q_shared=False, q_scale=None, k_scale=None, v_scale=None):
+        q_shared=False, q_scale=None, k_scale=None, v_scale=None, planned=False):
     """Backward of sum(do * O). Returns (dQ, dK, dV, dbias or None).
+
+    planned: `workspace` holds the work lists a fwd(..., plan_bwd=workspace) on the same problem
+    and offsets built (gdpa_bwd_planned: no scheduler launch here).
 
     q_shared: q (and so dQ) is one block [max_q, H, D] read by every sample; dQ is the sum of
     the samples' gradients. total_q is then do's row count.
     MX-fp8 inputs (uint8 codes with q_scale/k_scale/v_scale) go to gdpa_bwd_mx; the gradients
     are bf16.
     """
+    if planned and workspace is None:
+        raise ValueError("planned needs the workspace the forward planned")
     lib = load()
     total_q, H, D = q.shape
     if q_shared:
@@ -251,12 +271,14 @@ def bwd(q, k, v, o, do, lse, q_offsets, kv_offsets, *, act="softmax", causal=Fal
         if st != 0:
             raise GdpaError(st, "gdpa_bwd_mx")
         return dq, dk, dv, dbias
-    st = lib.gdpa_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
-                      _ptr(lse), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq),
-                      _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel(),
-                      _stream(stream))
+    if planned and workspace is None:
+        raise ValueError("planned needs the workspace the forward planned")
+    fn = lib.gdpa_bwd_planned if planned else lib.gdpa_bwd
+    st = fn(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+            _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(dbias), _ptr(workspace), workspace.numel(), _stream(stream))
     if st != 0:
-        raise GdpaError(st, "gdpa_bwd")
+        raise GdpaError(st, "gdpa_bwd_planned" if planned else "gdpa_bwd")
     return dq, dk, dv, dbias
 
 

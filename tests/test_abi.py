@@ -122,6 +122,30 @@ def test_fwd_rejects_host_checkable_errors_without_launching():
     assert st == 1
 
 
+def test_fwd_plan_bwd_rejects_host_checkable_errors_without_launching():
+    lib = gdpa.load()
+    p = gdpa.problem(2, 1, 32, 10, 10)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    big = 1 << 30
+    args = lambda bws, bbytes, ws_bytes=big: (ctypes.byref(p), fake, fake, fake, fake, fake, None,
+                                              fake, fake, fake, ws_bytes, bws, bbytes, None)
+    assert lib.gdpa_fwd_plan_bwd(*args(None, big)) == 1                     # no backward workspace
+    assert lib.gdpa_fwd_plan_bwd(*args(ctypes.c_void_p(0x1008), big)) == 1  # misaligned
+    assert lib.gdpa_fwd_plan_bwd(*args(fake, 16)) == 3                      # too small
+    assert lib.gdpa_fwd_plan_bwd(*args(fake, big, 16)) == 3                 # forward's too small
+    pm = gdpa.problem(2, 1, 128, 10, 10, dtype="mxfp8")
+    st = lib.gdpa_fwd_plan_bwd(ctypes.byref(pm), fake, fake, fake, fake, fake, None, fake, fake,
+                               fake, big, fake, big, None)
+    assert st == 2  # MX problems have no planned backward
+    # the planned backward validates like gdpa_bwd: null offsets, workspace too small
+    st = lib.gdpa_bwd_planned(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None,
+                              None, fake, fake, fake, None, fake, big, None)
+    assert st == 1
+    st = lib.gdpa_bwd_planned(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                              None, fake, fake, fake, None, fake, 16, None)
+    assert st == 3
+
+
 def test_block_problem_validation():
     """Block-aligned attention: the struct matches the header's layout (48 bytes), and argument
     errors are reported without any launch."""
