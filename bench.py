@@ -52,8 +52,10 @@ HBM_BOUND = (3, 4)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 warm-up steps (~70 ms on the JFA workload): the GPU's clocks are still rising during the
+    # first tens of milliseconds of work, and timed steps taken then run ~10 % slower
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
                     help="workload of the headline line (default: the causal JFA workload)")
     ap.add_argument("--reps", type=int, default=20, help="per-call reps for the medians")

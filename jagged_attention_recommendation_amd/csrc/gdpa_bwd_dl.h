@@ -31,7 +31,11 @@ constexpr int KL = BWD_K_LOOP;  // keys per tile in the dQ loop
 constexpr int KI = BWD_K_ITEM;  // keys per dK/dV item
 constexpr int QL = BWD_Q_LOOP;  // queries per tile in the dK/dV loop
 static_assert(QI == 128 && KI == 128 && KL == ROWS && QL == ROWS, "kernels assume these tiles");
-constexpr int DSP = 128;        // floats per row of a wave's skewed dS buffer
+// A wave's skewed dS buffer: 128 columns of 32 rows, column-major with DSC floats per column
+// (a multiple of 4 so that a column is read 16 bytes at a time, and 36 so that the 16 lanes of
+// such a read start on distinct 4-bank groups).
+constexpr int DSC = 36;
+constexpr int DS_WAVE = 128 * DSC;
 
 template <bool B>
 struct BoolC {
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char sv1_[TILE];
   __shared__ __attribute__((aligned(16))) float bwin_[BIAS ? BIAS_WMAX : 1];
   // bias-gradient buffer; at the start of an item, also where its dO and O rows land
-  __shared__ __attribute__((aligned(16))) float dsbuf_[4 * 32 * DSP];
+  __shared__ __attribute__((aligned(16))) float dsbuf_[4 * DS_WAVE];
   __shared__ __attribute__((aligned(16))) char sink_[4 * 1024];  // prefetch loads land here
   __shared__ int flag_, next_[2];
   GDPA_LDS char* sk0 = (GDPA_LDS char*)sk0_;
@@ -204,22 +208,24 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
   const float inv_scale = 1.0f / a.scale;
   if (win_ok)  // read at the first key tile, after its barrier
     for (int t = tid; t < wcnt; t += NT) bwin[t] *= inv_scale;
-  GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * 32 * DSP;
+  GDPA_LDS float* dsbuf = (GDPA_LDS float*)dsbuf_ + w * DS_WAVE;
   // Bias gradient: diagonal sums of each tile's 32 x 64 dS block. The block is stored skewed:
-  // entry (row s, key j) at column j - s + 64 of row s, so a diagonal (fixed j - s) is one column,
-  // and the columns a tile does not write stay zero. Lane t reads column 127 - t (diagonal
-  // t - 63: rows 0..t, zeros below) and column 63 - t (diagonal t + 1: rows t + 1..31, zeros
-  // above); for t >= 31 the first is the full diagonal t - 63 and the second is all zeros. Each
-  // row read is one ds_read2st64 (the two columns are 64 floats apart), every lane reads its own
-  // column (no bank conflicts), and the two sums need no selects. A tile's sums are taken during
-  // the next tile's score products (or after the loop), so the reads overlap matrix work and the
-  // partial-row store is not waited for at once.
-  const GDPA_LDS float* dsrd = dsbuf + (63 - lane);
-  GDPA_LDS float* dswr = dsbuf + l32 * (DSP - 1) + 64 + 4 * g;  // row l32, key 4g at column 4g - l32 + 64
+  // entry (row s, key j) in column j - s + 64, so a diagonal (fixed j - s) is one column, and the
+  // columns a tile does not write stay zero. Lane t reads column 127 - t (diagonal t - 63: rows
+  // 0..t, zeros below) and column 63 - t (diagonal t + 1: rows t + 1..31, zeros above); for
+  // t >= 31 the first is the full diagonal t - 63 and the second is all zeros. Columns are
+  // contiguous, so each lane reads its two columns with 8 + 8 16-byte loads, and the two sums
+  // need no selects. A tile's sums are taken during the next tile's score products (or after the
+  // loop), so the reads overlap matrix work and the partial-row store is not waited for at once.
+  const GDPA_LDS float* cola = dsbuf + (127 - lane) * DSC;
+  const GDPA_LDS float* colb = dsbuf + (63 - lane) * DSC;
+  // row l32, key 4g in column 4g - l32 + 64; key 4g + o is o columns further
+  GDPA_LDS float* dswr = dsbuf + (64 + 4 * g) * DSC - (DSC - 1) * l32;
   // (cleared at the first key tile, once every wave has read its rows from the buffer)
   auto clear_dsbuf = [&]() {  // each store covers 1 KiB of the buffer: 64 lanes on distinct banks
 #pragma unroll
-    for (int u = 0; u < 16; ++u) *(GDPA_LDS f32x4*)(dsbuf + 256 * u + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < DS_WAVE / 256; ++u)
+      *(GDPA_LDS f32x4*)(dsbuf + 256 * u + 4 * lane) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   };
   float carry = 0.0f;  // lanes t < 31: partial sum of diagonal t - 63 of the previous tile
   // partial row of this row block: canonical, or the chunk's slot row for a split tile
@@ -264,18 +270,18 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     emit(dabs, v, pend);
   };
   auto col_sums = [&](float& s_a, float& s_b) {
-    float va[32], vb[32];
+    f32x4 va[8], vb[8];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      va[e] = dsrd[e * DSP + 64];
-      vb[e] = dsrd[e * DSP];
+    for (int k = 0; k < 8; ++k) {
+      va[k] = *(const GDPA_LDS f32x4*)(cola + 4 * k);
+      vb[k] = *(const GDPA_LDS f32x4*)(colb + 4 * k);
     }
     s_a = 0.0f;
     s_b = 0.0f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      s_a += va[e];
-      s_b += vb[e];
+      s_a += va[e >> 2][e & 3];
+      s_b += vb[e >> 2][e & 3];
     }
   };
   int k0_last = -1;
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     }
     bf16x8 kt0[D / 32], kt1[D / 32], ku0[D / 32], ku1[D / 32];
     f32x2 sab = {0.0f, 0.0f};  // the two column sums advance together
-    float va[32], vb[32];
+    f32x4 va[8], vb[8];
     __builtin_amdgcn_sched_barrier(0);
     // A: per pair of products, the operands two steps ahead, the column reads of four rows, one
     // transposed operand, and the sums of the rows read two steps earlier
@@ -350,14 +356,11 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       sacc0 = mfma32(kr[s], qop[s], sacc0);
       dpacc0 = mfma32(vr[s], doop[s], dpacc0);
       if (BIAS) {
-#pragma unroll
-        for (int e = 4 * s; e < 4 * s + 4; ++e) {
-          va[e] = dsrd[e * DSP + 64];
-          vb[e] = dsrd[e * DSP];
-        }
+        va[s] = *(const GDPA_LDS f32x4*)(cola + 4 * s);
+        vb[s] = *(const GDPA_LDS f32x4*)(colb + 4 * s);
         if (s >= 2) {
 #pragma unroll
-          for (int e = 4 * s - 8; e < 4 * s - 4; ++e) sab += f32x2{va[e], vb[e]};
+          for (int e = 0; e < 4; ++e) sab += f32x2{va[s - 2][e], vb[s - 2][e]};
         }
       }
       if (s & 1) kt1[s >> 1] = tr_op(Ks, 16, s >> 1, lane);
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     }
     if (BIAS) {
 #pragma unroll
-      for (int e = 24; e < 32; ++e) sab += f32x2{va[e], vb[e]};
+      for (int e = 24; e < 32; ++e) sab += f32x2{va[e >> 2][e & 3], vb[e >> 2][e & 3]};
       finish(kp, sab[0], sab[1], kp >= 0);
     }
     seed(sacc1, k0, 1);  // (read here rather than with the first seed: measured faster)
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dswr[(r >> 2) * 8 + (r & 3)] = ds0[r];
+      for (int r = 0; r < 16; ++r) dswr[((r >> 2) * 8 + (r & 3)) * DSC] = ds0[r];
     }
     const bf16x8 d00 = pack8(&ds0[0]), d01 = pack8(&ds0[8]);
     __builtin_amdgcn_sched_barrier(0);
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(NT, 1) void dq_dl_kernel(BwdArgs a) {
     }
     if (BIAS) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dswr[32 + (r >> 2) * 8 + (r & 3)] = ds1[r];
+      for (int r = 0; r < 16; ++r) dswr[(32 + (r >> 2) * 8 + (r & 3)) * DSC] = ds1[r];
     }
     const bf16x8 d10 = pack8(&ds1[0]), d11 = pack8(&ds1[8]);
     __builtin_amdgcn_sched_barrier(0);
