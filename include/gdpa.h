@@ -148,8 +148,11 @@ int32_t gdpa_fwd_plan_bwd(const gdpa_problem* p, const void* Q, const void* K, c
 /* Backward on a workspace whose work-item lists gdpa_fwd_plan_bwd wrote. Arguments and results
  * as gdpa_bwd; the call must use the same problem *p and the same offsets (contents unchanged),
  * and be ordered after that gdpa_fwd_plan_bwd with no other call on the workspace in between:
- * one planned backward per plan (its kernels use up the lists' claim counters). None of this is
- * checked: lists planned for other offsets give unspecified results. */
+ * one planned backward per plan (its kernels use up the lists' claim counters). The library
+ * keeps, per workspace and device, a record of the last plan (problem fields and offset
+ * pointers; gdpa_bwd on the workspace drops it): without a matching record the call returns
+ * GDPA_EINVAL and enqueues nothing, and a matching record is used up. The offsets' contents are
+ * not checked: lists planned for other offset values give unspecified results. */
 int32_t gdpa_bwd_planned(const gdpa_problem* p, const void* Q, const void* K, const void* V,
                          const void* O, const void* dO, const float* lse, const int32_t* q_offsets,
                          const int32_t* kv_offsets, const float* bias, void* dQ, void* dK, void* dV,

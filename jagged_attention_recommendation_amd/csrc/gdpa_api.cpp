@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "gdpa.h"
 #include "gdpa_common.h"
@@ -365,6 +366,57 @@ int32_t gdpa_workspace_size(const gdpa_problem* p, int32_t for_bwd, size_t* byte
   return GDPA_OK;
 }
 
+// ---- plans. gdpa_fwd_plan_bwd records, per backward workspace and device, the problem and the
+// offset pointers it scheduled; gdpa_bwd_planned runs only on a workspace whose record matches
+// its own arguments, and uses the record up; gdpa_bwd (which rebuilds the lists) forgets it.
+struct PlanRec {
+  const void* ws;
+  int dev;
+  gdpa_problem p;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+};
+std::mutex g_plan_mu;
+std::vector<PlanRec> g_plans;
+
+bool same_problem(const gdpa_problem& a, const gdpa_problem& b) {
+  return a.B == b.B && a.H == b.H && a.D == b.D && a.dtype == b.dtype && a.total_q == b.total_q &&
+         a.total_kv == b.total_kv && a.max_q == b.max_q && a.max_kv == b.max_kv && a.act == b.act &&
+         a.causal == b.causal && a.scale == b.scale && a.bias_buckets == b.bias_buckets &&
+         a.window == b.window && a.q_shared == b.q_shared;
+}
+
+int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+void plan_record(const void* ws, const gdpa_problem* p, const int32_t* q_off, const int32_t* kv_off) {
+  const PlanRec rec{ws, current_device(), *p, q_off, kv_off};
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  for (PlanRec& r : g_plans)
+    if (r.ws == ws && r.dev == rec.dev) {
+      r = rec;
+      return;
+    }
+  if (g_plans.size() >= 4096) g_plans.erase(g_plans.begin());  // bounded: the oldest goes
+  g_plans.push_back(rec);
+}
+
+// Removes the record of ws on this device; true if it matched the given problem and offsets.
+bool plan_take(const void* ws, const gdpa_problem* p, const int32_t* q_off, const int32_t* kv_off) {
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  for (size_t i = 0; i < g_plans.size(); ++i) {
+    const PlanRec& r = g_plans[i];
+    if (r.ws != ws || r.dev != dev) continue;
+    const bool ok = same_problem(r.p, *p) && r.q_off == q_off && r.kv_off == kv_off;
+    g_plans.erase(g_plans.begin() + i);
+    return ok;
+  }
+  return false;
+}
+
 // The backward's two scheduler lists in workspace ws (layout L): query-tile items (dQ, D, bias
 // partials) and key-tile items (dK, dV).
 static void bwd_sched_args(const gdpa_problem* p, const Prob& pr, const BwdLayout& L, char* ws,
@@ -444,6 +496,7 @@ static int32_t fwd_impl(const gdpa_problem* p, const void* Q, const void* K, con
     SchedArgs sq, sk;
     bwd_sched_args(p, pr, LB, (char*)bwd_ws, q_offsets, kv_offsets, sq, sk);
     e = launch_sched3(sa, sq, sk, s);
+    if (e == hipSuccess) plan_record(bwd_ws, p, q_offsets, kv_offsets);
   } else {
     e = launch_sched(sa, s);
   }
@@ -532,11 +585,14 @@ static int32_t bwd_impl(const gdpa_problem* p, const void* Q, const void* K, con
   const Prob pr = to_prob(p);
   const int tq = bwd_q_item(p->dtype);
 
-  // query-tile and key-tile items, built in one launch (or already by gdpa_fwd_plan_bwd)
+  // query-tile and key-tile items, built in one launch (or already by gdpa_fwd_plan_bwd: then
+  // only on the workspace it planned, for the same problem and offsets, once)
+  if (planned && !plan_take(workspace, p, q_offsets, kv_offsets)) return GDPA_EINVAL;
   SchedArgs sq, sk;
   bwd_sched_args(p, pr, L, ws, q_offsets, kv_offsets, sq, sk);
   hipError_t e = hipSuccess;
   if (!planned) {
+    plan_take(workspace, p, q_offsets, kv_offsets);  // the lists are rebuilt: any plan is gone
     e = launch_sched2(sq, sk, s);
     if (e != hipSuccess) return map_hip(e);
   }

@@ -144,6 +144,10 @@ def test_fwd_plan_bwd_rejects_host_checkable_errors_without_launching():
     st = lib.gdpa_bwd_planned(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
                               None, fake, fake, fake, None, fake, 16, None)
     assert st == 3
+    # valid arguments on a workspace that no gdpa_fwd_plan_bwd planned: refused before any launch
+    st = lib.gdpa_bwd_planned(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                              None, fake, fake, fake, None, fake, big, None)
+    assert st == 1
 
 
 def test_block_problem_validation():

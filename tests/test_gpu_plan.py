@@ -132,3 +132,38 @@ def test_malformed_offsets_reach_both_workspaces():
              planned=True, **kw)
     assert gdpa.read_device_error(wf) & 1
     assert gdpa.read_device_error(wb) & 1
+
+
+def test_planned_backward_needs_its_plan():
+    """gdpa_bwd_planned runs only on the workspace the last gdpa_fwd_plan_bwd planned, for the same
+    problem and offsets, once; otherwise it raises GDPA_EINVAL and enqueues nothing."""
+    from jagged_attention_recommendation_amd import gdpa
+    p = ragged(413, 128, "softmax", True, 16)
+    d = to_device(p)
+    prob = gdpa.problem(p.B, p.H, p.D, int(p.q_off[-1]), int(p.kv_off[-1]), act=p.act,
+                        causal=True, scale=p.scale, bias_buckets=16)
+    wf = torch.empty(gdpa.workspace_size(prob, False), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(gdpa.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    kw = dict(act=p.act, causal=True, scale=p.scale, bias=d["bias"])
+    args = lambda q_off: (d["Q"], d["K"], d["V"], O, d["dO"], lse, q_off, d["kv_off"])
+
+    def einval(fn):
+        with pytest.raises(gdpa.GdpaError) as e:
+            fn()
+        assert e.value.status == 1
+
+    O, lse = gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, **kw)
+    einval(lambda: gdpa.bwd(*args(d["q_off"]), workspace=wb, planned=True, **kw))  # never planned
+    gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, plan_bwd=wb, **kw)
+    einval(lambda: gdpa.bwd(*args(d["q_off"].clone()), workspace=wb, planned=True, **kw))
+    # the mismatch used the record up: plan again, then one planned backward succeeds
+    gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, plan_bwd=wb, **kw)
+    good = [t.clone() for t in gdpa.bwd(*args(d["q_off"]), workspace=wb, planned=True, **kw)]
+    einval(lambda: gdpa.bwd(*args(d["q_off"]), workspace=wb, planned=True, **kw))  # used up
+    # an unplanned backward on the workspace drops a pending plan
+    gdpa.fwd(d["Q"], d["K"], d["V"], d["q_off"], d["kv_off"], workspace=wf, plan_bwd=wb, **kw)
+    plain = gdpa.bwd(*args(d["q_off"]), workspace=wb, **kw)
+    einval(lambda: gdpa.bwd(*args(d["q_off"]), workspace=wb, planned=True, **kw))
+    torch.cuda.synchronize()
+    for x, y in zip(good, plain):
+        assert torch.equal(x, y)
