@@ -136,7 +136,7 @@ int32_t gdpa_bwd(const gdpa_problem* p, const void* Q, const void* K, const void
  * Efficiency of Its LLM-Scale Ads Foundation Model", JFA and GDPA paragraphs, is the same one).
  * Arguments and results as gdpa_fwd (bf16 and fp32 only: GDPA_ENOTSUP for GDPA_MXFP8_E4M3),
  * plus the backward's workspace (16-byte aligned, at least gdpa_workspace_size(p, 1, ...) bytes,
- * else GDPA_EINVAL / GDPA_EWORKSPACE): the forward's scheduler launch also builds the backward's
+ * not overlapping the forward's, else GDPA_EINVAL / GDPA_EWORKSPACE): the forward's scheduler launch also builds the backward's
  * two work-item lists there, in workgroups of their own beside the forward's list, so that
  * gdpa_bwd_planned on that workspace needs no scheduler launch. Malformed offsets set the device
  * error word of both workspaces. */

@@ -492,6 +492,8 @@ static int32_t fwd_impl(const gdpa_problem* p, const void* Q, const void* K, con
     if (!aligned16(bwd_ws)) return GDPA_EINVAL;
     const BwdLayout LB = bwd_layout(p);
     if (bwd_ws_bytes < LB.total) return GDPA_EWORKSPACE;
+    const uintptr_t f0 = (uintptr_t)workspace, b0 = (uintptr_t)bwd_ws;
+    if (f0 < b0 + LB.total && b0 < f0 + L.total) return GDPA_EINVAL;  // the two must not overlap
     if (LB.max_q_items > INT32_MAX || LB.max_k_items > INT32_MAX) return GDPA_ENOTSUP;
     SchedArgs sq, sk;
     bwd_sched_args(p, pr, LB, (char*)bwd_ws, q_offsets, kv_offsets, sq, sk);

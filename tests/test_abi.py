@@ -133,6 +133,7 @@ def test_fwd_plan_bwd_rejects_host_checkable_errors_without_launching():
     assert lib.gdpa_fwd_plan_bwd(*args(ctypes.c_void_p(0x1008), big)) == 1  # misaligned
     assert lib.gdpa_fwd_plan_bwd(*args(fake, 16)) == 3                      # too small
     assert lib.gdpa_fwd_plan_bwd(*args(fake, big, 16)) == 3                 # forward's too small
+    assert lib.gdpa_fwd_plan_bwd(*args(fake, big)) == 1                     # same workspace twice
     pm = gdpa.problem(2, 1, 128, 10, 10, dtype="mxfp8")
     st = lib.gdpa_fwd_plan_bwd(ctypes.byref(pm), fake, fake, fake, fake, fake, None, fake, fake,
                                fake, big, fake, big, None)
