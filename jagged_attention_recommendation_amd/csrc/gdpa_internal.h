@@ -45,13 +45,16 @@ struct SchedArgs {
   int list;                  // 0: first list of the header, 1: second list
   int split;                 // 1: split long tiles into chunks
   int nslot;                 // concurrent workgroups the chunk length aims at (see above)
+  int defer;                 // set by the launch: a list without split tiles has its items
+                             // written by a second, many-workgroup launch
   int32_t* tile_base;        // optional [B + 1]: canonical index of each sample's first tile
   int32_t* split_slot;       // optional [canonical tiles * H]: first slot of a split tile, or -1
   int32_t* split_cnt;        // [2 * nslot] chunk counters, indexed by a split tile's first slot
   void* ws_header;
   void* items;
   // per-sample and per-group values of batches larger than one scheduler workgroup holds in LDS
-  // (sched_scratch_bytes; unused otherwise)
+  // (sched_scratch_bytes); for a deferred list, what the item-writing launch reads: each sample's
+  // item count, rank and inclusive tile end (scratch_at), and each group's first position
   unsigned long long* scratch_cost;  // [B]
   int32_t* scratch_nch;              // [B]
   int32_t* scratch_rank;             // [B]

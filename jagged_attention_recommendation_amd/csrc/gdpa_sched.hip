@@ -25,7 +25,9 @@
 // in one launch). Samples are walked in chunks of 1024, a scan of their tile counts gives each
 // tile a canonical index, and threads then take tiles (not samples) so long samples do not
 // serialise. Per-sample values live in LDS when the batch fits one chunk, else in workspace
-// scratch.
+// scratch. A long list whose tiles all fit one item is written by a second launch of one thread
+// per tile over many workgroups, from the ranks and positions the list's workgroup leaves in the
+// workspace.
 #include <atomic>
 
 #include "gdpa_common.h"
@@ -85,6 +87,33 @@ __device__ __forceinline__ int cost_bucket(unsigned long long c) {
 __device__ __forceinline__ int group_xcd(int r) {
   const int s = r & 15;
   return s < XCDS ? s : 2 * XCDS - 1 - s;
+}
+
+// List index of die x's q-th item. The dies' own counts are xtot; tgt[x] = indices below the list
+// length n that are x mod 8; a die with more items than that passes its surplus on, spre and dpre
+// being the prefix sums of surplus and shortfall over the dies (dpre[8] = total shortfall).
+__device__ __forceinline__ int list_position(const int* xtot, const int* tgt, const int* spre,
+                                             const int* dpre, int x, int q) {
+  if (q < tgt[x]) return XCDS * q + x;
+  const int k = spre[x] + (q - tgt[x]);  // surplus item k fills the k-th missing index
+  int y = 0;
+  while (y < XCDS - 1 && k >= dpre[y + 1]) ++y;
+  return XCDS * (xtot[y] + k - dpre[y]) + y;
+}
+
+// tgt, spre and dpre of list_position from the dies' own counts (one thread).
+__device__ __forceinline__ void die_tables(const int* xtot, int* tgt, int* spre, int* dpre) {
+  int n = 0;
+  for (int x = 0; x < XCDS; ++x) n += xtot[x];
+  int sp = 0, dp = 0;
+  for (int x = 0; x < XCDS; ++x) {
+    tgt[x] = n / XCDS + (x < n % XCDS ? 1 : 0);  // indices x, x + 8, ... below n
+    spre[x] = sp;
+    dpre[x] = dp;
+    sp += max(0, xtot[x] - tgt[x]);
+    dp += max(0, tgt[x] - xtot[x]);
+  }
+  dpre[XCDS] = dp;
 }
 
 // Inclusive scan over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4 and 8 within
@@ -365,103 +394,101 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedLists lists) {
   }
   __syncthreads();
   if (tid == 0) {
-    int n = 0;
-    for (int x = 0; x < XCDS; ++x) n += xtot[x];
-    int sp = 0, dp = 0;
-    for (int x = 0; x < XCDS; ++x) {
-      tgt[x] = n / XCDS + (x < n % XCDS ? 1 : 0);  // indices x, x + 8, ... below n
-      spre[x] = sp;
-      dpre[x] = dp;
-      sp += max(0, xtot[x] - tgt[x]);
-      dp += max(0, tgt[x] - xtot[x]);
-    }
-    dpre[XCDS] = dp;
+    die_tables(xtot, tgt, spre, dpre);
     split_count = 0;
     slot_count = 0;
     carry = 0;
   }
   __syncthreads();
-  // list index of die x's q-th item
-  auto position = [&](int x, int q) {
-    if (q < tgt[x]) return XCDS * q + x;
-    const int k = spre[x] + (q - tgt[x]);  // surplus item k fills the k-th missing index
-    int y = 0;
-    while (y < XCDS - 1 && k >= dpre[y + 1]) ++y;
-    return XCDS * (xtot[y] + k - dpre[y]) + y;
-  };
-  // 4. scatter the items (b, tile, h, canonical tile index, inner range, slot, chunk); a split
-  //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared.
-  //    Within a sample, chunks are numbered in tile order (sbuf scan); a group lists its
-  //    costliest tiles first: the last query tiles (causal), or the first key tiles. Tiles are
-  //    numbered in batches of SNT; the batch's items are then written one (tile, head) pair per
-  //    thread.
-  for (int base = 0; base < B; base += SNT) {
-    const int total = SMALL ? cnt[SNT - 1] : load_chunk(base);  // one chunk: still loaded
-    const int ns = min(SNT, B - base);
-    const int first = carry;
-    if (a.tile_base != nullptr && tid < ns) a.tile_base[base + tid] = first + (tid > 0 ? cnt[tid - 1] : 0);
-    int run = 0;  // chunks of the chunk's earlier tiles
-    for (int u0 = 0; u0 < total; u0 += SNT) {
-      const int u = u0 + tid;
-      int bl = 0, t = 0, c = 0, n = 0;
-      if (u < total) {
-        locate(u, ns, bl, t);
-        c = cost_of(bl, t);
-        n = chunks(c);
-      }
-      int ci = t;  // chunk number of the tile's first chunk within its sample
-      if (T != 0x7fffffff) {
-        __syncthreads();
-        sbuf[tid] = n;
-        block_scan(sbuf, wsum, tid);
-        const int e = run + sbuf[tid] - n;  // first chunk of this tile
-        if (u < total && t == 0) first_e[bl] = e;
-        __syncthreads();
-        run += sbuf[SNT - 1];
-        ci = e - first_e[bl];
-      }
-      int sbase = -1;
-      if (u < total && n > 1) {
-        sbase = atomicAdd(&slot_count, n * H);
-        atomicAdd(&split_count, H);
-        if (sbase + n * H > 2 * a.nslot) {
-          atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
-          sbase = -1;
-        } else {
-          for (int h = 0; h < H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
-        }
-      }
-      if (u < total && a.split_slot != nullptr)
-        for (int h = 0; h < H; ++h) a.split_slot[(int64_t)(first + u) * H + h] = sbase < 0 ? -1 : sbase + h * n;
-      __syncthreads();  // the previous batch's items are out
-      bt_bl[tid] = bl; bt_t[tid] = t; bt_c[tid] = c; bt_n[tid] = n; bt_ci[tid] = ci; bt_sb[tid] = sbase;
-      __syncthreads();
-      // items of the batch, one (tile, head) pair per thread at a time
-      const int nt_b = min(SNT, total - u0);
-      for (int pr = tid; pr < nt_b * H; pr += SNT) {
-        const int j = pr / H, h = pr - j * H;
-        const int bj = bt_bl[j], tj = bt_t[j], cj = bt_c[j], nj = bt_n[j], cij = bt_ci[j], sbj = bt_sb[j];
-        const int b = base + bj;
-        const int nb = SMALL ? cnch[bj] : nch_of(b);
-        const int r = rank_of(b) * H + h;
-        const int x = group_xcd(r), g0 = gpre_of(r);
-        Item it;
-        it.b = b; it.tile = tj; it.h = h; it.aux = first + u0 + j;
-        it.q0 = q0_c[bj]; it.lq = lq_c[bj]; it.kv0 = kv0_c[bj]; it.lk = lk_c[bj];
-        for (int k = 0; k < nj; ++k) {
-          it.lo = nj == 1 ? 0 : k * T;
-          it.hi = nj == 1 ? cj : min(cj, (k + 1) * T);
-          it.slot = sbj < 0 ? -1 : sbj + h * nj + k;
-          it.chunk = sbj < 0 ? 0 : k | (nj << 16);
-          const int w = qmode ? nb - 1 - (cij + k) : cij + k;
-          const int pos = position(x, g0 + w);
-          if (pos >= 0 && pos < a.max_items) items[pos] = it;
-        }
-      }
+  auto position = [&](int x, int q) { return list_position(xtot, tgt, spre, dpre, x, q); };
+  if (SMALL && a.defer && T == 0x7fffffff) {
+    // 4'. no split tile: sched_items_kernel writes the items from these tables (in LDS here)
+    const int total = cnt[SNT - 1];
+    if (tid < B) {
+      a.scratch_at[tid] = cnt[tid];
+      a.scratch_rank[tid] = s_rank[tid];
+      a.scratch_nch[tid] = cnch[tid];
+      if (a.tile_base != nullptr) a.tile_base[tid] = tid > 0 ? cnt[tid - 1] : 0;
     }
-    __syncthreads();
-    if (tid == 0) carry = first + total;
-    __syncthreads();
+    for (int r = tid; r < G; r += SNT) a.scratch_gpre[r] = s_gpre[r];
+    if (a.split_slot != nullptr)
+      for (int i = tid; i < total * H; i += SNT) a.split_slot[i] = -1;
+    if (tid == 0) carry = total;
+  } else {
+    // 4. scatter the items (b, tile, h, canonical tile index, inner range, slot, chunk); a split
+    //    tile takes n consecutive slots per head, and its counter (at the first slot) is cleared.
+    //    Within a sample, chunks are numbered in tile order (sbuf scan); a group lists its
+    //    costliest tiles first: the last query tiles (causal), or the first key tiles. Tiles are
+    //    numbered in batches of SNT; the batch's items are then written one (tile, head) pair per
+    //    thread.
+    for (int base = 0; base < B; base += SNT) {
+      const int total = SMALL ? cnt[SNT - 1] : load_chunk(base);  // one chunk: still loaded
+      const int ns = min(SNT, B - base);
+      const int first = carry;
+      if (a.tile_base != nullptr && tid < ns) a.tile_base[base + tid] = first + (tid > 0 ? cnt[tid - 1] : 0);
+      int run = 0;  // chunks of the chunk's earlier tiles
+      for (int u0 = 0; u0 < total; u0 += SNT) {
+        const int u = u0 + tid;
+        int bl = 0, t = 0, c = 0, n = 0;
+        if (u < total) {
+          locate(u, ns, bl, t);
+          c = cost_of(bl, t);
+          n = chunks(c);
+        }
+        int ci = t;  // chunk number of the tile's first chunk within its sample
+        if (T != 0x7fffffff) {
+          __syncthreads();
+          sbuf[tid] = n;
+          block_scan(sbuf, wsum, tid);
+          const int e = run + sbuf[tid] - n;  // first chunk of this tile
+          if (u < total && t == 0) first_e[bl] = e;
+          __syncthreads();
+          run += sbuf[SNT - 1];
+          ci = e - first_e[bl];
+        }
+        int sbase = -1;
+        if (u < total && n > 1) {
+          sbase = atomicAdd(&slot_count, n * H);
+          atomicAdd(&split_count, H);
+          if (sbase + n * H > 2 * a.nslot) {
+            atomicOr(&err, 4);  // cannot happen: the chunk length bounds the slot count
+            sbase = -1;
+          } else {
+            for (int h = 0; h < H; ++h) a.split_cnt[sbase + h * n] = 0;  // chunks done per tile
+          }
+        }
+        if (u < total && a.split_slot != nullptr)
+          for (int h = 0; h < H; ++h) a.split_slot[(int64_t)(first + u) * H + h] = sbase < 0 ? -1 : sbase + h * n;
+        __syncthreads();  // the previous batch's items are out
+        bt_bl[tid] = bl; bt_t[tid] = t; bt_c[tid] = c; bt_n[tid] = n; bt_ci[tid] = ci; bt_sb[tid] = sbase;
+        __syncthreads();
+        // items of the batch, one (tile, head) pair per thread at a time
+        const int nt_b = min(SNT, total - u0);
+        for (int pr = tid; pr < nt_b * H; pr += SNT) {
+          const int j = pr / H, h = pr - j * H;
+          const int bj = bt_bl[j], tj = bt_t[j], cj = bt_c[j], nj = bt_n[j], cij = bt_ci[j], sbj = bt_sb[j];
+          const int b = base + bj;
+          const int nb = SMALL ? cnch[bj] : nch_of(b);
+          const int r = rank_of(b) * H + h;
+          const int x = group_xcd(r), g0 = gpre_of(r);
+          Item it;
+          it.b = b; it.tile = tj; it.h = h; it.aux = first + u0 + j;
+          it.q0 = q0_c[bj]; it.lq = lq_c[bj]; it.kv0 = kv0_c[bj]; it.lk = lk_c[bj];
+          for (int k = 0; k < nj; ++k) {
+            it.lo = nj == 1 ? 0 : k * T;
+            it.hi = nj == 1 ? cj : min(cj, (k + 1) * T);
+            it.slot = sbj < 0 ? -1 : sbj + h * nj + k;
+            it.chunk = sbj < 0 ? 0 : k | (nj << 16);
+            const int w = qmode ? nb - 1 - (cij + k) : cij + k;
+            const int pos = position(x, g0 + w);
+            if (pos >= 0 && pos < a.max_items) items[pos] = it;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid == 0) carry = first + total;
+      __syncthreads();
+    }
   }
   if (tid == 0) {
     // Only the first list writes the error word (both lists see the same offsets); a list that
@@ -487,6 +514,75 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedLists lists) {
   }
 }
 
+// Items of deferred lists: one thread per canonical tile, writing the tile's items for every
+// head where the list kernel would have put them (same item words, same positions). Workgroups
+// [first[i], first[i + 1]) serve list i; a list that split tiles, or failed, was written (or
+// left empty) by the list kernel, and its workgroups return.
+constexpr int INT_ = 256;  // threads (tiles) per workgroup
+struct ItemsGrid {
+  int first[4];
+};
+
+__global__ __launch_bounds__(INT_) void sched_items_kernel(SchedLists lists, ItemsGrid grid) {
+  int li = 0;
+  while (li < 2 && (int)blockIdx.x >= grid.first[li + 1]) ++li;
+  const SchedArgs& a = lists.l[li];
+  const int part = (int)blockIdx.x - grid.first[li];
+  __shared__ int tend[SNT];  // inclusive tile end of each sample
+  __shared__ int xtot[XCDS], tgt[XCDS], spre[XCDS], dpre[XCDS + 1];
+  __shared__ int go;
+  const int tid = threadIdx.x;
+  const int B = a.B, H = a.H;
+  if (tid == 0) {
+    const WsHeader* hdr = (const WsHeader*)a.ws_header;
+    const int n = a.list == 0 ? hdr->n_items : hdr->n_items2;
+    const int chunk = a.list == 0 ? hdr->chunk : hdr->chunk2;
+    const int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
+    for (int x = 0; x < XCDS; ++x) xtot[x] = die[x];
+    die_tables(xtot, tgt, spre, dpre);
+    go = n > 0 && chunk == 0 && (int64_t)part * INT_ < (int64_t)n;
+  }
+  for (int i = tid; i < B; i += INT_) tend[i] = a.scratch_at[i];
+  __syncthreads();
+  if (!go) return;
+  const int u = part * INT_ + tid;
+  if (u >= tend[B - 1]) return;
+  int b = 0, hi = B - 1;  // first sample whose tiles end after u
+  while (b < hi) {
+    const int mid = (b + hi) >> 1;
+    if (tend[mid] > u) hi = mid; else b = mid + 1;
+  }
+  const int t = u - (b > 0 ? tend[b - 1] : 0);
+  const int q0 = a.q_off[b], q1 = a.q_off[b + 1], k0 = a.kv_off[b], k1 = a.kv_off[b + 1];
+  const int nb = a.scratch_nch[b], rank = a.scratch_rank[b], max_items = a.max_items;
+  const int tis = __builtin_ctz(a.tile_item), tls = __builtin_ctz(a.tile_loop);
+  const bool qmode = a.mode == SCHED_QTILES;
+  Item it;
+  it.b = b; it.tile = t; it.aux = u;
+  it.q0 = q0; it.lq = q1 - q0; it.kv0 = k0; it.lk = k1 - k0;
+  it.lo = 0;
+  it.hi = item_cost(a.mode, a.causal, a.win, it.lq, it.lk, t, tis, tls);
+  it.slot = -1; it.chunk = 0;
+  const int w = qmode ? nb - 1 - t : t;  // costliest tile first within the group
+  Item* items = (Item*)a.items;
+  const int32_t* gpre = a.scratch_gpre;
+  for (int h0 = 0; h0 < H; h0 += 8) {
+    int g0[8];  // the heads' group positions, loaded together before any item is stored
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g0[j] = h0 + j < H ? gpre[rank * H + h0 + j] : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int h = h0 + j;
+      if (h < H) {
+        const int r = rank * H + h;
+        const int pos = list_position(xtot, tgt, spre, dpre, group_xcd(r), g0[j] + w);
+        it.h = h;
+        if (pos >= 0 && pos < max_items) items[pos] = it;
+      }
+    }
+  }
+}
+
 int persistent_grid(int cap, int per_cu) {
   static std::atomic<int> cus[64];  // compute units per device, looked up once
   int dev = 0, c = 0;
@@ -502,16 +598,32 @@ int persistent_grid(int cap, int per_cu) {
 bool sched_small(const SchedArgs& a) { return a.B <= SNT && (int64_t)a.B * a.H <= GCAP; }
 
 // One workgroup per list (lists share the batch, so they all fit the LDS tables or none does).
+// A list of at least DEFER_ITEMS possible items has its items written by sched_items_kernel
+// (when no tile splits): one workgroup writing them all took 20-35 us on batches of a few
+// hundred samples, mostly spent placing items one by one.
+constexpr int64_t DEFER_ITEMS = 16384;
+
 static hipError_t launch_lists(int n, const SchedArgs& a, const SchedArgs& b, const SchedArgs& c, hipStream_t s) {
   prof_before(PROF_SCHED, s);
   SchedLists lists;
   lists.l[0] = a;
   lists.l[1] = b;
   lists.l[2] = c;
-  if (sched_small(a))
+  const bool small = sched_small(a);
+  ItemsGrid grid;
+  int wgs = 0;
+  for (int i = 0; i < 3; ++i) {
+    SchedArgs& l = lists.l[i];
+    grid.first[i] = wgs;
+    l.defer = i < n && small && l.H > 0 && (int64_t)l.max_items >= DEFER_ITEMS && l.scratch_at != nullptr;
+    if (l.defer) wgs += (int)((l.max_items / l.H + INT_ - 1) / INT_);  // max_items >= H * tiles
+  }
+  grid.first[3] = wgs;
+  if (small)
     hipLaunchKernelGGL(sched_kernel<true>, dim3(n), dim3(SNT), 0, s, lists);
   else
     hipLaunchKernelGGL(sched_kernel<false>, dim3(n), dim3(SNT), 0, s, lists);
+  if (wgs > 0) hipLaunchKernelGGL(sched_items_kernel, dim3(wgs), dim3(INT_), 0, s, lists, grid);
   prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }

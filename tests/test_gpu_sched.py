@@ -293,3 +293,16 @@ def test_batch_larger_than_one_scheduler_chunk():
     p = inputs.make_problem("sched-large-batch", seed=87, H=7, D=128, lq=lq, lk=lq, dtype="bf16",
                             act="softmax", causal=True, bias_buckets=32)
     run_and_check(p)
+
+
+def test_long_list_with_a_split_tile():
+    """A key-tile list long enough that a second launch would write its items, with key tiles
+    costlier than the chunk length: the list's own workgroup must write it (split chunks), and
+    the item launch must leave it alone. 599 samples of 1 query and 900 keys (8 key tiles of
+    cost 1) and one of 60,000 queries and 900 keys (8 key tiles visiting 938 query tiles each);
+    every query tile visits 15 key tiles, so the query lists stay balanced by item count."""
+    lq = np.array([60000] + [1] * 599)
+    lk = np.array([900] * 600)
+    p = inputs.make_problem("sched-long-split", seed=88, H=4, D=128, lq=lq, lk=lk, dtype="bf16",
+                            act="silu", causal=False)
+    run_and_check(p)
