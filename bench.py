@@ -18,7 +18,8 @@ step time. Prints one JSON line on stdout:
     that evicts the 256 MB last-level cache and the L2s; medians (and minima) over the reps;
   - warm_per_call: the same per-call medians without the eviction;
   - roofline: the dominant kernel's algorithmic flops (or bytes) per launch over its average
-    launch time, from HIP events the library records on the launch stream over the timed steps;
+    launch time, from HIP events the library records on the launch stream over the timed steps
+    (around that kernel only; the other kernels' averages come from a short probe before them);
   - workloads: the same figures for the cross-attention, PMA, MX-fp8 and block-aligned rotary
     workloads;
   - cpu_baseline: the fp64 oracle on the host cores, on a bounded sample of the same workload.
@@ -181,22 +182,38 @@ def per_call_medians(torch, calls, reps, flush=None):
     return {k: (float(np.median(v)), float(np.min(v))) for k, v in times.items()}
 
 
+PROBE_STEPS = 20  # untimed steps with events on every kernel, before the timed ones
+
+
 def timed_steps(torch, gdpa, step, steps, kernels):
-    """Host-clock time of `steps` back-to-back steps between two synchronisations, and every
-    selected kernel's average launch time from the library's HIP events over the same region."""
-    torch.cuda.synchronize()
-    gdpa.profile_start(kernels)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gdpa.profile_stop()
-    kern_ms = {}
-    for kern in kernels:
-        n, ms = gdpa.profile_read(kern)
-        kern_ms[kern] = ms / max(n, 1)
-    return (t1 - t0) * 1e3 / steps, kern_ms
+    """Host-clock time of `steps` back-to-back steps between two synchronisations, the dominant
+    kernel's average launch time from the library's HIP events over the same region, and every
+    kernel's average from a probe of PROBE_STEPS steps just before it. The probe, with events
+    around every selected kernel, names the dominant (longest) kernel; the timed steps then
+    record events around that kernel only, since each pair of events lengthens a step by a few
+    microseconds (about 14 us per step with three pairs on the JFA workload, 6 with one).
+    Returns (ms per step, {kernel: ms per launch}, dominant kernel)."""
+    def profiled(ks, n):
+        torch.cuda.synchronize()
+        gdpa.profile_start(ks)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gdpa.profile_stop()
+        out = {}
+        for kern in ks:
+            cnt, ms = gdpa.profile_read(kern)
+            out[kern] = ms / max(cnt, 1)
+        return (t1 - t0) * 1e3 / n, out
+
+    kern_ms = profiled(kernels, PROBE_STEPS)[1]
+    print("[bench] probe", {k: round(v, 4) for k, v in kern_ms.items()}, file=sys.stderr, flush=True)
+    dom = max(kern_ms, key=kern_ms.get)
+    ms_step, timed = profiled((dom,), steps)
+    kern_ms[dom] = timed[dom]
+    return ms_step, kern_ms, dom
 
 
 def run_bf16(args, config, torch, gdpa, inputs, workload, dev, flush, window=0, steps=None,
@@ -247,7 +264,7 @@ def run_bf16(args, config, torch, gdpa, inputs, workload, dev, flush, window=0, 
 
     for _ in range(args.warmup):
         step()
-    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("fwd", "dq", "dkdv"))
+    ms_step, kern_ms, dom = timed_steps(torch, gdpa, step, steps, ("fwd", "dq", "dkdv"))
     cold = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps, flush)
     warm = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps)
     for t in (O, *grads[:3]):
@@ -267,7 +284,6 @@ def run_bf16(args, config, torch, gdpa, inputs, workload, dev, flush, window=0, 
                 "bwd_gbs": round(workload.bwd_bytes(p) / (m["bwd"][0] * 1e-3) / 1e9, 1),
                 "reps": reps}
 
-    dom = max(kern_ms, key=kern_ms.get)
     if config in HBM_BOUND:
         # short keys (cross) or short queries (PMA): the kernels stream the long side once
         achieved = workload.kernel_bytes(p, dom) / (kern_ms[dom] * 1e-3) / 1e9
@@ -327,7 +343,7 @@ def run_mx(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=Non
 
     for _ in range(args.warmup):
         step()
-    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("fwd",))
+    ms_step, kern_ms, _ = timed_steps(torch, gdpa, step, steps, ("fwd",))
     cold = per_call_medians(torch, calls, reps, flush)
     warm = per_call_medians(torch, calls, reps)
     for a in acts:
@@ -401,7 +417,7 @@ def run_block(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=
 
     for _ in range(args.warmup):
         step()
-    ms_step, kern_ms = timed_steps(torch, gdpa, step, steps, ("block_fwd", "block_bwd"))
+    ms_step, kern_ms, dom = timed_steps(torch, gdpa, step, steps, ("block_fwd", "block_bwd"))
     cold = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps, flush)
     warm = per_call_medians(torch, {"fwd": fwd, "bwd": bwd}, reps)
     for t in (O, *grads):
@@ -416,7 +432,6 @@ def run_block(args, torch, gdpa, inputs, workload, dev, flush, steps=None, reps=
                 "fwd_gbs": gbs(fb, m["fwd"][0]), "bwd_gbs": gbs(bb, m["bwd"][0]), "reps": reps}
 
     kgbs = {"block_fwd": gbs(fb, kern_ms["block_fwd"]), "block_bwd": gbs(bb, kern_ms["block_bwd"])}
-    dom = max(kern_ms, key=kern_ms.get)
     res = {"p": p, "ms_step": ms_step, "value": (ff + bf) / (ms_step * 1e-3) / 1e12,
            "cold": split(cold), "warm": split(warm),
            "roofline": {"bound": "hbm", "kernel": dom, "achieved": kgbs[dom], "peak": PEAK_HBM_GBS,
