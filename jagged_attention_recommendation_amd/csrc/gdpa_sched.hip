@@ -518,12 +518,12 @@ __global__ __launch_bounds__(SNT) void sched_kernel(SchedLists lists) {
 // head where the list kernel would have put them (same item words, same positions). Workgroups
 // [first[i], first[i + 1]) serve list i; a list that split tiles, or failed, was written (or
 // left empty) by the list kernel, and its workgroups return.
-constexpr int INT_ = 256;  // threads (tiles) per workgroup
+constexpr int ITEM_NT = 256;  // threads (tiles) per workgroup
 struct ItemsGrid {
   int first[4];
 };
 
-__global__ __launch_bounds__(INT_) void sched_items_kernel(SchedLists lists, ItemsGrid grid) {
+__global__ __launch_bounds__(ITEM_NT) void sched_items_kernel(SchedLists lists, ItemsGrid grid) {
   int li = 0;
   while (li < 2 && (int)blockIdx.x >= grid.first[li + 1]) ++li;
   const SchedArgs& a = lists.l[li];
@@ -540,12 +540,12 @@ __global__ __launch_bounds__(INT_) void sched_items_kernel(SchedLists lists, Ite
     const int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
     for (int x = 0; x < XCDS; ++x) xtot[x] = die[x];
     die_tables(xtot, tgt, spre, dpre);
-    go = n > 0 && chunk == 0 && (int64_t)part * INT_ < (int64_t)n;
+    go = n > 0 && chunk == 0 && (int64_t)part * ITEM_NT < (int64_t)n;
   }
-  for (int i = tid; i < B; i += INT_) tend[i] = a.scratch_at[i];
+  for (int i = tid; i < B; i += ITEM_NT) tend[i] = a.scratch_at[i];
   __syncthreads();
   if (!go) return;
-  const int u = part * INT_ + tid;
+  const int u = part * ITEM_NT + tid;
   if (u >= tend[B - 1]) return;
   int b = 0, hi = B - 1;  // first sample whose tiles end after u
   while (b < hi) {
@@ -616,14 +616,14 @@ static hipError_t launch_lists(int n, const SchedArgs& a, const SchedArgs& b, co
     SchedArgs& l = lists.l[i];
     grid.first[i] = wgs;
     l.defer = i < n && small && l.H > 0 && (int64_t)l.max_items >= DEFER_ITEMS && l.scratch_at != nullptr;
-    if (l.defer) wgs += (int)((l.max_items / l.H + INT_ - 1) / INT_);  // max_items >= H * tiles
+    if (l.defer) wgs += (int)((l.max_items / l.H + ITEM_NT - 1) / ITEM_NT);  // max_items >= H * tiles
   }
   grid.first[3] = wgs;
   if (small)
     hipLaunchKernelGGL(sched_kernel<true>, dim3(n), dim3(SNT), 0, s, lists);
   else
     hipLaunchKernelGGL(sched_kernel<false>, dim3(n), dim3(SNT), 0, s, lists);
-  if (wgs > 0) hipLaunchKernelGGL(sched_items_kernel, dim3(wgs), dim3(INT_), 0, s, lists, grid);
+  if (wgs > 0) hipLaunchKernelGGL(sched_items_kernel, dim3(wgs), dim3(ITEM_NT), 0, s, lists, grid);
   prof_after(PROF_SCHED, s);
   return hipGetLastError();
 }
