@@ -540,9 +540,10 @@ __global__ __launch_bounds__(ITEM_NT) void sched_items_kernel(SchedLists lists, 
     const int* die = a.list == 0 ? hdr->die_items : hdr->die_items2;
     for (int x = 0; x < XCDS; ++x) xtot[x] = die[x];
     die_tables(xtot, tgt, spre, dpre);
-    go = n > 0 && chunk == 0 && (int64_t)part * ITEM_NT < (int64_t)n;
+    // (the launch defers only batches whose samples fit tend)
+    go = n > 0 && chunk == 0 && B <= SNT && (int64_t)part * ITEM_NT < (int64_t)n;
   }
-  for (int i = tid; i < B; i += ITEM_NT) tend[i] = a.scratch_at[i];
+  for (int i = tid; i < min(B, SNT); i += ITEM_NT) tend[i] = a.scratch_at[i];
   __syncthreads();
   if (!go) return;
   const int u = part * ITEM_NT + tid;
