@@ -199,3 +199,17 @@ def test_f32_window(D, act):
                             dtype="f32", act=act, causal=True, bias_buckets=24)
     for W in (1, 17, 64, 150):
         check_f32(p, W)
+
+
+@pytest.mark.timeout(300)
+def test_window_long_lists():
+    """1,000 samples of 350-550 tokens, 4 heads, a 64-entry bias table and a 100-key window: the
+    lists pass the size (16,384 possible items) above which a second scheduler launch writes the
+    items; that launch must also mark every dQ tile unsplit for the bias-gradient reduction.
+    Every output and gradient is checked against the oracle."""
+    rng = np.random.default_rng(131)
+    lq = rng.integers(350, 551, size=1000)
+    p = inputs.make_problem("win-long-lists", seed=131, H=4, D=128, lq=lq, lk=lq, dtype="bf16",
+                            act="softmax", causal=True, bias_buckets=64)
+    hf, hb = check(p, 100)
+    assert hf["items"] > 15000 and hb["items"] > 15000 and hb["split"] == 0, (hf, hb)
